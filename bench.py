@@ -1,0 +1,188 @@
+"""Throughput of the mapper apply step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+A step is one kvmap_apply over the whole cache: de-rotation of the selected source key
+layers, then the map GEMM for K and V of every target layer with bias and target RoPE
+fused.  Inputs are synthetic, seeded, and resident in HBM before timing starts.  Prints
+one JSON line (rank 0).
+
+value      mapped tokens/s: T tokens of the cache (K and V, all target layers) per step
+roofline   the map GEMM launch: algorithmic FLOP (2*T*F*N per target layer, K and V) over its
+           average duration from HIP events recorded on the apply's stream, against the
+           bf16 dense MFMA peak; traffic from the committed rocprofv3 counter summary if it
+           was taken on the current kernel source
+cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on the host cores
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mapped tokens/s (K+V, all target layers) at 14B→32B shape; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0
+GEMM_SRC = os.path.join(ROOT, "cross_model_kv_amd", "csrc", "gemm_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "map_bf16_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_entry(cfg_name):
+    """HBM bytes per launch of the map GEMM from the committed counter summary, if that summary
+    was taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != source_sha(GEMM_SRC) or t.get("workload") != cfg_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s=12.0):
+    """Time the fp64 oracle on whole target layers over the first `rows` tokens until the budget
+    is spent; scale to mapped tokens/s of the full workload (all target layers)."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    rows = np.arange(min(cfg.T, 2048))
+    rows_t = torch.as_tensor(rows, device="cuda:0")
+    f = lambda t: t.float().cpu().double().numpy()
+    sel = inp["layer_sel"]
+    done_layers, spent = 0, 0.0
+    for t in range(cfg.L_tgt):
+        need = [int(s) for s in sel[t]]
+        sk = {s: f(inp["src_k"][s][:, rows_t, :]) for s in need}
+        sv = {s: f(inp["src_v"][s][:, rows_t, :]) for s in need}
+        Wk, Wv = {t: f(inp["W_k"][t])}, {t: f(inp["W_v"][t])}
+        bk, bv = {t: f(inp["b_k"][t])}, {t: f(inp["b_v"][t])}
+        t0 = time.perf_counter()
+        oracle.apply_rows(sk, sv, sel, Wk, bk, Wv, bv, cfg.theta_src, cfg.theta_tgt, cfg.pos0 + rows,
+                          targets=[t])
+        spent += time.perf_counter() - t0
+        done_layers += 1
+        if spent >= budget_s:
+            break
+    # tokens of the full cache (all target layers) per second
+    per_token_all_layers = spent / (len(rows) * done_layers) * cfg.L_tgt
+    return {"value": 1.0 / per_token_all_layers, "unit": "tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{done_layers} of {cfg.L_tgt} target layers (K and V) x {len(rows)} tokens, fp64 numpy "
+                      f"oracle, {spent:.1f} s; scaled to all target layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the mapper needs no exchange between GPUs and this build "
+              "runs on one MI355X only (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from cross_model_kv_amd import kvmap as K
+    from synth.device import apply_inputs
+    from synth.workloads import APPLY_CONFIGS
+
+    cfg = APPLY_CONFIGS[args.config]
+    log(f"generating {cfg.name}: L {cfg.L_src}->{cfg.L_tgt} H={cfg.H} d={cfg.d} k={cfg.k} T={cfg.T}")
+    t0 = time.time()
+    inp = apply_inputs(cfg, "cuda:0", progress=lambda a, b: log(f"  inputs {a}/{b}") if a % 256 == 0 else None)
+    log(f"inputs resident in {time.time() - t0:.1f} s")
+    ctx = K.Context(0)
+    ctx.reserve(cfg.L_src, cfg.L_tgt, cfg.H, cfg.d, cfg.k, cfg.T, K.BF16 if cfg.dtype == "bf16" else K.F32)
+    out_k = torch.empty((cfg.L_tgt, cfg.H, cfg.T, cfg.d), dtype=inp["src_k"].dtype, device="cuda:0")
+    out_v = torch.empty_like(out_k)
+    stream = torch.cuda.current_stream()
+
+    def step(flags=K.FLAG_TIMING):
+        ctx.apply(inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"],
+                  cfg.theta_src, cfg.theta_tgt, pos0_src=cfg.pos0, out_k=out_k, out_v=out_v, stream=stream,
+                  flags=flags)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup}: kernels {ctx.last_timings()} ms")
+
+    gemm_ms, derope_ms = [], []
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step()
+        _, dr, gm = ctx.last_timings()  # waits for this step's last event
+        derope_ms.append(dr)
+        gemm_ms.append(gm)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, gemm {sum(gemm_ms) / len(gemm_ms):.3f} ms, "
+        f"derope {sum(derope_ms) / len(derope_ms):.3f} ms")
+
+    gemm_avg_s = sum(gemm_ms) / len(gemm_ms) / 1e3
+    derope_avg_s = sum(derope_ms) / len(derope_ms) / 1e3
+    achieved = cfg.flops / gemm_avg_s / 1e12
+    n_used = len({int(s) for row in inp["layer_sel"] for s in row})
+    derope_bytes = 2 * n_used * cfg.H * cfg.T * cfg.d * (2 if cfg.dtype == "bf16" else 4)
+    traffic = traffic_entry(cfg.name)
+    result = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian caches with LogNormal channel scales, random-init maps)",
+        "config": {"workload": f"{cfg.name} apply", "L_src": cfg.L_src, "L_tgt": cfg.L_tgt, "H_kv": cfg.H,
+                   "head_dim": cfg.d, "k": cfg.k, "T": cfg.T, "F": cfg.F, "N": cfg.N,
+                   "theta_src": cfg.theta_src, "theta_tgt": cfg.theta_tgt},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "map_bf16_kernel", "kernel_ms": gemm_avg_s * 1e3},
+        "derope": {"ms": derope_avg_s * 1e3, "bytes": derope_bytes,
+                   "GBps": derope_bytes / derope_avg_s / 1e9, "frac_hbm": derope_bytes / derope_avg_s / 1e9 / PEAK_HBM_GBPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle on a bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,558 @@
+// C-ABI of libkvmap: validation, the context (RoPE-table cache, workspace, scratch) and the
+// launch sequence of each call.  Declarations and the contract of every entry point are in
+// include/kvmap.h.
+
+#include "../../include/kvmap.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace kvmap;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int ok() {
+    g_err.clear();
+    return KVMAP_OK;
+}
+
+#define KVMAP_HIP(call)                                                                     \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail(e_ == hipErrorOutOfMemory ? KVMAP_ERR_OUT_OF_MEMORY : KVMAP_ERR_DEVICE, \
+                        "%s: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, __LINE__); \
+    } while (0)
+
+// Makes the context's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool okay = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        okay = (hipSetDevice(dev) == hipSuccess);
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+constexpr int kMaxRopeTables = 8;
+constexpr int kGramMaxSplits = 64;
+
+struct RopeEntry {
+    double theta = 0;
+    int64_t pos0 = 0;
+    int d = 0;
+    int64_t T_cap = 0;
+    float2* tab = nullptr;
+    uint64_t last_use = 0;
+};
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = (const char*)a;
+    const char* pb = (const char*)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+struct kvmap_ctx {
+    int device = 0;
+    std::vector<RopeEntry> ropes;
+    uint64_t clock = 0;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    int32_t* d_sel = nullptr;     // [L_tgt*k] selection + [L_src] used-layer list
+    size_t sel_cap = 0;           // int32 entries
+    int32_t* h_sel = nullptr;     // pinned staging
+    std::vector<int32_t> sel_cache;
+    unsigned int* d_count = nullptr;
+    float* gram = nullptr;
+    size_t gram_floats = 0;
+    hipEvent_t ev[4] = {};
+    bool timed = false;
+    float last_ms[3] = {0, 0, 0};
+};
+
+// ---------------------------------------------------------------------------------------
+// status / version
+// ---------------------------------------------------------------------------------------
+
+extern "C" const char* kvmap_status_string(int status) {
+    switch (status) {
+        case KVMAP_OK: return "KVMAP_OK";
+        case KVMAP_ERR_INVALID_ARGUMENT: return "KVMAP_ERR_INVALID_ARGUMENT";
+        case KVMAP_ERR_SHAPE: return "KVMAP_ERR_SHAPE";
+        case KVMAP_ERR_UNSUPPORTED: return "KVMAP_ERR_UNSUPPORTED";
+        case KVMAP_ERR_NONFINITE: return "KVMAP_ERR_NONFINITE";
+        case KVMAP_ERR_NOT_SPD: return "KVMAP_ERR_NOT_SPD";
+        case KVMAP_ERR_DEVICE: return "KVMAP_ERR_DEVICE";
+        case KVMAP_ERR_OUT_OF_MEMORY: return "KVMAP_ERR_OUT_OF_MEMORY";
+        default: return "KVMAP_ERR_UNKNOWN";
+    }
+}
+
+extern "C" const char* kvmap_last_error(void) { return g_err.c_str(); }
+
+extern "C" int kvmap_version(void) { return KVMAP_VERSION; }
+
+// ---------------------------------------------------------------------------------------
+// context
+// ---------------------------------------------------------------------------------------
+
+extern "C" int kvmap_create(kvmap_ctx** out, int device) {
+    if (!out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_create: out is NULL");
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0)
+        return fail(KVMAP_ERR_DEVICE, "kvmap_create: no HIP device visible");
+    if (device < 0 || device >= n)
+        return fail(KVMAP_ERR_DEVICE, "kvmap_create: device %d out of range [0, %d)", device, n);
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+        return fail(KVMAP_ERR_DEVICE, "kvmap_create: cannot query device %d", device);
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(KVMAP_ERR_DEVICE, "kvmap_create: device %d is %s, the kernels are built for gfx950",
+                    device, prop.gcnArchName);
+    DeviceGuard g(device);
+    if (!g.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipSetDevice(%d) failed", device);
+    kvmap_ctx* c = new kvmap_ctx();
+    c->device = device;
+    for (auto& e : c->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            kvmap_destroy(c);
+            return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipEventCreate failed");
+        }
+    }
+    if (hipMalloc((void**)&c->d_count, sizeof(unsigned int)) != hipSuccess) {
+        kvmap_destroy(c);
+        return fail(KVMAP_ERR_OUT_OF_MEMORY, "kvmap_create: hipMalloc failed");
+    }
+    *out = c;
+    return ok();
+}
+
+extern "C" int kvmap_destroy(kvmap_ctx* c) {
+    if (!c) return ok();
+    DeviceGuard g(c->device);
+    (void)hipDeviceSynchronize();
+    for (auto& r : c->ropes) (void)hipFree(r.tab);
+    (void)hipFree(c->ws);
+    (void)hipFree(c->d_sel);
+    (void)hipHostFree(c->h_sel);
+    (void)hipFree(c->d_count);
+    (void)hipFree(c->gram);
+    for (auto& e : c->ev)
+        if (e) (void)hipEventDestroy(e);
+    delete c;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------------------
+
+static int validate_rope(const kvmap_rope* r, const char* which, int64_t T) {
+    if (!r) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE descriptor is NULL", which);
+    if (r->style != KVMAP_ROPE_HALF_SPLIT)
+        return fail(KVMAP_ERR_UNSUPPORTED, "%s RoPE style %d refused: only the half-split form is mapped",
+                    which, (int)r->style);
+    if (!(r->theta > 0.0) || !std::isfinite(r->theta))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE theta must be finite and > 0", which);
+    if (r->pos0 < 0) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE pos0 must be >= 0", which);
+    if (r->pos0 > (int64_t(1) << 31) - T)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE pos0 + T exceeds 2^31", which);
+    return KVMAP_OK;
+}
+
+extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_sel,
+                                    const kvmap_rope* rs, const kvmap_rope* rt) {
+    if (!d) return fail(KVMAP_ERR_INVALID_ARGUMENT, "dims is NULL");
+    if (!layer_sel) return fail(KVMAP_ERR_INVALID_ARGUMENT, "layer_sel is NULL");
+    if (d->dtype != KVMAP_DTYPE_BF16 && d->dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "dtype %d unknown", (int)d->dtype);
+    if (d->L_src < 1 || d->L_tgt < 1 || d->H_kv < 1 || d->k < 1)
+        return fail(KVMAP_ERR_SHAPE, "L_src, L_tgt, H_kv and k must be >= 1");
+    if (d->T < 1) return fail(KVMAP_ERR_SHAPE, "T must be >= 1");
+    if (d->head_dim < 2 || (d->head_dim & 1))
+        return fail(KVMAP_ERR_SHAPE, "head_dim %d must be even", (int)d->head_dim);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(KVMAP_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", (int)d->head_dim);
+    if (d->k > d->L_src) return fail(KVMAP_ERR_SHAPE, "k=%d exceeds L_src=%d", (int)d->k, (int)d->L_src);
+    const int64_t N = (int64_t)d->H_kv * d->head_dim;
+    const int64_t F = N * d->k;
+    if (N * F >= (int64_t(1) << 31))
+        return fail(KVMAP_ERR_SHAPE, "one target layer's map (N*F = %lld) must stay below 2^31 entries",
+                    (long long)(N * F));
+    if (d->T * d->head_dim >= (int64_t(1) << 31))
+        return fail(KVMAP_ERR_SHAPE, "T*head_dim must stay below 2^31");
+    if ((int64_t)d->L_tgt * d->k >= (int64_t(1) << 24))
+        return fail(KVMAP_ERR_SHAPE, "L_tgt*k too large");
+    int st = validate_rope(rs, "source", d->T);
+    if (st) return st;
+    st = validate_rope(rt, "target", d->T);
+    if (st) return st;
+    std::vector<char> seen(d->L_src, 0);
+    for (int t = 0; t < d->L_tgt; ++t) {
+        for (int j = 0; j < d->k; ++j) {
+            const int32_t s = layer_sel[(size_t)t * d->k + j];
+            if (s < 0 || s >= d->L_src)
+                return fail(KVMAP_ERR_SHAPE, "layer_sel[%d][%d] = %d outside [0, %d)", t, j, (int)s, (int)d->L_src);
+            if (seen[s])
+                return fail(KVMAP_ERR_SHAPE, "layer_sel[%d] selects source layer %d twice", t, (int)s);
+            seen[s] = 1;
+        }
+        for (int j = 0; j < d->k; ++j) seen[layer_sel[(size_t)t * d->k + j]] = 0;
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------
+// apply
+// ---------------------------------------------------------------------------------------
+
+static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, hipStream_t s,
+                          float2** out, bool* built) {
+    *built = false;
+    for (auto& e : c->ropes) {
+        if (e.theta == r->theta && e.pos0 == r->pos0 && e.d == d && e.T_cap >= T) {
+            e.last_use = ++c->clock;
+            *out = e.tab;
+            return KVMAP_OK;
+        }
+    }
+    if ((int)c->ropes.size() >= kMaxRopeTables) {
+        // Evict the least recently used table once no queued work can still read it.
+        KVMAP_HIP(hipDeviceSynchronize());
+        auto it = std::min_element(c->ropes.begin(), c->ropes.end(),
+                                   [](const RopeEntry& a, const RopeEntry& b) { return a.last_use < b.last_use; });
+        (void)hipFree(it->tab);
+        c->ropes.erase(it);
+    }
+    RopeEntry e;
+    e.theta = r->theta;
+    e.pos0 = r->pos0;
+    e.d = d;
+    e.T_cap = T;
+    KVMAP_HIP(hipMalloc((void**)&e.tab, (size_t)T * (d / 2) * sizeof(float2)));
+    hipError_t err = launch_rope_table(e.tab, T, d, r->theta, r->pos0, s);
+    if (err != hipSuccess) {
+        (void)hipFree(e.tab);
+        return fail(KVMAP_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(err));
+    }
+    e.last_use = ++c->clock;
+    c->ropes.push_back(e);
+    *out = e.tab;
+    *built = true;
+    return KVMAP_OK;
+}
+
+// Upload layer_sel and the ascending list of source layers it uses; skipped when the
+// context already holds the same selection.
+static int upload_selection(kvmap_ctx* c, const kvmap_dims* d, const int32_t* layer_sel,
+                            hipStream_t s, int* n_used) {
+    const size_t nsel = (size_t)d->L_tgt * d->k;
+    std::vector<int32_t> want(layer_sel, layer_sel + nsel);
+    std::vector<char> used(d->L_src, 0);
+    for (size_t i = 0; i < nsel; ++i) used[want[i]] = 1;
+    for (int l = 0; l < d->L_src; ++l)
+        if (used[l]) want.push_back(l);
+    *n_used = (int)(want.size() - nsel);
+    want.push_back(d->L_src);  // sentinel: distinguishes equal selections over different L_src
+    if (want == c->sel_cache) return KVMAP_OK;
+    if (want.size() > c->sel_cap) {
+        KVMAP_HIP(hipStreamSynchronize(s));
+        (void)hipFree(c->d_sel);
+        (void)hipHostFree(c->h_sel);
+        c->d_sel = nullptr;
+        c->h_sel = nullptr;
+        c->sel_cap = 0;
+        c->sel_cache.clear();
+        KVMAP_HIP(hipMalloc((void**)&c->d_sel, want.size() * sizeof(int32_t)));
+        KVMAP_HIP(hipHostMalloc((void**)&c->h_sel, want.size() * sizeof(int32_t), hipHostMallocDefault));
+        c->sel_cap = want.size();
+    } else {
+        // The staging buffer may still feed an earlier queued copy.
+        KVMAP_HIP(hipStreamSynchronize(s));
+    }
+    memcpy(c->h_sel, want.data(), want.size() * sizeof(int32_t));
+    KVMAP_HIP(hipMemcpyAsync(c->d_sel, c->h_sel, want.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    c->sel_cache = want;
+    return KVMAP_OK;
+}
+
+static int ensure_workspace(kvmap_ctx* c, size_t bytes) {
+    if (bytes <= c->ws_bytes) return KVMAP_OK;
+    KVMAP_HIP(hipDeviceSynchronize());
+    (void)hipFree(c->ws);
+    c->ws = nullptr;
+    c->ws_bytes = 0;
+    KVMAP_HIP(hipMalloc(&c->ws, bytes));
+    c->ws_bytes = bytes;
+    return KVMAP_OK;
+}
+
+static size_t workspace_bytes(const kvmap_dims* d) {
+    const size_t es = d->dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    return (size_t)d->L_src * d->H_kv * (size_t)d->T * d->head_dim * es;
+}
+
+extern "C" int kvmap_reserve(kvmap_ctx* c, const kvmap_dims* d) {
+    if (!c || !d) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_reserve: NULL argument");
+    DeviceGuard g(c->device);
+    int st = ensure_workspace(c, workspace_bytes(d));
+    if (st) return st;
+    return ok();
+}
+
+extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k, const void* src_v,
+                           const int32_t* layer_sel, const void* W_k, const void* b_k, const void* W_v,
+                           const void* b_v, const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
+                           void* tgt_k, void* tgt_v, void* stream, uint32_t flags) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: ctx is NULL");
+    int st = kvmap_validate_apply(d, layer_sel, rope_src, rope_tgt);
+    if (st) return st;
+    if (!src_k || !src_v || !W_k || !b_k || !W_v || !b_v || !tgt_k || !tgt_v)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: NULL device pointer");
+    if (flags & ~(KVMAP_FLAG_CHECK_FINITE | KVMAP_FLAG_TIMING))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: unknown flag bits 0x%x", flags);
+    const void* ptrs[8] = {src_k, src_v, W_k, b_k, W_v, b_v, tgt_k, tgt_v};
+    for (const void* p : ptrs)
+        if (((uintptr_t)p) & 15) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: pointers must be 16-byte aligned");
+
+    const ApplyGeom g{d->L_src, d->L_tgt, d->H_kv, d->head_dim, d->k, d->T};
+    const size_t es = d->dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    const size_t src_bytes = (size_t)g.L_src * g.H * g.T * g.d * es;
+    const size_t tgt_bytes = (size_t)g.L_tgt * g.H * g.T * g.d * es;
+    const size_t w_bytes = (size_t)g.L_tgt * g.N() * g.F() * es;
+    const size_t b_bytes = (size_t)g.L_tgt * g.N() * es;
+    const void* ins[6] = {src_k, src_v, W_k, b_k, W_v, b_v};
+    const size_t insz[6] = {src_bytes, src_bytes, w_bytes, b_bytes, w_bytes, b_bytes};
+    for (int i = 0; i < 6; ++i)
+        if (ranges_overlap(ins[i], insz[i], tgt_k, tgt_bytes) || ranges_overlap(ins[i], insz[i], tgt_v, tgt_bytes))
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: an input overlaps an output");
+    if (ranges_overlap(tgt_k, tgt_bytes, tgt_v, tgt_bytes))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: tgt_k and tgt_v overlap");
+
+    DeviceGuard guard(c->device);
+    if (!guard.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_apply: hipSetDevice(%d) failed", c->device);
+    hipStream_t s = (hipStream_t)stream;
+    const bool timing = (flags & KVMAP_FLAG_TIMING) != 0;
+    c->timed = false;
+
+    if (timing) KVMAP_HIP(hipEventRecord(c->ev[0], s));
+    float2 *tab_src = nullptr, *tab_tgt = nullptr;
+    bool b1 = false, b2 = false;
+    st = get_rope_table(c, rope_src, g.d, g.T, s, &tab_src, &b1);
+    if (st) return st;
+    st = get_rope_table(c, rope_tgt, g.d, g.T, s, &tab_tgt, &b2);
+    if (st) return st;
+    int n_used = 0;
+    st = upload_selection(c, d, layer_sel, s, &n_used);
+    if (st) return st;
+    st = ensure_workspace(c, workspace_bytes(d));
+    if (st) return st;
+
+    const Elem e = d->dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
+    if (timing) KVMAP_HIP(hipEventRecord(c->ev[1], s));
+    KVMAP_HIP(launch_derope(e, src_k, c->ws, c->d_sel + (size_t)g.L_tgt * g.k, n_used, g, tab_src, s));
+    if (timing) KVMAP_HIP(hipEventRecord(c->ev[2], s));
+    MapArgs a{c->ws, src_v, c->d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
+    if (e == Elem::BF16)
+        KVMAP_HIP(launch_map_bf16(a, g, s));
+    else
+        KVMAP_HIP(launch_map_f32(a, g, s));
+    if (timing) {
+        KVMAP_HIP(hipEventRecord(c->ev[3], s));
+        c->timed = true;
+        c->last_ms[0] = (b1 || b2) ? -1.f : 0.f;  // resolved in kvmap_last_timings
+    }
+
+    if (flags & KVMAP_FLAG_CHECK_FINITE) {
+        const int64_t n = (int64_t)g.L_tgt * g.H * g.T * g.d;
+        KVMAP_HIP(hipMemsetAsync(c->d_count, 0, sizeof(unsigned int), s));
+        KVMAP_HIP(launch_count_nonfinite(e, tgt_k, n, c->d_count, s));
+        KVMAP_HIP(launch_count_nonfinite(e, tgt_v, n, c->d_count, s));
+        unsigned int h = 0;
+        KVMAP_HIP(hipMemcpyAsync(&h, c->d_count, sizeof h, hipMemcpyDeviceToHost, s));
+        KVMAP_HIP(hipStreamSynchronize(s));
+        if (h) return fail(KVMAP_ERR_NONFINITE, "kvmap_apply: %u non-finite values in the mapped cache", h);
+    }
+    return ok();
+}
+
+extern "C" int kvmap_last_timings(kvmap_ctx* c, float* ms, int n_ms) {
+    if (!c || !ms || n_ms < 3) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: bad arguments");
+    if (!c->timed) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: no timed apply recorded");
+    DeviceGuard g(c->device);
+    KVMAP_HIP(hipEventSynchronize(c->ev[3]));
+    float t01 = 0, t12 = 0, t23 = 0;
+    KVMAP_HIP(hipEventElapsedTime(&t01, c->ev[0], c->ev[1]));
+    KVMAP_HIP(hipEventElapsedTime(&t12, c->ev[1], c->ev[2]));
+    KVMAP_HIP(hipEventElapsedTime(&t23, c->ev[2], c->ev[3]));
+    ms[0] = c->last_ms[0] < 0 ? t01 : 0.f;
+    ms[1] = t12;
+    ms[2] = t23;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------
+// fit-side statistics
+// ---------------------------------------------------------------------------------------
+
+static int validate_state(const kvmap_gram_state* st, const char* which) {
+    if (!st) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state is NULL", which);
+    if (st->p < 4 || st->q < 4 || (st->p & 3) || (st->q & 3) || st->p > 65536 || st->q > 65536)
+        return fail(KVMAP_ERR_SHAPE, "%s state: p=%d, q=%d must be multiples of 4 in [4, 65536]", which,
+                    (int)st->p, (int)st->q);
+    if (st->n < 0) return fail(KVMAP_ERR_SHAPE, "%s state: n < 0", which);
+    if (!st->mean_x || !st->mean_y || !st->M_xx || !st->M_xy)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state: NULL array", which);
+    const void* arr[4] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy};
+    for (const void* a : arr)
+        if (((uintptr_t)a) & 15) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state: arrays must be 16-byte aligned", which);
+    return KVMAP_OK;
+}
+
+static int ensure_gram_scratch(kvmap_ctx* c, int p, int q) {
+    const size_t need = gram_scratch_floats(p, q, kGramMaxSplits);
+    if (need <= c->gram_floats) return KVMAP_OK;
+    KVMAP_HIP(hipDeviceSynchronize());
+    (void)hipFree(c->gram);
+    c->gram = nullptr;
+    c->gram_floats = 0;
+    KVMAP_HIP(hipMalloc((void**)&c->gram, need * sizeof(float)));
+    c->gram_floats = need;
+    return KVMAP_OK;
+}
+
+static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
+    GramScratch sc;
+    float* base = c->gram;
+    sc.part = base;
+    base += (size_t)kGramMaxSplits * (p + q);
+    sc.cx = base; base += p;
+    sc.cy = base; base += q;
+    sc.mx = base; base += p;
+    sc.my = base; base += q;
+    sc.dx = base; base += p;
+    sc.dy = base;
+    sc.splits = splits;
+    return sc;
+}
+
+extern "C" int kvmap_gram_reset(kvmap_ctx* c, kvmap_gram_state* st, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_reset: ctx is NULL");
+    int r = validate_state(st, "kvmap_gram_reset");
+    if (r) return r;
+    DeviceGuard g(c->device);
+    hipStream_t s = (hipStream_t)stream;
+    KVMAP_HIP(launch_fill_zero(st->mean_x, st->p, s));
+    KVMAP_HIP(launch_fill_zero(st->mean_y, st->q, s));
+    KVMAP_HIP(launch_fill_zero(st->M_xx, (int64_t)st->p * st->p, s));
+    KVMAP_HIP(launch_fill_zero(st->M_xy, (int64_t)st->p * st->q, s));
+    st->n = 0;
+    return ok();
+}
+
+extern "C" int kvmap_gram(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+                          kvmap_gram_state* st, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: ctx is NULL");
+    int r = validate_state(st, "kvmap_gram");
+    if (r) return r;
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_gram: dtype %d unknown", (int)dtype);
+    if (n_b < 0 || n_b > (int64_t(1) << 31)) return fail(KVMAP_ERR_SHAPE, "kvmap_gram: n_b out of range");
+    if (n_b == 0) return ok();
+    if (!X || !Y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: NULL batch");
+    if ((((uintptr_t)X) | ((uintptr_t)Y)) & 15)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: batch pointers must be 16-byte aligned");
+    DeviceGuard g(c->device);
+    r = ensure_gram_scratch(c, st->p, st->q);
+    if (r) return r;
+    int splits = (int)std::min<int64_t>(kGramMaxSplits, std::max<int64_t>(1, n_b / 64));
+    const GramScratch sc = gram_scratch(c, st->p, st->q, splits);
+    const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
+    KVMAP_HIP(launch_gram_batch(e, X, Y, n_b, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
+                                st->M_xy, sc, (hipStream_t)stream));
+    st->n += n_b;
+    return ok();
+}
+
+extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap_gram_state* src,
+                                void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: ctx is NULL");
+    int r = validate_state(dst, "kvmap_gram_merge dst");
+    if (r) return r;
+    r = validate_state(src, "kvmap_gram_merge src");
+    if (r) return r;
+    if (dst->p != src->p || dst->q != src->q)
+        return fail(KVMAP_ERR_SHAPE, "kvmap_gram_merge: p/q differ");
+    if (dst->M_xx == src->M_xx) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src alias");
+    if (src->n == 0) return ok();
+    DeviceGuard g(c->device);
+    r = ensure_gram_scratch(c, dst->p, dst->q);
+    if (r) return r;
+    const GramScratch sc = gram_scratch(c, dst->p, dst->q, 1);
+    KVMAP_HIP(launch_gram_merge(dst->p, dst->q, dst->n, src->n, dst->mean_x, dst->mean_y, dst->M_xx,
+                                dst->M_xy, src->mean_x, src->mean_y, src->M_xx, src->M_xy, sc,
+                                (hipStream_t)stream));
+    dst->n += src->n;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------
+// ridge solve
+// ---------------------------------------------------------------------------------------
+
+extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x, const float* mean_y,
+                                      const float* M_xx, const float* M_xy, double lambda, float* W_out,
+                                      float* b_out, int n_threads) {
+    if (p < 1 || q < 1) return fail(KVMAP_ERR_SHAPE, "kvmap_ridge_solve_host: p, q must be >= 1");
+    if (!mean_x || !mean_y || !M_xx || !M_xy || !W_out || !b_out)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_host: NULL pointer");
+    if (!(lambda >= 0.0) || !std::isfinite(lambda))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_host: lambda must be finite and >= 0");
+    if (ridge_solve_f64(p, q, mean_x, mean_y, M_xx, M_xy, lambda, W_out, b_out, n_threads))
+        return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_host: M_xx + lambda I is not positive definite");
+    return ok();
+}
+
+extern "C" int kvmap_ridge_solve(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, float* W_out,
+                                 float* b_out, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve: ctx is NULL");
+    int r = validate_state(st, "kvmap_ridge_solve");
+    if (r) return r;
+    if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve: NULL output");
+    DeviceGuard g(c->device);
+    const size_t p = st->p, q = st->q;
+    std::vector<float> mx(p), my(q), Mxx(p * p), Mxy(p * q);
+    hipStream_t s = (hipStream_t)stream;
+    KVMAP_HIP(hipMemcpyAsync(mx.data(), st->mean_x, p * 4, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipMemcpyAsync(my.data(), st->mean_y, q * 4, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipMemcpyAsync(Mxx.data(), st->M_xx, p * p * 4, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipMemcpyAsync(Mxy.data(), st->M_xy, p * q * 4, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipStreamSynchronize(s));
+    return kvmap_ridge_solve_host(st->p, st->q, mx.data(), my.data(), Mxx.data(), Mxy.data(), lambda, W_out,
+                                  b_out, 0);
+}

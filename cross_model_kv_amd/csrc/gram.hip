@@ -1,0 +1,376 @@
+// Fit-side statistics: centered co-moments of a batch, merged into a running state with
+// the Chan/Welford pairwise update (KVBridge README, fitting section headed "Loading":
+// batchwise Chan/Welford updates accumulate centered covariance directly instead of
+// subtracting large raw moments).
+//
+// Per batch of n_b rows (x in R^p, y in R^q):
+//   1. column sums (wavefront/LDS reduced)  -> shift c = fp32 column mean
+//   2. column sums of (x - c)               -> m = mean of the shifted batch (tiny)
+//      batch mean = c + m;  delta = batch mean - running mean;  running mean updated
+//   3. co-moments on the matrix cores in fp32 (v_mfma_f32_32x32x2_f32) of the shifted data
+//        G = sum (x - c)(x - c)^T,  C = sum (x - c)(y - c_y)^T
+//      fused with the merge in the epilogue:
+//        M_xx += G - n_b m m^T + (n n_b / n') delta delta^T       (n' = n + n_b)
+//   The shift makes every product small (the inputs carry offsets ~5 in the fit-stat
+//   workload), so nothing cancels; the rank-one n_b m m^T term turns the co-moments about c
+//   into co-moments about the exact batch mean.  Only the upper triangle of tiles of M_xx
+//   is computed; off-diagonal tiles are written to both triangles.
+
+#include "common.h"
+#include "internal.h"
+
+namespace kvmap {
+
+namespace {
+constexpr int CS_THREADS = 256;
+constexpr int CS_COLS = 4;                       // columns per lane
+constexpr int CS_TILE = 64 * CS_COLS;            // columns per workgroup (one wave wide)
+constexpr int GT = 128;                          // Gram tile (features x features)
+constexpr int GK = 32;                           // rows per K-step
+constexpr int GLD = GT + 32;                     // padded LDS row (floats)
+}  // namespace
+
+size_t gram_scratch_floats(int p, int q, int splits) {
+    return (size_t)splits * (p + q) + 3 * (size_t)(p + q);
+}
+
+// ---- 1/2: column sums ---------------------------------------------------------------
+// Lane owns 4 adjacent columns; the 4 waves of a workgroup take interleaved rows of the
+// workgroup's row split and are reduced through LDS; splits are reduced by the finalize
+// kernel in a fixed order (deterministic, no atomics).
+template <bool BF16>
+__global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const void* __restrict__ A,
+                                                            int64_t n, int cols,
+                                                            const float* __restrict__ shift,
+                                                            float* __restrict__ part,
+                                                            int part_stride, int col_off) {
+    __shared__ float4 red[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * CS_TILE + lane * CS_COLS;
+    const int splits = gridDim.y;
+    const int64_t r0 = n * blockIdx.y / splits, r1 = n * (blockIdx.y + 1) / splits;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c0 < cols) {
+        float4 sh = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (shift) sh = *(const float4*)(shift + c0);
+        for (int64_t r = r0 + wave; r < r1; r += 4) {
+            float4 v;
+            if (BF16) {
+                const uint2 w = *(const uint2*)((const uint16_t*)A + r * cols + c0);
+                v = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+            } else {
+                v = *(const float4*)((const float*)A + r * cols + c0);
+            }
+            acc.x += v.x - sh.x; acc.y += v.y - sh.y; acc.z += v.z - sh.z; acc.w += v.w - sh.w;
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && c0 < cols) {
+        float4 s = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const float4 o = red[w][lane];
+            s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+        }
+        *(float4*)(part + (size_t)blockIdx.y * part_stride + col_off + c0) = s;
+    }
+}
+
+// Reduce the split partial sums (float64, fixed order) and derive the phase's outputs.
+//   phase 0: c = sum / n_b
+//   phase 1: m = sum / n_b; batch mean = c + m; delta = batch mean - mean; mean updated
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(
+    const float* __restrict__ part, int splits, int p, int q, int64_t n_b, int64_t n_old,
+    int phase, float* __restrict__ cx, float* __restrict__ cy, float* __restrict__ mx,
+    float* __restrict__ my, float* __restrict__ dx, float* __restrict__ dy,
+    float* __restrict__ mean_x, float* __restrict__ mean_y) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    const int stride = p + q;
+    if (col >= stride) return;
+    double s = 0.0;
+    for (int y = 0; y < splits; ++y) s += (double)part[(size_t)y * stride + col];
+    const double mean_b = s / (double)n_b;
+    const bool isx = col < p;
+    const int c = isx ? col : col - p;
+    float* cc = isx ? cx : cy;
+    if (phase == 0) {
+        cc[c] = (float)mean_b;
+        return;
+    }
+    float* mm = isx ? mx : my;
+    float* dd = isx ? dx : dy;
+    float* mean = isx ? mean_x : mean_y;
+    mm[c] = (float)mean_b;
+    const double bm = (double)cc[c] + mean_b;
+    if (n_old == 0) {
+        dd[c] = 0.f;
+        mean[c] = (float)bm;
+    } else {
+        const double old = (double)mean[c];
+        const double delta = bm - old;
+        dd[c] = (float)delta;
+        mean[c] = (float)(old + delta * ((double)n_b / (double)(n_old + n_b)));
+    }
+}
+
+// ---- 3: shifted co-moments + merge ---------------------------------------------------
+__device__ __forceinline__ void tri_decode(int u, int nT, int& I, int& J) {
+    // upper triangle (I <= J), row-major: row I starts at I*nT - I*(I-1)/2
+    const double b = 2.0 * nT + 1.0;
+    int i = (int)((b - sqrt(b * b - 8.0 * (double)u)) * 0.5);
+    if (i < 0) i = 0;
+    while (i > 0 && (int64_t)i * nT - (int64_t)i * (i - 1) / 2 > u) --i;
+    while ((int64_t)(i + 1) * nT - (int64_t)(i + 1) * i / 2 <= u) ++i;
+    I = i;
+    J = i + (u - (int)((int64_t)i * nT - (int64_t)i * (i - 1) / 2));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* base, int64_t row, int64_t ld, int col) {
+    if (BF16) {
+        const uint2 w = *(const uint2*)((const uint16_t*)base + row * ld + col);
+        return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+    }
+    return *(const float4*)((const float*)base + row * ld + col);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256, 1) void gram_kernel(
+    const void* __restrict__ X, const void* __restrict__ Y, int64_t n_b, int p, int q,
+    const float* __restrict__ cx, const float* __restrict__ cy, const float* __restrict__ mx,
+    const float* __restrict__ my, const float* __restrict__ dx, const float* __restrict__ dy,
+    float coef, int fresh, float* __restrict__ M_xx, float* __restrict__ M_xy, int nTx, int nXX) {
+    __shared__ float4 lds[2][2][GK * GLD / 4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int I, J;
+    bool xy;
+    if ((int)blockIdx.x < nXX) {
+        tri_decode(blockIdx.x, nTx, I, J);
+        xy = false;
+    } else {
+        const int u = blockIdx.x - nXX;
+        I = u % nTx;
+        J = u / nTx;
+        xy = true;
+    }
+    const int i0 = I * GT, j0 = J * GT;
+    const void* B = xy ? Y : X;
+    const int ldb = xy ? q : p;
+    const float* cb = xy ? cy : cx;
+
+    // Load mapping: chunk idx = tid + 256*u (u < 4): row = idx / 32, col = 4 * (idx % 32).
+    const int lcol = (tid & 31) * 4;
+    const int acol = min(i0 + lcol, p - 4), bcol = min(j0 + lcol, ldb - 4);
+    const float4 sa = *(const float4*)(cx + acol);
+    const float4 sb = *(const float4*)(cb + bcol);
+    float4 ra[4], rb[4];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t row = (int64_t)kt * GK + (tid >> 5) + 8 * u;
+            if (row < n_b) {
+                float4 va = load4<BF16>(X, row, p, acol);
+                float4 vb = load4<BF16>(B, row, ldb, bcol);
+                ra[u] = make_float4(va.x - sa.x, va.y - sa.y, va.z - sa.z, va.w - sa.w);
+                rb[u] = make_float4(vb.x - sb.x, vb.y - sb.y, vb.z - sb.z, vb.w - sb.w);
+            } else {
+                ra[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                rb[u] = ra[u];
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = (tid >> 5) + 8 * u;
+            lds[buf][0][(row * GLD + lcol) / 4] = ra[u];
+            lds[buf][1][(row * GLD + lcol) / 4] = rb[u];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    const int wi = wave & 1, wj = wave >> 1;
+    const int nk = (int)((n_b + GK - 1) / GK);
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const float* As = (const float*)lds[buf][0];
+        const float* Bs = (const float*)lds[buf][1];
+#pragma unroll
+        for (int ks = 0; ks < GK / 2; ++ks) {
+            const int kr = (ks * 2 + (lane >> 5)) * GLD;
+            float fa[2], fb[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                fa[a] = As[kr + wi * 64 + a * 32 + (lane & 31)];
+                fb[a] = Bs[kr + wj * 64 + a * 32 + (lane & 31)];
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        }
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane holds G[i][j] for column j = lane & 31 of each 32x32 block and rows
+    // i = 8*(r/4) + 4*(lane/32) + r%4.
+    float* M = xy ? M_xy : M_xx;
+    const int ldm = xy ? q : p;
+    const float* mb = xy ? my : mx;
+    const float* db = xy ? dy : dx;
+    const float nbf = (float)n_b;
+    const bool mirror = !xy && I != J;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int j = j0 + wj * 64 + b * 32 + (lane & 31);
+        const bool jok = j < ldm;
+        const float mj = jok ? mb[j] : 0.f, dj = jok ? db[j] : 0.f;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ib = i0 + wi * 64 + a * 32 + g * 8 + (lane >> 5) * 4;
+                if (ib >= p || !jok) continue;
+                const float4 mi = *(const float4*)(mx + ib);
+                const float4 di = *(const float4*)(dx + ib);
+                float v[4];
+                const float mia[4] = {mi.x, mi.y, mi.z, mi.w};
+                const float dia[4] = {di.x, di.y, di.z, di.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = acc[a][b][g * 4 + r] - nbf * mia[r] * mj + coef * dia[r] * dj;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float* dst = M + (size_t)(ib + r) * ldm + j;
+                    *dst = fresh ? v[r] : *dst + v[r];
+                }
+                if (mirror) {
+                    float4* dst = (float4*)(M + (size_t)j * ldm + ib);
+                    float4 o = fresh ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
+                    o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
+                    *dst = o;
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
+                             int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
+                             float* M_xy, const GramScratch& sc, hipStream_t s) {
+    const bool bf = (e == Elem::BF16);
+    const dim3 gx((p + CS_TILE - 1) / CS_TILE, sc.splits), gy((q + CS_TILE - 1) / CS_TILE, sc.splits);
+    const int stride = p + q;
+    const unsigned fin = (unsigned)((stride + 255) / 256);
+    for (int phase = 0; phase < 2; ++phase) {
+        const float* shx = phase ? sc.cx : nullptr;
+        const float* shy = phase ? sc.cy : nullptr;
+        if (bf) {
+            hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
+            hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
+        } else {
+            hipLaunchKernelGGL(colsum_kernel<false>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
+            hipLaunchKernelGGL(colsum_kernel<false>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
+        }
+        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q,
+                           n_b, n_old, phase, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+    }
+    const int nTx = (p + GT - 1) / GT, nTy = (q + GT - 1) / GT;
+    const int nXX = nTx * (nTx + 1) / 2;
+    const int blocks = nXX + nTx * nTy;
+    const double n_new = (double)n_old + (double)n_b;
+    const float coef = (float)((double)n_old * (double)n_b / n_new);
+    const int fresh = (n_old == 0);
+    if (bf)
+        hipLaunchKernelGGL(gram_kernel<true>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
+                           sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
+    else
+        hipLaunchKernelGGL(gram_kernel<false>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
+                           sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
+    return hipGetLastError();
+}
+
+// ---- merging two states ----------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_delta_kernel(int p, int q, double frac, int fresh,
+                                                          float* __restrict__ mean_x,
+                                                          float* __restrict__ mean_y,
+                                                          const float* __restrict__ s_mean_x,
+                                                          const float* __restrict__ s_mean_y,
+                                                          float* __restrict__ dx,
+                                                          float* __restrict__ dy) {
+    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= p + q) return;
+    const bool isx = col < p;
+    const int c = isx ? col : col - p;
+    float* mean = isx ? mean_x : mean_y;
+    const float* sm = isx ? s_mean_x : s_mean_y;
+    float* d = isx ? dx : dy;
+    if (fresh) {
+        d[c] = 0.f;
+        mean[c] = sm[c];
+        return;
+    }
+    const double delta = (double)sm[c] - (double)mean[c];
+    d[c] = (float)delta;
+    mean[c] = (float)((double)mean[c] + delta * frac);
+}
+
+__global__ __launch_bounds__(256) void merge_moments_kernel(int rows, int cols, float coef,
+                                                            int fresh, float* __restrict__ M,
+                                                            const float* __restrict__ S,
+                                                            const float* __restrict__ da,
+                                                            const float* __restrict__ db) {
+    const int64_t n = (int64_t)rows * cols;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += stride) {
+        const int i = (int)(idx / cols), j = (int)(idx - (int64_t)i * cols);
+        const float v = S[idx] + coef * da[i] * db[j];
+        M[idx] = fresh ? S[idx] : M[idx] + v;
+    }
+}
+
+hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
+                             float* mean_y, float* M_xx, float* M_xy, const float* s_mean_x,
+                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy,
+                             const GramScratch& sc, hipStream_t s) {
+    const double n = (double)n_dst + (double)n_src;
+    const int fresh = (n_dst == 0);
+    const float coef = (float)((double)n_dst * (double)n_src / n);
+    hipLaunchKernelGGL(merge_delta_kernel, dim3((p + q + 255) / 256), dim3(256), 0, s, p, q,
+                       (double)n_src / n, fresh, mean_x, mean_y, s_mean_x, s_mean_y, sc.dx, sc.dy);
+    hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, p, coef, fresh, M_xx, s_M_xx,
+                       sc.dx, sc.dx);
+    hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, q, coef, fresh, M_xy, s_M_xy,
+                       sc.dx, sc.dy);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace kvmap

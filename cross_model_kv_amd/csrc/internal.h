@@ -1,0 +1,70 @@
+// Internal launch interface shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvmap {
+
+// Element storage types.
+enum class Elem : int { BF16 = 0, F32 = 1 };
+
+// Geometry of one apply call, in the notation of include/kvmap.h.
+struct ApplyGeom {
+    int L_src, L_tgt, H, d, k;
+    int64_t T;
+    int F() const { return k * H * d; }
+    int N() const { return H * d; }
+};
+
+// ---- RoPE tables / key de-rotation (rope.hip) -------------------------------------
+// tab[t][i] = (cos a, sin a), a = (pos0 + t) * theta^(-2i/d), formed in float64.
+hipError_t launch_rope_table(float2* tab, int64_t T, int d, double theta, int64_t pos0,
+                             hipStream_t s);
+
+// ws[l][h][t][:] = strip(src[l][h][t][:]) for every l in layers[0..n_layers).
+hipError_t launch_derope(Elem e, const void* src, void* ws, const int32_t* layers, int n_layers,
+                         const ApplyGeom& g, const float2* tab, hipStream_t s);
+
+// ---- map GEMMs (gemm_bf16.hip, gemm_f32.hip) ----------------------------------------
+struct MapArgs {
+    const void* xk;     // de-rotated source keys [L_src][H][T][d]
+    const void* xv;     // source values          [L_src][H][T][d]
+    const int32_t* sel; // device [L_tgt][k]
+    const void* Wk; const void* bk;
+    const void* Wv; const void* bv;
+    const float2* tab_tgt;  // [T][d/2]
+    void* outk; void* outv;
+};
+hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
+hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
+
+// Count of non-finite elements (bf16 or f32) added atomically into *count.
+hipError_t launch_count_nonfinite(Elem e, const void* p, int64_t n, unsigned int* count,
+                                  hipStream_t s);
+
+// ---- fit-side statistics (gram.hip) ------------------------------------------------
+struct GramScratch {
+    float* part;   // [splits][p + q] partial column sums
+    float* cx;     // [p]  batch shift (fp32 column mean of x)
+    float* cy;     // [q]
+    float* mx;     // [p]  mean of (x - cx) over the batch (tiny correction)
+    float* my;     // [q]
+    float* dx;     // [p]  delta = batch mean - running mean
+    float* dy;     // [q]
+    int splits;
+};
+// Sizes (floats) of the scratch for p, q.
+size_t gram_scratch_floats(int p, int q, int splits);
+hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
+                             int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
+                             float* M_xy, const GramScratch& sc, hipStream_t s);
+hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
+                             float* mean_y, float* M_xx, float* M_xy, const float* s_mean_x,
+                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy,
+                             const GramScratch& sc, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+}  // namespace kvmap
+
+#include "ridge.h"

@@ -1,0 +1,313 @@
+"""Python binding of libkvmap (ctypes).  Argument marshalling only: every step of the
+mapping runs in the library's HIP kernels; torch supplies device memory and streams.
+
+The names follow include/kvmap.h: ``Context.apply`` is ``kvmap_apply``, ``Context.gram``
+is ``kvmap_gram`` and so on.  If the library has not been built the import of this module
+succeeds but the first call raises ``KvmapError`` (there is no fallback of any kind).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvmap.so")
+
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_SHAPE = 2
+ERR_UNSUPPORTED = 3
+ERR_NONFINITE = 4
+ERR_NOT_SPD = 5
+ERR_DEVICE = 6
+ERR_OUT_OF_MEMORY = 7
+
+BF16 = 0
+F32 = 1
+ROPE_HALF_SPLIT = 0
+ROPE_INTERLEAVED = 1
+FLAG_CHECK_FINITE = 0x1
+FLAG_TIMING = 0x2
+
+
+class KvmapError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status) if _lib else status}: {detail}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("L_src", ctypes.c_int32), ("L_tgt", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k", ctypes.c_int32), ("T", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+class Rope(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_double), ("pos0", ctypes.c_int64), ("style", ctypes.c_int32)]
+
+
+class GramStateC(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("p", ctypes.c_int32), ("q", ctypes.c_int32),
+                ("mean_x", ctypes.c_void_p), ("mean_y", ctypes.c_void_p),
+                ("M_xx", ctypes.c_void_p), ("M_xy", ctypes.c_void_p)]
+
+
+_lib = None
+
+_SIGS = {
+    "kvmap_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvmap_last_error": (ctypes.c_char_p, []),
+    "kvmap_version": (ctypes.c_int, []),
+    "kvmap_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
+    "kvmap_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvmap_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims)]),
+    "kvmap_validate_apply": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Rope),
+                                            ctypes.POINTER(Rope)]),
+    "kvmap_apply": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32]),
+    "kvmap_last_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int]),
+    "kvmap_gram_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
+    "kvmap_gram": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
+    "kvmap_gram_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.POINTER(GramStateC),
+                                        ctypes.c_void_p]),
+    "kvmap_ridge_solve_host": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int]),
+    "kvmap_ridge_solve": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+}
+
+
+def lib():
+    """Load libkvmap.so (built in-tree). Raises KvmapError if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KvmapError(ERR_DEVICE, "load", f"{LIB_PATH} is not built; run "
+                             "`python -m cross_model_kv_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kvmap_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().kvmap_last_error().decode()
+
+
+def version() -> int:
+    return lib().kvmap_version()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise KvmapError(status, where, last_error())
+
+
+def _dims(L_src, L_tgt, H, d, k, T, dtype) -> Dims:
+    return Dims(int(L_src), int(L_tgt), int(H), int(d), int(k), int(T), int(dtype))
+
+
+def _sel_array(layer_sel) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(layer_sel.cpu() if hasattr(layer_sel, "cpu") else layer_sel),
+                             dtype=np.int32)
+    if a.ndim != 2:
+        raise ValueError("layer_sel must be [L_tgt][k]")
+    return a
+
+
+def validate_apply(L_src, L_tgt, H, d, k, T, dtype, layer_sel, theta_src, theta_tgt,
+                   pos0_src=0, pos0_tgt=0, style_src=ROPE_HALF_SPLIT, style_tgt=ROPE_HALF_SPLIT) -> int:
+    """kvmap_validate_apply; returns the status code (host only, needs no GPU)."""
+    sel = _sel_array(layer_sel)
+    dm = _dims(L_src, L_tgt, H, d, k, T, dtype)
+    rs, rt = Rope(theta_src, pos0_src, style_src), Rope(theta_tgt, pos0_tgt, style_tgt)
+    return lib().kvmap_validate_apply(ctypes.byref(dm), sel.ctypes.data, ctypes.byref(rs), ctypes.byref(rt))
+
+
+def ridge_solve_host(mean_x, mean_y, M_xx, M_xy, lam: float, n_threads: int = 0):
+    """kvmap_ridge_solve_host on host arrays; returns (W [q][p] output-major, b [q]) float32."""
+    mx = np.ascontiguousarray(mean_x, dtype=np.float32)
+    my = np.ascontiguousarray(mean_y, dtype=np.float32)
+    Mxx = np.ascontiguousarray(M_xx, dtype=np.float32)
+    Mxy = np.ascontiguousarray(M_xy, dtype=np.float32)
+    p, q = mx.shape[0], my.shape[0]
+    if Mxx.shape != (p, p) or Mxy.shape != (p, q):
+        raise ValueError("shape mismatch")
+    W = np.empty((q, p), dtype=np.float32)
+    b = np.empty(q, dtype=np.float32)
+    _check(lib().kvmap_ridge_solve_host(p, q, mx.ctypes.data, my.ctypes.data, Mxx.ctypes.data, Mxy.ctypes.data,
+                                        float(lam), W.ctypes.data, b.ctypes.data, int(n_threads)),
+           "kvmap_ridge_solve_host")
+    return W, b
+
+
+# ---------------------------------------------------------------------------------------
+# device side (torch tensors for memory, torch streams)
+# ---------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class GramState:
+    """Device-resident centered statistics (n, mean_x, mean_y, M_xx, M_xy) of kvmap_gram."""
+
+    def __init__(self, p: int, q: int, device):
+        torch = _torch()
+        self.p, self.q, self.device = int(p), int(q), torch.device(device)
+        kw = dict(dtype=torch.float32, device=self.device)
+        self.mean_x = torch.zeros(p, **kw)
+        self.mean_y = torch.zeros(q, **kw)
+        self.M_xx = torch.zeros(p, p, **kw)
+        self.M_xy = torch.zeros(p, q, **kw)
+        self.c = GramStateC(0, self.p, self.q, self.mean_x.data_ptr(), self.mean_y.data_ptr(),
+                            self.M_xx.data_ptr(), self.M_xy.data_ptr())
+
+    @property
+    def n(self) -> int:
+        return int(self.c.n)
+
+
+class Context:
+    """A libkvmap context on one HIP device (kvmap_create / kvmap_destroy)."""
+
+    def __init__(self, device: int = 0):
+        self.device = int(device)
+        h = ctypes.c_void_p()
+        _check(lib().kvmap_create(ctypes.byref(h), self.device), "kvmap_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().kvmap_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ---- apply ---------------------------------------------------------------------
+    def reserve(self, L_src, L_tgt, H, d, k, T, dtype=BF16):
+        dm = _dims(L_src, L_tgt, H, d, k, T, dtype)
+        _check(lib().kvmap_reserve(self._h, ctypes.byref(dm)), "kvmap_reserve")
+
+    def apply(self, src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src: float, theta_tgt: float,
+              pos0_src: int = 0, pos0_tgt: int | None = None, out_k=None, out_v=None, stream=None,
+              flags: int = 0, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT):
+        """kvmap_apply.  src_k/src_v [L_src][H][T][d], W_k/W_v [L_tgt][N][F] (output-major),
+        b_k/b_v [L_tgt][N] device tensors of one dtype (bf16 or fp32); layer_sel host
+        int [L_tgt][k].  Returns (tgt_k, tgt_v) [L_tgt][H][T][d] (allocated if not given)."""
+        torch = _torch()
+        sel = _sel_array(layer_sel)
+        L_src, H, T, d = src_k.shape
+        L_tgt, k = sel.shape
+        dt = _dtype_code(src_k)
+        for name, t in (("src_v", src_v), ("W_k", W_k), ("b_k", b_k), ("W_v", W_v), ("b_v", b_v)):
+            if t.dtype != src_k.dtype:
+                raise TypeError(f"{name} dtype {t.dtype} differs from src_k {src_k.dtype}")
+        N, F = H * d, k * H * d
+        if tuple(src_v.shape) != tuple(src_k.shape):
+            raise ValueError("src_v shape differs from src_k")
+        if tuple(W_k.shape) != (L_tgt, N, F) or tuple(W_v.shape) != (L_tgt, N, F):
+            raise ValueError(f"W must be [L_tgt={L_tgt}][N={N}][F={F}]")
+        if tuple(b_k.shape) != (L_tgt, N) or tuple(b_v.shape) != (L_tgt, N):
+            raise ValueError(f"b must be [L_tgt={L_tgt}][N={N}]")
+        if out_k is None:
+            out_k = torch.empty((L_tgt, H, T, d), dtype=src_k.dtype, device=src_k.device)
+        if out_v is None:
+            out_v = torch.empty((L_tgt, H, T, d), dtype=src_k.dtype, device=src_k.device)
+        for name, t in (("out_k", out_k), ("out_v", out_v)):
+            if tuple(t.shape) != (L_tgt, H, T, d) or t.dtype != src_k.dtype:
+                raise ValueError(f"{name} must be [L_tgt][H][T][d] of the input dtype")
+        dm = _dims(L_src, L_tgt, H, d, k, T, dt)
+        rs = Rope(float(theta_src), int(pos0_src), int(style_src))
+        rt = Rope(float(theta_tgt), int(pos0_src if pos0_tgt is None else pos0_tgt), int(style_tgt))
+        st = lib().kvmap_apply(self._h, ctypes.byref(dm), _dev_ptr(src_k, "src_k"), _dev_ptr(src_v, "src_v"),
+                               sel.ctypes.data, _dev_ptr(W_k, "W_k"), _dev_ptr(b_k, "b_k"),
+                               _dev_ptr(W_v, "W_v"), _dev_ptr(b_v, "b_v"), ctypes.byref(rs), ctypes.byref(rt),
+                               _dev_ptr(out_k, "out_k"), _dev_ptr(out_v, "out_v"),
+                               _stream_handle(stream, src_k.device), int(flags))
+        _check(st, "kvmap_apply")
+        return out_k, out_v
+
+    def last_timings(self):
+        """(rope_table_ms, derope_ms, map_gemm_ms) of the last FLAG_TIMING apply."""
+        ms = (ctypes.c_float * 3)()
+        _check(lib().kvmap_last_timings(self._h, ms, 3), "kvmap_last_timings")
+        return float(ms[0]), float(ms[1]), float(ms[2])
+
+    # ---- fit-side statistics ---------------------------------------------------------
+    def gram_state(self, p: int, q: int) -> GramState:
+        return GramState(p, q, f"cuda:{self.device}")
+
+    def gram_reset(self, st: GramState, stream=None):
+        _check(lib().kvmap_gram_reset(self._h, ctypes.byref(st.c), _stream_handle(stream, st.device)),
+               "kvmap_gram_reset")
+
+    def gram(self, st: GramState, X, Y, stream=None):
+        """kvmap_gram: merge the batch X [n_b][p], Y [n_b][q] (device, bf16 or fp32) into st."""
+        if X.dim() != 2 or Y.dim() != 2 or X.shape[0] != Y.shape[0]:
+            raise ValueError("X [n_b][p] and Y [n_b][q] must share n_b")
+        if X.shape[1] != st.p or Y.shape[1] != st.q:
+            raise ValueError("batch width does not match the state")
+        if X.dtype != Y.dtype:
+            raise TypeError("X and Y dtypes differ")
+        _check(lib().kvmap_gram(self._h, _dev_ptr(X, "X"), _dev_ptr(Y, "Y"), int(X.shape[0]), _dtype_code(X),
+                                ctypes.byref(st.c), _stream_handle(stream, st.device)), "kvmap_gram")
+
+    def gram_merge(self, dst: GramState, src: GramState, stream=None):
+        _check(lib().kvmap_gram_merge(self._h, ctypes.byref(dst.c), ctypes.byref(src.c),
+                                      _stream_handle(stream, dst.device)), "kvmap_gram_merge")
+
+    def ridge_solve(self, st: GramState, lam: float, stream=None):
+        """kvmap_ridge_solve: (W [q][p] output-major float32, b [q]) on the host."""
+        W = np.empty((st.q, st.p), dtype=np.float32)
+        b = np.empty(st.q, dtype=np.float32)
+        _check(lib().kvmap_ridge_solve(self._h, ctypes.byref(st.c), float(lam), W.ctypes.data, b.ctypes.data,
+                                       _stream_handle(stream, st.device)), "kvmap_ridge_solve")
+        return W, b

@@ -1,0 +1,224 @@
+/*
+ * libkvmap -- closed-form cross-model KV-cache mapping on AMD Instinct MI355X (gfx950).
+ *
+ * The mapping (Heo et al., "Cross-Model KV Cache Transfer in LLM Families"), as the
+ * pages describe it:
+ *   K_hat_t = rope_tgt( strip_rope_src(K_s) . W_K + b_K ),   V_hat_t = V_s . W_V + b_V
+ * with one ridge map per target (layer, KV head), fed by the top-k selected source
+ * layers' keys/values of ALL source KV heads concatenated into one feature row
+ * (VeloxQuant-MLX "Cross-Model KV Transfer", section "The mapping"; KVBridge README,
+ * "What ships" and "System design").  The fit side keeps only centered sufficient
+ * statistics merged batchwise with Chan/Welford updates and solves
+ * W = (X^T X + lambda I)^-1 X^T Y, b = Ybar - Xbar W (KVBridge README, fitting section
+ * headed "Loading"; reactapp.top article, section "Eine lineare Bruecke reicht").
+ *
+ * Conventions used by every call
+ *   L_src, L_tgt  source / target layer counts      H = H_kv   KV heads (matched)
+ *   d             head dim (64 or 128)              T          cached tokens
+ *   k             selected source layers per target layer
+ *   F = k*H*d     feature width of one row          N = H*d    output width per target layer
+ *   Cache layout  [layer][kv_head][token][dim], dim fastest (the order of the
+ *                 voidwest.dev "Before Mapping KV Caches" snapshot, "what became
+ *                 first-class"); keys stored rotated, as the model stores them.
+ *   Feature order row column (j*H + h)*d + e = selected rank j (order of layer_sel[t]),
+ *                 source head h, dim e.
+ *   Output order  column n = h*d + e of target layer t goes to tgt[t][h][token][e].
+ *   Map layout    W[t] is OUTPUT-major [N][F]: row n holds the F weights of output
+ *                 column n (the transpose of the logical F x N matrix).  b[t] is [N].
+ *   RoPE          half-split pairs (i, i + d/2), angle (pos0 + token) * theta^(-2i/d);
+ *                 the interleaved form is refused, as VeloxQuant-MLX's "honesty crux"
+ *                 item 7 refuses it.  Angles and their sines/cosines are formed in
+ *                 float64 and stored as float32 tables.
+ *   dtype         KVMAP_DTYPE_BF16: caches, maps and biases bf16, fp32 accumulation,
+ *                 bf16 outputs (round-to-nearest-even);  KVMAP_DTYPE_F32: all fp32.
+ *
+ * Memory and streams
+ *   Pointers named "device" are HIP device memory owned by the caller; the library
+ *   never frees them.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Device work is enqueued asynchronously on it.  One context must not be
+ *   used from two host threads at once, and calls that share a context should be
+ *   issued on one stream (or the caller orders them): the context's workspace and
+ *   tables are shared by its calls.
+ *
+ * Errors
+ *   Every call returns a kvmap_status.  All argument, shape and dtype validation
+ *   happens on the host before any device work; a refused call leaves outputs
+ *   untouched.  kvmap_last_error() returns a thread-local detail string for the
+ *   most recent failure on the calling thread.
+ */
+#ifndef KVMAP_H
+#define KVMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVMAP_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    KVMAP_OK = 0,
+    KVMAP_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad enum, lambda < 0, ...        */
+    KVMAP_ERR_SHAPE = 2,            /* inconsistent sizes, layer_sel out of range/dup */
+    KVMAP_ERR_UNSUPPORTED = 3,      /* valid but outside the matched-KV regime        */
+    KVMAP_ERR_NONFINITE = 4,        /* KVMAP_FLAG_CHECK_FINITE found NaN/Inf          */
+    KVMAP_ERR_NOT_SPD = 5,          /* ridge system not positive definite             */
+    KVMAP_ERR_DEVICE = 6,           /* HIP runtime / launch error                     */
+    KVMAP_ERR_OUT_OF_MEMORY = 7     /* workspace allocation failed                    */
+} kvmap_status;
+
+typedef enum { KVMAP_DTYPE_BF16 = 0, KVMAP_DTYPE_F32 = 1 } kvmap_dtype;
+
+typedef enum {
+    KVMAP_ROPE_HALF_SPLIT = 0,  /* pairs (i, i + d/2): supported               */
+    KVMAP_ROPE_INTERLEAVED = 1  /* pairs (2i, 2i + 1): refused (UNSUPPORTED)   */
+} kvmap_rope_style;
+
+/* Flags for kvmap_apply. */
+#define KVMAP_FLAG_CHECK_FINITE 0x1u /* after mapping, scan tgt_k/tgt_v; any NaN/Inf
+                                         returns KVMAP_ERR_NONFINITE (synchronises the
+                                         stream). The outputs are written regardless.   */
+#define KVMAP_FLAG_TIMING 0x2u       /* record HIP events around each kernel launch on
+                                         `stream`; read with kvmap_last_timings().       */
+
+typedef struct kvmap_ctx kvmap_ctx;
+
+typedef struct {
+    int32_t L_src, L_tgt, H_kv, head_dim, k;
+    int64_t T;
+    int32_t dtype; /* kvmap_dtype */
+} kvmap_dims;
+
+typedef struct {
+    double theta;  /* RoPE base of the model, > 0                     */
+    int64_t pos0;  /* absolute position of token 0 (>= 0)             */
+    int32_t style; /* kvmap_rope_style; only KVMAP_ROPE_HALF_SPLIT     */
+} kvmap_rope;
+
+/* ---- status / version ------------------------------------------------------------ */
+
+/* Static string naming a status code. Never NULL. */
+const char* kvmap_status_string(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* kvmap_last_error(void);
+/* KVMAP_VERSION of the built library. */
+int kvmap_version(void);
+
+/* ---- context ----------------------------------------------------------------------- */
+
+/* Create a context bound to HIP device `device`.  The context owns the RoPE-table cache,
+ * the de-rotated-key workspace and small scratch; it allocates on first use and keeps
+ * what it allocated until kvmap_destroy.  Returns KVMAP_ERR_DEVICE if the device does not
+ * exist or is not gfx950. *out is NULL on failure. */
+int kvmap_create(kvmap_ctx** out, int device);
+/* Free everything the context owns (synchronises its device first). NULL is a no-op. */
+int kvmap_destroy(kvmap_ctx* ctx);
+/* Pre-allocate the workspace kvmap_apply needs for `dims` so the first apply allocates
+ * nothing.  Synchronous. */
+int kvmap_reserve(kvmap_ctx* ctx, const kvmap_dims* dims);
+
+/* ---- apply (the hot path) ---------------------------------------------------------- */
+
+/* Host-only validation of an apply call: shapes, dtype, RoPE descriptors, and layer_sel
+ * (host int32 [L_tgt][k]: every entry in [0, L_src), entries of one row distinct).
+ * Refusals, following the matched-KV scope of the pages (VeloxQuant-MLX "honesty crux"
+ * item 7; KVBridge README "Scope and limitations"):
+ *   SHAPE        L_src, L_tgt, H_kv, k < 1; T < 1; k > L_src; odd head_dim;
+ *                layer_sel entry out of range or repeated within a row
+ *   UNSUPPORTED  head_dim not 64 or 128; style not half-split; dtype unknown
+ *   INVALID_ARGUMENT  NULL pointer; theta <= 0 or not finite; pos0 < 0;
+ *                pos0 + T beyond 2^31
+ * Needs no device. */
+int kvmap_validate_apply(const kvmap_dims* dims, const int32_t* layer_sel,
+                         const kvmap_rope* rope_src, const kvmap_rope* rope_tgt);
+
+/* Map a source KV cache into the target model's cache (the whole apply step).
+ *   src_k, src_v  device [L_src][H][T][d]   stored source cache (keys rotated by the
+ *                                           source model at positions rope_src->pos0 + t)
+ *   layer_sel     HOST   int32 [L_tgt][k]   selected source layers per target layer
+ *   W_k, W_v      device [L_tgt][N][F]      output-major maps
+ *   b_k, b_v      device [L_tgt][N]
+ *   tgt_k, tgt_v  device [L_tgt][H][T][d]   written completely; keys rotated by the
+ *                                           target model at positions rope_tgt->pos0 + t
+ * For every target layer t, token p and output column n = h*d + e:
+ *   X_K[p, (j*H + h')*d + e'] = strip_rope_src(src_k[layer_sel[t][j]][h'][p])[e']
+ *   X_V[p, (j*H + h')*d + e'] = src_v[layer_sel[t][j]][h'][p][e']
+ *   tgt_k[t][h][p] = rope_tgt( (X_K W_k[t]^T + b_k[t])[p, h*d : h*d + d] )
+ *   tgt_v[t][h][p][e] = (X_V W_v[t]^T + b_v[t])[p, h*d + e]
+ * Inputs must not overlap outputs; all pointers 16-byte aligned.  Asynchronous on
+ * `stream` (except KVMAP_FLAG_CHECK_FINITE).  Allocates only when the context's
+ * workspace or RoPE-table cache must grow (see kvmap_reserve).  In bf16 the de-rotated
+ * keys are rounded to bf16 before the map (fp32 accumulation, bf16 output). */
+int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
+                const void* src_k, const void* src_v, const int32_t* layer_sel,
+                const void* W_k, const void* b_k, const void* W_v, const void* b_v,
+                const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
+                void* tgt_k, void* tgt_v, void* stream, uint32_t flags);
+
+/* Durations (ms) of the kernels the last KVMAP_FLAG_TIMING apply on this context
+ * launched, measured with HIP events recorded on the apply's stream:
+ *   ms[0] RoPE-table build (0 if cached), ms[1] key de-rotation producer,
+ *   ms[2] map GEMM (K and V of all target layers, one launch).
+ * Synchronises on the events.  n_ms must be >= 3. */
+int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
+
+/* ---- fit-side statistics ----------------------------------------------------------- */
+
+/* Centered sufficient statistics of a stream of (x, y) rows, x in R^p, y in R^q:
+ *   n       rows merged so far (host integer, updated by the calls)
+ *   mean_x  device fp32 [p],  mean_y device fp32 [q]
+ *   M_xx    device fp32 [p][p]  = sum (x - mean_x)(x - mean_x)^T   (unnormalised, both
+ *                                 triangles stored)
+ *   M_xy    device fp32 [p][q]  = sum (x - mean_x)(y - mean_y)^T
+ * Buffers are caller-allocated device memory; the struct only points at them. */
+typedef struct {
+    int64_t n;
+    int32_t p, q;
+    float* mean_x;
+    float* mean_y;
+    float* M_xx;
+    float* M_xy;
+} kvmap_gram_state;
+
+/* Zero the state's device arrays on `stream` and set n = 0. */
+int kvmap_gram_reset(kvmap_ctx* ctx, kvmap_gram_state* st, void* stream);
+
+/* Merge one batch of n_b rows into st (Chan/Welford pairwise update, KVBridge README
+ * fitting section):  X device [n_b][p], Y device [n_b][q], row-major, in `dtype`
+ * (bf16 or fp32).  The batch is centred on its own column means before its co-moments
+ * are formed (fp32 MFMA), then
+ *   delta = mean_b - mean,  mean += delta * n_b / n',  M += M_b + (n * n_b / n') delta delta^T
+ * with n' = n + n_b.  n_b = 0 is a no-op.  p, q must be multiples of 4 and <= 65536,
+ * n_b <= 2^31.  Asynchronous on `stream`; st->n is updated on the host at once. */
+int kvmap_gram(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+               kvmap_gram_state* st, void* stream);
+
+/* dst <- Chan merge of dst and src (statistics of disjoint samples; same p, q).  Merging
+ * an empty state is the identity.  Asynchronous on `stream`. */
+int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_state* src,
+                     void* stream);
+
+/* ---- ridge solve (host, fp64) ------------------------------------------------------ */
+
+/* Closed-form ridge from statistics held in host memory (fp32 as kept on the device):
+ *   W = (M_xx + lambda I)^-1 M_xy,  b = mean_y - mean_x W
+ * solved by blocked Cholesky in float64 on `n_threads` host threads (0 = all cores).
+ * W_out is written OUTPUT-major [q][p] (the layout kvmap_apply takes), b_out [q], both
+ * fp32 host.  M_xx is read from its upper triangle.  Returns KVMAP_ERR_NOT_SPD if the
+ * factorisation meets a non-positive pivot, INVALID_ARGUMENT for lambda < 0 or NULLs. */
+int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x, const float* mean_y,
+                           const float* M_xx, const float* M_xy, double lambda,
+                           float* W_out, float* b_out, int n_threads);
+
+/* Same, from a device state: copies mean_x, mean_y, M_xx, M_xy to the host on `stream`,
+ * synchronises, and solves.  Synchronous. */
+int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
+                      float* W_out, float* b_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVMAP_H */

@@ -214,7 +214,8 @@ def pin_apply_rows_and_content_space():
         stored = oracle.rope(content, P + np.arange(T), ts)
         full = oracle.apply(stored, src_v, sel, Wk, bk, Wv, bv, ts, tt, pos0_src=P)
         rows = np.array([9, 0, 4])
-        part = oracle.apply_rows(stored, src_v, sel, Wk, bk, Wv, bv, ts, tt, rows, pos0_src=P)
+        part = oracle.apply_rows(stored[:, :, rows], src_v[:, :, rows], sel, Wk, bk, Wv, bv, ts, tt,
+                                 P + rows)
         for t in range(L_t):
             assert np.max(np.abs(part[t][0] - full[t][0][:, rows])) < 1e-12
             assert np.array_equal(part[t][1], full[t][1][:, rows])

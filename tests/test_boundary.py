@@ -1,0 +1,134 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every declared entry point,
+validates arguments on the host, and its host ridge solve matches the oracle."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from cross_model_kv_amd import kvmap as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvmap.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvmap_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.lib()
+    names = _declared()
+    assert "kvmap_apply" in names and "kvmap_gram" in names and len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert K.version() == 100
+    assert K.status_string(K.OK) == "KVMAP_OK"
+    assert K.status_string(K.ERR_NOT_SPD) == "KVMAP_ERR_NOT_SPD"
+    assert K.status_string(99) == "KVMAP_ERR_UNKNOWN"
+
+
+def test_create_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(K.KvmapError) as e:
+        K.Context(0)
+    assert e.value.status == K.ERR_DEVICE
+
+
+GOOD = dict(L_src=6, L_tgt=4, H=2, d=128, k=3, T=100, dtype=K.BF16, theta_src=1e4, theta_tgt=5e5)
+
+
+def _sel(L_t=4, k=3):
+    return np.array([[0, 2, 5], [1, 3, 4], [5, 4, 3], [0, 1, 2]][:L_t], dtype=np.int32)[:, :k]
+
+
+def _validate(**over):
+    args = dict(GOOD)
+    sel = over.pop("layer_sel", _sel())
+    args.update(over)
+    return K.validate_apply(args["L_src"], args["L_tgt"], args["H"], args["d"], args["k"], args["T"],
+                            args["dtype"], sel, args["theta_src"], args["theta_tgt"],
+                            args.get("pos0_src", 0), args.get("pos0_tgt", 0),
+                            args.get("style_src", 0), args.get("style_tgt", 0))
+
+
+def test_validate_accepts_good_call():
+    assert _validate() == K.OK
+    assert _validate(d=64) == K.OK
+    assert _validate(dtype=K.F32, T=1) == K.OK
+    assert _validate(pos0_src=2048, pos0_tgt=2048) == K.OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=7, layer_sel=np.zeros((4, 7), np.int32)), K.ERR_SHAPE),              # k > L_src
+    (dict(layer_sel=np.array([[0, 0, 1]] * 4, np.int32)), K.ERR_SHAPE),          # duplicate in a row
+    (dict(layer_sel=np.array([[0, 1, 6]] * 4, np.int32)), K.ERR_SHAPE),          # out of range
+    (dict(layer_sel=np.array([[0, 1, -1]] * 4, np.int32)), K.ERR_SHAPE),         # negative
+    (dict(d=127), K.ERR_SHAPE),                                                  # odd head dim
+    (dict(d=96), K.ERR_UNSUPPORTED),                                             # not built
+    (dict(style_src=K.ROPE_INTERLEAVED), K.ERR_UNSUPPORTED),                     # traditional RoPE
+    (dict(style_tgt=K.ROPE_INTERLEAVED), K.ERR_UNSUPPORTED),
+    (dict(theta_src=0.0), K.ERR_INVALID_ARGUMENT),
+    (dict(theta_tgt=float("nan")), K.ERR_INVALID_ARGUMENT),
+    (dict(pos0_src=-1), K.ERR_INVALID_ARGUMENT),
+    (dict(pos0_tgt=2 ** 31), K.ERR_INVALID_ARGUMENT),
+    (dict(T=0), K.ERR_SHAPE),
+    (dict(H=0), K.ERR_SHAPE),
+    (dict(dtype=7), K.ERR_UNSUPPORTED),
+])
+def test_validate_refusals(over, status):
+    assert _validate(**over) == status
+    assert K.last_error() != ""
+
+
+def test_validate_accepts_repeats_across_rows():
+    # a source layer may feed several target layers; only repeats within a row are refused
+    assert _validate(layer_sel=np.array([[0, 1, 2]] * 4, np.int32)) == K.OK
+
+
+def _random_stats(p, q, n, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((n, p)) * rng.lognormal(0, 0.5, p) + rng.normal(5, 1, p)
+    Y = X[:, :q] @ rng.standard_normal((q, q)) + rng.standard_normal((n, q))
+    return oracle.stats_two_pass(X, Y)
+
+
+@pytest.mark.parametrize("p,q,n", [(8, 4, 50), (64, 16, 500), (300, 40, 1000)])
+def test_ridge_solve_host_matches_oracle(p, q, n):
+    st = _random_stats(p, q, n, seed=p)
+    lam = 0.01
+    f32 = {k: (v.astype(np.float32) if isinstance(v, np.ndarray) else v) for k, v in st.items()}
+    W, b = K.ridge_solve_host(f32["mx"], f32["my"], np.triu(f32["Mxx"]), f32["Mxy"], lam, n_threads=4)
+    # the oracle solves the same fp32-rounded statistics in fp64
+    ref = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) else v) for k, v in f32.items()}
+    Wr, br = oracle.ridge(ref, lam)
+    assert W.shape == (q, p)
+    assert np.max(np.abs(W.T - Wr)) <= 1e-5 * max(1.0, np.max(np.abs(Wr)))
+    assert np.max(np.abs(b - br)) <= 1e-5 * max(1.0, np.max(np.abs(br)))
+
+
+def test_ridge_solve_host_refusals():
+    p, q = 6, 2
+    mx, my = np.zeros(p, np.float32), np.zeros(q, np.float32)
+    Mxy = np.ones((p, q), np.float32)
+    with pytest.raises(K.KvmapError) as e:
+        K.ridge_solve_host(mx, my, -np.eye(p, dtype=np.float32), Mxy, 0.0)
+    assert e.value.status == K.ERR_NOT_SPD
+    with pytest.raises(K.KvmapError) as e:
+        K.ridge_solve_host(mx, my, np.eye(p, dtype=np.float32), Mxy, -1.0)
+    assert e.value.status == K.ERR_INVALID_ARGUMENT
+    # rank-deficient Gram with lambda = 0 is refused, lambda > 0 makes it solvable
+    Z = np.zeros((p, p), np.float32)
+    with pytest.raises(K.KvmapError):
+        K.ridge_solve_host(mx, my, Z, Mxy, 0.0)
+    W, b = K.ridge_solve_host(mx, my, Z, Mxy, 0.5)
+    assert np.allclose(W, 2.0)

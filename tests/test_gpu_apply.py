@@ -1,0 +1,195 @@
+"""kvmap_apply on the GPU against the fp64 oracle, element by element.
+
+Small configurations are compared in full; the full-size Qwen3 14B->32B and
+Llama-3.1 8B->70B shapes are compared on sampled token rows (each output row depends
+only on its own source row and position, so a sampled row is exact) and via the
+determinism property that holds at any size.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import compare, to_f64
+from synth.device import apply_inputs
+from synth.workloads import APPLY_CONFIGS, ApplyConfig, b_layer, layer_sel, src_layer, to_f64 as s2f, w_layer
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from cross_model_kv_amd import kvmap as K
+    c = K.Context(0)
+    yield c
+    c.close()
+
+
+def _run(ctx, cfg, inp, **kw):
+    print(f"[apply] {cfg.name} T={cfg.T} L={cfg.L_src}->{cfg.L_tgt} H={cfg.H} d={cfg.d} k={cfg.k} {cfg.dtype}",
+          flush=True)
+    out = ctx.apply(inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"],
+                    inp["b_v"], cfg.theta_src, cfg.theta_tgt, pos0_src=cfg.pos0, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _host(cfg):
+    """Full host copies (float64) of a small configuration's inputs, drawn independently of the GPU."""
+    f = lambda a: s2f(a, cfg.dtype)
+    return dict(
+        src_k=np.stack([f(src_layer(cfg, "k", l)) for l in range(cfg.L_src)]),
+        src_v=np.stack([f(src_layer(cfg, "v", l)) for l in range(cfg.L_src)]),
+        W_k=np.stack([f(w_layer(cfg, "k", t)) for t in range(cfg.L_tgt)]),
+        W_v=np.stack([f(w_layer(cfg, "v", t)) for t in range(cfg.L_tgt)]),
+        b_k=np.stack([f(b_layer(cfg, "k", t)) for t in range(cfg.L_tgt)]),
+        b_v=np.stack([f(b_layer(cfg, "v", t)) for t in range(cfg.L_tgt)]),
+        layer_sel=layer_sel(cfg),
+    )
+
+
+def _full_check(ctx, cfg, targets=None):
+    inp = apply_inputs(cfg, "cuda:0")
+    ok_, ov_ = _run(ctx, cfg, inp)
+    h = _host(cfg)
+    ref = oracle.apply(h["src_k"], h["src_v"], h["layer_sel"], h["W_k"], h["b_k"], h["W_v"], h["b_v"],
+                       cfg.theta_src, cfg.theta_tgt, pos0_src=cfg.pos0, targets=targets)
+    report, worst = compare(to_f64(ok_), to_f64(ov_), ref, cfg.dtype)
+    print(f"[apply] worst {worst}", flush=True)
+    assert not report, "\n".join(report[:20])
+    return inp, ok_, ov_
+
+
+def test_tiny_fp32_pair(ctx):
+    """The tiny fp32 pair (4 -> 6 layers, H=2, d=64, T=256, k=2), every element."""
+    _full_check(ctx, APPLY_CONFIGS[1])
+
+
+EDGE = [
+    # ragged token tail, 1.5 feature tiles (H=3), L_tgt > L_src
+    ApplyConfig(201, "ragged-T300-H3", 5, 7, 3, 128, 300, 2, 1.0e4, 1.0e6, "bf16", 0.5),
+    # head dim 64 in bf16, a single token, k = 3
+    ApplyConfig(202, "d64-T1", 4, 3, 2, 64, 1, 3, 1.0e4, 5.0e5, "bf16", 0.5),
+    # continuation offset: positions start at 1000, different bases, k = 1
+    ApplyConfig(203, "pos0-1000-k1", 3, 2, 2, 128, 257, 1, 1.0e4, 5.0e5, "bf16", 0.5, pos0=1000),
+    # fp32 with d = 128 and a ragged tail
+    ApplyConfig(204, "fp32-d128-T70", 3, 2, 2, 128, 70, 2, 1.0e6, 1.0e6, "f32", 0.5),
+    # one head, d = 64 (N = 64: a partial feature tile), many K-steps (k*H*d = 320)
+    ApplyConfig(205, "H1-d64-k5", 6, 2, 1, 64, 513, 5, 1.0e4, 1.0e4, "bf16", 0.5),
+    # several token blocks and heads, small enough for the full oracle
+    ApplyConfig(206, "bf16-T1100-H8", 6, 3, 8, 128, 1100, 2, 1.0e6, 1.0e6, "bf16", 0.5),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_edge_cases(ctx, cfg):
+    _full_check(ctx, cfg)
+
+
+def test_qwen3_small_pair_full_layers(ctx):
+    """Qwen3 0.6B -> 1.7B shape (28 -> 28, H=8, d=128, T=4096, k=4): three target layers in
+    full, every target layer on sampled rows."""
+    cfg = APPLY_CONFIGS[2]
+    inp = apply_inputs(cfg, "cuda:0")
+    ok_, ov_ = _run(ctx, cfg, inp)
+    _check_sampled(cfg, inp, ok_, ov_, targets=[0, 13, 27], rows=np.arange(cfg.T))
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(2000, 2040), np.arange(cfg.T - 40, cfg.T)]))
+    _check_sampled(cfg, inp, ok_, ov_, targets=list(range(cfg.L_tgt)), rows=rows)
+
+
+def _check_sampled(cfg, inp, ok_, ov_, targets, rows):
+    rows_t = torch.as_tensor(rows, device="cuda:0")
+    sel = inp["layer_sel"]
+    need = sorted({int(s) for t in targets for s in sel[t]})
+    sk = {s: to_f64(inp["src_k"][s][:, rows_t, :]) for s in need}
+    sv = {s: to_f64(inp["src_v"][s][:, rows_t, :]) for s in need}
+    Wk = {t: to_f64(inp["W_k"][t]) for t in targets}
+    Wv = {t: to_f64(inp["W_v"][t]) for t in targets}
+    bk = {t: to_f64(inp["b_k"][t]) for t in targets}
+    bv = {t: to_f64(inp["b_v"][t]) for t in targets}
+    ref = oracle.apply_rows(sk, sv, sel, Wk, bk, Wv, bv, cfg.theta_src, cfg.theta_tgt, cfg.pos0 + rows,
+                            targets=targets)
+    gk = {t: to_f64(ok_[t][:, rows_t, :]) for t in targets}
+    gv = {t: to_f64(ov_[t][:, rows_t, :]) for t in targets}
+    report, worst = compare(gk, gv, ref, cfg.dtype)
+    print(f"[apply] sampled {len(rows)} rows x {len(targets)} layers: worst {worst}", flush=True)
+    assert not report, "\n".join(report[:20])
+
+
+def test_identity_map_copies_values_bit_exact(ctx):
+    """k = 1, W = I, b = 0, equal bases: values come back bit-exact; keys (stripped, rounded to
+    bf16 and re-rotated) within one bf16 step of each pair's norm."""
+    cfg = ApplyConfig(210, "identity", 3, 3, 2, 128, 333, 1, 1.0e6, 1.0e6, "bf16", 0.5)
+    inp = apply_inputs(cfg, "cuda:0")
+    N = cfg.N
+    eye = torch.eye(N, dtype=torch.bfloat16, device="cuda:0")
+    for t in range(cfg.L_tgt):
+        inp["W_k"][t].copy_(eye)
+        inp["W_v"][t].copy_(eye)
+    inp["b_k"].zero_()
+    inp["b_v"].zero_()
+    ok_, ov_ = _run(ctx, cfg, inp)
+    for t in range(cfg.L_tgt):
+        s = int(inp["layer_sel"][t][0])
+        assert torch.equal(ov_[t], inp["src_v"][s])
+        x = inp["src_k"][s].float()
+        err = (ok_[t].float() - x).abs()
+        half = cfg.d // 2
+        pair = torch.sqrt(x[..., :half] ** 2 + x[..., half:] ** 2).repeat(1, 1, 2)
+        # the de-rotated key is stored in bf16 before rotating back: one bf16 step of the pair norm
+        assert float((err / pair.clamp_min(1e-6)).max()) <= 2.0 ** -7
+
+
+def test_deterministic_and_stream_ordered(ctx):
+    """Two applies give bit-identical outputs (no atomics in the apply path); a second call on a
+    side stream is ordered by that stream."""
+    cfg = EDGE[0]
+    inp = apply_inputs(cfg, "cuda:0")
+    a = _run(ctx, cfg, inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = ctx.apply(inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"],
+                      inp["b_v"], cfg.theta_src, cfg.theta_tgt, stream=s)
+    s.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_check_finite_flag_and_refusal_leaves_outputs(ctx):
+    from cross_model_kv_amd import kvmap as K
+    cfg = EDGE[0]
+    inp = apply_inputs(cfg, "cuda:0")
+    ok_, ov_ = _run(ctx, cfg, inp, flags=K.FLAG_CHECK_FINITE)
+    inp["src_v"][:, 0, 5, 3] = float("nan")
+    with pytest.raises(K.KvmapError) as e:
+        _run(ctx, cfg, inp, out_k=ok_, out_v=ov_, flags=K.FLAG_CHECK_FINITE)
+    assert e.value.status == K.ERR_NONFINITE
+    # a refused call (duplicate selection) touches nothing
+    before = ok_.clone()
+    bad = inp["layer_sel"].copy()
+    bad[0, 1] = bad[0, 0]
+    with pytest.raises(K.KvmapError) as e:
+        ctx.apply(inp["src_k"], inp["src_v"], bad, inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"],
+                  cfg.theta_src, cfg.theta_tgt, out_k=ok_, out_v=ov_)
+    assert e.value.status == K.ERR_SHAPE
+    torch.cuda.synchronize()
+    assert torch.equal(before, ok_)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_full_size_sampled(ctx, cid):
+    """The full Qwen3 14B->32B (T=32768) and Llama-3.1 8B->70B (T=16384) shapes, in the launch
+    configuration the bench times, checked on sampled rows of the first, last and two middle
+    target layers (rows from the first, a middle and the last token block)."""
+    cfg = APPLY_CONFIGS[cid]
+    print(f"[apply] generating {cfg.name}", flush=True)
+    inp = apply_inputs(cfg, "cuda:0")
+    ok_, ov_ = _run(ctx, cfg, inp)
+    T = cfg.T
+    rows = np.unique(np.concatenate([np.arange(0, 24), np.arange(T // 2 - 12, T // 2 + 12), np.arange(T - 24, T)]))
+    targets = [0, cfg.L_tgt // 3, (2 * cfg.L_tgt) // 3, cfg.L_tgt - 1]
+    _check_sampled(cfg, inp, ok_, ov_, targets, rows)
+    # determinism at full size
+    ok2, ov2 = _run(ctx, cfg, inp)
+    assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)

@@ -1,0 +1,174 @@
+"""kvmap_gram / kvmap_gram_merge / kvmap_ridge_solve on the GPU against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth.device import fit_inputs, host_to_tensor
+from synth.workloads import FIT_STATS_CONFIG, FITCHECK, bf16_bits_to_f64, fit_batch, fit_hidden_map
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GRAM_REL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from cross_model_kv_amd import kvmap as K
+    c = K.Context(0)
+    yield c
+    c.close()
+
+
+def _rel(got, ref):
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def _check_state(st, ref, where):
+    torch.cuda.synchronize()
+    assert st.n == ref["n"], where
+    f = lambda t: t.double().cpu().numpy()
+    r_xx, r_xy = _rel(f(st.M_xx), ref["Mxx"]), _rel(f(st.M_xy), ref["Mxy"])
+    mx = np.max(np.abs(f(st.mean_x) - ref["mx"])) / np.max(np.abs(ref["mx"]))
+    my = np.max(np.abs(f(st.mean_y) - ref["my"])) / np.max(np.abs(ref["my"]))
+    print(f"[gram] {where}: rel M_xx {r_xx:.2e}  M_xy {r_xy:.2e}  mean_x {mx:.2e}  mean_y {my:.2e}", flush=True)
+    assert r_xx <= GRAM_REL and r_xy <= GRAM_REL and mx <= GRAM_REL and my <= GRAM_REL, where
+    # both triangles are stored
+    Mxx = f(st.M_xx)
+    assert np.array_equal(Mxx, Mxx.T) or np.max(np.abs(Mxx - Mxx.T)) <= 1e-6 * np.max(np.abs(Mxx))
+
+
+SMALL = FIT_STATS_CONFIG.replace(cid=401, p=520, q=68, n_tokens=2000, batch=700)
+
+
+def _batches(cfg, sizes, dtype="bf16"):
+    """Batches of the given row counts cut from the seeded stream (bf16 or widened to fp32)."""
+    xs, ys = [], []
+    b = 0
+    while sum(len(x) for x in xs) < sum(sizes):
+        x, y = fit_batch(cfg, b)
+        xs.append(bf16_bits_to_f64(x)); ys.append(bf16_bits_to_f64(y))
+        b += 1
+    X, Y = np.concatenate(xs), np.concatenate(ys)
+    out, r = [], 0
+    for n in sizes:
+        out.append((X[r:r + n], Y[r:r + n]))
+        r += n
+    return out
+
+
+def _dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).cuda()
+    return torch.from_numpy(a.astype(np.float32)).cuda()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gram_ragged_batches(ctx, dtype):
+    """Batches of 700, 1, 37 and 1262 rows (p = 520, q = 68: not tile multiples), mean offset ~5."""
+    parts = _batches(SMALL, [700, 1, 37, 1262])
+    st = ctx.gram_state(SMALL.p, SMALL.q)
+    ctx.gram_reset(st)
+    for X, Y in parts:
+        ctx.gram(st, _dev(X, dtype), _dev(Y, dtype))
+    ref = oracle.stats_two_pass(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    _check_state(st, ref, f"ragged {dtype}")
+
+
+def test_gram_merge_and_resume(ctx):
+    """Two states over disjoint halves merged = one state over the stream; an empty state merges
+    as the identity; a state is a checkpoint (continue streaming after a merge)."""
+    parts = _batches(SMALL, [500, 400, 300, 800])
+    a, b, e = ctx.gram_state(SMALL.p, SMALL.q), ctx.gram_state(SMALL.p, SMALL.q), ctx.gram_state(SMALL.p, SMALL.q)
+    for s in (a, b, e):
+        ctx.gram_reset(s)
+    ctx.gram(a, _dev(parts[0][0], "bf16"), _dev(parts[0][1], "bf16"))
+    ctx.gram(b, _dev(parts[1][0], "bf16"), _dev(parts[1][1], "bf16"))
+    ctx.gram(b, _dev(parts[2][0], "bf16"), _dev(parts[2][1], "bf16"))
+    ctx.gram_merge(a, b)
+    ctx.gram_merge(a, e)
+    ctx.gram(a, _dev(parts[3][0], "bf16"), _dev(parts[3][1], "bf16"))
+    ref = oracle.stats_two_pass(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    _check_state(a, ref, "merge+resume")
+    # merging into an empty state copies
+    ctx.gram_merge(e, a)
+    _check_state(e, ref, "merge into empty")
+
+
+def test_fitcheck_on_gpu(ctx):
+    """The tiny pair's fit check with GPU statistics and the library's ridge solve: maps that
+    match the oracle's fit, and holdout R^2 > 0.99999 through the GPU apply."""
+    from fitcheck_data import build_pairs
+    cfg = FITCHECK
+    pr = build_pairs(cfg)
+    nc = pr["n_calib"]
+    fit = oracle.fit_mapper(pr["src_k"][:nc], pr["src_v"][:nc], pr["tgt_k"][:nc], pr["tgt_v"][:nc],
+                            pr["pos"][:nc], cfg.theta_src, cfg.theta_tgt, cfg.k, cfg.lam)
+    sel = fit["layer_sel"]
+    assert np.array_equal(sel, pr["draws"]["true_sel"])
+    sk = np.stack([oracle.strip_rope(pr["src_k"][i], pr["pos"][i], cfg.theta_src) for i in range(nc)])
+    tk = np.stack([oracle.strip_rope(pr["tgt_k"][i], pr["pos"][i], cfg.theta_tgt) for i in range(nc)])
+    Wk = np.zeros((cfg.L_tgt, cfg.N, cfg.F), np.float32); Wv = np.zeros_like(Wk)
+    bk = np.zeros((cfg.L_tgt, cfg.N), np.float32); bv = np.zeros_like(bk)
+    for t in range(cfg.L_tgt):
+        for src, tgt, W, b, ref_W in ((sk, tk, Wk, bk, fit["W_k"]), (pr["src_v"][:nc], pr["tgt_v"][:nc], Wv, bv, fit["W_v"])):
+            X = np.concatenate([oracle.feature_rows([src[i, s] for s in sel[t]]) for i in range(nc)])
+            Y = np.concatenate([oracle.feature_rows([tgt[i, t]]) for i in range(nc)])
+            st = ctx.gram_state(cfg.F, cfg.N)
+            ctx.gram_reset(st)
+            for r in range(0, len(X), 512):
+                ctx.gram(st, _dev(X[r:r + 512], "f32"), _dev(Y[r:r + 512], "f32"))
+            W[t], b[t] = ctx.ridge_solve(st, cfg.lam)
+            assert np.max(np.abs(W[t] - ref_W[t])) < 1e-3
+    # holdout through the GPU apply (fp32 path)
+    from cross_model_kv_amd import kvmap as K
+    for s in range(nc, len(pr["pos"])):
+        P = int(pr["pos"][s][0])
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        ok_, ov_ = ctx.apply(dev(pr["src_k"][s]), dev(pr["src_v"][s]), sel, dev(Wk), dev(bk), dev(Wv), dev(bv),
+                             cfg.theta_src, cfg.theta_tgt, pos0_src=P)
+        torch.cuda.synchronize()
+        gk, gv = ok_.double().cpu().numpy(), ov_.double().cpu().numpy()
+        for t in range(cfg.L_tgt):
+            kc = oracle.strip_rope(gk[t], pr["pos"][s], cfg.theta_tgt)
+            r2 = np.concatenate([oracle.holdout_r2(pr["tgt_k_content"][s, t], kc),
+                                 oracle.holdout_r2(pr["tgt_v"][s, t], gv[t])])
+            assert r2.min() > 0.99999, (s, t, r2)
+    assert K.version() == 100
+
+
+def test_fit_stats_full_size(ctx):
+    """The fit-statistics stream at the 14B->32B shape: 262,144 tokens in batches of 4096,
+    p = 8192, q = 1024, per-channel offsets ~N(5, 1).  Sampled 96 x 96 blocks of M_xx and
+    96 x 64 of M_xy against the oracle's two-pass statistics of those columns; then the host
+    ridge solve recovers the hidden sparse map."""
+    cfg = FIT_STATS_CONFIG
+    rng = np.random.default_rng(5)
+    cx = np.sort(rng.choice(cfg.p, 96, replace=False))
+    cy = np.sort(rng.choice(cfg.q, 64, replace=False))
+    st = ctx.gram_state(cfg.p, cfg.q)
+    ctx.gram_reset(st)
+    hx, hy = [], []
+    for b, X, Y in fit_inputs(cfg, range(cfg.n_batches)):
+        ctx.gram(st, X, Y)
+        hx.append(X[:, torch.as_tensor(cx, device=X.device)].double().cpu().numpy())
+        hy.append(Y[:, torch.as_tensor(cy, device=Y.device)].double().cpu().numpy())
+        if b % 16 == 0:
+            print(f"[gram] batch {b}/{cfg.n_batches}", flush=True)
+    torch.cuda.synchronize()
+    ref = oracle.stats_two_pass(np.concatenate(hx), np.concatenate(hy))
+    f = lambda t: t.double().cpu().numpy()
+    Mxx = f(st.M_xx)[np.ix_(cx, cx)]
+    Mxy = f(st.M_xy)[np.ix_(cx, cy)]
+    r_xx, r_xy = _rel(Mxx, ref["Mxx"]), _rel(Mxy, ref["Mxy"])
+    mx = np.max(np.abs(f(st.mean_x)[cx] - ref["mx"])) / np.max(np.abs(ref["mx"]))
+    print(f"[gram] full size sampled: rel M_xx {r_xx:.2e} M_xy {r_xy:.2e} mean_x {mx:.2e}", flush=True)
+    assert st.n == cfg.n_tokens
+    assert r_xx <= GRAM_REL and r_xy <= GRAM_REL and mx <= GRAM_REL
+    W, b = ctx.ridge_solve(st, cfg.lam)
+    Wt, bt = fit_hidden_map(cfg)
+    err = np.max(np.abs(W.T - Wt))
+    print(f"[gram] ridge vs hidden map: max |W - W*| {err:.2e}", flush=True)
+    assert err < 2e-3
