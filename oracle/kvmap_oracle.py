@@ -140,34 +140,32 @@ def apply(src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src, theta_tgt,
     """
     if pos0_tgt is None:
         pos0_tgt = pos0_src
-    T = np.asarray(src_k).shape[2]
+    T = np.asarray(src_k[0]).shape[1]
     return apply_rows(src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src, theta_tgt,
-                      np.arange(T), pos0_src, pos0_tgt, targets)
+                      pos0_src + np.arange(T), pos0_tgt + np.arange(T), targets)
 
 
 def apply_rows(src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src, theta_tgt,
-               rows, pos0_src=0, pos0_tgt=None, targets=None):
-    """Like apply() but only for the token indices in `rows`.
+               pos_src, pos_tgt=None, targets=None):
+    """Map the token rows whose source positions are pos_src (and target positions pos_tgt).
 
-    Every output row depends only on the same row of the source cache and on its
-    own position, so a sampled subset is computed exactly as in the full map.
-    src_k / src_v may be any indexable of layers (e.g. a dict or lazy loader)
-    returning [H][T][d].  Returns dict t -> (K_hat [H][R][d], V_hat [H][R][d]).
+    src_k[s] / src_v[s] hold those rows of source layer s, [H][R][d] (any indexable of
+    layers, e.g. a dict holding only the selected layers).  Every output row depends only
+    on the same row of the source cache and on its positions, so a sampled subset of rows
+    is mapped exactly as in the full cache.  Returns dict t -> (K_hat [H][R][d], V_hat).
     """
-    if pos0_tgt is None:
-        pos0_tgt = pos0_src
-    rows = np.asarray(rows, dtype=np.int64)
-    L_tgt = len(layer_sel)
-    targets = range(L_tgt) if targets is None else targets
+    pos_src = np.asarray(pos_src, dtype=np.int64)
+    pos_tgt = pos_src if pos_tgt is None else np.asarray(pos_tgt, dtype=np.int64)
+    targets = range(len(layer_sel)) if targets is None else targets
     out = {}
     for t in targets:
         sel = [int(s) for s in layer_sel[t]]
-        ks = [np.asarray(src_k[s], dtype=np.float64)[:, rows, :] for s in sel]
-        vs = [np.asarray(src_v[s], dtype=np.float64)[:, rows, :] for s in sel]
+        ks = [np.asarray(src_k[s], dtype=np.float64) for s in sel]
+        vs = [np.asarray(src_v[s], dtype=np.float64) for s in sel]
         H = ks[0].shape[0]
-        xk = feature_rows([strip_rope(l, pos0_src + rows, theta_src) for l in ks])
+        xk = feature_rows([strip_rope(l, pos_src, theta_src) for l in ks])
         xv = feature_rows(vs)
-        k_hat = rope(_heads(affine(xk, W_k[t], b_k[t]), H), pos0_tgt + rows, theta_tgt)
+        k_hat = rope(_heads(affine(xk, W_k[t], b_k[t]), H), pos_tgt, theta_tgt)
         v_hat = _heads(affine(xv, W_v[t], b_v[t]), H)
         out[t] = (k_hat, v_hat)
     return out
