@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (the reference dispatch for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the mapper needs no exchange between GPUs and this build "
@@ -112,6 +114,14 @@ def main():
     from synth.workloads import APPLY_CONFIGS
 
     cfg = APPLY_CONFIGS[args.config]
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {a.numel() * 2} bytes read, {b.numel() * 2} bytes written")
+        del a, b
     log(f"generating {cfg.name}: L {cfg.L_src}->{cfg.L_tgt} H={cfg.H} d={cfg.d} k={cfg.k} T={cfg.T}")
     t0 = time.time()
     inp = apply_inputs(cfg, "cuda:0", progress=lambda a, b: log(f"  inputs {a}/{b}") if a % 256 == 0 else None)

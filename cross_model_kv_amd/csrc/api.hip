@@ -199,6 +199,7 @@ extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_se
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(KVMAP_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", (int)d->head_dim);
     if (d->k > d->L_src) return fail(KVMAP_ERR_SHAPE, "k=%d exceeds L_src=%d", (int)d->k, (int)d->L_src);
+    if (d->k > 64) return fail(KVMAP_ERR_UNSUPPORTED, "k=%d: at most 64 selected layers are built", (int)d->k);
     const int64_t N = (int64_t)d->H_kv * d->head_dim;
     const int64_t F = N * d->k;
     if (N * F >= (int64_t(1) << 31))

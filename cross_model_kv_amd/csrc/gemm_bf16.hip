@@ -29,8 +29,9 @@ namespace {
 
 constexpr int BM = 256;  // output features per tile
 constexpr int BN = 256;  // tokens per tile
-constexpr int BK = 64;   // features (reduction) per K-step
-constexpr int CHUNKS = BM * BK / 8;  // 16-byte chunks per operand tile (2048)
+constexpr int BK = 32;   // features (reduction) per K-step
+constexpr int STAGE_CHUNKS = BM * BK / 8;  // 16-byte chunks per operand per stage (1024)
+constexpr int EPI_ROW = 68;                // uint32 words per staged output row (256 B + 16 B pad)
 
 struct TileId {
     int t, kv, pb, nb;
@@ -54,7 +55,43 @@ __device__ __forceinline__ bool decode_tile(int bid, int L_tgt, int nP, int nN, 
     return o.pb < nP;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// LDS slot of the 16-byte chunk c (0..3) of tile row r.  Rows are 64 bytes; the slot bits
+// (b2, b1^b3) of the row make the 16 rows read by any 16 consecutive lanes of a
+// ds_read_b128 fall on 16 distinct 16-byte bank groups of a 256-byte (64-bank) window,
+// and every 8 consecutive lanes on distinct groups of a 128-byte window.
+__device__ __forceinline__ int slot_xor(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes) for raw buffer loads (gfx9 dword3 = 0x00020000).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    const i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                       __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)), (int)bytes, 0x00020000};
+    return r;
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voff + soff into LDS at
+// m0 + 16 * lane.  Written as inline assembly so that the compiler's conservative waits
+// for direct-to-LDS loads (it cannot tell the pipeline's stage buffers apart and would
+// drain every load before issuing the next stage) stay out of the pipeline; the kernel
+// orders these loads itself with explicit vmcnt waits and barriers.  Nothing else in the
+// kernel uses m0.
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds_addr, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "vmcnt");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
 
 }  // namespace
 
@@ -66,54 +103,27 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
     return ((S + 7) / 8) * pg * nN * 8;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9 dword3 = 0x00020000).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// One K-step of the main loop on LDS buffers (curA, curB), with the next K-step's tiles
-// streamed straight from HBM into (nxtA, nxtB) by buffer_load_dwordx4 ... lds (no staging
-// registers, no ds_write).  LDS slot u of a tile holds the 16-byte chunk (row u/8,
-// column (u%8) ^ (row&7)): wave w's i-th load fills slots i*256 + w*64 + lane.  Per-lane
-// byte offsets are fixed for the whole K loop; the K-step moves only scalar state (the W
-// soffset and the gathered slab's resource base).
-#define KVMAP_STEP(kt, curA, curB, nxtA, nxtB)                                              \
-    do {                                                                                    \
-        if ((kt) + 1 < nk) {                                                                \
-            const int k1 = ((kt) + 1) * BK;                                                 \
-            const int s1 = k1 / D, e1 = k1 - s1 * D;                                        \
-            const int j1 = s1 / H, h1 = s1 - j1 * H;                                        \
-            const __amdgpu_buffer_rsrc_t xr =                                               \
-                make_rsrc(X + ((size_t)sel[j1] * H + h1) * slab + e1, slab_bytes);          \
-            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                 \
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(                                   \
-                    wr, (lds_ptr_t)((nxtA) + i * 256 + wave * 64), 16, aoff[i], k1 * 2, 0, 0); \
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(                                   \
-                    xr, (lds_ptr_t)((nxtB) + i * 256 + wave * 64), 16, boff[i], 0, 0, 0);   \
-            }                                                                               \
-        }                                                                                   \
-        _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                            \
-            const int ch = ks * 2 + khalf;                                                  \
-            bf16x8_t fa[4], fb[4];                                                          \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-                fa[i] = __builtin_bit_cast(bf16x8_t, (curA)[swz(arow0 + 32 * i, ch)]);      \
-                fb[i] = __builtin_bit_cast(bf16x8_t, (curB)[swz(brow0 + 32 * i, ch)]);      \
-            }                                                                               \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < 4; ++j)                               \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],       \
-                                                                        acc[i][j], 0, 0, 0); \
-        }                                                                                   \
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                    \
-        __syncthreads();                                                                    \
-    } while (0)
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
-                                                          int64_t T, int nP, int nN) {
-    __shared__ uint4 ldsA0[CHUNKS], ldsB0[CHUNKS], ldsA1[CHUNKS], ldsB1[CHUNKS];
+// NS-stage software pipeline over K-steps of 32 features.  Stage kt lives in LDS buffer
+// kt % NS and is filled by buffer_load_dwordx4 ... lds issued NS-1 K-steps ahead (4 loads
+// per wave per stage: 2 for the W tile, 2 for the X tile).  A K-step is two substeps of
+// 8 MFMAs per wave; the fragments of the next substep are read from LDS between the MFMAs
+// of the current one.  Between the two substeps a wave waits until its loads of stage
+// kt+1 have landed (vmcnt counts the later stages still in flight), meets the other waves
+// at a barrier (all loads of stage kt+1 visible, all reads of stage kt-1 done) and issues
+// stage kt+NS-1 into the buffer stage kt-1 used.  Every K-step issues exactly one stage,
+// so every wait count is a constant.
+//
+// 8 waves, two per SIMD: wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
+// tokens (w >> 1) * 64 .. + 63.  With two waves per SIMD, the load instructions one wave
+// stalls on while the memory pipeline drains are covered by the other wave's MFMAs.
+template <int D, int NS>
+__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
+                                                       int64_t T, int nP, int nN) {
+    constexpr int LOADS = 4;  // per wave per stage
+    constexpr int MAIN_BYTES = NS * 2 * STAGE_CHUNKS * 16;
+    constexpr int EPI_BYTES = 8 * 64 * EPI_ROW * 4;
+    __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
+    uint4* lds = (uint4*)smem;  // [stage][A=W | B=X][1024 chunks]
 
     TileId tl;
     if (!decode_tile(blockIdx.x, L_tgt, nP, nN, tl)) return;
@@ -123,84 +133,161 @@ __global__ __launch_bounds__(256, 1) void map_bf16_kernel(MapArgs a, int L_tgt, 
     const int n0 = tl.nb * BM, p0 = tl.pb * BN;
     const uint16_t* __restrict__ X = (const uint16_t*)(tl.kv ? a.xv : a.xk);
     const uint16_t* __restrict__ W = (const uint16_t*)(tl.kv ? a.Wv : a.Wk) + (size_t)tl.t * N * F;
-    const int32_t* __restrict__ sel = a.sel + tl.t * k;
+    // Lane j keeps selected source layer j of this target layer (k <= 64); a K-step reads it
+    // back with v_readlane, so the loop issues no memory load besides the pipeline's own.
+    const int selv = lane < k ? a.sel[tl.t * k + lane] : 0;
     const size_t slab = (size_t)T * D;
-
-    // Byte offsets (within a K-step) of the chunks this lane streams into LDS.
-    int aoff[8], boff[8];
-    {
-        const int r8 = lane >> 3;
-        const int col = (lane & 7) ^ (r8 & 7);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = i * 32 + wave * 8 + r8;
-            const int n = min(n0 + r, N - 1);
-            const int64_t p = min((int64_t)(p0 + r), T - 1);
-            aoff[i] = (n * F + col * 8) * 2;
-            boff[i] = ((int)(p * D) + col * 8) * 2;
-        }
-    }
     const uint32_t slab_bytes = (uint32_t)(slab * 2);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
+    const i32x4_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-    f32x16_t acc[4][4];
+    // Loads: LDS slot u = i*512 + wave*64 + lane of a stage holds row u/4, chunk
+    // (u%4) ^ slot_xor(row).  Byte offsets within one K-step, fixed for the whole loop.
+    int aoff[2], boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = i * 128 + wave * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ slot_xor(r);
+        const int n = min(n0 + r, N - 1);
+        const int64_t p = min((int64_t)(p0 + r), T - 1);
+        aoff[i] = (n * F + c * 8) * 2;
+        boff[i] = ((int)(p * D) + c * 8) * 2;
+    }
+    const int nk = F / BK;
+
+    // Issue state: LDS buffer, W byte offset and gathered-slab position (element e within
+    // head h of selected layer j) of the next K-step to load.  Advanced with selects only,
+    // so the loop body has no branches.  Past the last K-step the W loads fall outside the
+    // buffer range (the hardware returns zeros) and j is clamped, so the extra stages the
+    // branch-free pipeline loads at the end are harmless and never read.
+    int i_stage = 0, i_soff = 0, i_e = 0, i_h = 0, i_j = 0;
+    auto issue_next = [&]() {
+        const int l1 = __builtin_amdgcn_readlane(selv, min(i_j, k - 1));
+        const i32x4_t xr = make_rsrc(X + ((size_t)l1 * H + i_h) * slab + i_e, slab_bytes);
+        const uint32_t la = lds_base + (uint32_t)i_stage * (2 * STAGE_CHUNKS * 16) + wave_s * 1024u;
+        const uint32_t lb = la + STAGE_CHUNKS * 16;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            lds_dma16(wr, la + i * 8192, aoff[i], i_soff);
+            lds_dma16(xr, lb + i * 8192, boff[i], 0);
+        }
+        i_stage = (i_stage + 1 == NS) ? 0 : i_stage + 1;
+        i_soff += BK * 2;
+        i_e += BK;
+        const int we = (i_e == D);
+        i_e = we ? 0 : i_e;
+        i_h += we;
+        const int wh = (i_h == H);
+        i_h = wh ? 0 : i_h;
+        i_j += wh;
+    };
+
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int wn = wave & 1, wp = wave >> 1;
-    const int arow0 = wn * 128 + (lane & 31);
-    const int brow0 = wp * 128 + (lane & 31);
     const int khalf = lane >> 5;
-    const int nk = F / BK;
+    const int fx = slot_xor(lane & 31);             // rows read by this lane: r % 32 = lane % 32
+    const int arow = (wn * 128 + (lane & 31)) * 4;  // chunk index of the lane's first A row
+    const int brow = (wp * 64 + (lane & 31)) * 4;   // ... and of its first B row
 
-    // prologue: K-step 0 into buffer 0
-    {
-        const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (size_t)sel[0] * H * slab, slab_bytes);
+    // Fragments of one 16-feature substep: lane holds rows (lane % 32) + 32 i of its A and B
+    // blocks, features 8 * (lane / 32) .. + 7 of the substep.
+    auto read_frags = [&](int stage, int ks, bf16x8_t* fa, bf16x8_t* fb) {
+        const uint4* la = lds + (stage * 2) * STAGE_CHUNKS;
+        const uint4* lb = la + STAGE_CHUNKS;
+        const int slot = (ks * 2 + khalf) ^ fx;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(ldsA0 + i * 256 + wave * 64), 16, aoff[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(ldsB0 + i * 256 + wave * 64), 16, boff[i], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + slot]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + slot]);
+    };
+    auto mfmas = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // Interleave: one fragment read after each of the first 6 MFMAs of a substep.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-    int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-        KVMAP_STEP(kt, ldsA0, ldsB0, ldsA1, ldsB1);
-        KVMAP_STEP(kt + 1, ldsA1, ldsB1, ldsA0, ldsB0);
-    }
-    if (kt < nk) KVMAP_STEP(kt, ldsA0, ldsB0, ldsA1, ldsB1);  // odd number of K-steps
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+    // All waves' loads of a stage are visible once each wave has waited for its own (vmcnt
+    // counts the later stages still in flight) and the waves have met at the barrier.  A
+    // plain s_barrier: a release fence would add a vmcnt(0) that drains the pipeline.
+    auto sync = [&]() {
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+    };
 
-    // ---- epilogue: + bias, target RoPE on keys, bf16 store into [t][h][p][e] ----
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue_next();  // stages 0 .. NS-2
+
+    bf16x8_t f0a[4], f0b[2], f1a[4], f1b[2];
+    wait_vmcnt<LOADS * (NS - 2)>();
+    sync();
+    read_frags(0, 0, f0a, f0b);
+    int cs = 0;  // LDS buffer of the K-step being computed
+    for (int kt = 0; kt < nk; ++kt) {
+        // substep 0 of stage kt, reading substep 1 meanwhile
+        read_frags(cs, 1, f1a, f1b);
+        mfmas(f0a, f0b);
+        interleave();
+        // stage kt+1 complete; every wave is past its reads of stage kt-1, whose buffer now
+        // takes stage kt+NS-1
+        wait_vmcnt<LOADS * (NS - 3)>();
+        sync();
+        issue_next();
+        cs = (cs + 1 == NS) ? 0 : cs + 1;
+        // substep 1 of stage kt, reading substep 0 of stage kt+1 meanwhile (after the last
+        // K-step this reads a buffer that is never used)
+        read_frags(cs, 0, f0a, f0b);
+        mfmas(f1a, f1b);
+        interleave();
+    }
+    wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
+    __syncthreads();  // every wave is done reading the pipeline buffers
+
+    // ---- epilogue: + bias, target RoPE on keys, bf16 -> LDS (per-wave [64 tokens][128
+    // features], padded rows), then full 256-byte rows to the target cache [t][h][p][e] ----
     // Lane holds D[n][p] for p = col (lane & 31) and n = 8*(r/4) + 4*(lane/32) + r%4 of each
-    // 32x32 block: 4 consecutive features per register group -> one 8-byte store.
+    // 32x32 block: 4 consecutive features per register group.
     constexpr int HALF = D / 2;
     constexpr int PB = HALF / 32;  // block distance between the two members of a pair
     const uint16_t* __restrict__ bias = (const uint16_t*)(tl.kv ? a.bv : a.bk) + (size_t)tl.t * N;
     uint16_t* __restrict__ out = (uint16_t*)(tl.kv ? a.outv : a.outk);
     const int nw = n0 + wn * 128;
+    const int pw = p0 + wp * 64;
     const bool rope = (tl.kv == 0);
+    uint32_t* stg = (uint32_t*)smem + wave * (64 * EPI_ROW);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if ((i / PB) & 1) continue;  // i is the low member; i + PB the high one
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int nl = i * 32 + g * 8 + khalf * 4;          // feature offset in wave
-            const int nlo = nw + nl, nhi = nlo + HALF;
-            if (nlo >= N) continue;
-            const int h = nlo / D, elo = nlo - h * D;
+            const int nl = i * 32 + g * 8 + khalf * 4;  // feature offset in the wave (low member)
+            const int nlo = min(nw + nl, N - 4), nhi = nlo + HALF;
+            const int elo = nlo % D;
             const uint2 blo = *(const uint2*)(bias + nlo);
             const uint2 bhi = *(const uint2*)(bias + nhi);
             const float bl[4] = {bf16lo(blo.x), bf16hi(blo.x), bf16lo(blo.y), bf16hi(blo.y)};
             const float bh[4] = {bf16lo(bhi.x), bf16hi(bhi.x), bf16lo(bhi.y), bf16hi(bhi.y)};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t p = p0 + wp * 128 + j * 32 + (lane & 31);
-                if (p >= T) continue;
+            for (int j = 0; j < 2; ++j) {
+                const int pl = j * 32 + (lane & 31);
+                const int64_t p = min((int64_t)(pw + pl), T - 1);
                 float ylo[4], yhi[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -208,8 +295,8 @@ __global__ __launch_bounds__(256, 1) void map_bf16_kernel(MapArgs a, int L_tgt, 
                     yhi[r] = acc[i + PB][j][g * 4 + r] + bh[r];
                 }
                 if (rope) {
-                    const float4* cs = (const float4*)(a.tab_tgt + p * HALF + elo);
-                    const float4 c01 = cs[0], c23 = cs[1];
+                    const float4* cs4 = (const float4*)(a.tab_tgt + p * HALF + elo);
+                    const float4 c01 = cs4[0], c23 = cs4[1];
                     const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
                     const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
 #pragma unroll
@@ -219,22 +306,40 @@ __global__ __launch_bounds__(256, 1) void map_bf16_kernel(MapArgs a, int L_tgt, 
                         yhi[r] = fmaf(l, ss[r], hh * cc[r]);
                     }
                 }
-                uint16_t* o = out + (((size_t)tl.t * H + h) * T + p) * D + elo;
-                *(uint2*)o = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
-                *(uint2*)(o + HALF) = make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
+                uint32_t* row = stg + pl * EPI_ROW;
+                *(uint2*)(row + nl / 2) = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
+                *(uint2*)(row + (nl + HALF) / 2) = make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
             }
         }
     }
+    __syncthreads();
+    // 16 lanes per staged row, 16 bytes each: 4 full rows per store instruction.
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int pl = it * 4 + (lane >> 4);
+        const int c = lane & 15;                    // 16-byte chunk = features c*8 .. c*8+7
+        const int64_t p = pw + pl;
+        const int n = nw + c * 8;
+        if (p >= T || n >= N) continue;
+        const int h = n / D, e = n - h * D;
+        const uint4 v = *(const uint4*)(stg + pl * EPI_ROW + c * 4);
+        *(uint4*)(out + (((size_t)tl.t * H + h) * T + p) * D + e) = v;
+    }
 }
+
+#ifndef KVMAP_MAP_STAGES
+#define KVMAP_MAP_STAGES 5
+#endif
 
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s) {
     const int N = g.N();
     const int nP = (int)((g.T + BN - 1) / BN), nN = (N + BM - 1) / BM;
     const int grid = map_bf16_grid(g.L_tgt, g.T, N);
+    constexpr int NS = KVMAP_MAP_STAGES;
     if (g.d == 128)
-        hipLaunchKernelGGL(map_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<128, NS>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     else
-        hipLaunchKernelGGL(map_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<64, NS>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ int kvmap_reserve(kvmap_ctx* ctx, const kvmap_dims* dims);
  * item 7; KVBridge README "Scope and limitations"):
  *   SHAPE        L_src, L_tgt, H_kv, k < 1; T < 1; k > L_src; odd head_dim;
  *                layer_sel entry out of range or repeated within a row
- *   UNSUPPORTED  head_dim not 64 or 128; style not half-split; dtype unknown
+ *   UNSUPPORTED  head_dim not 64 or 128; k > 64; style not half-split; dtype unknown
  *   INVALID_ARGUMENT  NULL pointer; theta <= 0 or not finite; pos0 < 0;
  *                pos0 + T beyond 2^31
  * Needs no device. */
