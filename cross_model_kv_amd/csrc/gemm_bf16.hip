@@ -29,8 +29,8 @@ namespace {
 
 constexpr int BM = 256;  // output features per tile
 constexpr int BN = 256;  // tokens per tile
-constexpr int BK = 32;   // features (reduction) per K-step
-constexpr int STAGE_CHUNKS = BM * BK / 8;  // 16-byte chunks per operand per stage (1024)
+constexpr int BK = 64;   // features (reduction) per K-step: one 128-byte line per tile row
+constexpr int STAGE_CHUNKS = BM * BK / 8;  // 16-byte chunks per operand per stage (2048)
 constexpr int EPI_ROW = 68;                // uint32 words per staged output row (256 B + 16 B pad)
 
 struct TileId {
@@ -55,11 +55,12 @@ __device__ __forceinline__ bool decode_tile(int bid, int L_tgt, int nP, int nN, 
     return o.pb < nP;
 }
 
-// LDS slot of the 16-byte chunk c (0..3) of tile row r.  Rows are 64 bytes; the slot bits
-// (b2, b1^b3) of the row make the 16 rows read by any 16 consecutive lanes of a
-// ds_read_b128 fall on 16 distinct 16-byte bank groups of a 256-byte (64-bank) window,
-// and every 8 consecutive lanes on distinct groups of a 128-byte window.
-__device__ __forceinline__ int slot_xor(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+// LDS slot of the 16-byte chunk c (0..7) of tile row r is c ^ slot_xor(r).  Rows are 128
+// bytes.  For the rows r..r+15 read by 16 consecutive lanes of a ds_read_b128 (one chunk
+// index), (r & 1, c ^ slot_xor(r)) covers all 16 bank groups of a 256-byte (64-bank)
+// window, and for 8 consecutive lanes c ^ slot_xor(r) covers the 8 groups of a 128-byte
+// window: conflict free under either bank count.
+__device__ __forceinline__ int slot_xor(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -85,7 +86,7 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds_addr, int v
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "vmcnt");
+    static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "vmcnt");  // per-wave loads
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -103,15 +104,15 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
     return ((S + 7) / 8) * pg * nN * 8;
 }
 
-// NS-stage software pipeline over K-steps of 32 features.  Stage kt lives in LDS buffer
-// kt % NS and is filled by buffer_load_dwordx4 ... lds issued NS-1 K-steps ahead (4 loads
-// per wave per stage: 2 for the W tile, 2 for the X tile).  A K-step is two substeps of
-// 8 MFMAs per wave; the fragments of the next substep are read from LDS between the MFMAs
-// of the current one.  Between the two substeps a wave waits until its loads of stage
-// kt+1 have landed (vmcnt counts the later stages still in flight), meets the other waves
-// at a barrier (all loads of stage kt+1 visible, all reads of stage kt-1 done) and issues
-// stage kt+NS-1 into the buffer stage kt-1 used.  Every K-step issues exactly one stage,
-// so every wait count is a constant.
+// Two-stage software pipeline over K-steps of 64 features (one 128-byte line per tile row,
+// so every 8 lanes of a load cover a whole cache line).  Stage kt lives in LDS buffer
+// kt % 2 and is filled by buffer_load_dwordx4 ... lds issued one K-step ahead (8 loads per
+// wave per stage: 4 for the W tile, 4 for the X tile).  A K-step is four substeps of 8
+// MFMAs per wave; the fragments of the next substep are read from LDS between the MFMAs
+// of the current one.  Before the last substep a wave waits until its loads of stage kt+1
+// have landed, meets the other waves at a barrier (all loads of stage kt+1 visible, all
+// reads of stage kt done) and issues stage kt+2 into the buffer stage kt used.  Every
+// K-step issues exactly one stage, so every wait count is a constant.
 //
 // 8 waves, two per SIMD: wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
 // tokens (w >> 1) * 64 .. + 63.  With two waves per SIMD, the load instructions one wave
@@ -119,11 +120,12 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
 template <int D, int NS>
 __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
                                                        int64_t T, int nP, int nN) {
-    constexpr int LOADS = 4;  // per wave per stage
+    static_assert(NS == 2, "two LDS stages of 64 KB");
+    constexpr int LOADS = 8;  // per wave per stage
     constexpr int MAIN_BYTES = NS * 2 * STAGE_CHUNKS * 16;
     constexpr int EPI_BYTES = 8 * 64 * EPI_ROW * 4;
     __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
-    uint4* lds = (uint4*)smem;  // [stage][A=W | B=X][1024 chunks]
+    uint4* lds = (uint4*)smem;  // [stage][A=W | B=X][2048 chunks]
 
     TileId tl;
     if (!decode_tile(blockIdx.x, L_tgt, nP, nN, tl)) return;
@@ -142,13 +144,13 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-    // Loads: LDS slot u = i*512 + wave*64 + lane of a stage holds row u/4, chunk
-    // (u%4) ^ slot_xor(row).  Byte offsets within one K-step, fixed for the whole loop.
-    int aoff[2], boff[2];
+    // Loads: LDS slot u = i*512 + wave*64 + lane of a stage holds row u/8, chunk
+    // (u%8) ^ slot_xor(row).  Byte offsets within one K-step, fixed for the whole loop.
+    int aoff[4], boff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = i * 128 + wave * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ slot_xor(r);
+    for (int i = 0; i < 4; ++i) {
+        const int r = i * 64 + wave * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ slot_xor(r);
         const int n = min(n0 + r, N - 1);
         const int64_t p = min((int64_t)(p0 + r), T - 1);
         aoff[i] = (n * F + c * 8) * 2;
@@ -168,11 +170,11 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         const uint32_t la = lds_base + (uint32_t)i_stage * (2 * STAGE_CHUNKS * 16) + wave_s * 1024u;
         const uint32_t lb = la + STAGE_CHUNKS * 16;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
             lds_dma16(wr, la + i * 8192, aoff[i], i_soff);
             lds_dma16(xr, lb + i * 8192, boff[i], 0);
         }
-        i_stage = (i_stage + 1 == NS) ? 0 : i_stage + 1;
+        i_stage ^= 1;
         i_soff += BK * 2;
         i_e += BK;
         const int we = (i_e == D);
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     const int wn = wave & 1, wp = wave >> 1;
     const int khalf = lane >> 5;
     const int fx = slot_xor(lane & 31);             // rows read by this lane: r % 32 = lane % 32
-    const int arow = (wn * 128 + (lane & 31)) * 4;  // chunk index of the lane's first A row
-    const int brow = (wp * 64 + (lane & 31)) * 4;   // ... and of its first B row
+    const int arow = (wn * 128 + (lane & 31)) * 8;  // chunk index of the lane's first A row
+    const int brow = (wp * 64 + (lane & 31)) * 8;   // ... and of its first B row
 
     // Fragments of one 16-feature substep: lane holds rows (lane % 32) + 32 i of its A and B
     // blocks, features 8 * (lane / 32) .. + 7 of the substep.
@@ -204,9 +206,9 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         const uint4* lb = la + STAGE_CHUNKS;
         const int slot = (ks * 2 + khalf) ^ fx;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + slot]);
+        for (int i = 0; i < 4; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 256 + slot]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + slot]);
+        for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 256 + slot]);
     };
     auto mfmas = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
 #pragma unroll
@@ -232,29 +234,33 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         asm volatile("" ::: "memory");  // no LDS read moves above the barrier
     };
 
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue_next();  // stages 0 .. NS-2
-
-    bf16x8_t f0a[4], f0b[2], f1a[4], f1b[2];
-    wait_vmcnt<LOADS * (NS - 2)>();
+    issue_next();  // stage 0 -> buffer 0
+    issue_next();  // stage 1 -> buffer 1
+    bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
+    wait_vmcnt<LOADS>();
     sync();
-    read_frags(0, 0, f0a, f0b);
+    read_frags(0, 0, fa0, fb0);
     int cs = 0;  // LDS buffer of the K-step being computed
     for (int kt = 0; kt < nk; ++kt) {
-        // substep 0 of stage kt, reading substep 1 meanwhile
-        read_frags(cs, 1, f1a, f1b);
-        mfmas(f0a, f0b);
+        read_frags(cs, 1, fa1, fb1);
+        mfmas(fa0, fb0);
         interleave();
-        // stage kt+1 complete; every wave is past its reads of stage kt-1, whose buffer now
-        // takes stage kt+NS-1
-        wait_vmcnt<LOADS * (NS - 3)>();
+        read_frags(cs, 2, fa0, fb0);
+        mfmas(fa1, fb1);
+        interleave();
+        read_frags(cs, 3, fa1, fb1);
+        mfmas(fa0, fb0);
+        interleave();
+        // All reads of stage kt are issued; once they have returned, and stage kt+1 has
+        // landed, the barrier frees buffer cs for stage kt+2.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
         sync();
         issue_next();
-        cs = (cs + 1 == NS) ? 0 : cs + 1;
-        // substep 1 of stage kt, reading substep 0 of stage kt+1 meanwhile (after the last
-        // K-step this reads a buffer that is never used)
-        read_frags(cs, 0, f0a, f0b);
-        mfmas(f1a, f1b);
+        cs ^= 1;
+        // (after the last K-step this reads a buffer that is never used)
+        read_frags(cs, 0, fa0, fb0);
+        mfmas(fa1, fb1);
         interleave();
     }
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
 }
 
 #ifndef KVMAP_MAP_STAGES
-#define KVMAP_MAP_STAGES 5
+#define KVMAP_MAP_STAGES 2
 #endif
 
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s) {
