@@ -104,28 +104,35 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
     return ((S + 7) / 8) * pg * nN * 8;
 }
 
-// Two-stage software pipeline over K-steps of 64 features (one 128-byte line per tile row,
-// so every 8 lanes of a load cover a whole cache line).  Stage kt lives in LDS buffer
-// kt % 2 and is filled by buffer_load_dwordx4 ... lds issued one K-step ahead (8 loads per
-// wave per stage: 4 for the W tile, 4 for the X tile).  A K-step is four substeps of 8
-// MFMAs per wave; the fragments of the next substep are read from LDS between the MFMAs
-// of the current one.  Before the last substep a wave waits until its loads of stage kt+1
-// have landed, meets the other waves at a barrier (all loads of stage kt+1 visible, all
-// reads of stage kt done) and issues stage kt+2 into the buffer stage kt used.  Every
-// K-step issues exactly one stage, so every wait count is a constant.
+// Software pipeline over K-steps of 64 features (one 128-byte line per tile row, so every
+// 8 lanes of a load cover a whole cache line).  LDS holds two rings of 32 KB tile buffers:
+// a 2-deep ring for the W tile and a 3-deep ring for the gathered X tile (160 KB).  Both
+// are filled by buffer_load_dwordx4 ... lds: W one K-step ahead, X -- which misses to HBM
+// on its first touch -- two K-steps ahead.  A K-step is two substeps of 32 MFMAs per
+// wave (8 x 4 blocks of 16 x 16, 32 features deep); the fragments of the next substep are read from LDS
+// between the MFMAs of the current one.  Before the second substep a wave waits until its
+// loads of K-step kt+1 have landed, meets the other waves at a barrier (K-step kt+1
+// visible everywhere, every read of K-step kt done) and issues W(kt+2) and X(kt+3) into
+// the buffers K-step kt used.  Every K-step issues exactly one W and one X stage, W
+// first, so every wait count is a constant: only X(kt+2) may still be in flight.
 //
-// 8 waves, two per SIMD: wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
-// tokens (w >> 1) * 64 .. + 63.  With two waves per SIMD, the load instructions one wave
-// stalls on while the memory pipeline drains are covered by the other wave's MFMAs.
-template <int D, int NS>
-__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
-                                                       int64_t T, int nP, int nN) {
-    static_assert(NS == 2, "two LDS stages of 64 KB");
-    constexpr int LOADS = 8;  // per wave per stage
-    constexpr int MAIN_BYTES = NS * 2 * STAGE_CHUNKS * 16;
-    constexpr int EPI_BYTES = 8 * 64 * EPI_ROW * 4;
+// NW waves: wave w computes features (w & 1) * 128 .. + 127 (whole heads) of tokens
+// (w >> 1) * TW .. + TW - 1, TW = 512 / NW.  With 8 waves (two per SIMD) the load
+// instructions one wave stalls on while the memory pipeline drains are covered by the other
+// wave's MFMAs.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
+                                                           int64_t T, int nP, int nN) {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    constexpr int TW = 512 / NW;          // tokens per wave
+    constexpr int JB = TW / 16;           // 16-token MFMA blocks per wave
+    constexpr int LPO = 32 / NW;          // loads per wave per operand per stage (2048 chunks / 64 lanes / NW)
+    constexpr int TILE = STAGE_CHUNKS * 16;            // 32 KB: one operand tile of one K-step
+    constexpr int NW_BUF = 2, NX_BUF = 3;
+    constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
+    constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
     __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
-    uint4* lds = (uint4*)smem;  // [stage][A=W | B=X][2048 chunks]
+    uint4* lds = (uint4*)smem;  // W buffers 0..1, then X buffers 0..2, 2048 chunks each
 
     TileId tl;
     if (!decode_tile(blockIdx.x, L_tgt, nP, nN, tl)) return;
@@ -144,12 +151,12 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-    // Loads: LDS slot u = i*512 + wave*64 + lane of a stage holds row u/8, chunk
+    // Loads: LDS slot u = i*64*NW + wave*64 + lane of a tile buffer holds row u/8, chunk
     // (u%8) ^ slot_xor(row).  Byte offsets within one K-step, fixed for the whole loop.
-    int aoff[4], boff[4];
+    int aoff[LPO], boff[LPO];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = i * 64 + wave * 8 + (lane >> 3);
+    for (int i = 0; i < LPO; ++i) {
+        const int r = i * 8 * NW + wave * 8 + (lane >> 3);
         const int c = (lane & 7) ^ slot_xor(r);
         const int n = min(n0 + r, N - 1);
         const int64_t p = min((int64_t)(p0 + r), T - 1);
@@ -158,73 +165,80 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     }
     const int nk = F / BK;
 
-    // Issue state: LDS buffer, W byte offset and gathered-slab position (element e within
-    // head h of selected layer j) of the next K-step to load.  Advanced with selects only,
-    // so the loop body has no branches.  Past the last K-step the W loads fall outside the
-    // buffer range (the hardware returns zeros) and j is clamped, so the extra stages the
-    // branch-free pipeline loads at the end are harmless and never read.
-    int i_stage = 0, i_soff = 0, i_e = 0, i_h = 0, i_j = 0;
-    auto issue_next = [&]() {
-        const int l1 = __builtin_amdgcn_readlane(selv, min(i_j, k - 1));
-        const i32x4_t xr = make_rsrc(X + ((size_t)l1 * H + i_h) * slab + i_e, slab_bytes);
-        const uint32_t la = lds_base + (uint32_t)i_stage * (2 * STAGE_CHUNKS * 16) + wave_s * 1024u;
-        const uint32_t lb = la + STAGE_CHUNKS * 16;
+    // Issue state of each ring: next buffer, and for W the byte offset of the next K-step,
+    // for X its gathered-slab position (element e within head h of selected layer j).
+    // Advanced with selects only, so the loop body has no branches.  Past the last K-step
+    // the W loads fall outside the buffer range (the hardware returns zeros) and j is
+    // clamped, so the extra stages the branch-free pipeline loads at the end are harmless
+    // and never read.
+    int w_buf = 0, w_soff = 0;
+    int x_buf = 0, x_e = 0, x_h = 0, x_j = 0;
+    auto issue_w = [&]() {
+        const uint32_t la = lds_base + (uint32_t)w_buf * TILE + wave_s * 1024u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lds_dma16(wr, la + i * 8192, aoff[i], i_soff);
-            lds_dma16(xr, lb + i * 8192, boff[i], 0);
-        }
-        i_stage ^= 1;
-        i_soff += BK * 2;
-        i_e += BK;
-        const int we = (i_e == D);
-        i_e = we ? 0 : i_e;
-        i_h += we;
-        const int wh = (i_h == H);
-        i_h = wh ? 0 : i_h;
-        i_j += wh;
+        for (int i = 0; i < LPO; ++i) lds_dma16(wr, la + i * 1024 * NW, aoff[i], w_soff);
+        w_buf ^= 1;
+        w_soff += BK * 2;
+    };
+    auto issue_x = [&]() {
+        const int l1 = __builtin_amdgcn_readlane(selv, min(x_j, k - 1));
+        const i32x4_t xr = make_rsrc(X + ((size_t)l1 * H + x_h) * slab + x_e, slab_bytes);
+        const uint32_t lb = lds_base + (uint32_t)(NW_BUF + x_buf) * TILE + wave_s * 1024u;
+#pragma unroll
+        for (int i = 0; i < LPO; ++i) lds_dma16(xr, lb + i * 1024 * NW, boff[i], 0);
+        x_buf = (x_buf + 1 == NX_BUF) ? 0 : x_buf + 1;
+        x_e += BK;
+        const int we = (x_e == D);
+        x_e = we ? 0 : x_e;
+        x_h += we;
+        const int wh = (x_h == H);
+        x_h = wh ? 0 : x_h;
+        x_j += wh;
     };
 
-    f32x16_t acc[4][2];
+    // v_mfma_f32_16x16x32_bf16 blocks: IB = 8 blocks of 16 features x JB blocks of 16 tokens.
+    // (Per FLOP it moves half the accumulator registers of the 32 x 32 x 16 form.)
+    constexpr int IB = 8;
+    f32x4_t acc[IB][JB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
     const int wn = wave & 1, wp = wave >> 1;
-    const int khalf = lane >> 5;
-    const int fx = slot_xor(lane & 31);             // rows read by this lane: r % 32 = lane % 32
-    const int arow = (wn * 128 + (lane & 31)) * 8;  // chunk index of the lane's first A row
-    const int brow = (wp * 64 + (lane & 31)) * 8;   // ... and of its first B row
+    const int kq = lane >> 4;                       // which 8-feature quarter of a 32-feature substep
+    const int fx = slot_xor(lane & 15);             // rows read by this lane: r % 16 = lane % 16
+    const int arow = (wn * 128 + (lane & 15)) * 8;  // chunk index of the lane's first A row
+    const int brow = (wp * TW + (lane & 15)) * 8;   // ... and of its first B row
 
-    // Fragments of one 16-feature substep: lane holds rows (lane % 32) + 32 i of its A and B
-    // blocks, features 8 * (lane / 32) .. + 7 of the substep.
-    auto read_frags = [&](int stage, int ks, bf16x8_t* fa, bf16x8_t* fb) {
-        const uint4* la = lds + (stage * 2) * STAGE_CHUNKS;
-        const uint4* lb = la + STAGE_CHUNKS;
-        const int slot = (ks * 2 + khalf) ^ fx;
+    // Fragments of one 32-feature substep: lane holds rows (lane % 16) + 16 i of its A and B
+    // blocks, features 8 * (lane / 16) .. + 7 of the substep.
+    auto read_frags = [&](int wb, int xb, int ks, bf16x8_t* fa, bf16x8_t* fb) {
+        const uint4* la = lds + wb * STAGE_CHUNKS;
+        const uint4* lb = lds + (NW_BUF + xb) * STAGE_CHUNKS;
+        const int slot = (ks * 4 + kq) ^ fx;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 256 + slot]);
+        for (int i = 0; i < IB; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + slot]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 256 + slot]);
+        for (int j = 0; j < JB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + slot]);
     };
     auto mfmas = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < JB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
-    // Interleave: one fragment read after each of the first 6 MFMAs of a substep.
+    // Interleave: one fragment read after each of the first IB + JB MFMAs of a substep.
     auto interleave = [&]() {
 #pragma unroll
-        for (int r = 0; r < 6; ++r) {
+        for (int r = 0; r < IB + JB; ++r) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, IB * JB - (IB + JB), 0);
     };
     // All waves' loads of a stage are visible once each wave has waited for its own (vmcnt
     // counts the later stages still in flight) and the waves have met at the barrier.  A
@@ -234,94 +248,91 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         asm volatile("" ::: "memory");  // no LDS read moves above the barrier
     };
 
-    issue_next();  // stage 0 -> buffer 0
-    issue_next();  // stage 1 -> buffer 1
-    bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
-    wait_vmcnt<LOADS>();
+    // prologue: W(0) X(0) W(1) X(1) X(2); K-step 0 complete once only W(1) X(1) X(2) remain
+    issue_w();
+    issue_x();
+    issue_w();
+    issue_x();
+    issue_x();
+    bf16x8_t fa0[IB], fb0[JB], fa1[IB], fb1[JB];
+    wait_vmcnt<3 * LPO>();
     sync();
-    read_frags(0, 0, fa0, fb0);
-    int cs = 0;  // LDS buffer of the K-step being computed
+    int cw = 0, cx = 0;  // ring buffers of the K-step being computed
+    read_frags(cw, cx, 0, fa0, fb0);
     for (int kt = 0; kt < nk; ++kt) {
-        read_frags(cs, 1, fa1, fb1);
+        read_frags(cw, cx, 1, fa1, fb1);
         mfmas(fa0, fb0);
         interleave();
-        read_frags(cs, 2, fa0, fb0);
-        mfmas(fa1, fb1);
-        interleave();
-        read_frags(cs, 3, fa1, fb1);
-        mfmas(fa0, fb0);
-        interleave();
-        // All reads of stage kt are issued; once they have returned, and stage kt+1 has
-        // landed, the barrier frees buffer cs for stage kt+2.
+        // All reads of K-step kt are issued; once they have returned and K-step kt+1 has
+        // landed (only X(kt+2) may be outstanding), the barrier frees K-step kt's buffers.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        wait_vmcnt<0>();
+        wait_vmcnt<LPO>();
         sync();
-        issue_next();
-        cs ^= 1;
-        // (after the last K-step this reads a buffer that is never used)
-        read_frags(cs, 0, fa0, fb0);
+        issue_w();  // W(kt+2) -> W buffer of K-step kt
+        issue_x();  // X(kt+3) -> X buffer of K-step kt
+        cw ^= 1;
+        cx = (cx + 1 == NX_BUF) ? 0 : cx + 1;
+        // (after the last K-step this reads buffers that are never used)
+        read_frags(cw, cx, 0, fa0, fb0);
         mfmas(fa1, fb1);
         interleave();
     }
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
     __syncthreads();  // every wave is done reading the pipeline buffers
 
-    // ---- epilogue: + bias, target RoPE on keys, bf16 -> LDS (per-wave [64 tokens][128
+    // ---- epilogue: + bias, target RoPE on keys, bf16 -> LDS (per-wave [TW tokens][128
     // features], padded rows), then full 256-byte rows to the target cache [t][h][p][e] ----
-    // Lane holds D[n][p] for p = col (lane & 31) and n = 8*(r/4) + 4*(lane/32) + r%4 of each
-    // 32x32 block: 4 consecutive features per register group.
+    // Lane holds D[n][p] for p = col (lane & 15) and n = 4 * (lane / 16) + r of each 16 x 16
+    // block: 4 consecutive features -> one 8-byte LDS store.
     constexpr int HALF = D / 2;
-    constexpr int PB = HALF / 32;  // block distance between the two members of a pair
+    constexpr int PB = HALF / 16;  // block distance between the two members of a RoPE pair
     const uint16_t* __restrict__ bias = (const uint16_t*)(tl.kv ? a.bv : a.bk) + (size_t)tl.t * N;
     uint16_t* __restrict__ out = (uint16_t*)(tl.kv ? a.outv : a.outk);
     const int nw = n0 + wn * 128;
-    const int pw = p0 + wp * 64;
+    const int pw = p0 + wp * TW;
     const bool rope = (tl.kv == 0);
-    uint32_t* stg = (uint32_t*)smem + wave * (64 * EPI_ROW);
+    uint32_t* stg = (uint32_t*)smem + wave * (TW * EPI_ROW);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < IB; ++i) {
         if ((i / PB) & 1) continue;  // i is the low member; i + PB the high one
+        const int nl = i * 16 + kq * 4;  // feature offset in the wave (low member)
+        const int nlo = min(nw + nl, N - 4), nhi = nlo + HALF;
+        const int elo = nlo % D;
+        const uint2 blo = *(const uint2*)(bias + nlo);
+        const uint2 bhi = *(const uint2*)(bias + nhi);
+        const float bl[4] = {bf16lo(blo.x), bf16hi(blo.x), bf16lo(blo.y), bf16hi(blo.y)};
+        const float bh[4] = {bf16lo(bhi.x), bf16hi(bhi.x), bf16lo(bhi.y), bf16hi(bhi.y)};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nl = i * 32 + g * 8 + khalf * 4;  // feature offset in the wave (low member)
-            const int nlo = min(nw + nl, N - 4), nhi = nlo + HALF;
-            const int elo = nlo % D;
-            const uint2 blo = *(const uint2*)(bias + nlo);
-            const uint2 bhi = *(const uint2*)(bias + nhi);
-            const float bl[4] = {bf16lo(blo.x), bf16hi(blo.x), bf16lo(blo.y), bf16hi(blo.y)};
-            const float bh[4] = {bf16lo(bhi.x), bf16hi(bhi.x), bf16lo(bhi.y), bf16hi(bhi.y)};
+        for (int j = 0; j < JB; ++j) {
+            const int pl = j * 16 + (lane & 15);
+            const int64_t p = min((int64_t)(pw + pl), T - 1);
+            float ylo[4], yhi[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int pl = j * 32 + (lane & 31);
-                const int64_t p = min((int64_t)(pw + pl), T - 1);
-                float ylo[4], yhi[4];
+            for (int r = 0; r < 4; ++r) {
+                ylo[r] = acc[i][j][r] + bl[r];
+                yhi[r] = acc[i + PB][j][r] + bh[r];
+            }
+            if (rope) {
+                const float4* cs4 = (const float4*)(a.tab_tgt + p * HALF + elo);
+                const float4 c01 = cs4[0], c23 = cs4[1];
+                const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+                const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    ylo[r] = acc[i][j][g * 4 + r] + bl[r];
-                    yhi[r] = acc[i + PB][j][g * 4 + r] + bh[r];
+                    const float l = ylo[r], hh = yhi[r];
+                    ylo[r] = fmaf(-hh, ss[r], l * cc[r]);
+                    yhi[r] = fmaf(l, ss[r], hh * cc[r]);
                 }
-                if (rope) {
-                    const float4* cs4 = (const float4*)(a.tab_tgt + p * HALF + elo);
-                    const float4 c01 = cs4[0], c23 = cs4[1];
-                    const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
-                    const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float l = ylo[r], hh = yhi[r];
-                        ylo[r] = fmaf(-hh, ss[r], l * cc[r]);
-                        yhi[r] = fmaf(l, ss[r], hh * cc[r]);
-                    }
-                }
-                uint32_t* row = stg + pl * EPI_ROW;
-                *(uint2*)(row + nl / 2) = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
-                *(uint2*)(row + (nl + HALF) / 2) = make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
             }
+            uint32_t* row = stg + pl * EPI_ROW;
+            *(uint2*)(row + nl / 2) = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
+            *(uint2*)(row + (nl + HALF) / 2) = make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
         }
     }
     __syncthreads();
     // 16 lanes per staged row, 16 bytes each: 4 full rows per store instruction.
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < TW / 4; ++it) {
         const int pl = it * 4 + (lane >> 4);
         const int c = lane & 15;                    // 16-byte chunk = features c*8 .. c*8+7
         const int64_t p = pw + pl;
@@ -333,19 +344,19 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     }
 }
 
-#ifndef KVMAP_MAP_STAGES
-#define KVMAP_MAP_STAGES 2
+#ifndef KVMAP_MAP_WAVES
+#define KVMAP_MAP_WAVES 8
 #endif
 
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s) {
     const int N = g.N();
     const int nP = (int)((g.T + BN - 1) / BN), nN = (N + BM - 1) / BM;
     const int grid = map_bf16_grid(g.L_tgt, g.T, N);
-    constexpr int NS = KVMAP_MAP_STAGES;
+    constexpr int NW = KVMAP_MAP_WAVES;
     if (g.d == 128)
-        hipLaunchKernelGGL((map_bf16_kernel<128, NS>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<128, NW>), dim3(grid), dim3(64 * NW), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     else
-        hipLaunchKernelGGL((map_bf16_kernel<64, NS>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<64, NW>), dim3(grid), dim3(64 * NW), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     return hipGetLastError();
 }
 
