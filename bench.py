@@ -18,7 +18,6 @@ cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on the h
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,7 +29,6 @@ sys.path.insert(0, ROOT)
 METRIC = "mapped tokens/s (K+V, all target layers) at 14B→32B shape; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
-GEMM_SRC = os.path.join(ROOT, "cross_model_kv_amd", "csrc", "gemm_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "map_bf16_traffic.json")
 
 
@@ -38,20 +36,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def traffic_entry(cfg_name):
     """HBM bytes per launch of the map GEMM from the committed counter summary, if that summary
-    was taken on the current kernel source and this workload; else None."""
+    was taken on the current kernel code and this workload; else None."""
+    from cross_model_kv_amd.profiling import kernel_fingerprint
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != source_sha(GEMM_SRC) or t.get("workload") != cfg_name:
+    if t.get("kernel_code_fingerprint") != kernel_fingerprint() or t.get("workload") != cfg_name:
         return None
     return t.get("hbm_bytes_per_launch")
 

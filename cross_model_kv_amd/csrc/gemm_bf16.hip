@@ -8,13 +8,16 @@
 //
 // Mapping of the work (VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping": one ridge map
 // per target head, for K and for V; KVBridge README "What ships": cross-head features):
-//   * output tile 256 features x 256 tokens, 4 waves of 128 x 128; a wave's 128 features
-//     are whole heads, so both members (e, e + d/2) of every RoPE pair sit in the same lane;
-//   * v_mfma_f32_32x32x16_bf16 (gfx950): A = W rows (features), B = X rows (tokens),
+//   * output tile 256 features x 256 tokens per workgroup of 8 waves (2 x 4), each wave
+//     128 features x 64 tokens; a wave's 128 features are whole heads, so both members
+//     (e, e + d/2) of every RoPE pair sit in the same lane;
+//   * v_mfma_f32_16x16x32_bf16 (gfx950): A = W rows (features), B = X rows (tokens),
 //     both K-contiguous in memory and in LDS;
-//   * LDS double buffer (2 x 64 KB) filled straight from HBM by buffer_load ... lds, 16-byte
-//     chunks XOR-swizzled by row so the MFMA fragment reads are bank-conflict free; one
-//     barrier per K-step;
+//   * K-steps of 64 features, so every tile row is one whole 128-byte line; the stages are
+//     filled straight from HBM by buffer_load ... lds into two LDS rings, 2 stages for W and
+//     3 for X (5 x 32 KB), with 16-byte chunks XOR-swizzled by row so the MFMA fragment
+//     reads are bank-conflict free; one barrier per K-step, with W fetched one K-step and
+//     X two K-steps ahead of the step being computed;
 //   * tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD walks
 //     "super-tiles" of 8 token blocks x 4 feature tiles of one (t, K|V), so the A rows and
 //     the W slab each tile needs are shared through that XCD's L2, and the 8 XCDs work on

@@ -6,8 +6,9 @@ FETCH_CSV / WRITE_CSV are the `*_counter_collection.csv` files of two single-cou
 (`rocprofv3 --pmc FETCH_SIZE ...` and `--pmc WRITE_SIZE ...`) of
 `bench.py --copy-calibration`.  That bench option first runs one plain device copy of 1 GiB,
 whose counter reading gives the bytes-per-KiB factor of each counter; the map GEMM dispatches'
-readings are scaled by it.  The output records the source hash of the kernel it was taken
-on, so bench.py can drop the figure once the kernel changes.
+readings are scaled by it.  The output records a fingerprint of the kernel's code (its
+sources with comments and layout removed) so that bench.py can drop the figure once the
+kernel's code changes.
 """
 
 from __future__ import annotations
@@ -17,11 +18,27 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-GEMM_SRC = os.path.join(HERE, "csrc", "gemm_bf16.hip")
+GEMM_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("gemm_bf16.hip", "common.h")]
 COPY_BYTES = 1 << 30
+
+
+_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def kernel_fingerprint(paths=GEMM_SOURCES):
+    """Hash of the map GEMM's code: string literals kept, comments dropped, whitespace runs
+    collapsed, so that edits to comments or layout keep counter summaries valid."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        norm = _TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+        h.update(" ".join(norm.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def _per_dispatch(path, counter):
@@ -54,9 +71,7 @@ def traffic(fetch_csv, write_csv, workload, out_json):
         raise SystemExit("no map_bf16_kernel dispatches in the counter files")
     fetch = sum(fk) / len(fk) * 1024.0 * fs
     write = sum(wk) / len(wk) * 1024.0 * ws
-    with open(GEMM_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    out = {"kernel": "map_bf16_kernel", "workload": workload, "kernel_source_sha": sha,
+    out = {"kernel": "map_bf16_kernel", "workload": workload, "kernel_code_fingerprint": kernel_fingerprint(),
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "hbm_bytes_per_launch": fetch + write, "fetch_scale_bytes_per_KiB": fs * 1024.0,
            "write_scale_bytes_per_KiB": ws * 1024.0, "dispatches": len(fk)}
