@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds_addr, int v
                  :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
+// c ? a : b on uniform values, as one s_cselect.  Written out because the compiler turns a
+// select between a v_readlane result and an add into a branch, which would split the loop.
+__device__ __forceinline__ uint32_t uniform_select(uint32_t c, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("s_cmp_lg_u32 %1, 0\n\ts_cselect_b32 %0, %2, %3"
+        : "=s"(r)
+        : "s"(__builtin_amdgcn_readfirstlane(c)), "s"(a), "s"(b)
+        : "scc");
+    return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "vmcnt");  // per-wave loads
@@ -145,11 +156,13 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     const int n0 = tl.nb * BM, p0 = tl.pb * BN;
     const uint16_t* __restrict__ X = (const uint16_t*)(tl.kv ? a.xv : a.xk);
     const uint16_t* __restrict__ W = (const uint16_t*)(tl.kv ? a.Wv : a.Wk) + (size_t)tl.t * N * F;
-    // Lane j keeps selected source layer j of this target layer (k <= 64); a K-step reads it
-    // back with v_readlane, so the loop issues no memory load besides the pipeline's own.
-    const int selv = lane < k ? a.sel[tl.t * k + lane] : 0;
+    // Lane j keeps the address of head 0 of selected source layer j of this target layer
+    // (k <= 64); the loop reads it back with v_readlane, so it issues no memory load besides
+    // the pipeline's own.
     const size_t slab = (size_t)T * D;
     const uint32_t slab_bytes = (uint32_t)(slab * 2);
+    const uint64_t lbase = (uint64_t)(uintptr_t)(X + (size_t)(lane < k ? a.sel[tl.t * k + lane] : 0) * H * slab);
+    const int lb_lo = (int)(uint32_t)lbase, lb_hi = (int)(uint32_t)(lbase >> 32);
     const i32x4_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -169,34 +182,59 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     const int nk = F / BK;
 
     // Issue state of each ring: next buffer, and for W the byte offset of the next K-step,
-    // for X its gathered-slab position (element e within head h of selected layer j).
-    // Advanced with selects only, so the loop body has no branches.  Past the last K-step
-    // the W loads fall outside the buffer range (the hardware returns zeros) and j is
-    // clamped, so the extra stages the branch-free pipeline loads at the end are harmless
-    // and never read.
-    int w_buf = 0, w_soff = 0;
-    int x_buf = 0, x_e = 0, x_h = 0, x_j = 0;
-    auto issue_w = [&]() {
-        const uint32_t la = lds_base + (uint32_t)w_buf * TILE + wave_s * 1024u;
-#pragma unroll
-        for (int i = 0; i < LPO; ++i) lds_dma16(wr, la + i * 1024 * NW, aoff[i], w_soff);
-        w_buf ^= 1;
-        w_soff += BK * 2;
+    // for X the address of the gathered slab (head h of selected layer j, a [T][d] block)
+    // and the byte offset of the K-step's 64 features in its rows.  Advanced with adds and
+    // selects only, so the loop body has no branches.  Past the last K-step the W offset
+    // and j stop at their last values: the extra stages that the branch-free pipeline loads
+    // at the end repeat the last one, stay in bounds and are never read.
+    //
+    // Each issue is planned (buffer, offsets, descriptor: scalar arithmetic only) one
+    // substep before it is issued, so that after the barrier only the loads themselves stand
+    // between the waves and their next MFMAs.
+    struct WIssue {
+        uint32_t la;
+        int soff;
     };
-    auto issue_x = [&]() {
-        const int l1 = __builtin_amdgcn_readlane(selv, min(x_j, k - 1));
-        const i32x4_t xr = make_rsrc(X + ((size_t)l1 * H + x_h) * slab + x_e, slab_bytes);
-        const uint32_t lb = lds_base + (uint32_t)(NW_BUF + x_buf) * TILE + wave_s * 1024u;
-#pragma unroll
-        for (int i = 0; i < LPO; ++i) lds_dma16(xr, lb + i * 1024 * NW, boff[i], 0);
+    struct XIssue {
+        i32x4_t rsrc;
+        uint32_t la;
+        int soff;
+    };
+    const int w_last = (nk - 1) * BK * 2;
+    int w_buf = 0, w_soff = 0;
+    int x_buf = 0, x_eb = 0, x_h = 0, x_j = 0;
+    uint32_t x_lo = (uint32_t)__builtin_amdgcn_readlane(lb_lo, 0);  // slab address, two halves
+    uint32_t x_hi = (uint32_t)__builtin_amdgcn_readlane(lb_hi, 0);
+    auto plan_w = [&]() {
+        const WIssue r = {lds_base + (uint32_t)w_buf * TILE + wave_s * 1024u, w_soff};
+        w_buf ^= 1;
+        w_soff = min(w_soff + BK * 2, w_last);
+        return r;
+    };
+    auto plan_x = [&]() {
+        const i32x4_t rs = {(int)x_lo, (int)x_hi, (int)slab_bytes, 0x00020000};
+        const XIssue r = {rs, lds_base + (uint32_t)(NW_BUF + x_buf) * TILE + wave_s * 1024u, x_eb};
         x_buf = (x_buf + 1 == NX_BUF) ? 0 : x_buf + 1;
-        x_e += BK;
-        const int we = (x_e == D);
-        x_e = we ? 0 : x_e;
+        x_eb += BK * 2;
+        const int we = (x_eb == D * 2);  // next head
+        x_eb = we ? 0 : x_eb;
         x_h += we;
-        const int wh = (x_h == H);
+        const int wh = (x_h == H);  // next selected layer
         x_h = wh ? 0 : x_h;
-        x_j += wh;
+        x_j = min(x_j + wh, k - 1);
+        const uint32_t a_lo = x_lo + (we ? slab_bytes : 0u);
+        const uint32_t a_hi = x_hi + (a_lo < x_lo ? 1u : 0u);
+        x_lo = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_lo, x_j), a_lo);
+        x_hi = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j), a_hi);
+        return r;
+    };
+    auto issue_w = [&](const WIssue& r) {
+#pragma unroll
+        for (int i = 0; i < LPO; ++i) lds_dma16(wr, r.la + i * 1024 * NW, aoff[i], r.soff);
+    };
+    auto issue_x = [&](const XIssue& r) {
+#pragma unroll
+        for (int i = 0; i < LPO; ++i) lds_dma16(r.rsrc, r.la + i * 1024 * NW, boff[i], r.soff);
     };
 
     // v_mfma_f32_16x16x32_bf16 blocks: IB = 8 blocks of 16 features x JB blocks of 16 tokens.
@@ -243,6 +281,20 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
         }
         __builtin_amdgcn_sched_group_barrier(0x008, IB * JB - (IB + JB), 0);
     };
+    // The same, and then up to two scalar or vector ALU instructions (the planning of the
+    // next issue) after each remaining MFMA, so that they never hold the matrix pipe up.
+    auto interleave_plan = [&]() {
+#pragma unroll
+        for (int r = 0; r < IB + JB; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < IB * JB - (IB + JB); ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+        }
+    };
     // All waves' loads of a stage are visible once each wave has waited for its own (vmcnt
     // counts the later stages still in flight) and the waves have met at the barrier.  A
     // plain s_barrier: a release fence would add a vmcnt(0) that drains the pipeline.
@@ -252,11 +304,13 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     };
 
     // prologue: W(0) X(0) W(1) X(1) X(2); K-step 0 complete once only W(1) X(1) X(2) remain
-    issue_w();
-    issue_x();
-    issue_w();
-    issue_x();
-    issue_x();
+    issue_w(plan_w());
+    issue_x(plan_x());
+    issue_w(plan_w());
+    issue_x(plan_x());
+    issue_x(plan_x());
+    WIssue w_next = plan_w();  // W(2) and X(3): the first issues inside the loop
+    XIssue x_next = plan_x();
     bf16x8_t fa0[IB], fb0[JB], fa1[IB], fb1[JB];
     wait_vmcnt<3 * LPO>();
     sync();
@@ -271,13 +325,15 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wait_vmcnt<LPO>();
         sync();
-        issue_w();  // W(kt+2) -> W buffer of K-step kt
-        issue_x();  // X(kt+3) -> X buffer of K-step kt
+        issue_w(w_next);  // W(kt+2) -> W buffer of K-step kt
+        issue_x(x_next);  // X(kt+3) -> X buffer of K-step kt
         cw ^= 1;
         cx = (cx + 1 == NX_BUF) ? 0 : cx + 1;
         // (after the last K-step this reads buffers that are never used)
         read_frags(cw, cx, 0, fa0, fb0);
         mfmas(fa1, fb1);
+        w_next = plan_w();
+        x_next = plan_x();
         interleave();
     }
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
