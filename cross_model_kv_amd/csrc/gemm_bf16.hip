@@ -36,6 +36,11 @@ constexpr int BK = 64;   // features (reduction) per K-step: one 128-byte line p
 constexpr int STAGE_CHUNKS = BM * BK / 8;  // 16-byte chunks per operand per stage (2048)
 constexpr int EPI_ROW = 68;                // uint32 words per staged output row (256 B + 16 B pad)
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 struct TileId {
     int t, kv, pb, nb;
 };
@@ -100,12 +105,10 @@ __device__ __forceinline__ uint32_t uniform_select(uint32_t c, uint32_t a, uint3
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "vmcnt");  // per-wave loads
+    static_assert(N == 0 || N == 4 || N == 8, "vmcnt");  // per-wave loads still in flight
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
 }  // namespace
@@ -120,28 +123,36 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
 
 // Software pipeline over K-steps of 64 features (one 128-byte line per tile row, so every
 // 8 lanes of a load cover a whole cache line).  LDS holds two rings of 32 KB tile buffers:
-// a 2-deep ring for the W tile and a 3-deep ring for the gathered X tile (160 KB).  Both
-// are filled by buffer_load_dwordx4 ... lds: W one K-step ahead, X -- which misses to HBM
-// on its first touch -- two K-steps ahead.  A K-step is two substeps of 32 MFMAs per
-// wave (8 x 4 blocks of 16 x 16, 32 features deep); the fragments of the next substep are read from LDS
-// between the MFMAs of the current one.  Before the second substep a wave waits until its
-// loads of K-step kt+1 have landed, meets the other waves at a barrier (K-step kt+1
-// visible everywhere, every read of K-step kt done) and issues W(kt+2) and X(kt+3) into
-// the buffers K-step kt used.  Every K-step issues exactly one W and one X stage, W
-// first, so every wait count is a constant: only X(kt+2) may still be in flight.
+// a 2-deep ring for the W tile and a 3-deep ring for the gathered X tile (160 KB), filled
+// by buffer_load_dwordx4 ... lds.  A K-step is two substeps of 32 MFMAs per wave (8 x 4
+// blocks of 16 x 16, 32 features deep), one barrier between them.  Each substep is
+// written as 8 chunks (the 4 MFMAs of one A block, the fragment reads of the other
+// substep's A block and, in 4 of them, of a B block), fenced off from each other, so that
+// single loads can sit between chosen chunks and no burst of loads ever stalls a wave's
+// MFMA issue:
+//   * first substep of K-step kt: MFMAs of its first 32 features; fragment reads of its
+//     second 32; the 4 loads of X(kt+2), one every other chunk, into the X buffer that
+//     K-step kt-1 used (freed at the last barrier).
+//   * wait until this wave's W(kt+1) and X(kt+1) have landed (only X(kt+2) may still be in
+//     flight), barrier: K-step kt+1 is visible everywhere and every read of K-step kt is done.
+//   * second substep: MFMAs of the second 32 features of K-step kt; fragment reads of the
+//     first 32 of K-step kt+1; the 4 loads of W(kt+2), one every other chunk, into the W
+//     buffer of K-step kt.
+// X -- which misses to HBM on its first touch -- is thus requested about 1.5 K-steps before
+// it is needed and W, which the other token blocks of the super-tile keep in L2, one.
+// Every K-step issues exactly one W and one X stage in the same order, so every wait count
+// is a constant.
 //
-// NW waves: wave w computes features (w & 1) * 128 .. + 127 (whole heads) of tokens
-// (w >> 1) * TW .. + TW - 1, TW = 512 / NW.  With 8 waves (two per SIMD) the load
-// instructions one wave stalls on while the memory pipeline drains are covered by the other
-// wave's MFMAs.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k,
-                                                           int64_t T, int nP, int nN) {
-    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-    constexpr int TW = 512 / NW;          // tokens per wave
-    constexpr int JB = TW / 16;           // 16-token MFMA blocks per wave
-    constexpr int LPO = 32 / NW;          // loads per wave per operand per stage (2048 chunks / 64 lanes / NW)
-    constexpr int TILE = STAGE_CHUNKS * 16;            // 32 KB: one operand tile of one K-step
+// 8 waves (two per SIMD): wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
+// tokens (w >> 1) * 64 .. + 63.
+template <int D>
+__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
+                                                       int nP, int nN) {
+    constexpr int NW = 8;                  // waves
+    constexpr int TW = 64;                 // tokens per wave
+    constexpr int JB = TW / 16;            // 16-token MFMA blocks per wave
+    constexpr int LPO = 4;                 // loads per wave per operand per stage (2048 chunks / 64 lanes / NW)
+    constexpr int TILE = STAGE_CHUNKS * 16;  // 32 KB: one operand tile of one K-step
     constexpr int NW_BUF = 2, NX_BUF = 3;
     constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
     constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
@@ -188,9 +199,8 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     // and j stop at their last values: the extra stages that the branch-free pipeline loads
     // at the end repeat the last one, stay in bounds and are never read.
     //
-    // Each issue is planned (buffer, offsets, descriptor: scalar arithmetic only) one
-    // substep before it is issued, so that after the barrier only the loads themselves stand
-    // between the waves and their next MFMAs.
+    // Each stage's issue is planned (buffer, offsets, descriptor: scalar arithmetic only)
+    // in a chunk before the ones that issue its loads.
     struct WIssue {
         uint32_t la;
         int soff;
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     uint32_t x_hi = (uint32_t)__builtin_amdgcn_readlane(lb_hi, 0);
     auto plan_w = [&]() {
         const WIssue r = {lds_base + (uint32_t)w_buf * TILE + wave_s * 1024u, w_soff};
-        w_buf ^= 1;
+        w_buf = (w_buf + 1 == NW_BUF) ? 0 : w_buf + 1;
         w_soff = min(w_soff + BK * 2, w_last);
         return r;
     };
@@ -228,13 +238,16 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
         x_hi = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j), a_hi);
         return r;
     };
+    // load i (of LPO) of a stage
+    auto issue_w1 = [&](const WIssue& r, int i) { lds_dma16(wr, r.la + i * 1024 * NW, aoff[i], r.soff); };
+    auto issue_x1 = [&](const XIssue& r, int i) { lds_dma16(r.rsrc, r.la + i * 1024 * NW, boff[i], r.soff); };
     auto issue_w = [&](const WIssue& r) {
 #pragma unroll
-        for (int i = 0; i < LPO; ++i) lds_dma16(wr, r.la + i * 1024 * NW, aoff[i], r.soff);
+        for (int i = 0; i < LPO; ++i) issue_w1(r, i);
     };
     auto issue_x = [&](const XIssue& r) {
 #pragma unroll
-        for (int i = 0; i < LPO; ++i) lds_dma16(r.rsrc, r.la + i * 1024 * NW, boff[i], r.soff);
+        for (int i = 0; i < LPO; ++i) issue_x1(r, i);
     };
 
     // v_mfma_f32_16x16x32_bf16 blocks: IB = 8 blocks of 16 features x JB blocks of 16 tokens.
@@ -254,46 +267,20 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     const int arow = (wn * 128 + (lane & 15)) * 8;  // chunk index of the lane's first A row
     const int brow = (wp * TW + (lane & 15)) * 8;   // ... and of its first B row
 
-    // Fragments of one 32-feature substep: lane holds rows (lane % 16) + 16 i of its A and B
-    // blocks, features 8 * (lane / 16) .. + 7 of the substep.
-    auto read_frags = [&](int wb, int xb, int ks, bf16x8_t* fa, bf16x8_t* fb) {
+    // Fragments of substep ks (0, 1) of a K-step: lane holds row (lane % 16) + 16 i of A block
+    // i (B block j), features 32 ks + 8 (lane / 16) .. + 7 of the K-step.
+    auto rd_a = [&](int wb, int ks, int i, bf16x8_t* fa) {
         const uint4* la = lds + wb * STAGE_CHUNKS;
+        fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + ((ks * 4 + kq) ^ fx)]);
+    };
+    auto rd_b = [&](int xb, int ks, int j, bf16x8_t* fb) {
         const uint4* lb = lds + (NW_BUF + xb) * STAGE_CHUNKS;
-        const int slot = (ks * 4 + kq) ^ fx;
-#pragma unroll
-        for (int i = 0; i < IB; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + slot]);
-#pragma unroll
-        for (int j = 0; j < JB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + slot]);
+        fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + ((ks * 4 + kq) ^ fx)]);
     };
-    auto mfmas = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
+    auto mrow = [&](const bf16x8_t* fa, const bf16x8_t* fb, int i) {  // the MFMAs of A block i
 #pragma unroll
-        for (int i = 0; i < IB; ++i)
-#pragma unroll
-            for (int j = 0; j < JB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    };
-    // Interleave: one fragment read after each of the first IB + JB MFMAs of a substep.
-    auto interleave = [&]() {
-#pragma unroll
-        for (int r = 0; r < IB + JB; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, IB * JB - (IB + JB), 0);
-    };
-    // The same, and then up to two scalar or vector ALU instructions (the planning of the
-    // next issue) after each remaining MFMA, so that they never hold the matrix pipe up.
-    auto interleave_plan = [&]() {
-#pragma unroll
-        for (int r = 0; r < IB + JB; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < IB * JB - (IB + JB); ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
-        }
+        for (int j = 0; j < JB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
     // All waves' loads of a stage are visible once each wave has waited for its own (vmcnt
     // counts the later stages still in flight) and the waves have met at the barrier.  A
@@ -303,38 +290,49 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
         asm volatile("" ::: "memory");  // no LDS read moves above the barrier
     };
 
-    // prologue: W(0) X(0) W(1) X(1) X(2); K-step 0 complete once only W(1) X(1) X(2) remain
+    // prologue: W(0) X(0) W(1) X(1); K-step 0 is complete once only W(1) X(1) remain
     issue_w(plan_w());
     issue_x(plan_x());
     issue_w(plan_w());
     issue_x(plan_x());
-    issue_x(plan_x());
-    WIssue w_next = plan_w();  // W(2) and X(3): the first issues inside the loop
-    XIssue x_next = plan_x();
+    XIssue x_next = plan_x();  // X(2), issued during K-step 0
+    WIssue w_next;             // W(kt+2), planned during K-step kt
     bf16x8_t fa0[IB], fb0[JB], fa1[IB], fb1[JB];
-    wait_vmcnt<3 * LPO>();
+    wait_vmcnt<2 * LPO>();
     sync();
     int cw = 0, cx = 0;  // ring buffers of the K-step being computed
-    read_frags(cw, cx, 0, fa0, fb0);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        rd_a(cw, 0, i, fa0);
+        if (i < JB) rd_b(cx, 0, i, fb0);
+    }
     for (int kt = 0; kt < nk; ++kt) {
-        read_frags(cw, cx, 1, fa1, fb1);
-        mfmas(fa0, fb0);
-        interleave();
-        // All reads of K-step kt are issued; once they have returned and K-step kt+1 has
-        // landed (only X(kt+2) may be outstanding), the barrier frees K-step kt's buffers.
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+            rd_a(cw, 1, i, fa1);
+            if (i < JB) rd_b(cx, 1, i, fb1);
+            mrow(fa0, fb0, i);
+            if (i & 1) issue_x1(x_next, i >> 1);  // X(kt+2) -> X buffer of K-step kt-1
+            if (i == 2) w_next = plan_w();
+            __builtin_amdgcn_sched_barrier(0);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wait_vmcnt<LPO>();
         sync();
-        issue_w(w_next);  // W(kt+2) -> W buffer of K-step kt
-        issue_x(x_next);  // X(kt+3) -> X buffer of K-step kt
-        cw ^= 1;
-        cx = (cx + 1 == NX_BUF) ? 0 : cx + 1;
+        const int cw1 = (cw + 1 == NW_BUF) ? 0 : cw + 1;
+        const int cx1 = (cx + 1 == NX_BUF) ? 0 : cx + 1;
         // (after the last K-step this reads buffers that are never used)
-        read_frags(cw, cx, 0, fa0, fb0);
-        mfmas(fa1, fb1);
-        w_next = plan_w();
-        x_next = plan_x();
-        interleave();
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+            if ((i & 1) == 0) issue_w1(w_next, i >> 1);  // W(kt+2) -> W buffer of K-step kt
+            rd_a(cw1, 0, i, fa0);
+            if (i < JB) rd_b(cx1, 0, i, fb0);
+            mrow(fa1, fb1, i);
+            if (i == 3) x_next = plan_x();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cw = cw1;
+        cx = cx1;
     }
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
     __syncthreads();  // every wave is done reading the pipeline buffers
@@ -342,80 +340,120 @@ __global__ __launch_bounds__(64 * NW) void map_bf16_kernel(MapArgs a, int L_tgt,
     // ---- epilogue: + bias, target RoPE on keys, bf16 -> LDS (per-wave [TW tokens][128
     // features], padded rows), then full 256-byte rows to the target cache [t][h][p][e] ----
     // Lane holds D[n][p] for p = col (lane & 15) and n = 4 * (lane / 16) + r of each 16 x 16
-    // block: 4 consecutive features -> one 8-byte LDS store.
+    // block: 4 consecutive features -> one 8-byte LDS store.  Each wave stages and stores only
+    // its own rows, so no barrier is needed between the two phases.
     constexpr int HALF = D / 2;
     constexpr int PB = HALF / 16;  // block distance between the two members of a RoPE pair
+    constexpr int NLO = IB / 2;    // blocks holding low members: i = lo_block(li)
+    constexpr int JC = 2;          // token blocks whose table entries are loaded together
     const uint16_t* __restrict__ bias = (const uint16_t*)(tl.kv ? a.bv : a.bk) + (size_t)tl.t * N;
     uint16_t* __restrict__ out = (uint16_t*)(tl.kv ? a.outv : a.outk);
     const int nw = n0 + wn * 128;
     const int pw = p0 + wp * TW;
-    const bool rope = (tl.kv == 0);
     uint32_t* stg = (uint32_t*)smem + wave * (TW * EPI_ROW);
+    auto lo_block = [](int li) { return (li / PB) * 2 * PB + li % PB; };
+    // A block's head lies inside the target cache or wholly past its last head (partial last
+    // feature tile); the latter is neither read from the bias nor stored.
+    auto head_ok = [&](int i) { return nw + (i * 16 / D) * D < N; };
+
+    auto finish = [&](auto rope_tag) {
+        constexpr bool ROPE = decltype(rope_tag)::value;
+        uint2 blo[NLO], bhi[NLO];
 #pragma unroll
-    for (int i = 0; i < IB; ++i) {
-        if ((i / PB) & 1) continue;  // i is the low member; i + PB the high one
-        const int nl = i * 16 + kq * 4;  // feature offset in the wave (low member)
-        const int nlo = min(nw + nl, N - 4), nhi = nlo + HALF;
-        const int elo = nlo % D;
-        const uint2 blo = *(const uint2*)(bias + nlo);
-        const uint2 bhi = *(const uint2*)(bias + nhi);
-        const float bl[4] = {bf16lo(blo.x), bf16hi(blo.x), bf16lo(blo.y), bf16hi(blo.y)};
-        const float bh[4] = {bf16lo(bhi.x), bf16hi(bhi.x), bf16lo(bhi.y), bf16hi(bhi.y)};
+        for (int li = 0; li < NLO; ++li) {
+            const int i = lo_block(li);
+            const int n = nw + i * 16 + kq * 4;
+            blo[li] = head_ok(i) ? *(const uint2*)(bias + n) : make_uint2(0, 0);
+            bhi[li] = head_ok(i) ? *(const uint2*)(bias + n + HALF) : make_uint2(0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const int pl = j * 16 + (lane & 15);
-            const int64_t p = min((int64_t)(pw + pl), T - 1);
-            float ylo[4], yhi[4];
+        for (int jc = 0; jc < JB; jc += JC) {
+            float4 cs[JC][NLO][2];  // (cos, sin) of the lane's 4 pairs per block
+            if constexpr (ROPE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                ylo[r] = acc[i][j][r] + bl[r];
-                yhi[r] = acc[i + PB][j][r] + bh[r];
-            }
-            if (rope) {
-                const float4* cs4 = (const float4*)(a.tab_tgt + p * HALF + elo);
-                const float4 c01 = cs4[0], c23 = cs4[1];
-                const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
-                const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
+                for (int jj = 0; jj < JC; ++jj) {
+                    const int64_t p = min((int64_t)(pw + (jc + jj) * 16 + (lane & 15)), T - 1);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float l = ylo[r], hh = yhi[r];
-                    ylo[r] = fmaf(-hh, ss[r], l * cc[r]);
-                    yhi[r] = fmaf(l, ss[r], hh * cc[r]);
+                    for (int li = 0; li < NLO; ++li) {
+                        const int elo = (lo_block(li) * 16 + kq * 4) % D;
+                        const float4* c4 = (const float4*)(a.tab_tgt + p * HALF + elo);
+                        cs[jj][li][0] = c4[0];
+                        cs[jj][li][1] = c4[1];
+                    }
                 }
             }
-            uint32_t* row = stg + pl * EPI_ROW;
-            *(uint2*)(row + nl / 2) = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
-            *(uint2*)(row + (nl + HALF) / 2) = make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
+#pragma unroll
+            for (int jj = 0; jj < JC; ++jj) {
+                const int j = jc + jj;
+                const int pl = j * 16 + (lane & 15);
+                uint32_t* row = stg + pl * EPI_ROW;
+#pragma unroll
+                for (int li = 0; li < NLO; ++li) {
+                    const int i = lo_block(li);
+                    const int nl = i * 16 + kq * 4;
+                    float ylo[4], yhi[4];
+                    const float bl[4] = {bf16lo(blo[li].x), bf16hi(blo[li].x), bf16lo(blo[li].y), bf16hi(blo[li].y)};
+                    const float bh[4] = {bf16lo(bhi[li].x), bf16hi(bhi[li].x), bf16lo(bhi[li].y), bf16hi(bhi[li].y)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ylo[r] = acc[i][j][r] + bl[r];
+                        yhi[r] = acc[i + PB][j][r] + bh[r];
+                    }
+                    if constexpr (ROPE) {
+                        const float4 c01 = cs[jj][li][0], c23 = cs[jj][li][1];
+                        const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+                        const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float l = ylo[r], hh = yhi[r];
+                            ylo[r] = fmaf(-hh, ss[r], l * cc[r]);
+                            yhi[r] = fmaf(l, ss[r], hh * cc[r]);
+                        }
+                    }
+                    *(uint2*)(row + nl / 2) = make_uint2(pack_bf16(ylo[0], ylo[1]), pack_bf16(ylo[2], ylo[3]));
+                    *(uint2*)(row + (nl + HALF) / 2) =
+                        make_uint2(pack_bf16(yhi[0], yhi[1]), pack_bf16(yhi[2], yhi[3]));
+                }
+            }
+        }
+    };
+    if (tl.kv == 0)
+        finish(BoolTag<true>{});
+    else
+        finish(BoolTag<false>{});
+
+    // 16 lanes per staged row, 16 bytes each: 4 full rows per store instruction.
+    const int c = lane & 15;  // 16-byte chunk = features c*8 .. c*8+7 of the wave's 128
+    if (pw + TW <= T && nw + 128 <= N) {
+        const int h = (nw + c * 8) / D, e = (nw + c * 8) % D;
+        uint16_t* dst = out + (((size_t)tl.t * H + h) * T + pw + (lane >> 4)) * D + e;
+        uint4 v[TW / 4];
+#pragma unroll
+        for (int it = 0; it < TW / 4; ++it) v[it] = *(const uint4*)(stg + (it * 4 + (lane >> 4)) * EPI_ROW + c * 4);
+#pragma unroll
+        for (int it = 0; it < TW / 4; ++it) *(uint4*)(dst + (size_t)it * 4 * D) = v[it];
+    } else {
+#pragma unroll 4
+        for (int it = 0; it < TW / 4; ++it) {
+            const int pl = it * 4 + (lane >> 4);
+            const int64_t p = pw + pl;
+            const int n = nw + c * 8;
+            if (p >= T || n >= N) continue;
+            const int h = n / D, e = n - h * D;
+            const uint4 v = *(const uint4*)(stg + pl * EPI_ROW + c * 4);
+            *(uint4*)(out + (((size_t)tl.t * H + h) * T + p) * D + e) = v;
         }
     }
-    __syncthreads();
-    // 16 lanes per staged row, 16 bytes each: 4 full rows per store instruction.
-#pragma unroll 4
-    for (int it = 0; it < TW / 4; ++it) {
-        const int pl = it * 4 + (lane >> 4);
-        const int c = lane & 15;                    // 16-byte chunk = features c*8 .. c*8+7
-        const int64_t p = pw + pl;
-        const int n = nw + c * 8;
-        if (p >= T || n >= N) continue;
-        const int h = n / D, e = n - h * D;
-        const uint4 v = *(const uint4*)(stg + pl * EPI_ROW + c * 4);
-        *(uint4*)(out + (((size_t)tl.t * H + h) * T + p) * D + e) = v;
-    }
 }
-
-#ifndef KVMAP_MAP_WAVES
-#define KVMAP_MAP_WAVES 8
-#endif
 
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s) {
     const int N = g.N();
     const int nP = (int)((g.T + BN - 1) / BN), nN = (N + BM - 1) / BM;
     const int grid = map_bf16_grid(g.L_tgt, g.T, N);
-    constexpr int NW = KVMAP_MAP_WAVES;
     if (g.d == 128)
-        hipLaunchKernelGGL((map_bf16_kernel<128, NW>), dim3(grid), dim3(64 * NW), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<128>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     else
-        hipLaunchKernelGGL((map_bf16_kernel<64, NW>), dim3(grid), dim3(64 * NW), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<64>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     return hipGetLastError();
 }
 
