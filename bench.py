@@ -13,6 +13,9 @@ roofline   the map GEMM launch: algorithmic FLOP (2*T*F*N per target layer, K an
            bf16 dense MFMA peak; traffic from the committed rocprofv3 counter summary if it
            was taken on the current kernel source
 cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on the host cores
+fit        the fit side on its own workload (262,144 calibration tokens, p 8192, q 1024, batches of
+           4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
+           with HIP events on its stream, and one host ridge solve of the merged state
 """
 
 from __future__ import annotations
@@ -29,6 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "mapped tokens/s (K+V, all target layers) at 14B→32B shape; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_MFMA_TFLOPS = 157.3                    # dense fp32 matrix peak
+PEAK_FP16_TFLOPS = PEAK_BF16_TFLOPS              # dense fp16 matrix peak (same as bf16)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "map_bf16_traffic.json")
 
 
@@ -87,6 +92,70 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
                       f"oracle, {spent:.1f} s; scaled to all target layers"}
 
 
+def fit_cpu_baseline(C, X, Y, budget_s=10.0):
+    """The fp64 oracle's streamed statistics (two-pass per batch, Chan merge) on the first
+    rows of one resident batch until the budget is spent; tokens/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    rows = 1024
+    xs = X[:rows].float().cpu().double().numpy()
+    ys = Y[:rows].float().cpu().double().numpy()
+    st, done, spent = oracle.stats_empty(C.p, C.q), 0, 0.0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        st = oracle.chan_merge(st, oracle.stats_two_pass(xs, ys))
+        spent += time.perf_counter() - t0
+        done += rows
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{done // rows} batches of {rows} tokens (p {C.p}, q {C.q}), fp64 numpy two-pass "
+                      f"statistics + Chan merge, {spent:.1f} s"}
+
+
+def fit_leg(K, batches_timed=16, warmup=2, cpu=True):
+    """Time kvmap_gram on the fit-statistics workload: a few distinct batches resident in HBM,
+    cycled; then one host ridge solve of the merged state."""
+    import torch
+    from synth.device import fit_inputs
+    from synth.workloads import FIT_STATS_CONFIG as C
+    dev = "cuda:0"
+    resident = [(X, Y) for _, X, Y in fit_inputs(C, range(4), dev)]
+    ctx = K.Context(0)
+    st = ctx.gram_state(C.p, C.q)
+    stream = torch.cuda.current_stream()
+    ctx.gram_reset(st, stream)
+    for i in range(warmup):
+        X, Y = resident[i % len(resident)]
+        ctx.gram(st, X, Y, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(batches_timed):
+        X, Y = resident[i % len(resident)]
+        ctx.gram(st, X, Y, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / batches_timed
+    nb, p, q = C.batch, C.p, C.q
+    flops = 2.0 * nb * (p * (p + 1) / 2 + p * q)      # upper triangle of X^T X, all of X^T Y
+    in_bytes = nb * (p + q) * 2
+    t0 = time.perf_counter()
+    W, b = ctx.ridge_solve(st, C.lam, stream)
+    ridge_s = time.perf_counter() - t0
+    ctx.close()
+    log(f"fit: {ms:.3f} ms per batch of {nb}; ridge solve {ridge_s:.2f} s")
+    base = fit_cpu_baseline(C, *resident[0]) if cpu else None
+    return {"cpu_baseline": base, "workload": f"{C.name}: p {p}, q {q}, batches of {nb}, bf16", "ms_per_batch": ms,
+            "tokens_per_s": nb / (ms / 1e3), "ms_per_fit_pass": ms * C.n_batches,
+            "algorithmic_tflops": flops / (ms / 1e3) / 1e12, "flop_per_batch": flops,
+            "input_GBps": in_bytes / (ms / 1e3) / 1e9, "ridge_solve_s": ridge_s,
+            "ridge_flop": p ** 3 / 3 + 2 * p * p * q}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +163,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fit", action="store_true", help="skip the fit-side measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (the reference dispatch for HBM counters)")
     args = ap.parse_args()
@@ -185,6 +255,10 @@ def main():
         log("cpu baseline (fp64 oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     ctx.close()
+    if not args.no_fit:
+        del inp, out_k, out_v
+        torch.cuda.empty_cache()
+        result["fit"] = fit_leg(K, cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 
