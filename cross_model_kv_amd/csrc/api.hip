@@ -89,6 +89,8 @@ struct kvmap_ctx {
     unsigned int* d_count = nullptr;
     float* gram = nullptr;
     size_t gram_floats = 0;
+    uint16_t* gram_split = nullptr;  // bf16 co-moment operands of one sub-batch
+    size_t gram_split_elems = 0;
     hipEvent_t ev[4] = {};
     bool timed = false;
     float last_ms[3] = {0, 0, 0};
@@ -162,6 +164,7 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipHostFree(c->h_sel);
     (void)hipFree(c->d_count);
     (void)hipFree(c->gram);
+    (void)hipFree(c->gram_split);
     for (auto& e : c->ev)
         if (e) (void)hipEventDestroy(e);
     delete c;
@@ -435,15 +438,25 @@ static int validate_state(const kvmap_gram_state* st, const char* which) {
     return KVMAP_OK;
 }
 
-static int ensure_gram_scratch(kvmap_ctx* c, int p, int q) {
+static int ensure_gram_scratch(kvmap_ctx* c, int p, int q, int64_t split_rows) {
     const size_t need = gram_scratch_floats(p, q, kGramMaxSplits);
-    if (need <= c->gram_floats) return KVMAP_OK;
-    KVMAP_HIP(hipDeviceSynchronize());
-    (void)hipFree(c->gram);
-    c->gram = nullptr;
-    c->gram_floats = 0;
-    KVMAP_HIP(hipMalloc((void**)&c->gram, need * sizeof(float)));
-    c->gram_floats = need;
+    if (need > c->gram_floats) {
+        KVMAP_HIP(hipDeviceSynchronize());
+        (void)hipFree(c->gram);
+        c->gram = nullptr;
+        c->gram_floats = 0;
+        KVMAP_HIP(hipMalloc((void**)&c->gram, need * sizeof(float)));
+        c->gram_floats = need;
+    }
+    const size_t need_split = split_rows > 0 ? gram_split_elems(p, q, split_rows) : 0;
+    if (need_split > c->gram_split_elems) {
+        KVMAP_HIP(hipDeviceSynchronize());
+        (void)hipFree(c->gram_split);
+        c->gram_split = nullptr;
+        c->gram_split_elems = 0;
+        KVMAP_HIP(hipMalloc((void**)&c->gram_split, need_split * sizeof(uint16_t)));
+        c->gram_split_elems = need_split;
+    }
     return KVMAP_OK;
 }
 
@@ -458,7 +471,9 @@ static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
     sc.my = base; base += q;
     sc.dx = base; base += p;
     sc.dy = base;
+    sc.split = c->gram_split;
     sc.splits = splits;
+    sc.max_splits = kGramMaxSplits;
     return sc;
 }
 
@@ -489,14 +504,22 @@ extern "C" int kvmap_gram(kvmap_ctx* c, const void* X, const void* Y, int64_t n_
     if ((((uintptr_t)X) | ((uintptr_t)Y)) & 15)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: batch pointers must be 16-byte aligned");
     DeviceGuard g(c->device);
-    r = ensure_gram_scratch(c, st->p, st->q);
-    if (r) return r;
-    int splits = (int)std::min<int64_t>(kGramMaxSplits, std::max<int64_t>(1, n_b / 64));
-    const GramScratch sc = gram_scratch(c, st->p, st->q, splits);
     const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
-    KVMAP_HIP(launch_gram_batch(e, X, Y, n_b, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
-                                st->M_xy, sc, (hipStream_t)stream));
-    st->n += n_b;
+    const int64_t sub = e == Elem::BF16 ? std::min<int64_t>(n_b, kGramSubBatch) : n_b;
+    r = ensure_gram_scratch(c, st->p, st->q, e == Elem::BF16 ? sub : 0);
+    if (r) return r;
+    // sub-batches of at most kGramSubBatch rows, merged in turn (Chan merges compose exactly)
+    const size_t esz = e == Elem::BF16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n_b; r0 += sub) {
+        const int64_t nr = std::min<int64_t>(sub, n_b - r0);
+        const int splits = (int)std::min<int64_t>(kGramMaxSplits, std::max<int64_t>(1, nr / 64));
+        const GramScratch sc = gram_scratch(c, st->p, st->q, splits);
+        const char* xb = (const char*)X + (size_t)r0 * st->p * esz;
+        const char* yb = (const char*)Y + (size_t)r0 * st->q * esz;
+        KVMAP_HIP(launch_gram_batch(e, xb, yb, nr, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
+                                    st->M_xy, sc, (hipStream_t)stream));
+        st->n += nr;
+    }
     return ok();
 }
 
@@ -512,7 +535,7 @@ extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap
     if (dst->M_xx == src->M_xx) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src alias");
     if (src->n == 0) return ok();
     DeviceGuard g(c->device);
-    r = ensure_gram_scratch(c, dst->p, dst->q);
+    r = ensure_gram_scratch(c, dst->p, dst->q, 0);
     if (r) return r;
     const GramScratch sc = gram_scratch(c, dst->p, dst->q, 1);
     KVMAP_HIP(launch_gram_merge(dst->p, dst->q, dst->n, src->n, dst->mean_x, dst->mean_y, dst->M_xx,

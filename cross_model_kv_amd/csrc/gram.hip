@@ -78,11 +78,12 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const void* __restri
 }
 
 // Reduce the split partial sums (float64, fixed order) and derive the phase's outputs.
-//   phase 0: c = sum / n_b
+//   phase 0: c = sum / n_b (rounded to bf16 when round_c: the split co-moment path shifts
+//            bf16 data by a bf16 value, so that x - c is exact)
 //   phase 1: m = sum / n_b; batch mean = c + m; delta = batch mean - mean; mean updated
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     const float* __restrict__ part, int splits, int p, int q, int64_t n_b, int64_t n_old,
-    int phase, float* __restrict__ cx, float* __restrict__ cy, float* __restrict__ mx,
+    int phase, int round_c, float* __restrict__ cx, float* __restrict__ cy, float* __restrict__ mx,
     float* __restrict__ my, float* __restrict__ dx, float* __restrict__ dy,
     float* __restrict__ mean_x, float* __restrict__ mean_y) {
     const int col = blockIdx.x * blockDim.x + threadIdx.x;
@@ -95,7 +96,13 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     const int c = isx ? col : col - p;
     float* cc = isx ? cx : cy;
     if (phase == 0) {
-        cc[c] = (float)mean_b;
+        float cf = (float)mean_b;
+        if (round_c) {
+            uint32_t u = __float_as_uint(cf);
+            u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even, to bf16
+            cf = __uint_as_float(u & 0xffff0000u);
+        }
+        cc[c] = cf;
         return;
     }
     float* mm = isx ? mx : my;
@@ -277,31 +284,40 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
     const dim3 gx((p + CS_TILE - 1) / CS_TILE, sc.splits), gy((q + CS_TILE - 1) / CS_TILE, sc.splits);
     const int stride = p + q;
     const unsigned fin = (unsigned)((stride + 255) / 256);
+    const double n_new = (double)n_old + (double)n_b;
+    const float coef = (float)((double)n_old * (double)n_b / n_new);
+    const int fresh = (n_old == 0);
+    if (bf) {
+        // column sums -> c = bf16(mean); split (d, hi, lo, transposed) with the sums of d;
+        // m, delta, mean; co-moments on the bf16 matrix cores
+        hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, nullptr, sc.part, stride, 0);
+        hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, nullptr, sc.part, stride, p);
+        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q, n_b, n_old,
+                           0, 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+        const int ss = gram_split_blocks(n_b, sc.max_splits);
+        uint16_t* Sx = sc.split;
+        uint16_t* Sy = sc.split + gram_split_elems(p, 0, n_b);
+        hipError_t err = launch_gram_split(X, n_b, p, sc.cx, Sx, sc.part, stride, 0, ss, s);
+        if (err != hipSuccess) return err;
+        err = launch_gram_split(Y, n_b, q, sc.cy, Sy, sc.part, stride, p, ss, s);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, ss, p, q, n_b, n_old, 1, 0,
+                           sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+        return launch_gram_x3(Sx, Sy, n_b, p, q, sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, s);
+    }
     for (int phase = 0; phase < 2; ++phase) {
         const float* shx = phase ? sc.cx : nullptr;
         const float* shy = phase ? sc.cy : nullptr;
-        if (bf) {
-            hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
-            hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
-        } else {
-            hipLaunchKernelGGL(colsum_kernel<false>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
-            hipLaunchKernelGGL(colsum_kernel<false>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
-        }
+        hipLaunchKernelGGL(colsum_kernel<false>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
+        hipLaunchKernelGGL(colsum_kernel<false>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
         hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q,
-                           n_b, n_old, phase, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+                           n_b, n_old, phase, 0, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
     }
     const int nTx = (p + GT - 1) / GT, nTy = (q + GT - 1) / GT;
     const int nXX = nTx * (nTx + 1) / 2;
     const int blocks = nXX + nTx * nTy;
-    const double n_new = (double)n_old + (double)n_b;
-    const float coef = (float)((double)n_old * (double)n_b / n_new);
-    const int fresh = (n_old == 0);
-    if (bf)
-        hipLaunchKernelGGL(gram_kernel<true>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
-                           sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
-    else
-        hipLaunchKernelGGL(gram_kernel<false>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
-                           sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
+    hipLaunchKernelGGL(gram_kernel<false>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
+                       sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
     return hipGetLastError();
 }
 

@@ -52,13 +52,25 @@ struct GramScratch {
     float* my;     // [q]
     float* dx;     // [p]  delta = batch mean - running mean
     float* dy;     // [q]
-    int splits;
+    uint16_t* split;  // bf16 path: [p + q][ceil(n_b / 32)][64] shifted, split, transposed batch
+    int splits;       // row splits of the column sums
+    int max_splits;   // rows of `part`
 };
 // Sizes (floats) of the scratch for p, q.
 size_t gram_scratch_floats(int p, int q, int splits);
 hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
                              int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
                              float* M_xy, const GramScratch& sc, hipStream_t s);
+// Rows per kvmap_gram sub-batch: larger batches are merged in pieces of at most this many
+// rows (the split operands' scratch and 32-bit tile offsets are sized for it).
+constexpr int64_t kGramSubBatch = 16384;
+size_t gram_split_elems(int p, int q, int64_t n_b);  // uint16 elements of `split` for n_b rows
+int gram_split_blocks(int64_t n_b, int max_splits);
+hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,
+                             float* part, int part_stride, int col_off, int splits, hipStream_t s);
+hipError_t launch_gram_x3(const uint16_t* Sx, const uint16_t* Sy, int64_t n_b, int p, int q, const float* mx,
+                          const float* my, const float* dx, const float* dy, float coef, int fresh,
+                          float* M_xx, float* M_xy, hipStream_t s);
 hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
                              float* mean_y, float* M_xx, float* M_xy, const float* s_mean_x,
                              const float* s_mean_y, const float* s_M_xx, const float* s_M_xy,

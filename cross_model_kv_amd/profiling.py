@@ -22,7 +22,7 @@ import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("gemm_bf16.hip", "common.h")]
+GEMM_SOURCES = [os.path.join(HERE, "csrc", n) for n in ("gemm_bf16.hip", "lds_dma.h", "common.h")]
 COPY_BYTES = 1 << 30
 
 

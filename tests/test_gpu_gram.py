@@ -77,6 +77,17 @@ def test_gram_ragged_batches(ctx, dtype):
     _check_state(st, ref, f"ragged {dtype}")
 
 
+def test_gram_call_larger_than_sub_batch(ctx):
+    """One call of 16384 + 1000 + 3 rows (the library merges it in sub-batches of at most
+    16384 rows), p = 264, q = 36 (q not a multiple of 8), bf16."""
+    cfg = FIT_STATS_CONFIG.replace(cid=402, p=264, q=36, n_tokens=17387, batch=4096)
+    (X, Y), = _batches(cfg, [17387])
+    st = ctx.gram_state(cfg.p, cfg.q)
+    ctx.gram_reset(st)
+    ctx.gram(st, _dev(X, "bf16"), _dev(Y, "bf16"))
+    _check_state(st, oracle.stats_two_pass(X, Y), "one call over sub-batches")
+
+
 def test_gram_merge_and_resume(ctx):
     """Two states over disjoint halves merged = one state over the stream; an empty state merges
     as the identity; a state is a checkpoint (continue streaming after a merge)."""
