@@ -46,7 +46,7 @@ __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_fl
 
 // ---- 1: shift, split, transpose -------------------------------------------------------
 // Workgroup: 256 columns; it walks token blocks blockIdx.y, + gridDim.y, ...  A thread reads
-// 8 adjacent columns (16 bytes) of 4 rows per block; the block goes through LDS as
+// 8 adjacent columns (two 8-byte halves) of 4 rows per block; the block goes through LDS as
 // (hi | lo << 16) per (column, token) and leaves as whole 128-byte lines, 8 lanes per line.
 __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restrict__ A, int64_t n_b, int cols,
                                                          int nkb, const float* __restrict__ c,
