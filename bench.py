@@ -13,6 +13,8 @@ roofline   the map GEMM launch: algorithmic FLOP (2*T*F*N per target layer, K an
            bf16 dense MFMA peak; traffic from the committed rocprofv3 counter summary if it
            was taken on the current kernel source
 cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on the host cores
+recode     kvmap_recode (identity map: RoPE re-encode, one rotation per pair) of the workload's
+           whole source key cache, timed with HIP events; GB/s against the 8 TB/s HBM peak
 fit        the fit side on its own workload (262,144 calibration tokens, p 8192, q 1024, batches of
            4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
            with HIP events on its stream, and one host ridge solve of the merged state
@@ -92,6 +94,30 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
                       f"oracle, {spent:.1f} s; scaled to all target layers"}
 
 
+def recode_leg(K, ctx, cfg, src, iters=10, warmup=2):
+    """kvmap_recode of the whole source key cache [L_src][H][T][d] into a fresh buffer."""
+    import torch
+    out = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ctx.recode(src, cfg.theta_src, cfg.theta_tgt, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        ctx.recode(src, cfg.theta_src, cfg.theta_tgt, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 2 * src.numel() * src.element_size()
+    del out
+    log(f"recode: {ms:.3f} ms for {nbytes / 1e9:.2f} GB")
+    return {"workload": f"{cfg.name} source keys [{cfg.L_src}][{cfg.H}][{cfg.T}][{cfg.d}] {cfg.dtype}, "
+                        f"theta {cfg.theta_src:g} -> {cfg.theta_tgt:g}",
+            "ms": ms, "bytes": nbytes, "GBps": nbytes / (ms / 1e3) / 1e9,
+            "frac_hbm": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+
+
 def fit_cpu_baseline(C, X, Y, budget_s=10.0):
     """The fp64 oracle's streamed statistics (two-pass per batch, Chan merge) on the first
     rows of one resident batch until the budget is spent; tokens/s."""
@@ -164,6 +190,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fit", action="store_true", help="skip the fit-side measurement")
+    ap.add_argument("--no-recode", action="store_true", help="skip the RoPE-recode measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (the reference dispatch for HBM counters)")
     args = ap.parse_args()
@@ -254,6 +281,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    if not args.no_recode:
+        result["recode"] = recode_leg(K, ctx, cfg, inp["src_k"])
     ctx.close()
     if not args.no_fit:
         del inp, out_k, out_v

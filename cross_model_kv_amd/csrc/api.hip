@@ -62,6 +62,9 @@ constexpr int kGramMaxSplits = 64;
 struct RopeEntry {
     double theta = 0;
     int64_t pos0 = 0;
+    bool diff = false;  // recode table of (theta, pos0) -> (theta2, pos0_2)
+    double theta2 = 0;
+    int64_t pos0_2 = 0;
     int d = 0;
     int64_t T_cap = 0;
     float2* tab = nullptr;
@@ -87,6 +90,7 @@ struct kvmap_ctx {
     int32_t* h_sel = nullptr;     // pinned staging
     std::vector<int32_t> sel_cache;
     unsigned int* d_count = nullptr;
+    int32_t* d_zero = nullptr;    // the one-entry layer list {0} of kvmap_recode
     float* gram = nullptr;
     size_t gram_floats = 0;
     uint16_t* gram_split = nullptr;  // bf16 co-moment operands of one sub-batch
@@ -146,9 +150,15 @@ extern "C" int kvmap_create(kvmap_ctx** out, int device) {
             return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipEventCreate failed");
         }
     }
-    if (hipMalloc((void**)&c->d_count, sizeof(unsigned int)) != hipSuccess) {
+    const int32_t zero = 0;
+    if (hipMalloc((void**)&c->d_count, sizeof(unsigned int)) != hipSuccess ||
+        hipMalloc((void**)&c->d_zero, sizeof(int32_t)) != hipSuccess) {
         kvmap_destroy(c);
         return fail(KVMAP_ERR_OUT_OF_MEMORY, "kvmap_create: hipMalloc failed");
+    }
+    if (hipMemcpy(c->d_zero, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) {
+        kvmap_destroy(c);
+        return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipMemcpy failed");
     }
     *out = c;
     return ok();
@@ -163,6 +173,7 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipFree(c->d_sel);
     (void)hipHostFree(c->h_sel);
     (void)hipFree(c->d_count);
+    (void)hipFree(c->d_zero);
     (void)hipFree(c->gram);
     (void)hipFree(c->gram_split);
     for (auto& e : c->ev)
@@ -235,11 +246,15 @@ extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_se
 // apply
 // ---------------------------------------------------------------------------------------
 
+// Cached fp32 tables built in fp64: a RoPE table of r, or (r2 given) the recode table
+// from r to r2.
 static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, hipStream_t s,
-                          float2** out, bool* built) {
+                          float2** out, bool* built, const kvmap_rope* r2 = nullptr) {
     *built = false;
+    const bool diff = r2 != nullptr;
     for (auto& e : c->ropes) {
-        if (e.theta == r->theta && e.pos0 == r->pos0 && e.d == d && e.T_cap >= T) {
+        if (e.theta == r->theta && e.pos0 == r->pos0 && e.d == d && e.T_cap >= T && e.diff == diff &&
+            (!diff || (e.theta2 == r2->theta && e.pos0_2 == r2->pos0))) {
             e.last_use = ++c->clock;
             *out = e.tab;
             return KVMAP_OK;
@@ -256,10 +271,14 @@ static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, h
     RopeEntry e;
     e.theta = r->theta;
     e.pos0 = r->pos0;
+    e.diff = diff;
+    e.theta2 = diff ? r2->theta : 0.0;
+    e.pos0_2 = diff ? r2->pos0 : 0;
     e.d = d;
     e.T_cap = T;
     KVMAP_HIP(hipMalloc((void**)&e.tab, (size_t)T * (d / 2) * sizeof(float2)));
-    hipError_t err = launch_rope_table(e.tab, T, d, r->theta, r->pos0, s);
+    hipError_t err = diff ? launch_rope_diff_table(e.tab, T, d, r->theta, r->pos0, r2->theta, r2->pos0, s)
+                          : launch_rope_table(e.tab, T, d, r->theta, r->pos0, s);
     if (err != hipSuccess) {
         (void)hipFree(e.tab);
         return fail(KVMAP_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(err));
@@ -394,7 +413,7 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
 
     if (flags & KVMAP_FLAG_CHECK_FINITE) {
         const int64_t n = (int64_t)g.L_tgt * g.H * g.T * g.d;
-        KVMAP_HIP(hipMemsetAsync(c->d_count, 0, sizeof(unsigned int), s));
+        KVMAP_HIP(launch_fill_zero((float*)c->d_count, 1, s));  // a kernel, not a memset node
         KVMAP_HIP(launch_count_nonfinite(e, tgt_k, n, c->d_count, s));
         KVMAP_HIP(launch_count_nonfinite(e, tgt_v, n, c->d_count, s));
         unsigned int h = 0;
@@ -402,6 +421,44 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
         KVMAP_HIP(hipStreamSynchronize(s));
         if (h) return fail(KVMAP_ERR_NONFINITE, "kvmap_apply: %u non-finite values in the mapped cache", h);
     }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------------------
+// RoPE recode (identity map: one rotation per pair)
+// ---------------------------------------------------------------------------------------
+
+extern "C" int kvmap_recode(kvmap_ctx* c, int32_t rows, int64_t T, int32_t head_dim, int32_t dtype,
+                            const void* src, void* dst, const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
+                            void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: ctx is NULL");
+    if (rows < 1 || T < 1 || T > (int64_t(1) << 31) || (int64_t)rows * T > (int64_t(1) << 40))
+        return fail(KVMAP_ERR_SHAPE, "kvmap_recode: rows=%d, T=%lld out of range", (int)rows, (long long)T);
+    int st = validate_rope(rope_src, "source", T);
+    if (st) return st;
+    st = validate_rope(rope_tgt, "target", T);
+    if (st) return st;
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_recode: dtype %d unknown", (int)dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_recode: head_dim %d (64 or 128 supported)", (int)head_dim);
+    if (!src || !dst) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: NULL device pointer");
+    if ((((uintptr_t)src) | ((uintptr_t)dst)) & 15)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: pointers must be 16-byte aligned");
+    const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    const size_t bytes = (size_t)rows * (size_t)T * head_dim * es;
+    if (ranges_overlap(src, bytes, dst, bytes)) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: src and dst overlap");
+    DeviceGuard guard(c->device);
+    if (!guard.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_recode: hipSetDevice(%d) failed", c->device);
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = nullptr;
+    bool built = false;
+    st = get_rope_table(c, rope_src, head_dim, T, s, &tab, &built, rope_tgt);
+    if (st) return st;
+    // all rows as the heads of one layer, listed by the single entry {0}
+    const ApplyGeom g{1, 1, rows, head_dim, 1, T};
+    const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
+    KVMAP_HIP(launch_derope(e, src, dst, c->d_zero, 1, g, tab, s));
     return ok();
 }
 

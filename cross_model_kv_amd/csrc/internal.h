@@ -22,7 +22,12 @@ struct ApplyGeom {
 hipError_t launch_rope_table(float2* tab, int64_t T, int d, double theta, int64_t pos0,
                              hipStream_t s);
 
-// ws[l][h][t][:] = strip(src[l][h][t][:]) for every l in layers[0..n_layers).
+// tab[t][i] = (cos A, sin A), A = (pos0_s + t) theta_s^(-2i/d) - (pos0_t + t) theta_t^(-2i/d),
+// formed in float64: rotating by -A re-encodes a source-roped key to the target RoPE.
+hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, double theta_s, int64_t pos0_s,
+                                  double theta_t, int64_t pos0_t, hipStream_t s);
+// ws[l][h][t][:] = every pair of src[l][h][t][:] rotated by -a (a from tab), for every l in
+// layers[0..n_layers).
 hipError_t launch_derope(Elem e, const void* src, void* ws, const int32_t* layers, int n_layers,
                          const ApplyGeom& g, const float2* tab, hipStream_t s);
 

@@ -30,6 +30,35 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
     tab[idx] = make_float2((float)c, (float)s);
 }
 
+// Recode table: (cos A, sin A) with A = (pos0_s + t) f_s,i - (pos0_t + t) f_t,i, formed in
+// float64 (the two products reach ~3e4 rad at 32K positions; their difference in fp32 would
+// be off by ~1e-3).  Rotating a source-roped key by -A strips the source RoPE and applies the
+// target one in a single rotation (VeloxQuant-MLX "Cross-Model KV Transfer", section "Metal
+// kernel": both rotations act on the same pair at the same position).
+__global__ __launch_bounds__(256) void rope_diff_table_kernel(float2* __restrict__ tab, int64_t T, int d,
+                                                               double theta_s, int64_t pos0_s, double theta_t,
+                                                               int64_t pos0_t) {
+    const int half = d / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T * half) return;
+    const int64_t t = idx / half;
+    const int i = (int)(idx - t * half);
+    const double e = -2.0 * (double)i / (double)d;
+    const double a = (double)(pos0_s + t) * pow(theta_s, e) - (double)(pos0_t + t) * pow(theta_t, e);
+    double s, c;
+    sincos(a, &s, &c);
+    tab[idx] = make_float2((float)c, (float)s);
+}
+
+hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, double theta_s, int64_t pos0_s,
+                                  double theta_t, int64_t pos0_t, hipStream_t s) {
+    const int64_t n = T * (d / 2);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(rope_diff_table_kernel, dim3(blocks), dim3(256), 0, s, tab, T, d, theta_s, pos0_s, theta_t,
+                       pos0_t);
+    return hipGetLastError();
+}
+
 hipError_t launch_rope_table(float2* tab, int64_t T, int d, double theta, int64_t pos0,
                              hipStream_t s) {
     const int64_t n = T * (d / 2);

@@ -70,6 +70,9 @@ _SIGS = {
                                    ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32]),
     "kvmap_last_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int]),
+    "kvmap_recode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
+                                    ctypes.c_void_p]),
     "kvmap_gram_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
     "kvmap_gram": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
@@ -280,6 +283,27 @@ class Context:
         ms = (ctypes.c_float * 3)()
         _check(lib().kvmap_last_timings(self._h, ms, 3), "kvmap_last_timings")
         return float(ms[0]), float(ms[1]), float(ms[2])
+
+    def recode(self, src, theta_src: float, theta_tgt: float, pos0_src: int = 0, pos0_tgt: int | None = None,
+               out=None, stream=None, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT):
+        """kvmap_recode: re-encode keys src [..., T, d] (device, bf16 or fp32; leading dims
+        are the rows) from RoPE (theta_src, pos0_src) to (theta_tgt, pos0_tgt).  Returns out
+        (allocated if not given), of src's shape and dtype."""
+        torch = _torch()
+        if src.dim() < 2:
+            raise ValueError("src must be [..., T, d]")
+        T, d = int(src.shape[-2]), int(src.shape[-1])
+        rows = int(src.numel() // max(1, T * d))
+        if out is None:
+            out = torch.empty_like(src)
+        if tuple(out.shape) != tuple(src.shape) or out.dtype != src.dtype:
+            raise ValueError("out must match src's shape and dtype")
+        rs = Rope(float(theta_src), int(pos0_src), int(style_src))
+        rt = Rope(float(theta_tgt), int(pos0_src if pos0_tgt is None else pos0_tgt), int(style_tgt))
+        _check(lib().kvmap_recode(self._h, rows, T, d, _dtype_code(src), _dev_ptr(src, "src"), _dev_ptr(out, "out"),
+                                  ctypes.byref(rs), ctypes.byref(rt), _stream_handle(stream, src.device)),
+               "kvmap_recode")
+        return out
 
     # ---- fit-side statistics ---------------------------------------------------------
     def gram_state(self, p: int, q: int) -> GramState:

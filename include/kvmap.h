@@ -164,6 +164,27 @@ int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
  * Synchronises on the events.  n_ms must be >= 3. */
 int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
 
+/* ---- RoPE recode (identity map) ---------------------------------------------------- */
+
+/* Re-encode a key cache from the source model's RoPE to the target's without a map:
+ *   dst[r][t][:] = rope(strip(src[r][t][:], pos0_s + t, theta_s), pos0_t + t, theta_t)
+ * for every row r (layers x heads flattened), which is one rotation of every pair
+ * (e, e + d/2) by (pos0_t + t) f_t,e - (pos0_s + t) f_s,e, f_e = theta^(-2e/d)
+ * (VeloxQuant-MLX "Cross-Model KV Transfer", section "Metal kernel": the strip and the
+ * target rotation act on the same pair at the same position and compose into one rotation
+ * by the per-dimension angle difference).  The angle is formed in float64 into a cached fp32
+ * cos/sin table [T][d/2] (built on first use of the (theta, pos0) pair, like the apply's
+ * tables); the rotation runs in fp32 and is rounded once to `dtype`.
+ *   src, dst  device [rows][T][head_dim], row-major, bf16 or fp32, 16-byte aligned, not
+ *             overlapping (dst is fully overwritten)
+ *   head_dim  64 or 128;  rope styles must be half-split;  T <= 2^31, pos0 + T <= 2^31
+ * Asynchronous on `stream`.  Errors: INVALID_ARGUMENT (NULLs, alignment, overlap, bad rope
+ * fields), UNSUPPORTED (dtype, head_dim, rope style), SHAPE (rows < 1, T < 1 or too large);
+ * nothing is written on a refused call. */
+int kvmap_recode(kvmap_ctx* ctx, int32_t rows, int64_t T, int32_t head_dim, int32_t dtype,
+                 const void* src, void* dst, const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
+                 void* stream);
+
 /* ---- fit-side statistics ----------------------------------------------------------- */
 
 /* Centered sufficient statistics of a stream of (x, y) rows, x in R^p, y in R^q:
