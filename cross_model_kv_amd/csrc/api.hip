@@ -335,9 +335,21 @@ static int ensure_workspace(kvmap_ctx* c, size_t bytes) {
     return KVMAP_OK;
 }
 
-static size_t workspace_bytes(const kvmap_dims* d) {
+// De-rotated source keys, then (short bf16 caches) the split-K partial sums.
+static size_t derope_bytes(const kvmap_dims* d) {
     const size_t es = d->dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
-    return (size_t)d->L_src * d->H_kv * (size_t)d->T * d->head_dim * es;
+    return ((size_t)d->L_src * d->H_kv * (size_t)d->T * d->head_dim * es + 255) & ~(size_t)255;
+}
+
+static bool small_path(const kvmap_dims* d) { return d->dtype == KVMAP_DTYPE_BF16 && d->T <= kSmallT; }
+
+static size_t workspace_bytes(const kvmap_dims* d) {
+    size_t b = derope_bytes(d);
+    if (small_path(d)) {
+        const ApplyGeom g{d->L_src, d->L_tgt, d->H_kv, d->head_dim, d->k, d->T};
+        b += map_bf16_small_plan(g).part_bytes;
+    }
+    return b;
 }
 
 extern "C" int kvmap_reserve(kvmap_ctx* c, const kvmap_dims* d) {
@@ -401,7 +413,9 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     KVMAP_HIP(launch_derope(e, src_k, c->ws, c->d_sel + (size_t)g.L_tgt * g.k, n_used, g, tab_src, s));
     if (timing) KVMAP_HIP(hipEventRecord(c->ev[2], s));
     MapArgs a{c->ws, src_v, c->d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
-    if (e == Elem::BF16)
+    if (small_path(d))
+        KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g), (float*)((char*)c->ws + derope_bytes(d)), s));
+    else if (e == Elem::BF16)
         KVMAP_HIP(launch_map_bf16(a, g, s));
     else
         KVMAP_HIP(launch_map_f32(a, g, s));

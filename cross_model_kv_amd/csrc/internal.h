@@ -44,6 +44,21 @@ struct MapArgs {
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 
+// Short caches (gemm_bf16_small.hip): bf16 applies with T <= kSmallT tokens take the split-K
+// path (fp32 partial sums in `part`, then a deterministic reduce with bias and target RoPE);
+// measured faster than the long-cache kernel up to 64 tokens and slower from 128 on.
+#ifndef KVMAP_SMALL_T
+#define KVMAP_SMALL_T 64
+#endif
+constexpr int64_t kSmallT = KVMAP_SMALL_T;
+struct SmallPlan {
+    int nN, nP, KS, kps;  // feature tiles, token tiles, K splits, K-steps per split
+    size_t part_bytes;    // fp32 partial sums [KS][L_tgt][2][T][N]
+};
+SmallPlan map_bf16_small_plan(const ApplyGeom& g);
+hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,
+                                 hipStream_t s);
+
 // Count of non-finite elements (bf16 or f32) added atomically into *count.
 hipError_t launch_count_nonfinite(Elem e, const void* p, int64_t n, unsigned int* count,
                                   hipStream_t s);

@@ -49,12 +49,11 @@ __device__ __forceinline__ uint32_t uniform_select(uint32_t c, uint32_t a, uint3
     return r;
 }
 
+// Wait until at most N of this wave's vector memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N == 0 || N == 4 || N == 8, "vmcnt");  // per-wave loads still in flight
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 }  // namespace

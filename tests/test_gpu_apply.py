@@ -193,3 +193,36 @@ def test_full_size_sampled(ctx, cid):
     # determinism at full size
     ok2, ov2 = _run(ctx, cfg, inp)
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
+
+
+# ---- short caches (T <= 256: the split-K path with a separate reduce) -------------------
+
+SHORT = [
+    # 1.5 feature tiles (H=3), 64 tokens exactly one token tile, L_tgt > L_src
+    ApplyConfig(221, "short-T64-H3", 5, 7, 3, 128, 64, 2, 1.0e4, 1.0e6, "bf16", 0.5),
+    # d = 64, ragged 37 tokens, continuation offset, k = 3
+    ApplyConfig(222, "short-d64-T37-pos0", 4, 3, 2, 64, 37, 3, 1.0e6, 5.0e5, "bf16", 0.5, pos0=1000),
+    # 256 tokens (the largest short cache): four token tiles, K split 1
+    ApplyConfig(223, "short-T256-H8", 4, 2, 8, 128, 256, 2, 1.0e6, 1.0e6, "bf16", 0.5),
+    # one head of d = 64 (N = 64, a partial feature tile), k = 5 (320 features: 5 K-steps)
+    ApplyConfig(224, "short-H1-d64-k5-T129", 6, 2, 1, 64, 129, 5, 1.0e4, 1.0e4, "bf16", 0.5),
+]
+
+
+@pytest.mark.parametrize("cfg", SHORT, ids=lambda c: c.name)
+def test_short_caches(ctx, cfg):
+    _full_check(ctx, cfg)
+
+
+def test_short_cache_full_layer_shape(ctx):
+    """The Qwen3 14B->32B layer shape (L 40->64, H 8, d 128, k 8) at T = 64, where the K
+    reduction is split across workgroups: every row of sampled target layers against the
+    oracle, and bit-identical outputs on a second call (the partial sums are added in a
+    fixed order)."""
+    cfg = APPLY_CONFIGS[3].replace(cid=225, name="qwen3-14b-to-32b-T64", T=64)
+    inp = apply_inputs(cfg, "cuda:0")
+    ok_, ov_ = _run(ctx, cfg, inp)
+    targets = [0, 21, 42, 63]
+    _check_sampled(cfg, inp, ok_, ov_, targets, np.arange(cfg.T))
+    ok2, ov2 = _run(ctx, cfg, inp)
+    assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
