@@ -17,7 +17,8 @@ recode     kvmap_recode (identity map: RoPE re-encode, one rotation per pair) of
            whole source key cache, timed with HIP events; GB/s against the 8 TB/s HBM peak
 fit        the fit side on its own workload (262,144 calibration tokens, p 8192, q 1024, batches of
            4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
-           with HIP events on its stream, and one host ridge solve of the merged state
+           with HIP events on its stream; one ridge solve of the merged state on the host and one
+           on the device (fp64, W written in bf16 output-major)
 """
 
 from __future__ import annotations
@@ -172,13 +173,21 @@ def fit_leg(K, batches_timed=16, warmup=2, cpu=True):
     t0 = time.perf_counter()
     W, b = ctx.ridge_solve(st, C.lam, stream)
     ridge_s = time.perf_counter() - t0
+    ctx.ridge_solve_device(st, C.lam, dtype=torch.bfloat16, stream=stream)  # first call sizes the scratch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ctx.ridge_solve_device(st, C.lam, dtype=torch.bfloat16, stream=stream)
+    ridge_dev_s = time.perf_counter() - t0
     ctx.close()
-    log(f"fit: {ms:.3f} ms per batch of {nb}; ridge solve {ridge_s:.2f} s")
+    log(f"fit: {ms:.3f} ms per batch of {nb}; ridge solve {ridge_s:.2f} s on the host, "
+        f"{ridge_dev_s * 1e3:.1f} ms on the device")
     base = fit_cpu_baseline(C, *resident[0]) if cpu else None
     return {"cpu_baseline": base, "workload": f"{C.name}: p {p}, q {q}, batches of {nb}, bf16", "ms_per_batch": ms,
             "tokens_per_s": nb / (ms / 1e3), "ms_per_fit_pass": ms * C.n_batches,
             "algorithmic_tflops": flops / (ms / 1e3) / 1e12, "flop_per_batch": flops,
             "input_GBps": in_bytes / (ms / 1e3) / 1e9, "ridge_solve_s": ridge_s,
+            "ridge_solve_device_s": ridge_dev_s,
+            "ridge_device_fp64_tflops": (p ** 3 / 3 + 2 * p * p * q) / ridge_dev_s / 1e12,
             "ridge_flop": p ** 3 / 3 + 2 * p * p * q}
 
 

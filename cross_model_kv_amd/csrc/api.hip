@@ -91,6 +91,8 @@ struct kvmap_ctx {
     std::vector<int32_t> sel_cache;
     unsigned int* d_count = nullptr;
     int32_t* d_zero = nullptr;    // the one-entry layer list {0} of kvmap_recode
+    void* ridge = nullptr;        // fp64 factor and right-hand sides of the device ridge solve
+    size_t ridge_bytes = 0;
     float* gram = nullptr;
     size_t gram_floats = 0;
     uint16_t* gram_split = nullptr;  // bf16 co-moment operands of one sub-batch
@@ -174,6 +176,7 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipHostFree(c->h_sel);
     (void)hipFree(c->d_count);
     (void)hipFree(c->d_zero);
+    (void)hipFree(c->ridge);
     (void)hipFree(c->gram);
     (void)hipFree(c->gram_split);
     for (auto& e : c->ev)
@@ -630,6 +633,48 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_host: lambda must be finite and >= 0");
     if (ridge_solve_f64(p, q, mean_x, mean_y, M_xx, M_xy, lambda, W_out, b_out, n_threads))
         return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_host: M_xx + lambda I is not positive definite");
+    return ok();
+}
+
+extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, void* W_out,
+                                        void* b_out, int32_t dtype, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: ctx is NULL");
+    int r = validate_state(st, "kvmap_ridge_solve_device");
+    if (r) return r;
+    if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: NULL output");
+    if (!(lambda >= 0.0) || !std::isfinite(lambda))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: lambda must be finite and >= 0");
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_ridge_solve_device: dtype %d unknown", (int)dtype);
+    const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    const size_t wb = (size_t)st->p * st->q * es, bb = (size_t)st->q * es;
+    if ((((uintptr_t)W_out) | ((uintptr_t)b_out)) & 3)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: outputs must be 4-byte aligned");
+    if (ranges_overlap(W_out, wb, b_out, bb)) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: W_out and b_out overlap");
+    const void* ins[4] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy};
+    const size_t insz[4] = {(size_t)st->p * 4, (size_t)st->q * 4, (size_t)st->p * st->p * 4, (size_t)st->p * st->q * 4};
+    for (int i = 0; i < 4; ++i)
+        if (ranges_overlap(ins[i], insz[i], W_out, wb) || ranges_overlap(ins[i], insz[i], b_out, bb))
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: an output overlaps the state");
+    DeviceGuard g(c->device);
+    const size_t need = ridge_dev_scratch_bytes(st->p, st->q);
+    if (need > c->ridge_bytes) {
+        KVMAP_HIP(hipDeviceSynchronize());
+        (void)hipFree(c->ridge);
+        c->ridge = nullptr;
+        c->ridge_bytes = 0;
+        KVMAP_HIP(hipMalloc(&c->ridge, need));
+        c->ridge_bytes = need;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    int* bad = (int*)((char*)c->ridge + need - 256);  // pivot flag, in the scratch's last 256 bytes
+    KVMAP_HIP(launch_fill_zero((float*)bad, 1, s));
+    KVMAP_HIP(launch_ridge_dev(st->p, st->q, st->mean_x, st->mean_y, st->M_xx, st->M_xy, lambda, W_out, b_out,
+                               dtype == KVMAP_DTYPE_BF16, c->ridge, bad, s));
+    int h = 0;
+    KVMAP_HIP(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipStreamSynchronize(s));
+    if (h) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_device: M_xx + lambda I is not positive definite");
     return ok();
 }
 

@@ -97,6 +97,12 @@ hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* 
                              const GramScratch& sc, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
+// ---- ridge solve on the device (ridge_dev.hip), float64 --------------------------------
+size_t ridge_dev_scratch_bytes(int p, int q);
+hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
+                            const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
+                            void* scratch, int* bad, hipStream_t s);
+
 }  // namespace kvmap
 
 #include "ridge.h"

@@ -83,6 +83,8 @@ _SIGS = {
                                               ctypes.c_void_p, ctypes.c_int]),
     "kvmap_ridge_solve": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvmap_ridge_solve_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
 }
 
 
@@ -327,6 +329,25 @@ class Context:
     def gram_merge(self, dst: GramState, src: GramState, stream=None):
         _check(lib().kvmap_gram_merge(self._h, ctypes.byref(dst.c), ctypes.byref(src.c),
                                       _stream_handle(stream, dst.device)), "kvmap_gram_merge")
+
+    def ridge_solve_device(self, st: GramState, lam: float, W_out=None, b_out=None, dtype=None, stream=None):
+        """kvmap_ridge_solve_device: (W [q][p] output-major, b [q]) device tensors in bf16 or fp32
+        (allocated if not given; dtype defaults to that of W_out, else fp32)."""
+        torch = _torch()
+        if dtype is None:
+            dtype = W_out.dtype if W_out is not None else torch.float32
+        if W_out is None:
+            W_out = torch.empty((st.q, st.p), dtype=dtype, device=st.device)
+        if b_out is None:
+            b_out = torch.empty((st.q,), dtype=dtype, device=st.device)
+        if tuple(W_out.shape) != (st.q, st.p) or tuple(b_out.shape) != (st.q,):
+            raise ValueError("W_out must be [q][p] and b_out [q]")
+        if W_out.dtype != dtype or b_out.dtype != dtype:
+            raise TypeError("W_out and b_out must share the dtype")
+        _check(lib().kvmap_ridge_solve_device(self._h, ctypes.byref(st.c), float(lam), _dev_ptr(W_out, "W_out"),
+                                              _dev_ptr(b_out, "b_out"), _dtype_code(W_out),
+                                              _stream_handle(stream, st.device)), "kvmap_ridge_solve_device")
+        return W_out, b_out
 
     def ridge_solve(self, st: GramState, lam: float, stream=None):
         """kvmap_ridge_solve: (W [q][p] output-major float32, b [q]) on the host."""

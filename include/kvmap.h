@@ -244,6 +244,20 @@ int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x, const floa
 int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
                       float* W_out, float* b_out, void* stream);
 
+/* Same solve on the device in float64 (no copy of the statistics to the host): blocked
+ * Cholesky of sym(M_xx) + lambda I (read from M_xx's upper triangle) with 64-wide blocks,
+ * then forward and back substitution for the q right-hand sides, then b = mean_y - mean_x W.
+ *   W_out  device [q][p] output-major (the layout kvmap_apply takes for one target layer),
+ *   b_out  device [q], both in `dtype` (bf16: rounded to nearest even; fp32), 4-byte aligned,
+ *          not overlapping each other or the state.
+ * The context keeps an fp64 scratch of (P^2 + P Q) * 8 bytes, P and Q being p and q rounded
+ * up to multiples of 64 (576 MiB at p 8192, q 1024), allocated on first use.  Synchronous:
+ * returns after the solve, KVMAP_ERR_NOT_SPD if a pivot was not positive and finite (the
+ * outputs are then undefined), INVALID_ARGUMENT / UNSUPPORTED on refused arguments (nothing
+ * written). */
+int kvmap_ridge_solve_device(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, void* W_out,
+                             void* b_out, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -183,3 +183,47 @@ def test_fit_stats_full_size(ctx):
     err = np.max(np.abs(W.T - Wt))
     print(f"[gram] ridge vs hidden map: max |W - W*| {err:.2e}", flush=True)
     assert err < 2e-3
+    # the same solve on the device (fp64), fp32 and bf16 outputs
+    Wd, bd = ctx.ridge_solve_device(st, cfg.lam, dtype=torch.float32)
+    Wd, bd = Wd.double().cpu().numpy(), bd.double().cpu().numpy()
+    rw, rb = _rel(Wd, W.astype(np.float64)), _rel(bd, b.astype(np.float64))
+    errd = np.max(np.abs(Wd.T - Wt))
+    print(f"[gram] device ridge vs host: rel W {rw:.2e} b {rb:.2e}; vs hidden map {errd:.2e}", flush=True)
+    assert rw <= 1e-5 and rb <= 1e-5 and errd < 2e-3
+    Wb, bb = ctx.ridge_solve_device(st, cfg.lam, dtype=torch.bfloat16)
+    Wb = Wb.double().cpu().numpy()
+    assert np.all(np.abs(Wb - W) <= 2.0 ** -8 * (1 + 1e-5) * np.abs(W) + 1e-30)
+
+
+def test_ridge_solve_device_matches_oracle(ctx):
+    """kvmap_ridge_solve_device on a GPU-built state (p = 520, q = 68: both padded to multiples
+    of 64 inside), against the oracle's fp64 ridge on the same (fp32) statistics and against
+    the host solver; lambda = 0.01 and a larger lambda."""
+    from cross_model_kv_amd import kvmap as K
+    parts = _batches(SMALL, [700, 1300])
+    st = ctx.gram_state(SMALL.p, SMALL.q)
+    ctx.gram_reset(st)
+    for X, Y in parts:
+        ctx.gram(st, _dev(X, "bf16"), _dev(Y, "bf16"))
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    stats = dict(n=st.n, mx=f(st.mean_x), my=f(st.mean_y), Mxx=np.triu(f(st.M_xx)) + np.triu(f(st.M_xx), 1).T,
+                 Mxy=f(st.M_xy))
+    for lam in (0.01, 3.0):
+        Wr, br = oracle.ridge(stats, lam)  # W [p][q], b [q]
+        Wd, bd = ctx.ridge_solve_device(st, lam, dtype=torch.float32)
+        Wh, bh = ctx.ridge_solve(st, lam)
+        rw, rb = _rel(f(Wd).T, Wr), _rel(f(bd), br)
+        rh = _rel(f(Wd), Wh.astype(np.float64))
+        print(f"[ridge] device lambda {lam}: rel W {rw:.2e} b {rb:.2e}; vs host {rh:.2e}", flush=True)
+        assert rw <= 1e-5 and rb <= 1e-5 and rh <= 1e-5
+
+
+def test_ridge_solve_device_not_spd(ctx):
+    """An empty state with lambda = 0 has a zero pivot: KVMAP_ERR_NOT_SPD."""
+    from cross_model_kv_amd import kvmap as K
+    st = ctx.gram_state(64, 8)
+    ctx.gram_reset(st)
+    with pytest.raises(K.KvmapError) as e:
+        ctx.ridge_solve_device(st, 0.0)
+    assert e.value.status == K.ERR_NOT_SPD
