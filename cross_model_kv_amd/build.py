@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libkvmap.so")
 
-HIP_SOURCES = ["api.hip", "rope.hip", "gemm_bf16.hip", "gemm_bf16_small.hip", "gemm_f32.hip", "gram.hip", "gram_x3.hip", "ridge_dev.hip"]
+HIP_SOURCES = ["api.hip", "rope.hip", "gemm_bf16.hip", "gemm_bf16_small.hip", "gemm_f32.hip", "gram.hip", "gram_x3.hip",
+               "ridge_dev.hip", "fit.hip"]
 HOST_SOURCES = ["ridge.cpp"]
 ARCH = "gfx950"
 

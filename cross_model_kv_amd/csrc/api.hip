@@ -79,6 +79,16 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
+int kvmap::report(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
 struct kvmap_ctx {
     int device = 0;
     std::vector<RopeEntry> ropes;
@@ -101,6 +111,8 @@ struct kvmap_ctx {
     bool timed = false;
     float last_ms[3] = {0, 0, 0};
 };
+
+int kvmap::context_device(const kvmap_ctx* c) { return c ? c->device : -1; }
 
 // ---------------------------------------------------------------------------------------
 // status / version
@@ -479,6 +491,54 @@ extern "C" int kvmap_recode(kvmap_ctx* c, int32_t rows, int64_t T, int32_t head_
     return ok();
 }
 
+// ---------------------------------------------------------------------------------------
+// fit-side rows from calibration caches
+// ---------------------------------------------------------------------------------------
+
+extern "C" int kvmap_cache_rows(kvmap_ctx* c, const void* cache, int32_t L, int32_t H, int64_t T, int32_t head_dim,
+                                int32_t dtype, const int32_t* layers, int32_t n_layers, const kvmap_rope* rope,
+                                void* out, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_cache_rows: ctx is NULL");
+    if (L < 1 || H < 1 || T < 1 || T > (int64_t(1) << 31))
+        return fail(KVMAP_ERR_SHAPE, "kvmap_cache_rows: L=%d, H=%d, T=%lld out of range", (int)L, (int)H, (long long)T);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_cache_rows: head_dim %d (64 or 128 supported)", (int)head_dim);
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_cache_rows: dtype %d unknown", (int)dtype);
+    if (!layers || n_layers < 1 || n_layers > kMaxRowLayers)
+        return fail(KVMAP_ERR_SHAPE, "kvmap_cache_rows: n_layers must be in [1, %d]", kMaxRowLayers);
+    RowLayers rl{};
+    for (int j = 0; j < n_layers; ++j) {
+        if (layers[j] < 0 || layers[j] >= L)
+            return fail(KVMAP_ERR_SHAPE, "kvmap_cache_rows: layers[%d] = %d outside [0, %d)", j, (int)layers[j], (int)L);
+        rl.l[j] = layers[j];
+    }
+    if (rope) {
+        int st = validate_rope(rope, "rows", T);
+        if (st) return st;
+    }
+    if (!cache || !out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_cache_rows: NULL device pointer");
+    if ((((uintptr_t)cache) | ((uintptr_t)out)) & 15)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_cache_rows: pointers must be 16-byte aligned");
+    const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    const size_t in_bytes = (size_t)L * H * (size_t)T * head_dim * es;
+    const size_t out_bytes = (size_t)n_layers * H * (size_t)T * head_dim * es;
+    if (ranges_overlap(cache, in_bytes, out, out_bytes))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_cache_rows: out overlaps the cache");
+    DeviceGuard guard(c->device);
+    if (!guard.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_cache_rows: hipSetDevice(%d) failed", c->device);
+    hipStream_t s = (hipStream_t)stream;
+    float2* tab = nullptr;
+    if (rope) {
+        bool built = false;
+        int st = get_rope_table(c, rope, head_dim, T, s, &tab, &built);
+        if (st) return st;
+    }
+    const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
+    KVMAP_HIP(launch_rows(e, cache, out, rl, n_layers, H, T, head_dim, tab, s));
+    return ok();
+}
+
 extern "C" int kvmap_last_timings(kvmap_ctx* c, float* ms, int n_ms) {
     if (!c || !ms || n_ms < 3) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: bad arguments");
     if (!c->timed) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: no timed apply recorded");
@@ -506,7 +566,7 @@ static int validate_state(const kvmap_gram_state* st, const char* which) {
     if (st->n < 0) return fail(KVMAP_ERR_SHAPE, "%s state: n < 0", which);
     if (!st->mean_x || !st->mean_y || !st->M_xx || !st->M_xy)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state: NULL array", which);
-    const void* arr[4] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy};
+    const void* arr[5] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy, st->ss_y};
     for (const void* a : arr)
         if (((uintptr_t)a) & 15) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state: arrays must be 16-byte aligned", which);
     return KVMAP_OK;
@@ -539,6 +599,8 @@ static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
     float* base = c->gram;
     sc.part = base;
     base += (size_t)kGramMaxSplits * (p + q);
+    sc.part2 = base;
+    base += (size_t)kGramMaxSplits * (p + q);
     sc.cx = base; base += p;
     sc.cy = base; base += q;
     sc.mx = base; base += p;
@@ -561,6 +623,7 @@ extern "C" int kvmap_gram_reset(kvmap_ctx* c, kvmap_gram_state* st, void* stream
     KVMAP_HIP(launch_fill_zero(st->mean_y, st->q, s));
     KVMAP_HIP(launch_fill_zero(st->M_xx, (int64_t)st->p * st->p, s));
     KVMAP_HIP(launch_fill_zero(st->M_xy, (int64_t)st->p * st->q, s));
+    if (st->ss_y) KVMAP_HIP(launch_fill_zero(st->ss_y, st->q, s));
     st->n = 0;
     return ok();
 }
@@ -591,7 +654,7 @@ extern "C" int kvmap_gram(kvmap_ctx* c, const void* X, const void* Y, int64_t n_
         const char* xb = (const char*)X + (size_t)r0 * st->p * esz;
         const char* yb = (const char*)Y + (size_t)r0 * st->q * esz;
         KVMAP_HIP(launch_gram_batch(e, xb, yb, nr, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
-                                    st->M_xy, sc, (hipStream_t)stream));
+                                    st->M_xy, st->ss_y, sc, (hipStream_t)stream));
         st->n += nr;
     }
     return ok();
@@ -607,13 +670,16 @@ extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap
     if (dst->p != src->p || dst->q != src->q)
         return fail(KVMAP_ERR_SHAPE, "kvmap_gram_merge: p/q differ");
     if (dst->M_xx == src->M_xx) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src alias");
+    if (!dst->ss_y != !src->ss_y)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: ss_y kept by one state only");
     if (src->n == 0) return ok();
     DeviceGuard g(c->device);
     r = ensure_gram_scratch(c, dst->p, dst->q, 0);
     if (r) return r;
     const GramScratch sc = gram_scratch(c, dst->p, dst->q, 1);
     KVMAP_HIP(launch_gram_merge(dst->p, dst->q, dst->n, src->n, dst->mean_x, dst->mean_y, dst->M_xx,
-                                dst->M_xy, src->mean_x, src->mean_y, src->M_xx, src->M_xy, sc,
+                                dst->M_xy, dst->ss_y, src->mean_x, src->mean_y, src->M_xx, src->M_xy,
+                                src->ss_y, sc,
                                 (hipStream_t)stream));
     dst->n += src->n;
     return ok();
@@ -634,6 +700,20 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
     if (ridge_solve_f64(p, q, mean_x, mean_y, M_xx, M_xy, lambda, W_out, b_out, n_threads))
         return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_host: M_xx + lambda I is not positive definite");
     return ok();
+}
+
+static int ensure_ridge_scratch(kvmap_ctx* c, int p, int q, size_t* need_out) {
+    const size_t need = ridge_dev_scratch_bytes(p, q);
+    if (need > c->ridge_bytes) {
+        KVMAP_HIP(hipDeviceSynchronize());
+        (void)hipFree(c->ridge);
+        c->ridge = nullptr;
+        c->ridge_bytes = 0;
+        KVMAP_HIP(hipMalloc(&c->ridge, need));
+        c->ridge_bytes = need;
+    }
+    *need_out = need;
+    return KVMAP_OK;
 }
 
 extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, void* W_out,
@@ -657,15 +737,9 @@ extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st
         if (ranges_overlap(ins[i], insz[i], W_out, wb) || ranges_overlap(ins[i], insz[i], b_out, bb))
             return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: an output overlaps the state");
     DeviceGuard g(c->device);
-    const size_t need = ridge_dev_scratch_bytes(st->p, st->q);
-    if (need > c->ridge_bytes) {
-        KVMAP_HIP(hipDeviceSynchronize());
-        (void)hipFree(c->ridge);
-        c->ridge = nullptr;
-        c->ridge_bytes = 0;
-        KVMAP_HIP(hipMalloc(&c->ridge, need));
-        c->ridge_bytes = need;
-    }
+    size_t need = 0;
+    r = ensure_ridge_scratch(c, st->p, st->q, &need);
+    if (r) return r;
     hipStream_t s = (hipStream_t)stream;
     int* bad = (int*)((char*)c->ridge + need - 256);  // pivot flag, in the scratch's last 256 bytes
     KVMAP_HIP(launch_fill_zero((float*)bad, 1, s));
@@ -675,6 +749,40 @@ extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st
     KVMAP_HIP(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s));
     KVMAP_HIP(hipStreamSynchronize(s));
     if (h) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_device: M_xx + lambda I is not positive definite");
+    return ok();
+}
+
+extern "C" int kvmap_ridge_r2(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, int32_t group,
+                              double* r2_out, void* stream) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: ctx is NULL");
+    int r = validate_state(st, "kvmap_ridge_r2");
+    if (r) return r;
+    if (!st->ss_y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: the state keeps no ss_y");
+    if (!r2_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: NULL output");
+    if (group < 1 || st->q % group)
+        return fail(KVMAP_ERR_SHAPE, "kvmap_ridge_r2: group %d must divide q = %d", (int)group, (int)st->q);
+    if (!(lambda >= 0.0) || !std::isfinite(lambda))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: lambda must be finite and >= 0");
+    if (((uintptr_t)r2_out) & 7) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: r2_out must be 8-byte aligned");
+    const size_t ob = (size_t)(st->q / group) * 8;
+    const void* ins[5] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy, st->ss_y};
+    const size_t insz[5] = {(size_t)st->p * 4, (size_t)st->q * 4, (size_t)st->p * st->p * 4,
+                            (size_t)st->p * st->q * 4, (size_t)st->q * 4};
+    for (int i = 0; i < 5; ++i)
+        if (ranges_overlap(ins[i], insz[i], r2_out, ob))
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: r2_out overlaps the state");
+    DeviceGuard g(c->device);
+    size_t need = 0;
+    r = ensure_ridge_scratch(c, st->p, st->q, &need);
+    if (r) return r;
+    hipStream_t s = (hipStream_t)stream;
+    int* bad = (int*)((char*)c->ridge + need - 256);
+    KVMAP_HIP(launch_fill_zero((float*)bad, 1, s));
+    KVMAP_HIP(launch_ridge_r2(st->p, st->q, st->M_xx, st->M_xy, st->ss_y, lambda, group, r2_out, c->ridge, bad, s));
+    int h = 0;
+    KVMAP_HIP(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s));
+    KVMAP_HIP(hipStreamSynchronize(s));
+    if (h) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_r2: M_xx + lambda I is not positive definite");
     return ok();
 }
 

@@ -1,0 +1,395 @@
+// End-to-end fit driver over the C-ABI (KVBridge README, fitting section headed "Loading":
+// a two-stage, multi-pass fit over re-iterable calibration data that keeps only centered
+// statistics, with target-layer blocks bounding memory; "What ships": head-averaged
+// single-source R^2 selects the top-k source layers per target layer, then per-target-layer
+// ridge maps for K and V).
+//
+// The driver owns the statistics of one stage at a time and calls the library's own entry
+// points for every step: kvmap_cache_rows (gather + strip RoPE into token rows), kvmap_gram
+// (Chan-merged centered statistics), kvmap_ridge_r2 (stage-1 scores per target head) and
+// kvmap_ridge_solve_device (stage-2 maps).  The selection itself (average over heads and
+// {K, V}, top-k) is the one kernel of this file.
+
+#include "../../include/kvmap.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+
+using namespace kvmap;
+
+namespace kvmap {
+
+namespace {
+
+constexpr int kMaxFitSrcLayers = 1024;
+constexpr int kMaxGramWidth = 65536;
+
+// a ranks above b: larger score, then lower index; NaN scores rank below every number
+__device__ __forceinline__ bool ranks_above(double a, int ia, double b, int ib) {
+    const bool na = a != a, nb = b != b;
+    if (na != nb) return nb;
+    if (!na && a != b) return a > b;
+    return ia < ib;
+}
+
+// One workgroup per target layer; lane 0 selects (L_src <= 1024, k <= L_src).
+__global__ __launch_bounds__(64) void fit_select_kernel(const double* __restrict__ r2, int L_src, int L_tgt,
+                                                        int H, int k, double* __restrict__ scores,
+                                                        int32_t* __restrict__ sel) {
+    __shared__ double sc[kMaxFitSrcLayers];
+    __shared__ unsigned char taken[kMaxFitSrcLayers];
+    const int t = blockIdx.x;
+    for (int s = threadIdx.x; s < L_src; s += 64) {
+        double acc = 0.0;
+        for (int kv = 0; kv < 2; ++kv)
+            for (int h = 0; h < H; ++h) acc += r2[(((size_t)kv * L_src + s) * L_tgt + t) * H + h];
+        const double v = acc / (2.0 * H);
+        sc[s] = v;
+        taken[s] = 0;
+        scores[(size_t)t * L_src + s] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int s = 0; s < L_src; ++s)
+            if (!taken[s] && (best < 0 || ranks_above(sc[s], s, sc[best], best))) best = s;
+        taken[best] = 1;
+    }
+    int o = 0;
+    for (int s = 0; s < L_src; ++s)
+        if (taken[s]) sel[(size_t)t * k + o++] = s;
+}
+
+}  // namespace
+
+hipError_t launch_fit_select(const double* r2, int L_src, int L_tgt, int H, int k, double* scores, int32_t* sel,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(fit_select_kernel, dim3(L_tgt), dim3(64), 0, s, r2, L_src, L_tgt, H, k, scores, sel);
+    return hipGetLastError();
+}
+
+}  // namespace kvmap
+
+// ---------------------------------------------------------------------------------------
+// the driver
+// ---------------------------------------------------------------------------------------
+
+struct kvmap_fit {
+    kvmap_ctx* ctx = nullptr;
+    kvmap_fit_config cfg{};
+    int device = 0;
+    int N = 0, F = 0;                  // H*d, k*H*d
+    int sel_block = 0, map_block = 0;  // target layers per pass of each stage
+    int sel_passes = 0, map_passes = 0;
+    int pass = -1;                     // index of the open pass, -1 before the first
+    int stage = 0, t0 = 0, t1 = 0;
+    int64_t n_pass = 0, n_first = -1;  // tokens fed to the open pass / to the first pass
+    std::vector<int32_t> sel;          // host copy of layer_sel [L_tgt][k]
+    std::vector<kvmap_gram_state> states;
+    float* state_mem = nullptr;
+    double* r2 = nullptr;              // [2][L_src][L_tgt][H]
+    double* own_scores = nullptr;      // when cfg.scores is NULL
+    void* xrows = nullptr;
+    void* yrows = nullptr;
+    size_t xcap = 0, ycap = 0;
+};
+
+namespace {
+
+#define FIT_HIP(call)                                                                                 \
+    do {                                                                                              \
+        hipError_t e_ = (call);                                                                       \
+        if (e_ != hipSuccess)                                                                         \
+            return report(e_ == hipErrorOutOfMemory ? KVMAP_ERR_OUT_OF_MEMORY : KVMAP_ERR_DEVICE,     \
+                          "%s: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, __LINE__);         \
+    } while (0)
+
+#define FIT_TRY(call)             \
+    do {                          \
+        const int r_ = (call);    \
+        if (r_ != KVMAP_OK) return r_; \
+    } while (0)
+
+struct FitDevice {
+    int prev = -1;
+    explicit FitDevice(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        (void)hipSetDevice(dev);
+    }
+    ~FitDevice() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+size_t esize(int32_t dtype) { return dtype == KVMAP_DTYPE_BF16 ? 2 : 4; }
+
+void free_stage(kvmap_fit* f) {
+    if (f->state_mem) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(f->state_mem);
+    }
+    f->state_mem = nullptr;
+    f->states.clear();
+}
+
+// Lay out n states of (p, q) in one allocation; every array starts 16-byte aligned since p, q
+// are multiples of 64.
+int alloc_states(kvmap_fit* f, int n, int p, int q, bool keep_ss_y) {
+    free_stage(f);
+    const size_t per = (size_t)p + q + (size_t)p * p + (size_t)p * q + (keep_ss_y ? q : 0);
+    FIT_HIP(hipMalloc((void**)&f->state_mem, per * n * sizeof(float)));
+    f->states.resize(n);
+    float* b = f->state_mem;
+    for (int i = 0; i < n; ++i) {
+        kvmap_gram_state& st = f->states[i];
+        st.n = 0;
+        st.p = p;
+        st.q = q;
+        st.mean_x = b; b += p;
+        st.mean_y = b; b += q;
+        st.M_xx = b; b += (size_t)p * p;
+        st.M_xy = b; b += (size_t)p * q;
+        st.ss_y = keep_ss_y ? b : nullptr;
+        b += keep_ss_y ? q : 0;
+    }
+    return KVMAP_OK;
+}
+
+int ensure_rows(void** buf, size_t* cap, size_t need, hipStream_t s) {
+    if (need <= *cap) return KVMAP_OK;
+    FIT_HIP(hipStreamSynchronize(s));
+    (void)hipFree(*buf);
+    *buf = nullptr;
+    *cap = 0;
+    FIT_HIP(hipMalloc(buf, need));
+    *cap = need;
+    return KVMAP_OK;
+}
+
+// Open pass number f->pass (0-based over both stages): block bounds, states sized and reset.
+int open_pass(kvmap_fit* f, hipStream_t s) {
+    const kvmap_fit_config& c = f->cfg;
+    f->n_pass = 0;
+    if (f->pass < f->sel_passes) {
+        f->stage = 1;
+        f->t0 = f->pass * f->sel_block;
+        f->t1 = std::min(c.L_tgt, f->t0 + f->sel_block);
+        if (f->pass == 0) FIT_TRY(alloc_states(f, 2 * c.L_src, f->N, f->sel_block * f->N, true));
+        for (auto& st : f->states) {
+            st.q = (f->t1 - f->t0) * f->N;
+            FIT_TRY(kvmap_gram_reset(f->ctx, &st, s));
+        }
+        return KVMAP_OK;
+    }
+    const int b = f->pass - f->sel_passes;
+    f->stage = 2;
+    f->t0 = b * f->map_block;
+    f->t1 = std::min(c.L_tgt, f->t0 + f->map_block);
+    if (b == 0) FIT_TRY(alloc_states(f, 2 * f->map_block, f->F, f->N, false));
+    for (int i = 0; i < 2 * (f->t1 - f->t0); ++i) FIT_TRY(kvmap_gram_reset(f->ctx, &f->states[i], s));
+    return KVMAP_OK;
+}
+
+// Close the open pass: stage 1 scores its block (and the last one selects); stage 2 solves.
+int close_pass(kvmap_fit* f, hipStream_t s) {
+    const kvmap_fit_config& c = f->cfg;
+    if (f->n_pass == 0) return report(KVMAP_ERR_SHAPE, "kvmap_fit_next_pass: pass %d saw no tokens", f->pass);
+    if (f->n_first >= 0 && f->n_pass != f->n_first)
+        return report(KVMAP_ERR_SHAPE, "kvmap_fit_next_pass: pass %d saw %lld tokens, the first pass %lld", f->pass,
+                      (long long)f->n_pass, (long long)f->n_first);
+    if (f->n_first < 0) f->n_first = f->n_pass;
+    if (f->stage == 1) {
+        const int H = c.H_kv;
+        for (int kv = 0; kv < 2; ++kv)
+            for (int sl = 0; sl < c.L_src; ++sl) {
+                double* out = f->r2 + (((size_t)kv * c.L_src + sl) * c.L_tgt + f->t0) * H;
+                FIT_TRY(kvmap_ridge_r2(f->ctx, &f->states[kv * c.L_src + sl], c.lambda, c.head_dim, out, s));
+            }
+        if (f->pass == f->sel_passes - 1) {
+            double* scores = c.scores ? c.scores : f->own_scores;
+            FIT_HIP(launch_fit_select(f->r2, c.L_src, c.L_tgt, H, c.k, scores, c.layer_sel, s));
+            FIT_HIP(hipMemcpyAsync(f->sel.data(), c.layer_sel, f->sel.size() * sizeof(int32_t),
+                                   hipMemcpyDeviceToHost, s));
+            FIT_HIP(hipStreamSynchronize(s));
+            free_stage(f);
+        }
+        return KVMAP_OK;
+    }
+    const size_t es = esize(c.out_dtype);
+    for (int t = f->t0; t < f->t1; ++t)
+        for (int kv = 0; kv < 2; ++kv) {
+            char* W = (char*)(kv ? c.W_v : c.W_k) + (size_t)t * f->N * f->F * es;
+            char* b = (char*)(kv ? c.b_v : c.b_k) + (size_t)t * f->N * es;
+            FIT_TRY(kvmap_ridge_solve_device(f->ctx, &f->states[2 * (t - f->t0) + kv], c.lambda, W, b, c.out_dtype,
+                                             s));
+        }
+    if (f->pass == f->sel_passes + f->map_passes - 1) free_stage(f);
+    return KVMAP_OK;
+}
+
+void destroy(kvmap_fit* f) {
+    if (!f) return;
+    FitDevice g(f->device);
+    (void)hipDeviceSynchronize();
+    free_stage(f);
+    (void)hipFree(f->r2);
+    (void)hipFree(f->own_scores);
+    (void)hipFree(f->xrows);
+    (void)hipFree(f->yrows);
+    delete f;
+}
+
+}  // namespace
+
+extern "C" int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvmap_fit** out) {
+    if (!out) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: out is NULL");
+    *out = nullptr;
+    if (!ctx || !cfg) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: ctx or cfg is NULL");
+    const kvmap_fit_config& c = *cfg;
+    if (c.head_dim != 64 && c.head_dim != 128)
+        return report(KVMAP_ERR_UNSUPPORTED, "kvmap_fit_create: head_dim %d (64 or 128 supported)", (int)c.head_dim);
+    if (c.L_src < 1 || c.L_src > kMaxFitSrcLayers || c.L_tgt < 1 || c.H_kv < 1 || c.k < 1 || c.k > c.L_src)
+        return report(KVMAP_ERR_SHAPE, "kvmap_fit_create: L_src=%d (1..%d), L_tgt=%d, H_kv=%d, k=%d out of range",
+                      (int)c.L_src, kMaxFitSrcLayers, (int)c.L_tgt, (int)c.H_kv, (int)c.k);
+    const int64_t N = (int64_t)c.H_kv * c.head_dim, F = N * c.k;
+    if (F > kMaxGramWidth || c.k > kMaxRowLayers)
+        return report(KVMAP_ERR_SHAPE, "kvmap_fit_create: k*H*d = %lld exceeds %d (or k > %d)", (long long)F,
+                      kMaxGramWidth, kMaxRowLayers);
+    for (int32_t dt : {c.dtype, c.out_dtype})
+        if (dt != KVMAP_DTYPE_BF16 && dt != KVMAP_DTYPE_F32)
+            return report(KVMAP_ERR_UNSUPPORTED, "kvmap_fit_create: dtype %d unknown", (int)dt);
+    if (!(c.theta_src > 0.0) || !(c.theta_tgt > 0.0) || !std::isfinite(c.theta_src) || !std::isfinite(c.theta_tgt))
+        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: RoPE bases must be finite and > 0");
+    if (!(c.lambda >= 0.0) || !std::isfinite(c.lambda))
+        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: lambda must be finite and >= 0");
+    const int max_sel_block = (int)std::min<int64_t>(kMaxRowLayers, kMaxGramWidth / N);
+    if (c.select_block < 0 || c.select_block > max_sel_block || c.map_block < 0)
+        return report(KVMAP_ERR_SHAPE, "kvmap_fit_create: select_block %d (0..%d), map_block %d", (int)c.select_block,
+                      max_sel_block, (int)c.map_block);
+    if (!c.layer_sel || !c.W_k || !c.b_k || !c.W_v || !c.b_v)
+        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: NULL output");
+    if (((uintptr_t)c.layer_sel | (uintptr_t)c.W_k | (uintptr_t)c.b_k | (uintptr_t)c.W_v | (uintptr_t)c.b_v) & 3)
+        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: outputs must be 4-byte aligned");
+    if (((uintptr_t)c.scores) & 7)
+        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: scores must be 8-byte aligned");
+    const int dev = context_device(ctx);
+    FitDevice g(dev);
+    kvmap_fit* f = new kvmap_fit;
+    f->ctx = ctx;
+    f->cfg = c;
+    f->device = dev;
+    f->N = (int)N;
+    f->F = (int)F;
+    f->sel.assign((size_t)c.L_tgt * c.k, 0);
+    f->sel_block = c.select_block ? c.select_block : std::min<int>(c.L_tgt, max_sel_block);
+    f->map_block = c.map_block ? std::min<int>(c.map_block, c.L_tgt) : c.L_tgt;
+    f->sel_passes = c.given_sel ? 0 : (c.L_tgt + f->sel_block - 1) / f->sel_block;
+    f->map_passes = (c.L_tgt + f->map_block - 1) / f->map_block;
+    int st = KVMAP_OK;
+    if (c.given_sel) {
+        hipError_t e = hipMemcpy(f->sel.data(), c.layer_sel, f->sel.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) st = report(KVMAP_ERR_DEVICE, "kvmap_fit_create: reading layer_sel: %s", hipGetErrorString(e));
+        for (int t = 0; t < c.L_tgt && st == KVMAP_OK; ++t) {
+            std::vector<char> seen(c.L_src, 0);
+            for (int j = 0; j < c.k && st == KVMAP_OK; ++j) {
+                const int v = f->sel[(size_t)t * c.k + j];
+                if (v < 0 || v >= c.L_src || seen[v])
+                    st = report(KVMAP_ERR_SHAPE, "kvmap_fit_create: layer_sel[%d][%d] = %d out of range or repeated", t,
+                                j, v);
+                else
+                    seen[v] = 1;
+            }
+        }
+    } else {
+        hipError_t e = hipMalloc((void**)&f->r2, (size_t)2 * c.L_src * c.L_tgt * c.H_kv * sizeof(double));
+        if (e == hipSuccess && !c.scores) e = hipMalloc((void**)&f->own_scores, (size_t)c.L_tgt * c.L_src * sizeof(double));
+        if (e != hipSuccess)
+            st = report(e == hipErrorOutOfMemory ? KVMAP_ERR_OUT_OF_MEMORY : KVMAP_ERR_DEVICE,
+                        "kvmap_fit_create: %s", hipGetErrorString(e));
+    }
+    if (st != KVMAP_OK) {
+        destroy(f);
+        return st;
+    }
+    *out = f;
+    return report(KVMAP_OK, "%s", "");
+}
+
+extern "C" int kvmap_fit_next_pass(kvmap_fit* f, kvmap_fit_pass* info, void* stream) {
+    if (!f || !info) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_next_pass: NULL argument");
+    FitDevice g(f->device);
+    hipStream_t s = (hipStream_t)stream;
+    const int passes = f->sel_passes + f->map_passes;
+    if (f->pass >= passes) {
+        *info = kvmap_fit_pass{0, 0, 0, passes, passes};
+        return report(KVMAP_OK, "%s", "");
+    }
+    if (f->pass >= 0) FIT_TRY(close_pass(f, s));
+    ++f->pass;
+    if (f->pass >= passes) {
+        f->stage = 0;
+        *info = kvmap_fit_pass{0, 0, 0, passes, passes};
+        return report(KVMAP_OK, "%s", "");
+    }
+    FIT_TRY(open_pass(f, s));
+    *info = kvmap_fit_pass{f->stage, f->t0, f->t1, f->pass, passes};
+    return report(KVMAP_OK, "%s", "");
+}
+
+extern "C" int kvmap_fit_add(kvmap_fit* f, const void* src_k, const void* src_v, const void* tgt_k,
+                             const void* tgt_v, int64_t T, int64_t pos0, void* stream) {
+    if (!f) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_add: fit is NULL");
+    if (f->stage == 0) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_add: no pass is open");
+    if (!src_k || !src_v || !tgt_k || !tgt_v) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_add: NULL cache");
+    if (T < 1 || T > (int64_t(1) << 31)) return report(KVMAP_ERR_SHAPE, "kvmap_fit_add: T=%lld out of range", (long long)T);
+    if (pos0 < 0) return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_add: pos0 < 0");
+    const kvmap_fit_config& c = f->cfg;
+    FitDevice g(f->device);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t es = esize(c.dtype);
+    const int d = c.head_dim, H = c.H_kv;
+    const kvmap_rope rs{c.theta_src, pos0, KVMAP_ROPE_HALF_SPLIT};
+    const kvmap_rope rt{c.theta_tgt, pos0, KVMAP_ROPE_HALF_SPLIT};
+    const void* src[2] = {src_k, src_v};
+    const void* tgt[2] = {tgt_k, tgt_v};
+    if (f->stage == 1) {
+        const int nb = f->t1 - f->t0;
+        FIT_TRY(ensure_rows(&f->xrows, &f->xcap, (size_t)T * f->N * es, s));
+        FIT_TRY(ensure_rows(&f->yrows, &f->ycap, (size_t)T * nb * f->N * es, s));
+        std::vector<int32_t> block(nb);
+        for (int j = 0; j < nb; ++j) block[j] = f->t0 + j;
+        for (int kv = 0; kv < 2; ++kv) {
+            FIT_TRY(kvmap_cache_rows(f->ctx, tgt[kv], c.L_tgt, H, T, d, c.dtype, block.data(), nb, kv ? nullptr : &rt,
+                                     f->yrows, s));
+            for (int32_t sl = 0; sl < c.L_src; ++sl) {
+                FIT_TRY(kvmap_cache_rows(f->ctx, src[kv], c.L_src, H, T, d, c.dtype, &sl, 1, kv ? nullptr : &rs,
+                                         f->xrows, s));
+                FIT_TRY(kvmap_gram(f->ctx, f->xrows, f->yrows, T, c.dtype, &f->states[kv * c.L_src + sl], s));
+            }
+        }
+    } else {
+        FIT_TRY(ensure_rows(&f->xrows, &f->xcap, (size_t)T * f->F * es, s));
+        FIT_TRY(ensure_rows(&f->yrows, &f->ycap, (size_t)T * f->N * es, s));
+        for (int32_t t = f->t0; t < f->t1; ++t)
+            for (int kv = 0; kv < 2; ++kv) {
+                FIT_TRY(kvmap_cache_rows(f->ctx, src[kv], c.L_src, H, T, d, c.dtype, &f->sel[(size_t)t * c.k], c.k,
+                                         kv ? nullptr : &rs, f->xrows, s));
+                FIT_TRY(kvmap_cache_rows(f->ctx, tgt[kv], c.L_tgt, H, T, d, c.dtype, &t, 1, kv ? nullptr : &rt,
+                                         f->yrows, s));
+                FIT_TRY(kvmap_gram(f->ctx, f->xrows, f->yrows, T, c.dtype, &f->states[2 * (t - f->t0) + kv], s));
+            }
+    }
+    f->n_pass += T;
+    return report(KVMAP_OK, "%s", "");
+}
+
+extern "C" int kvmap_fit_destroy(kvmap_fit* f) {
+    destroy(f);
+    return report(KVMAP_OK, "%s", "");
+}

@@ -31,7 +31,7 @@ constexpr int GLD = GT + 32;                     // padded LDS row (floats)
 }  // namespace
 
 size_t gram_scratch_floats(int p, int q, int splits) {
-    return (size_t)splits * (p + q) + 3 * (size_t)(p + q);
+    return 2 * (size_t)splits * (p + q) + 3 * (size_t)(p + q);  // part, part2, c, m, delta
 }
 
 // ---- 1/2: column sums ---------------------------------------------------------------
@@ -43,13 +43,15 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const void* __restri
                                                             int64_t n, int cols,
                                                             const float* __restrict__ shift,
                                                             float* __restrict__ part,
-                                                            int part_stride, int col_off) {
+                                                            int part_stride, int col_off,
+                                                            float* __restrict__ part2) {
     __shared__ float4 red[4][64];
+    __shared__ float4 red2[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c0 = blockIdx.x * CS_TILE + lane * CS_COLS;
     const int splits = gridDim.y;
     const int64_t r0 = n * blockIdx.y / splits, r1 = n * (blockIdx.y + 1) / splits;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acc2 = acc;
     if (c0 < cols) {
         float4 sh = make_float4(0.f, 0.f, 0.f, 0.f);
         if (shift) sh = *(const float4*)(shift + c0);
@@ -61,31 +63,40 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const void* __restri
             } else {
                 v = *(const float4*)((const float*)A + r * cols + c0);
             }
-            acc.x += v.x - sh.x; acc.y += v.y - sh.y; acc.z += v.z - sh.z; acc.w += v.w - sh.w;
+            const float4 dv = make_float4(v.x - sh.x, v.y - sh.y, v.z - sh.z, v.w - sh.w);
+            acc.x += dv.x; acc.y += dv.y; acc.z += dv.z; acc.w += dv.w;
+            acc2.x += dv.x * dv.x; acc2.y += dv.y * dv.y; acc2.z += dv.z * dv.z; acc2.w += dv.w * dv.w;
         }
     }
     red[wave][lane] = acc;
+    red2[wave][lane] = acc2;
     __syncthreads();
     if (wave == 0 && c0 < cols) {
-        float4 s = red[0][lane];
+        float4 s = red[0][lane], s2 = red2[0][lane];
 #pragma unroll
         for (int w = 1; w < 4; ++w) {
-            const float4 o = red[w][lane];
+            const float4 o = red[w][lane], o2 = red2[w][lane];
             s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+            s2.x += o2.x; s2.y += o2.y; s2.z += o2.z; s2.w += o2.w;
         }
         *(float4*)(part + (size_t)blockIdx.y * part_stride + col_off + c0) = s;
+        if (part2) *(float4*)(part2 + (size_t)blockIdx.y * part_stride + col_off + c0) = s2;
     }
 }
 
 // Reduce the split partial sums (float64, fixed order) and derive the phase's outputs.
 //   phase 0: c = sum / n_b (rounded to bf16 when round_c: the split co-moment path shifts
 //            bf16 data by a bf16 value, so that x - c is exact)
-//   phase 1: m = sum / n_b; batch mean = c + m; delta = batch mean - mean; mean updated
+//   phase 1: m = sum / n_b; batch mean = c + m; delta = batch mean - mean; mean updated;
+//            with ss_y (and the partial sums of squares of the shifted y in part2): the
+//            centered sum of squares of y merged the same way (Chan):
+//            ss_y += (sum2 - n_b m^2) + n n_b / n' delta^2
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     const float* __restrict__ part, int splits, int p, int q, int64_t n_b, int64_t n_old,
     int phase, int round_c, float* __restrict__ cx, float* __restrict__ cy, float* __restrict__ mx,
     float* __restrict__ my, float* __restrict__ dx, float* __restrict__ dy,
-    float* __restrict__ mean_x, float* __restrict__ mean_y) {
+    float* __restrict__ mean_x, float* __restrict__ mean_y, const float* __restrict__ part2,
+    float* __restrict__ ss_y) {
     const int col = blockIdx.x * blockDim.x + threadIdx.x;
     const int stride = p + q;
     if (col >= stride) return;
@@ -110,14 +121,22 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     float* mean = isx ? mean_x : mean_y;
     mm[c] = (float)mean_b;
     const double bm = (double)cc[c] + mean_b;
+    double delta = 0.0;
     if (n_old == 0) {
         dd[c] = 0.f;
         mean[c] = (float)bm;
     } else {
         const double old = (double)mean[c];
-        const double delta = bm - old;
+        delta = bm - old;
         dd[c] = (float)delta;
         mean[c] = (float)(old + delta * ((double)n_b / (double)(n_old + n_b)));
+    }
+    if (!isx && ss_y) {
+        double s2 = 0.0;
+        for (int y = 0; y < splits; ++y) s2 += (double)part2[(size_t)y * stride + col];
+        const double ssb = s2 - (double)n_b * mean_b * mean_b;
+        const double coef = (double)n_old * (double)n_b / (double)(n_old + n_b);
+        ss_y[c] = (float)((n_old == 0 ? 0.0 : (double)ss_y[c]) + ssb + coef * delta * delta);
     }
 }
 
@@ -279,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
 
 hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
                              int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
-                             float* M_xy, const GramScratch& sc, hipStream_t s) {
+                             float* M_xy, float* ss_y, const GramScratch& sc, hipStream_t s) {
     const bool bf = (e == Elem::BF16);
     const dim3 gx((p + CS_TILE - 1) / CS_TILE, sc.splits), gy((q + CS_TILE - 1) / CS_TILE, sc.splits);
     const int stride = p + q;
@@ -290,28 +309,33 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
     if (bf) {
         // column sums -> c = bf16(mean); split (d, hi, lo, transposed) with the sums of d;
         // m, delta, mean; co-moments on the bf16 matrix cores
-        hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, nullptr, sc.part, stride, 0);
-        hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, nullptr, sc.part, stride, p);
+        hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, nullptr, sc.part, stride, 0,
+                           nullptr);
+        hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, nullptr, sc.part, stride, p,
+                           nullptr);
         hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q, n_b, n_old,
-                           0, 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+                           0, 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, nullptr, nullptr);
         const int ss = gram_split_blocks(n_b, sc.max_splits);
         uint16_t* Sx = sc.split;
         uint16_t* Sy = sc.split + gram_split_elems(p, 0, n_b);
-        hipError_t err = launch_gram_split(X, n_b, p, sc.cx, Sx, sc.part, stride, 0, ss, s);
+        hipError_t err = launch_gram_split(X, n_b, p, sc.cx, Sx, sc.part, stride, 0, nullptr, ss, s);
         if (err != hipSuccess) return err;
-        err = launch_gram_split(Y, n_b, q, sc.cy, Sy, sc.part, stride, p, ss, s);
+        err = launch_gram_split(Y, n_b, q, sc.cy, Sy, sc.part, stride, p, ss_y ? sc.part2 : nullptr, ss, s);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, ss, p, q, n_b, n_old, 1, 0,
-                           sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+                           sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, sc.part2, ss_y);
         return launch_gram_x3(Sx, Sy, n_b, p, q, sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, s);
     }
     for (int phase = 0; phase < 2; ++phase) {
         const float* shx = phase ? sc.cx : nullptr;
         const float* shy = phase ? sc.cy : nullptr;
-        hipLaunchKernelGGL(colsum_kernel<false>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0);
-        hipLaunchKernelGGL(colsum_kernel<false>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p);
+        hipLaunchKernelGGL(colsum_kernel<false>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, shx, sc.part, stride, 0,
+                           nullptr);
+        hipLaunchKernelGGL(colsum_kernel<false>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, shy, sc.part, stride, p,
+                           (phase == 1 && ss_y) ? sc.part2 : nullptr);
         hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q,
-                           n_b, n_old, phase, 0, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y);
+                           n_b, n_old, phase, 0, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y,
+                           sc.part2, phase == 1 ? ss_y : nullptr);
     }
     const int nTx = (p + GT - 1) / GT, nTy = (q + GT - 1) / GT;
     const int nXX = nTx * (nTx + 1) / 2;
@@ -328,7 +352,8 @@ __global__ __launch_bounds__(256) void merge_delta_kernel(int p, int q, double f
                                                           const float* __restrict__ s_mean_x,
                                                           const float* __restrict__ s_mean_y,
                                                           float* __restrict__ dx,
-                                                          float* __restrict__ dy) {
+                                                          float* __restrict__ dy, float* __restrict__ ss_y,
+                                                          const float* __restrict__ s_ss_y, double coef) {
     const int col = blockIdx.x * blockDim.x + threadIdx.x;
     if (col >= p + q) return;
     const bool isx = col < p;
@@ -339,11 +364,13 @@ __global__ __launch_bounds__(256) void merge_delta_kernel(int p, int q, double f
     if (fresh) {
         d[c] = 0.f;
         mean[c] = sm[c];
+        if (!isx && ss_y) ss_y[c] = s_ss_y[c];
         return;
     }
     const double delta = (double)sm[c] - (double)mean[c];
     d[c] = (float)delta;
     mean[c] = (float)((double)mean[c] + delta * frac);
+    if (!isx && ss_y) ss_y[c] = (float)((double)ss_y[c] + (double)s_ss_y[c] + coef * delta * delta);
 }
 
 __global__ __launch_bounds__(256) void merge_moments_kernel(int rows, int cols, float coef,
@@ -361,14 +388,15 @@ __global__ __launch_bounds__(256) void merge_moments_kernel(int rows, int cols, 
 }
 
 hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
-                             float* mean_y, float* M_xx, float* M_xy, const float* s_mean_x,
-                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy,
+                             float* mean_y, float* M_xx, float* M_xy, float* ss_y, const float* s_mean_x,
+                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy, const float* s_ss_y,
                              const GramScratch& sc, hipStream_t s) {
     const double n = (double)n_dst + (double)n_src;
     const int fresh = (n_dst == 0);
     const float coef = (float)((double)n_dst * (double)n_src / n);
     hipLaunchKernelGGL(merge_delta_kernel, dim3((p + q + 255) / 256), dim3(256), 0, s, p, q,
-                       (double)n_src / n, fresh, mean_x, mean_y, s_mean_x, s_mean_y, sc.dx, sc.dy);
+                       (double)n_src / n, fresh, mean_x, mean_y, s_mean_x, s_mean_y, sc.dx, sc.dy, ss_y, s_ss_y,
+                       (double)n_dst * (double)n_src / n);
     hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, p, coef, fresh, M_xx, s_M_xx,
                        sc.dx, sc.dx);
     hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, q, coef, fresh, M_xy, s_M_xy,

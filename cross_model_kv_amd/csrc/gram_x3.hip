@@ -51,20 +51,22 @@ __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_fl
 __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restrict__ A, int64_t n_b, int cols,
                                                          int nkb, const float* __restrict__ c,
                                                          uint16_t* __restrict__ S, float* __restrict__ part,
-                                                         int part_stride, int col_off) {
+                                                         int part_stride, int col_off, float* __restrict__ part2) {
     __shared__ uint32_t t[SP_COLS * SP_LD];
     __shared__ float red[8][SP_COLS];
+    __shared__ float red2[8][SP_COLS];
     const int tid = threadIdx.x;
     const int c0 = blockIdx.x * SP_COLS;
     const int rc = (tid & 31) * 8;  // first of the thread's 8 columns within the workgroup
     const int rr = tid >> 5;        // row within each group of 8
     // cols is a multiple of 4: each half (4 columns) of the thread's 8 is wholly in or out
     const bool cok0 = c0 + rc < cols, cok1 = c0 + rc + 4 < cols;
-    float sh[8], sum[8];
+    float sh[8], sum[8], sum2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         sh[e] = (e < 4 ? cok0 : cok1) ? c[c0 + rc + e] : 0.f;
         sum[e] = 0.f;
+        sum2[e] = 0.f;
     }
     for (int kb = blockIdx.y; kb < nkb; kb += gridDim.y) {
 #pragma unroll
@@ -81,6 +83,7 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
                 const uint32_t bits = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
                 const float d = (e < 4 ? ok0 : ok1) ? bf16_bits_f32(bits) - sh[e] : 0.f;  // exact
                 sum[e] += d;
+                sum2[e] += d * d;
                 const uint32_t hi = bf16_rne_bits(d);
                 const uint32_t lo = bf16_rne_bits(d - bf16_bits_f32(hi));
                 t[(rc + e) * SP_LD + tok] = hi | (lo << 16);
@@ -106,13 +109,20 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
         __syncthreads();
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rr][rc + e] = sum[e];
+    for (int e = 0; e < 8; ++e) {
+        red[rr][rc + e] = sum[e];
+        red2[rr][rc + e] = sum2[e];
+    }
     __syncthreads();
     if (c0 + tid < cols) {
-        float s = 0.f;
+        float s = 0.f, s2 = 0.f;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) s += red[g][tid];
+        for (int g = 0; g < 8; ++g) {
+            s += red[g][tid];
+            s2 += red2[g][tid];
+        }
         part[(size_t)blockIdx.y * part_stride + col_off + c0 + tid] = s;
+        if (part2) part2[(size_t)blockIdx.y * part_stride + col_off + c0 + tid] = s2;
     }
 }
 
@@ -352,11 +362,11 @@ int gram_split_blocks(int64_t n_b, int max_splits) {
 }
 
 hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,
-                             float* part, int part_stride, int col_off, int splits, hipStream_t s) {
+                             float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s) {
     const int nkb = (int)((n_b + SP_TOK - 1) / SP_TOK);
     const dim3 grid((cols + SP_COLS - 1) / SP_COLS, splits);
     hipLaunchKernelGGL(gram_split_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c, S, part,
-                       part_stride, col_off);
+                       part_stride, col_off, part2);
     return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct kvmap_ctx;
+
 namespace kvmap {
 
 // Element storage types.
@@ -30,6 +32,14 @@ hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, double theta_s,
 // layers[0..n_layers).
 hipError_t launch_derope(Elem e, const void* src, void* ws, const int32_t* layers, int n_layers,
                          const ApplyGeom& g, const float2* tab, hipStream_t s);
+
+// rows[t][(j*H + h)*d + e] = src[layers[j]][h][t][e], stripped with tab when tab != NULL.
+constexpr int kMaxRowLayers = 128;
+struct RowLayers {
+    int32_t l[kMaxRowLayers];
+};
+hipError_t launch_rows(Elem e, const void* src, void* out, const RowLayers& layers, int n_layers, int H,
+                       int64_t T, int d, const float2* tab, hipStream_t s);
 
 // ---- map GEMMs (gemm_bf16.hip, gemm_f32.hip) ----------------------------------------
 struct MapArgs {
@@ -66,6 +76,7 @@ hipError_t launch_count_nonfinite(Elem e, const void* p, int64_t n, unsigned int
 // ---- fit-side statistics (gram.hip) ------------------------------------------------
 struct GramScratch {
     float* part;   // [splits][p + q] partial column sums
+    float* part2;  // [splits][p + q] partial column sums of squares (y of a state with ss_y)
     float* cx;     // [p]  batch shift (fp32 column mean of x)
     float* cy;     // [q]
     float* mx;     // [p]  mean of (x - cx) over the batch (tiny correction)
@@ -80,20 +91,20 @@ struct GramScratch {
 size_t gram_scratch_floats(int p, int q, int splits);
 hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
                              int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
-                             float* M_xy, const GramScratch& sc, hipStream_t s);
+                             float* M_xy, float* ss_y, const GramScratch& sc, hipStream_t s);
 // Rows per kvmap_gram sub-batch: larger batches are merged in pieces of at most this many
 // rows (the split operands' scratch and 32-bit tile offsets are sized for it).
 constexpr int64_t kGramSubBatch = 16384;
 size_t gram_split_elems(int p, int q, int64_t n_b);  // uint16 elements of `split` for n_b rows
 int gram_split_blocks(int64_t n_b, int max_splits);
 hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,
-                             float* part, int part_stride, int col_off, int splits, hipStream_t s);
+                             float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s);
 hipError_t launch_gram_x3(const uint16_t* Sx, const uint16_t* Sy, int64_t n_b, int p, int q, const float* mx,
                           const float* my, const float* dx, const float* dy, float coef, int fresh,
                           float* M_xx, float* M_xy, hipStream_t s);
 hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
-                             float* mean_y, float* M_xx, float* M_xy, const float* s_mean_x,
-                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy,
+                             float* mean_y, float* M_xx, float* M_xy, float* ss_y, const float* s_mean_x,
+                             const float* s_mean_y, const float* s_M_xx, const float* s_M_xy, const float* s_ss_y,
                              const GramScratch& sc, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
@@ -102,6 +113,20 @@ size_t ridge_dev_scratch_bytes(int p, int q);
 hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
                             const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
                             void* scratch, int* bad, hipStream_t s);
+// r2_out[g] = in-sample R^2 of the ridge fit pooled over y columns g*group .. +group-1
+hipError_t launch_ridge_r2(int p, int q, const float* M_xx, const float* M_xy, const float* ss_y, double lambda,
+                           int group, double* r2_out, void* scratch, int* bad, hipStream_t s);
+
+// ---- fit driver's scoring kernel (fit.hip) ----------------------------------------------
+// scores[t][s] = mean over {K, V} and heads of r2[kv][s][t][h]; sel[t] = the k best s, ties to
+// the lower index, ascending.
+hipError_t launch_fit_select(const double* r2, int L_src, int L_tgt, int H, int k, double* scores,
+                             int32_t* sel, hipStream_t s);
+
+// Error reporting shared by the C-ABI files: sets the calling thread's last-error string.
+int report(int status, const char* fmt, ...);
+// HIP device a context is bound to (-1 for NULL).
+int context_device(const struct ::kvmap_ctx* c);
 
 }  // namespace kvmap
 

@@ -7,7 +7,9 @@
 //   A = L L^T    right-looking blocked Cholesky, 64-wide blocks: factor the diagonal block in
 //                one workgroup, solve the panel below it, update the trailing lower triangle
 //   L Z = B, L^T W = Z   blocked forward / back substitution over all right-hand sides
-//   b = mean_y - mean_x W;  W written output-major [q][p] in bf16 or fp32 (the apply's layout)
+//   b = mean_y - mean_x W;  W written output-major [q][p] in bf16 or fp32 (the apply's layout),
+//   or, for layer scoring, the in-sample R^2 of the fit pooled over groups of y columns, from
+//   the statistics alone: RSS_c = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2
 // Every update is a 64 x 64 fp64 tile C -= op(A) op(B) with K = 64 on the vector ALUs
 // (fp64 FMA runs at the same rate as the fp64 matrix cores on this chip).  A non-positive or
 // non-finite pivot sets a device flag that the host turns into KVMAP_ERR_NOT_SPD.
@@ -253,16 +255,64 @@ __global__ __launch_bounds__(256) void ridge_finalize_kernel(const double* __res
     }
 }
 
+// In-sample residual sum of squares of column c from the statistics alone.  With
+// yc = y - mean_y, xc = x - mean_x and (M_xx + lambda I) w = m (m = M_xy[:, c]):
+//   sum (yc - xc w)^2 = ss_y[c] - 2 w.m + w^T M_xx w = ss_y[c] - w.m - lambda |w|^2,
+// since w^T M_xx w = w^T (m - lambda w).  Workgroup: 64 columns; the 4 row groups are
+// reduced in a fixed order.
+__global__ __launch_bounds__(256) void ridge_rss_kernel(const double* __restrict__ W, int Q, int p, int q,
+                                                        const float* __restrict__ M_xy,
+                                                        const float* __restrict__ ss_y, double lambda,
+                                                        double* __restrict__ rss) {
+    __shared__ double pd[4][RB];
+    __shared__ double pn[4][RB];
+    const int tid = threadIdx.x;
+    const int cx = tid & 63, ry = tid >> 6;
+    const int c = (int)blockIdx.x * RB + cx;
+    double dot = 0.0, nrm = 0.0;
+    if (c < q) {
+        for (int i = ry; i < p; i += 4) {
+            const double w = W[(size_t)i * Q + c];
+            dot += w * (double)M_xy[(size_t)i * q + c];
+            nrm += w * w;
+        }
+    }
+    pd[ry][cx] = dot;
+    pn[ry][cx] = nrm;
+    __syncthreads();
+    if (ry == 0 && c < q) {
+        const double d = ((pd[0][cx] + pd[1][cx]) + pd[2][cx]) + pd[3][cx];
+        const double n2 = ((pn[0][cx] + pn[1][cx]) + pn[2][cx]) + pn[3][cx];
+        rss[c] = (double)ss_y[c] - d - lambda * n2;
+    }
+}
+
+// R^2 of group g (columns g*group .. g*group + group - 1) pooled over its columns:
+// 1 - sum RSS / sum ss_y; NaN when the group's total sum of squares is 0.
+__global__ __launch_bounds__(256) void ridge_r2_group_kernel(const double* __restrict__ rss,
+                                                             const float* __restrict__ ss_y, int groups,
+                                                             int group, double* __restrict__ r2) {
+    const int g = (int)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= groups) return;
+    double r = 0.0, t = 0.0;
+    for (int j = 0; j < group; ++j) {
+        r += rss[(size_t)g * group + j];
+        t += (double)ss_y[(size_t)g * group + j];
+    }
+    r2[g] = t > 0.0 ? 1.0 - r / t : __builtin_nan("");
+}
+
 // ---------------------------------------------------------------------------------------
 
 size_t ridge_dev_scratch_bytes(int p, int q) {
     const size_t P = ((size_t)p + RB - 1) / RB * RB, Q = ((size_t)q + RB - 1) / RB * RB;
-    return (P * P + P * Q) * sizeof(double) + 256;
+    return (P * P + P * Q + Q) * sizeof(double) + 256;  // A, B (then W), rss, pivot flag
 }
 
-hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
-                            const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
-                            void* scratch, int* bad, hipStream_t s) {
+// A = sym(M_xx) + lambda I = L L^T (lower triangle of A), then W = A^-1 M_xy in B = A + P^2,
+// row-major [P][Q].
+static void ridge_dev_solve(int p, int q, const float* M_xx, const float* M_xy, double lambda, void* scratch,
+                            int* bad, hipStream_t s) {
     const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
     const int nb = P / RB, nq = Q / RB;
     double* A = (double*)scratch;
@@ -290,12 +340,34 @@ hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean
         hipLaunchKernelGGL(ridge_trsm_rhs_kernel<false>, dim3(nq), dim3(RB), 0, s, A, P, B, Q, kb);
         if (kb > 0) hipLaunchKernelGGL(ridge_update_kernel<2>, dim3(kb * nq), dim3(256), 0, s, A, P, B, Q, kb, nq);
     }
+}
+
+hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
+                            const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
+                            void* scratch, int* bad, hipStream_t s) {
+    const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
+    const int nq = Q / RB;
+    const double* B = (const double*)scratch + (size_t)P * P;
+    ridge_dev_solve(p, q, M_xx, M_xy, lambda, scratch, bad, s);
     if (bf16)
         hipLaunchKernelGGL(ridge_finalize_kernel<true>, dim3(nq), dim3(256), 0, s, B, P, Q, p, q, mean_x, mean_y,
                            W_out, b_out);
     else
         hipLaunchKernelGGL(ridge_finalize_kernel<false>, dim3(nq), dim3(256), 0, s, B, P, Q, p, q, mean_x, mean_y,
                            W_out, b_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ridge_r2(int p, int q, const float* M_xx, const float* M_xy, const float* ss_y, double lambda,
+                           int group, double* r2_out, void* scratch, int* bad, hipStream_t s) {
+    const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
+    const double* B = (const double*)scratch + (size_t)P * P;
+    double* rss = (double*)scratch + (size_t)P * P + (size_t)P * Q;
+    ridge_dev_solve(p, q, M_xx, M_xy, lambda, scratch, bad, s);
+    hipLaunchKernelGGL(ridge_rss_kernel, dim3(Q / RB), dim3(256), 0, s, B, Q, p, q, M_xy, ss_y, lambda, rss);
+    const int groups = q / group;
+    hipLaunchKernelGGL(ridge_r2_group_kernel, dim3((groups + 255) / 256), dim3(256), 0, s, rss, ss_y, groups, group,
+                       r2_out);
     return hipGetLastError();
 }
 

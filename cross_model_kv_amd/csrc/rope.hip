@@ -195,6 +195,90 @@ hipError_t launch_derope(Elem e, const void* src, void* ws, const int32_t* layer
 }
 
 // ---------------------------------------------------------------------------------------
+// Rows for the fit-side statistics: out[t][(j*H + h)*d + e] = layer layers[j], head h, token t,
+// element e of a cache [L][H][T][d], optionally with its RoPE stripped (the content space in
+// which the maps are fitted, VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping": keys are
+// de-rotated with each model's own rotation before any statistics).  Same thread layout as the
+// producer above; each (layer, head) slab of a token row lands as d contiguous elements of
+// the output row.
+// ---------------------------------------------------------------------------------------
+
+template <bool BF16, int D, bool STRIP>
+__global__ __launch_bounds__(256) void rows_kernel(const void* __restrict__ src, void* __restrict__ out,
+                                                   RowLayers layers, int n_layers, int H, int64_t T,
+                                                   const float2* __restrict__ tab) {
+    using V = Vec16<BF16>;
+    constexpr int ES = BF16 ? 2 : 4;
+    constexpr int VEC = V::N;
+    constexpr int HALF = D / 2;
+    constexpr int TPR = HALF / VEC;
+    constexpr int RPB = 256 / TPR;
+    const int tid = threadIdx.x;
+    const int q = tid % TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+    if (row >= T) return;
+    float c[VEC], s[VEC];
+    if (STRIP) {
+        const float4* tr = (const float4*)(tab + row * HALF + q * VEC);
+#pragma unroll
+        for (int v = 0; v < VEC / 2; ++v) {
+            const float4 cs = tr[v];
+            c[2 * v] = cs.x; s[2 * v] = cs.y;
+            c[2 * v + 1] = cs.z; s[2 * v + 1] = cs.w;
+        }
+    }
+    const char* srcb = (const char*)src;
+    char* outb = (char*)out;
+    const int nslabs = n_layers * H;
+    for (int sl = blockIdx.y; sl < nslabs; sl += gridDim.y) {
+        const int j = sl / H, h = sl - (sl / H) * H;
+        const size_t in_off = ((((size_t)layers.l[j] * H + h) * (size_t)T + (size_t)row) * D + q * VEC) * ES;
+        const size_t out_off = (((size_t)row * nslabs + sl) * D + q * VEC) * ES;
+        V lo, hi;
+        lo.load(srcb + in_off);
+        hi.load(srcb + in_off + HALF * ES);
+        float ol[VEC], oh[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float xl = lo.get(v), xh = hi.get(v);
+            if (STRIP) {
+                ol[v] = fmaf(xh, s[v], xl * c[v]);  // rotate by -a
+                oh[v] = fmaf(-xl, s[v], xh * c[v]);
+            } else {
+                ol[v] = xl;
+                oh[v] = xh;
+            }
+        }
+        V::store(outb + out_off, ol);
+        V::store(outb + out_off + HALF * ES, oh);
+    }
+}
+
+hipError_t launch_rows(Elem e, const void* src, void* out, const RowLayers& layers, int n_layers, int H,
+                       int64_t T, int d, const float2* tab, hipStream_t s) {
+    const int vec = (e == Elem::BF16) ? 8 : 4;
+    const int rpb = 256 / ((d / 2) / vec);
+    const int64_t bx = (T + rpb - 1) / rpb;
+    const int nslabs = n_layers * H;
+    int64_t by = (4096 + bx - 1) / bx;
+    if (by > nslabs) by = nslabs;
+    if (by < 1) by = 1;
+    const dim3 grid((unsigned)bx, (unsigned)by);
+#define KVMAP_ROWS(B, D, S) \
+    hipLaunchKernelGGL((rows_kernel<B, D, S>), grid, dim3(256), 0, s, src, out, layers, n_layers, H, T, tab)
+    const bool strip = tab != nullptr;
+    if (e == Elem::BF16) {
+        if (d == 128) { if (strip) KVMAP_ROWS(true, 128, true); else KVMAP_ROWS(true, 128, false); }
+        else { if (strip) KVMAP_ROWS(true, 64, true); else KVMAP_ROWS(true, 64, false); }
+    } else {
+        if (d == 128) { if (strip) KVMAP_ROWS(false, 128, true); else KVMAP_ROWS(false, 128, false); }
+        else { if (strip) KVMAP_ROWS(false, 64, true); else KVMAP_ROWS(false, 64, false); }
+    }
+#undef KVMAP_ROWS
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // Non-finite scan (optional guard: reject NaN/Inf mapped caches rather than pass them on,
 // as the KVBridge README's "Failure is a first-class outcome" section asks of a guarded
 // transfer).

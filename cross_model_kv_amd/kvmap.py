@@ -51,7 +51,22 @@ class Rope(ctypes.Structure):
 class GramStateC(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("p", ctypes.c_int32), ("q", ctypes.c_int32),
                 ("mean_x", ctypes.c_void_p), ("mean_y", ctypes.c_void_p),
-                ("M_xx", ctypes.c_void_p), ("M_xy", ctypes.c_void_p)]
+                ("M_xx", ctypes.c_void_p), ("M_xy", ctypes.c_void_p), ("ss_y", ctypes.c_void_p)]
+
+
+class FitConfigC(ctypes.Structure):
+    _fields_ = [("L_src", ctypes.c_int32), ("L_tgt", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("select_block", ctypes.c_int32), ("map_block", ctypes.c_int32),
+                ("given_sel", ctypes.c_int32), ("theta_src", ctypes.c_double), ("theta_tgt", ctypes.c_double),
+                ("lambda_", ctypes.c_double), ("layer_sel", ctypes.c_void_p), ("scores", ctypes.c_void_p),
+                ("W_k", ctypes.c_void_p), ("b_k", ctypes.c_void_p), ("W_v", ctypes.c_void_p),
+                ("b_v", ctypes.c_void_p)]
+
+
+class FitPassC(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_int32), ("t_begin", ctypes.c_int32), ("t_end", ctypes.c_int32),
+                ("pass_", ctypes.c_int32), ("passes", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +88,9 @@ _SIGS = {
     "kvmap_recode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
                                     ctypes.c_void_p]),
+    "kvmap_cache_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.POINTER(Rope), ctypes.c_void_p, ctypes.c_void_p]),
     "kvmap_gram_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
     "kvmap_gram": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
@@ -85,6 +103,13 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "kvmap_ridge_solve_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "kvmap_ridge_r2": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "kvmap_fit_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(FitConfigC), ctypes.POINTER(ctypes.c_void_p)]),
+    "kvmap_fit_next_pass": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(FitPassC), ctypes.c_void_p]),
+    "kvmap_fit_add": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "kvmap_fit_destroy": (ctypes.c_int, [ctypes.c_void_p]),
 }
 
 
@@ -191,10 +216,16 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-class GramState:
-    """Device-resident centered statistics (n, mean_x, mean_y, M_xx, M_xy) of kvmap_gram."""
+def _chain(first, rest):
+    yield from first
+    yield from rest
 
-    def __init__(self, p: int, q: int, device):
+
+class GramState:
+    """Device-resident centered statistics (n, mean_x, mean_y, M_xx, M_xy and, with
+    keep_ss_y, the per-column centered sum of squares ss_y) of kvmap_gram."""
+
+    def __init__(self, p: int, q: int, device, keep_ss_y: bool = False):
         torch = _torch()
         self.p, self.q, self.device = int(p), int(q), torch.device(device)
         kw = dict(dtype=torch.float32, device=self.device)
@@ -202,8 +233,10 @@ class GramState:
         self.mean_y = torch.zeros(q, **kw)
         self.M_xx = torch.zeros(p, p, **kw)
         self.M_xy = torch.zeros(p, q, **kw)
+        self.ss_y = torch.zeros(q, **kw) if keep_ss_y else None
         self.c = GramStateC(0, self.p, self.q, self.mean_x.data_ptr(), self.mean_y.data_ptr(),
-                            self.M_xx.data_ptr(), self.M_xy.data_ptr())
+                            self.M_xx.data_ptr(), self.M_xy.data_ptr(),
+                            self.ss_y.data_ptr() if keep_ss_y else None)
 
     @property
     def n(self) -> int:
@@ -308,8 +341,26 @@ class Context:
         return out
 
     # ---- fit-side statistics ---------------------------------------------------------
-    def gram_state(self, p: int, q: int) -> GramState:
-        return GramState(p, q, f"cuda:{self.device}")
+    def cache_rows(self, cache, layers, theta: float | None = None, pos0: int = 0, out=None, stream=None,
+                   style: int = ROPE_HALF_SPLIT):
+        """kvmap_cache_rows: rows [T][len(layers) * H * d] of the layers of cache [L][H][T][d]
+        (device, bf16 or fp32), RoPE stripped at (theta, pos0) unless theta is None."""
+        torch = _torch()
+        L, H, T, d = (int(x) for x in cache.shape)
+        lay = np.ascontiguousarray(np.asarray(layers, dtype=np.int32).reshape(-1))
+        width = len(lay) * H * d
+        if out is None:
+            out = torch.empty((T, width), dtype=cache.dtype, device=cache.device)
+        if tuple(out.shape) != (T, width) or out.dtype != cache.dtype:
+            raise ValueError(f"out must be [T={T}][{width}] of the cache dtype")
+        rope = None if theta is None else ctypes.byref(Rope(float(theta), int(pos0), int(style)))
+        _check(lib().kvmap_cache_rows(self._h, _dev_ptr(cache, "cache"), L, H, T, d, _dtype_code(cache),
+                                      lay.ctypes.data, len(lay), rope, _dev_ptr(out, "out"),
+                                      _stream_handle(stream, cache.device)), "kvmap_cache_rows")
+        return out
+
+    def gram_state(self, p: int, q: int, keep_ss_y: bool = False) -> GramState:
+        return GramState(p, q, f"cuda:{self.device}", keep_ss_y)
 
     def gram_reset(self, st: GramState, stream=None):
         _check(lib().kvmap_gram_reset(self._h, ctypes.byref(st.c), _stream_handle(stream, st.device)),
@@ -348,6 +399,88 @@ class Context:
                                               _dev_ptr(b_out, "b_out"), _dtype_code(W_out),
                                               _stream_handle(stream, st.device)), "kvmap_ridge_solve_device")
         return W_out, b_out
+
+    def ridge_r2(self, st: GramState, lam: float, group: int, out=None, stream=None):
+        """kvmap_ridge_r2: in-sample R^2 of the ridge fit of st, pooled over groups of `group`
+        y columns -> device float64 [q / group].  The state must keep ss_y."""
+        torch = _torch()
+        if out is None:  # a group that does not divide q is the library's to refuse
+            out = torch.empty((max(1, st.q // max(1, int(group))),), dtype=torch.float64, device=st.device)
+        elif out.dtype != torch.float64 or out.numel() * int(group) != st.q:
+            raise ValueError("out must be float64 [q / group]")
+        _check(lib().kvmap_ridge_r2(self._h, ctypes.byref(st.c), float(lam), int(group), _dev_ptr(out, "out"),
+                                    _stream_handle(stream, st.device)), "kvmap_ridge_r2")
+        return out
+
+    def fit(self, calibration, *, L_src: int, L_tgt: int, H: int, d: int, k: int, theta_src: float,
+            theta_tgt: float, lam: float, out_dtype=None, layer_sel=None, select_block: int = 0,
+            map_block: int = 0, stream=None) -> dict:
+        """kvmap_fit_*: the two-stage fit (selection, then maps) over re-iterable calibration data.
+
+        `calibration` is a callable returning an iterable of (src_k, src_v, tgt_k, tgt_v, pos0):
+        device caches [L_src][H][T][d] and [L_tgt][H][T][d] of one sequence (keys stored rotated)
+        and its first position; it is called once per pass and must yield the same sequences
+        each time.  layer_sel (device int32 [L_tgt][k]) skips the selection stage.
+        Returns dict(layer_sel, scores (None with a given layer_sel), W_k, b_k, W_v, b_v); the maps
+        are output-major [L_tgt][H*d][k*H*d] in out_dtype (default: the caches' dtype)."""
+        torch = _torch()
+        dev = torch.device(f"cuda:{self.device}")
+        N, F = H * d, k * H * d
+        given = layer_sel is not None
+        if given:
+            layer_sel = layer_sel.to(device=dev, dtype=torch.int32).contiguous()
+            if tuple(layer_sel.shape) != (L_tgt, k):
+                raise ValueError(f"layer_sel must be [{L_tgt}][{k}]")
+            scores = None
+        else:
+            layer_sel = torch.empty((L_tgt, k), dtype=torch.int32, device=dev)
+            scores = torch.empty((L_tgt, L_src), dtype=torch.float64, device=dev)
+        maps = {}
+        dtype_in = None
+        h = ctypes.c_void_p()
+        try:
+            info = FitPassC()
+            first = True
+            while True:
+                if first:
+                    # the caches' dtype fixes the config: peek at the first sequence
+                    it = iter(calibration())
+                    seq = next(it, None)
+                    if seq is None:
+                        raise ValueError("calibration yields no sequence")
+                    dtype_in = seq[0].dtype
+                    odt = out_dtype if out_dtype is not None else dtype_in
+                    for name, shape in (("W_k", (L_tgt, N, F)), ("b_k", (L_tgt, N)), ("W_v", (L_tgt, N, F)),
+                                        ("b_v", (L_tgt, N))):
+                        maps[name] = torch.empty(shape, dtype=odt, device=dev)
+                    cfg = FitConfigC(int(L_src), int(L_tgt), int(H), int(d), int(k), _dtype_code(seq[0]),
+                                     _dtype_code(maps["W_k"]), int(select_block), int(map_block), int(given),
+                                     float(theta_src), float(theta_tgt), float(lam), layer_sel.data_ptr(),
+                                     scores.data_ptr() if scores is not None else None,
+                                     *(maps[n].data_ptr() for n in ("W_k", "b_k", "W_v", "b_v")))
+                    _check(lib().kvmap_fit_create(self._h, ctypes.byref(cfg), ctypes.byref(h)), "kvmap_fit_create")
+                    seqs = [seq]
+                    first = False
+                else:
+                    it, seqs = iter(calibration()), []
+                sh = _stream_handle(stream, dev)
+                _check(lib().kvmap_fit_next_pass(h, ctypes.byref(info), sh), "kvmap_fit_next_pass")
+                if info.stage == 0:
+                    break
+                for seq in _chain(seqs, it):
+                    sk, sv, tk, tv, pos0 = seq
+                    if (tuple(sk.shape) != (L_src, H, sk.shape[2], d) or tuple(sv.shape) != tuple(sk.shape)
+                            or tuple(tk.shape) != (L_tgt, H, sk.shape[2], d) or tuple(tv.shape) != tuple(tk.shape)):
+                        raise ValueError("calibration caches must be [L_src][H][T][d] / [L_tgt][H][T][d]")
+                    if any(t.dtype != dtype_in for t in (sk, sv, tk, tv)):
+                        raise TypeError("calibration caches must share one dtype")
+                    _check(lib().kvmap_fit_add(h, _dev_ptr(sk, "src_k"), _dev_ptr(sv, "src_v"), _dev_ptr(tk, "tgt_k"),
+                                               _dev_ptr(tv, "tgt_v"), int(sk.shape[2]), int(pos0), sh),
+                           "kvmap_fit_add")
+        finally:
+            if h.value:
+                lib().kvmap_fit_destroy(h)
+        return dict(layer_sel=layer_sel, scores=scores, **maps)
 
     def ridge_solve(self, st: GramState, lam: float, stream=None):
         """kvmap_ridge_solve: (W [q][p] output-major float32, b [q]) on the host."""

@@ -187,13 +187,32 @@ int kvmap_recode(kvmap_ctx* ctx, int32_t rows, int64_t T, int32_t head_dim, int3
 
 /* ---- fit-side statistics ----------------------------------------------------------- */
 
+/* Rows of calibration caches for kvmap_gram (KVBridge README "What ships": cross-head
+ * features of the selected layers; VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping":
+ * keys are moved to content space with the model's own rotation before any statistics):
+ *   out[t][(j * H + h) * head_dim + e] = strip(cache[layers[j]][h][t][:], pos0 + t, theta)[e]
+ * for j < n_layers (the order given), or the plain value when rope == NULL (values, or keys
+ * already in content space).
+ *   cache   device [L][H][T][head_dim], bf16 or fp32;  out  device [T][n_layers * H * head_dim]
+ *   layers  host [n_layers], each in [0, L), 1 <= n_layers <= 128;  head_dim 64 or 128
+ * Pointers 16-byte aligned, out not overlapping the cache.  Asynchronous on `stream`.
+ * Errors: SHAPE, UNSUPPORTED, INVALID_ARGUMENT (nothing written). */
+int kvmap_cache_rows(kvmap_ctx* ctx, const void* cache, int32_t L, int32_t H, int64_t T, int32_t head_dim,
+                     int32_t dtype, const int32_t* layers, int32_t n_layers, const kvmap_rope* rope, void* out,
+                     void* stream);
+
 /* Centered sufficient statistics of a stream of (x, y) rows, x in R^p, y in R^q:
  *   n       rows merged so far (host integer, updated by the calls)
  *   mean_x  device fp32 [p],  mean_y device fp32 [q]
  *   M_xx    device fp32 [p][p]  = sum (x - mean_x)(x - mean_x)^T   (unnormalised, both
  *                                 triangles stored)
  *   M_xy    device fp32 [p][q]  = sum (x - mean_x)(y - mean_y)^T
- * Buffers are caller-allocated device memory; the struct only points at them. */
+ *   ss_y    device fp32 [q] or NULL = sum (y - mean_y)^2 per column (the diagonal of the
+ *           y-y co-moments, which the fit itself never needs; layer scoring takes the total
+ *           sum of squares from it).  NULL: not kept.  States merged together must agree
+ *           on keeping it.
+ * Buffers are caller-allocated device memory, 16-byte aligned; the struct only points at
+ * them. */
 typedef struct {
     int64_t n;
     int32_t p, q;
@@ -201,6 +220,7 @@ typedef struct {
     float* mean_y;
     float* M_xx;
     float* M_xy;
+    float* ss_y;
 } kvmap_gram_state;
 
 /* Zero the state's device arrays on `stream` and set n = 0. */
@@ -257,6 +277,88 @@ int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
  * written). */
 int kvmap_ridge_solve_device(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, void* W_out,
                              void* b_out, int32_t dtype, void* stream);
+
+/* In-sample R^2 of that ridge fit, pooled over groups of `group` consecutive y columns
+ * (one target KV head's head_dim outputs: the per-head score of the layer selection, KVBridge
+ * README "What ships": head-averaged single-source R^2).  For group g
+ *   R^2_g = 1 - sum_c RSS_c / sum_c ss_y[c]   over its columns c,
+ *   RSS_c = sum_rows (y_c - yhat_c)^2 = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2,
+ * the last form following from (M_xx + lambda I) w_c = M_xy[:, c]; it needs the state's
+ * ss_y (INVALID_ARGUMENT without it).  The solve is the fp64 one of kvmap_ridge_solve_device
+ * (same scratch, plus q doubles).  r2_out: device fp64 [q / group], 8-byte aligned; NaN for a
+ * group whose total sum of squares is 0.  group must divide q (SHAPE).  Synchronous;
+ * KVMAP_ERR_NOT_SPD as kvmap_ridge_solve_device. */
+int kvmap_ridge_r2(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, int32_t group, double* r2_out,
+                   void* stream);
+
+/* ---- end-to-end fit: layer selection, then the maps (KVBridge README, fitting section
+ * headed "Loading": a two-stage, multi-pass fit over re-iterable calibration data that keeps
+ * only centered statistics and bounds memory by blocks of target layers) -------------------
+ *
+ * Stage 1, selection: for every target layer t and source layer s, single-source ridge maps
+ *   from all H*d features of source layer s to all H*d outputs of target layer t, for K and
+ *   for V; the in-sample R^2 pooled per target head, averaged over heads and {K, V}, scores
+ *   the pair; the k best s per t win (ties to the lower index), kept ascending ("What ships":
+ *   head-averaged single-source R^2, then top-k cross-layer features).  One Gram state per
+ *   (source layer, K/V) against the rows of a block of target layers (X = the source layer's
+ *   rows, p = H*d; Y = the block's rows, q = block*H*d), so M_xx is shared by the block.
+ * Stage 2, maps: per (target layer, K/V) the statistics of the selected layers' rows
+ *   (p = k*H*d) against the target layer's rows (q = H*d), solved on the device in fp64 into
+ *   the apply's layout.
+ * Keys enter every statistic in content space: each model's own RoPE is stripped first
+ * (VeloxQuant-MLX "The mapping").  Rows are tokens; columns follow kvmap_cache_rows.
+ *
+ * Protocol: kvmap_fit_next_pass ends the open pass (if any) and opens the next one; the
+ * caller then feeds the SAME calibration sequences, in any order, with kvmap_fit_add, and
+ * calls kvmap_fit_next_pass again, until it reports stage 0 (done).  Every pass must see the
+ * same number of tokens (SHAPE otherwise). */
+typedef struct {
+    int32_t L_src, L_tgt, H_kv, head_dim, k;
+    int32_t dtype;         /* kvmap_dtype of the calibration caches                          */
+    int32_t out_dtype;     /* kvmap_dtype of W and b                                          */
+    int32_t select_block;  /* target layers per selection pass; 0 = as many as fit one state
+                              (block*H*d <= 65536, <= 128 layers)                              */
+    int32_t map_block;     /* target layers per map pass; 0 = all                             */
+    int32_t given_sel;     /* nonzero: layer_sel is an input and there is no selection stage  */
+    double theta_src;      /* RoPE bases of the two models (> 0)                              */
+    double theta_tgt;
+    double lambda;         /* ridge penalty on the unnormalised centered Gram (>= 0)          */
+    int32_t* layer_sel;    /* device [L_tgt][k] int32: written by stage 1, or read (given_sel) */
+    double* scores;        /* device [L_tgt][L_src] fp64 selection scores, or NULL            */
+    void* W_k;             /* device [L_tgt][H*d][k*H*d] output-major, out_dtype              */
+    void* b_k;             /* device [L_tgt][H*d], out_dtype                                   */
+    void* W_v;
+    void* b_v;
+} kvmap_fit_config;
+
+typedef struct {
+    int32_t stage;         /* 1 selection, 2 maps, 0 done                                     */
+    int32_t t_begin;       /* target layers of this pass: [t_begin, t_end)                    */
+    int32_t t_end;
+    int32_t pass;          /* 0-based index of this pass among all passes                      */
+    int32_t passes;        /* total passes of the fit                                          */
+} kvmap_fit_pass;
+
+typedef struct kvmap_fit kvmap_fit;
+
+/* Validate cfg and create a fit on ctx (the fit uses ctx's scratch: one fit per context at a
+ * time).  Device memory is allocated per stage: stage 1 holds 2*L_src states of
+ * 4*(p + 2q + p^2 + p*q) bytes (p = H*d, q = block*H*d), stage 2 holds 2*block states of
+ * 4*(F + N + F^2 + F*N) bytes (F = k*H*d, N = H*d), plus row buffers of T rows.  With
+ * given_sel the selection is copied to the host and checked (distinct, in range) here.
+ * Synchronous. */
+int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvmap_fit** out);
+/* End the open pass (stage 1: score its block; the last stage-1 pass also selects and
+ * writes layer_sel / scores; stage 2: solve its block's maps into W / b) and open the next.
+ * Synchronous.  *info describes the pass now open (stage 0: the fit is complete). */
+int kvmap_fit_next_pass(kvmap_fit* fit, kvmap_fit_pass* info, void* stream);
+/* Feed one calibration sequence of T tokens at positions pos0 .. pos0 + T - 1 to the open
+ * pass: src_k/src_v device [L_src][H][T][d], tgt_k/tgt_v device [L_tgt][H][T][d], keys stored
+ * rotated by their model, in cfg.dtype, 16-byte aligned.  Asynchronous on `stream`. */
+int kvmap_fit_add(kvmap_fit* fit, const void* src_k, const void* src_v, const void* tgt_k, const void* tgt_v,
+                  int64_t T, int64_t pos0, void* stream);
+/* Free the fit's device memory (synchronises the device). NULL is a no-op. */
+int kvmap_fit_destroy(kvmap_fit* fit);
 
 #ifdef __cplusplus
 }

@@ -177,11 +177,17 @@ def apply_rows(src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src, theta_tgt
 # ---------------------------------------------------------------------------
 
 def stats_empty(p: int, q: int) -> dict:
-    return dict(n=0, mx=np.zeros(p), my=np.zeros(q), Mxx=np.zeros((p, p)), Mxy=np.zeros((p, q)))
+    return dict(n=0, mx=np.zeros(p), my=np.zeros(q), Mxx=np.zeros((p, p)), Mxy=np.zeros((p, q)),
+                ssy=np.zeros(q))
 
 
 def stats_two_pass(X: np.ndarray, Y: np.ndarray) -> dict:
-    """Textbook two-pass statistics: means, then unnormalised centered co-moments."""
+    """Textbook two-pass statistics: means, then unnormalised centered co-moments.
+
+    ssy is the per-column centered sum of squares of y (the diagonal of the y-y co-moments):
+    the total sum of squares that an R^2 of a fitted map divides by ([KVB] "What ships":
+    layers are ranked by R^2).
+    """
     X = np.asarray(X, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
     n = X.shape[0]
@@ -189,14 +195,15 @@ def stats_two_pass(X: np.ndarray, Y: np.ndarray) -> dict:
         return stats_empty(X.shape[1], Y.shape[1])
     mx, my = X.mean(axis=0), Y.mean(axis=0)
     Xc, Yc = X - mx, Y - my
-    return dict(n=n, mx=mx, my=my, Mxx=Xc.T @ Xc, Mxy=Xc.T @ Yc)
+    return dict(n=n, mx=mx, my=my, Mxx=Xc.T @ Xc, Mxy=Xc.T @ Yc, ssy=np.sum(Yc * Yc, axis=0))
 
 
 def chan_merge(a: dict, b: dict) -> dict:
     """Combine two statistics of disjoint samples (Chan, Golub & LeVeque pairwise update).
 
     n = na + nb, delta = mean_b - mean_a, mean = mean_a + delta * nb / n,
-    M = Ma + Mb + (na * nb / n) * delta_x delta_y^T.  An empty side is the identity.
+    M = Ma + Mb + (na * nb / n) * delta_x delta_y^T (ssy likewise, with delta_y squared).
+    An empty side is the identity.
     """
     na, nb = a["n"], b["n"]
     if nb == 0:
@@ -210,7 +217,8 @@ def chan_merge(a: dict, b: dict) -> dict:
                 mx=a["mx"] + dx * (nb / n),
                 my=a["my"] + dy * (nb / n),
                 Mxx=a["Mxx"] + b["Mxx"] + f * np.outer(dx, dx),
-                Mxy=a["Mxy"] + b["Mxy"] + f * np.outer(dx, dy))
+                Mxy=a["Mxy"] + b["Mxy"] + f * np.outer(dx, dy),
+                ssy=a["ssy"] + b["ssy"] + f * dy * dy)
 
 
 def stats_streamed(batches) -> dict:
@@ -233,7 +241,8 @@ def stats_exact(X, Y) -> dict:
     Mxx = [[sum((r[i] - mx[i]) * (r[j] - mx[j]) for r in Xf) for j in range(p)] for i in range(p)]
     Mxy = [[sum((rx[i] - mx[i]) * (ry[j] - my[j]) for rx, ry in zip(Xf, Yf)) for j in range(q)]
            for i in range(p)]
-    return dict(n=n, mx=mx, my=my, Mxx=Mxx, Mxy=Mxy)
+    ssy = [sum((ry[j] - my[j]) ** 2 for ry in Yf) for j in range(q)]
+    return dict(n=n, mx=mx, my=my, Mxx=Mxx, Mxy=Mxy, ssy=ssy)
 
 
 # ---------------------------------------------------------------------------

@@ -258,6 +258,8 @@ def pin_stats_exact_rational():
     for key in ("Mxx", "Mxy"):
         ref = np.array([[float(v) for v in row] for row in ex[key]])
         assert np.max(np.abs(st[key] - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+    ref = np.array([float(v) for v in ex["ssy"]])
+    assert np.max(np.abs(st["ssy"] - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
 
 
 def pin_chan_streaming_equals_two_pass():
@@ -272,13 +274,13 @@ def pin_chan_streaming_equals_two_pass():
         for order in (parts, parts[::-1]):
             st = oracle.stats_streamed(order)
             assert st["n"] == ref["n"]
-            for key in ("mx", "my", "Mxx", "Mxy"):
+            for key in ("mx", "my", "Mxx", "Mxy", "ssy"):
                 assert np.allclose(st[key], ref[key], rtol=1e-12, atol=1e-10)
     e = oracle.stats_empty(6, 4)
     m = oracle.chan_merge(ref, e)
-    assert all(np.array_equal(m[k], ref[k]) for k in ("mx", "my", "Mxx", "Mxy"))
+    assert all(np.array_equal(m[k], ref[k]) for k in ("mx", "my", "Mxx", "Mxy", "ssy"))
     m = oracle.chan_merge(e, ref)
-    assert all(np.array_equal(m[k], ref[k]) for k in ("mx", "my", "Mxx", "Mxy"))
+    assert all(np.array_equal(m[k], ref[k]) for k in ("mx", "my", "Mxx", "Mxy", "ssy"))
 
 
 # ---------------------------------------------------------------------------
@@ -323,6 +325,25 @@ def pin_ridge_recovers_hidden_map():
     assert np.max(np.abs(b - bt)) < 1e-3
 
 
+def pin_r2_textbook():
+    """r2_pooled of an ordinary least-squares fit with intercept of one column on one regressor
+    is the squared Pearson correlation (numpy.corrcoef); predicting the column means gives 0,
+    an exact prediction 1; pooling two columns weights each by its total sum of squares."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(500) * 2.0 + 1.0
+    y = 0.3 * x + rng.standard_normal(500) - 4.0
+    slope, icept = np.polyfit(x, y, 1)
+    r2 = oracle.r2_pooled(y[:, None], (slope * x + icept)[:, None])
+    assert abs(r2 - np.corrcoef(x, y)[0, 1] ** 2) < 1e-12
+    Y = np.stack([y, 10.0 * rng.standard_normal(500) + 7.0], axis=1)
+    assert abs(oracle.r2_pooled(Y, np.broadcast_to(Y.mean(0), Y.shape))) < 1e-15
+    assert oracle.r2_pooled(Y, Y) == 1.0
+    # column 0 fitted as above, column 1 by its mean: pooled R^2 = (r2 * tss0) / (tss0 + tss1)
+    yhat = np.stack([slope * x + icept, np.full(500, Y[:, 1].mean())], axis=1)
+    t0, t1 = np.var(Y[:, 0]) * 500, np.var(Y[:, 1]) * 500
+    assert abs(oracle.r2_pooled(Y, yhat) - r2 * t0 / (t0 + t1)) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # Selection + full fit (KVBridge README "Thirty-second proof" and "Local evidence")
 # ---------------------------------------------------------------------------
@@ -361,5 +382,5 @@ ALL_PINS = [
     pin_rope_identity_at_zero_and_norm, pin_recode_single_rotation, pin_identity_map_copies_cache,
     pin_identity_map_recodes_keys, pin_apply_brute_force, pin_apply_rows_and_content_space,
     pin_planner_shape_arithmetic, pin_stats_exact_rational, pin_chan_streaming_equals_two_pass,
-    pin_ridge_limits, pin_ridge_recovers_hidden_map, pin_fitcheck_recovers_hidden_map,
+    pin_ridge_limits, pin_ridge_recovers_hidden_map, pin_r2_textbook, pin_fitcheck_recovers_hidden_map,
 ]

@@ -7,6 +7,8 @@ import oracle
 import oracle.kvmap_oracle as K
 import oracle_pins as P
 
+_ORIG = {"chan_merge": K.chan_merge}
+
 
 def _patch(monkeypatch, name, fn):
     monkeypatch.setattr(K, name, fn)
@@ -73,6 +75,18 @@ def _merge_wrong_weight(a, b):
                 Mxx=a["Mxx"] + b["Mxx"] + f * np.outer(dx, dx), Mxy=a["Mxy"] + b["Mxy"] + f * np.outer(dx, dy))
 
 
+def _merge_ssy_no_cross_term(a, b):
+    m = _ORIG["chan_merge"](a, b)
+    if a["n"] and b["n"]:
+        m["ssy"] = a["ssy"] + b["ssy"]
+    return m
+
+
+def _r2_uncentered_total(y, yhat):
+    y = np.asarray(y, dtype=np.float64)
+    return 1.0 - np.sum((y - yhat) ** 2) / np.sum(y ** 2)
+
+
 def _ridge_wrong_intercept(st, lam):
     W = np.linalg.solve(st["Mxx"] + lam * np.eye(st["Mxx"].shape[0]), st["Mxy"])
     return W, st["my"] + st["mx"] @ W
@@ -107,6 +121,8 @@ MUTANTS = {
     "head-split-interleaved": ("_heads", _heads_interleaved),
     "chan-missing-cross-term": ("chan_merge", _merge_no_cross_term),
     "chan-wrong-mean-weight": ("chan_merge", _merge_wrong_weight),
+    "chan-ssy-missing-cross-term": ("chan_merge", _merge_ssy_no_cross_term),
+    "r2-total-not-centered": ("r2_pooled", _r2_uncentered_total),
     "ridge-intercept-sign": ("ridge", _ridge_wrong_intercept),
     "ridge-lambda-times-n": ("ridge", _ridge_penalise_scaled),
     "stats-not-centered": ("stats_two_pass", _two_pass_uncentered),
