@@ -19,6 +19,8 @@ fit        the fit side on its own workload (262,144 calibration tokens, p 8192,
            4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
            with HIP events on its stream; one ridge solve of the merged state on the host and one
            on the device (fp64, W written in bf16 output-major)
+fit_driver the complete two-stage fit (layer selection, then the maps) at the 14B->32B model shape
+           over --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per stage
 """
 
 from __future__ import annotations
@@ -191,6 +193,84 @@ def fit_leg(K, batches_timed=16, warmup=2, cpu=True):
             "ridge_flop": p ** 3 / 3 + 2 * p * p * q}
 
 
+def fit_driver_cpu_baseline(n_tok, L_src, L_tgt, H, d, k, lam, budget_s=30.0):
+    """The oracle's fit on a bounded sample: one selection unit (single-source ridge + in-sample
+    R^2 of one (target, source) pair, K or V) and one map unit (ridge of k*H*d features to H*d
+    outputs) on n_tok seeded tokens, extrapolated to the whole fit (2 L_src L_tgt selection units,
+    2 L_tgt map units); calibration tokens/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    rng = np.random.default_rng(77)
+    N, F = H * d, k * H * d
+    n = min(n_tok, 4096)
+    Y = rng.standard_normal((n, N))
+    t0 = time.perf_counter()
+    X = rng.standard_normal((n, N))
+    W, b = oracle.ridge(oracle.stats_two_pass(X, Y), lam)
+    Yh = X @ W + b
+    _ = [oracle.r2_pooled(Y[:, h * d:(h + 1) * d], Yh[:, h * d:(h + 1) * d]) for h in range(H)]
+    t_sel = time.perf_counter() - t0
+    X = rng.standard_normal((n, F))
+    t0 = time.perf_counter()
+    oracle.ridge(oracle.stats_two_pass(X, Y), lam)
+    t_map = time.perf_counter() - t0
+    # statistics scale with the tokens, the solves do not: scale the whole unit (a lower bound)
+    total = (2 * L_src * L_tgt * t_sel + 2 * L_tgt * t_map) * (n_tok / n)
+    return {"value": n_tok / total, "unit": "calibration tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"1 selection unit ({t_sel:.2f} s) and 1 map unit ({t_map:.2f} s) on {n} tokens, fp64 numpy, "
+                      f"extrapolated to {2 * L_src * L_tgt} + {2 * L_tgt} units over {n_tok} tokens: {total:.0f} s"}
+
+
+def fit_driver_leg(K, n_seqs=8, T=4096, cpu=True):
+    """The complete two-stage fit (kvmap_fit_*) at the 14B->32B model shape: 40 source and 64
+    target layers, H 8, d 128, k 8, lambda 0.01, over n_seqs seeded bf16 calibration sequences
+    of T tokens resident in HBM.  Stage 1 scores all 2560 (target, source) pairs for K and V;
+    stage 2 fits and solves 128 maps of 8192 x 1024.  Wall time per pass from the pass callbacks
+    (each kvmap_fit_next_pass returns after the solves of the pass it closes)."""
+    import torch
+    L_src, L_tgt, H, d, k, lam = 40, 64, 8, 128, 8, 0.01
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(20261202)
+
+    def cache(L):
+        scale = torch.exp(0.5 * torch.randn((L, H, 1, d), generator=g, device=dev))  # LogNormal(0, 0.5) channels
+        return (torch.randn((L, H, T, d), generator=g, device=dev) * scale).to(torch.bfloat16)
+
+    seqs = [(cache(L_src), cache(L_src), cache(L_tgt), cache(L_tgt), 0) for _ in range(n_seqs)]
+    torch.cuda.synchronize()
+    ctx = K.Context(0)
+    stamps = []
+
+    def on_pass(stage, t0, t1, i, n):
+        torch.cuda.synchronize()
+        stamps.append((time.perf_counter(), stage))
+        log(f"fit driver: pass {i}/{n} stage {stage} targets [{t0}, {t1})")
+
+    t_start = time.perf_counter()
+    res = ctx.fit(lambda: seqs, L_src=L_src, L_tgt=L_tgt, H=H, d=d, k=k, theta_src=1.0e6, theta_tgt=1.0e6, lam=lam,
+                  on_pass=on_pass)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t_start
+    ctx.close()
+    # stamps[i] opens pass i; the last one marks the end of the last pass
+    sel_s = sum(stamps[i + 1][0] - stamps[i][0] for i in range(len(stamps) - 1) if stamps[i][1] == 1)
+    map_s = sum(stamps[i + 1][0] - stamps[i][0] for i in range(len(stamps) - 1) if stamps[i][1] == 2)
+    n_tok = n_seqs * T
+    del seqs, res
+    torch.cuda.empty_cache()
+    log(f"fit driver: {total:.2f} s ({sel_s:.2f} s selection, {map_s:.2f} s maps) over {n_tok} calibration tokens")
+    base = fit_driver_cpu_baseline(n_tok, L_src, L_tgt, H, d, k, lam) if cpu else None
+    return {"workload": f"qwen3-14b-to-32b fit: L {L_src}->{L_tgt}, H {H}, d {d}, k {k}, {n_seqs} x {T} bf16 "
+                        f"calibration tokens, lambda {lam}",
+            "seconds": total, "selection_s": sel_s, "maps_s": map_s, "calibration_tokens": n_tok,
+            "calibration_tokens_per_s": n_tok / total, "cpu_baseline": base}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +280,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fit", action="store_true", help="skip the fit-side measurement")
     ap.add_argument("--no-recode", action="store_true", help="skip the RoPE-recode measurement")
+    ap.add_argument("--no-fit-driver", action="store_true", help="skip the end-to-end fit measurement")
+    ap.add_argument("--fit-seqs", type=int, default=8, help="calibration sequences of 4096 tokens for the fit driver")
+    ap.add_argument("--fit-driver-only", action="store_true",
+                    help="run only the end-to-end fit measurement and print its object as the JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (the reference dispatch for HBM counters)")
     args = ap.parse_args()
@@ -212,6 +296,10 @@ def main():
     from cross_model_kv_amd import kvmap as K
     from synth.device import apply_inputs
     from synth.workloads import APPLY_CONFIGS
+
+    if args.fit_driver_only:
+        print(json.dumps(fit_driver_leg(K, n_seqs=args.fit_seqs, cpu=not args.no_cpu_baseline)), flush=True)
+        return
 
     cfg = APPLY_CONFIGS[args.config]
     if args.copy_calibration:
@@ -297,6 +385,9 @@ def main():
         del inp, out_k, out_v
         torch.cuda.empty_cache()
         result["fit"] = fit_leg(K, cpu=not args.no_cpu_baseline)
+    if not args.no_fit_driver:
+        torch.cuda.empty_cache()
+        result["fit_driver"] = fit_driver_leg(K, n_seqs=args.fit_seqs, cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 

@@ -702,8 +702,7 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
     return ok();
 }
 
-static int ensure_ridge_scratch(kvmap_ctx* c, int p, int q, size_t* need_out) {
-    const size_t need = ridge_dev_scratch_bytes(p, q);
+static int ensure_ridge_scratch(kvmap_ctx* c, size_t need) {
     if (need > c->ridge_bytes) {
         KVMAP_HIP(hipDeviceSynchronize());
         (void)hipFree(c->ridge);
@@ -712,78 +711,163 @@ static int ensure_ridge_scratch(kvmap_ctx* c, int p, int q, size_t* need_out) {
         KVMAP_HIP(hipMalloc(&c->ridge, need));
         c->ridge_bytes = need;
     }
-    *need_out = need;
     return KVMAP_OK;
 }
 
-extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, void* W_out,
-                                        void* b_out, int32_t dtype, void* stream) {
-    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: ctx is NULL");
-    int r = validate_state(st, "kvmap_ridge_solve_device");
+// The device solves of n states of one (p, q), in batches of up to kRidgeMaxBatch systems that
+// share one scratch of at most about kRidgeScratchBudget bytes (at least one system).  Each
+// batch is checked for non-positive pivots before the next starts.  r2: R^2 per group of y
+// columns into r2o[i]; else W[i], b[i] in bf16 or fp32.
+constexpr size_t kRidgeScratchBudget = size_t(8) << 30;
+
+static int run_ridge(kvmap_ctx* c, const kvmap_gram_state* const* st, int n, double lambda, bool r2, int group,
+                     bool bf16, void* const* W, void* const* b, double* const* r2o, hipStream_t s, const char* who) {
+    const int p = st[0]->p, q = st[0]->q;
+    const size_t per = ridge_dev_scratch_bytes(p, q, 1) - 256;
+    const int chunk = (int)std::min<size_t>(std::min<size_t>(kRidgeMaxBatch, (size_t)n),
+                                            std::max<size_t>(1, kRidgeScratchBudget / per));
+    int r = ensure_ridge_scratch(c, ridge_dev_scratch_bytes(p, q, chunk));
     if (r) return r;
-    if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: NULL output");
-    if (!(lambda >= 0.0) || !std::isfinite(lambda))
-        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: lambda must be finite and >= 0");
-    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
-        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_ridge_solve_device: dtype %d unknown", (int)dtype);
+    int flags[kRidgeMaxBatch];
+    for (int i0 = 0; i0 < n; i0 += chunk) {
+        const int m = std::min(chunk, n - i0);
+        RidgeSys sys[kRidgeMaxBatch];
+        for (int j = 0; j < m; ++j) {
+            const kvmap_gram_state* t = st[i0 + j];
+            sys[j] = RidgeSys{t->M_xx, t->M_xy, t->mean_x, t->mean_y, t->ss_y,
+                              r2 ? nullptr : W[i0 + j], r2 ? nullptr : b[i0 + j], r2 ? r2o[i0 + j] : nullptr};
+        }
+        int* bad = ridge_dev_flags(c->ridge, p, q, m);
+        KVMAP_HIP(launch_fill_zero((float*)bad, m, s));
+        if (r2) KVMAP_HIP(launch_ridge_r2(m, p, q, sys, lambda, group, c->ridge, s));
+        else KVMAP_HIP(launch_ridge_dev(m, p, q, sys, lambda, bf16, c->ridge, s));
+        KVMAP_HIP(hipMemcpyAsync(flags, bad, m * sizeof(int), hipMemcpyDeviceToHost, s));
+        KVMAP_HIP(hipStreamSynchronize(s));
+        for (int j = 0; j < m; ++j)
+            if (flags[j])
+                return fail(KVMAP_ERR_NOT_SPD, "%s: system %d: M_xx + lambda I is not positive definite", who, i0 + j);
+    }
+    return KVMAP_OK;
+}
+
+// Arguments of one device solve (state, outputs): nothing written when refused.
+static int check_solve_args(const kvmap_gram_state* st, const void* W_out, const void* b_out, int32_t dtype,
+                            const char* who) {
+    int r = validate_state(st, who);
+    if (r) return r;
+    if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL output", who);
     const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
     const size_t wb = (size_t)st->p * st->q * es, bb = (size_t)st->q * es;
     if ((((uintptr_t)W_out) | ((uintptr_t)b_out)) & 3)
-        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: outputs must be 4-byte aligned");
-    if (ranges_overlap(W_out, wb, b_out, bb)) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: W_out and b_out overlap");
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: outputs must be 4-byte aligned", who);
+    if (ranges_overlap(W_out, wb, b_out, bb)) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: W_out and b_out overlap", who);
     const void* ins[4] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy};
     const size_t insz[4] = {(size_t)st->p * 4, (size_t)st->q * 4, (size_t)st->p * st->p * 4, (size_t)st->p * st->q * 4};
     for (int i = 0; i < 4; ++i)
         if (ranges_overlap(ins[i], insz[i], W_out, wb) || ranges_overlap(ins[i], insz[i], b_out, bb))
-            return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_device: an output overlaps the state");
-    DeviceGuard g(c->device);
-    size_t need = 0;
-    r = ensure_ridge_scratch(c, st->p, st->q, &need);
-    if (r) return r;
-    hipStream_t s = (hipStream_t)stream;
-    int* bad = (int*)((char*)c->ridge + need - 256);  // pivot flag, in the scratch's last 256 bytes
-    KVMAP_HIP(launch_fill_zero((float*)bad, 1, s));
-    KVMAP_HIP(launch_ridge_dev(st->p, st->q, st->mean_x, st->mean_y, st->M_xx, st->M_xy, lambda, W_out, b_out,
-                               dtype == KVMAP_DTYPE_BF16, c->ridge, bad, s));
-    int h = 0;
-    KVMAP_HIP(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s));
-    KVMAP_HIP(hipStreamSynchronize(s));
-    if (h) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_device: M_xx + lambda I is not positive definite");
-    return ok();
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: an output overlaps the state", who);
+    return KVMAP_OK;
 }
 
-extern "C" int kvmap_ridge_r2(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, int32_t group,
-                              double* r2_out, void* stream) {
-    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: ctx is NULL");
-    int r = validate_state(st, "kvmap_ridge_r2");
+static int check_r2_args(const kvmap_gram_state* st, int32_t group, const double* r2_out, const char* who) {
+    int r = validate_state(st, who);
     if (r) return r;
-    if (!st->ss_y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: the state keeps no ss_y");
-    if (!r2_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: NULL output");
+    if (!st->ss_y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: the state keeps no ss_y", who);
+    if (!r2_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL output", who);
     if (group < 1 || st->q % group)
-        return fail(KVMAP_ERR_SHAPE, "kvmap_ridge_r2: group %d must divide q = %d", (int)group, (int)st->q);
-    if (!(lambda >= 0.0) || !std::isfinite(lambda))
-        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: lambda must be finite and >= 0");
-    if (((uintptr_t)r2_out) & 7) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: r2_out must be 8-byte aligned");
+        return fail(KVMAP_ERR_SHAPE, "%s: group %d must divide q = %d", who, (int)group, (int)st->q);
+    if (((uintptr_t)r2_out) & 7) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: r2_out must be 8-byte aligned", who);
     const size_t ob = (size_t)(st->q / group) * 8;
     const void* ins[5] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy, st->ss_y};
     const size_t insz[5] = {(size_t)st->p * 4, (size_t)st->q * 4, (size_t)st->p * st->p * 4,
                             (size_t)st->p * st->q * 4, (size_t)st->q * 4};
     for (int i = 0; i < 5; ++i)
         if (ranges_overlap(ins[i], insz[i], r2_out, ob))
-            return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_r2: r2_out overlaps the state");
-    DeviceGuard g(c->device);
-    size_t need = 0;
-    r = ensure_ridge_scratch(c, st->p, st->q, &need);
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: r2_out overlaps the state", who);
+    return KVMAP_OK;
+}
+
+static int check_common(kvmap_ctx* c, double lambda, const char* who) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: ctx is NULL", who);
+    if (!(lambda >= 0.0) || !std::isfinite(lambda))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: lambda must be finite and >= 0", who);
+    return KVMAP_OK;
+}
+
+extern "C" int kvmap_ridge_solve_device(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, void* W_out,
+                                        void* b_out, int32_t dtype, void* stream) {
+    const char* who = "kvmap_ridge_solve_device";
+    int r = check_common(c, lambda, who);
     if (r) return r;
-    hipStream_t s = (hipStream_t)stream;
-    int* bad = (int*)((char*)c->ridge + need - 256);
-    KVMAP_HIP(launch_fill_zero((float*)bad, 1, s));
-    KVMAP_HIP(launch_ridge_r2(st->p, st->q, st->M_xx, st->M_xy, st->ss_y, lambda, group, r2_out, c->ridge, bad, s));
-    int h = 0;
-    KVMAP_HIP(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s));
-    KVMAP_HIP(hipStreamSynchronize(s));
-    if (h) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_r2: M_xx + lambda I is not positive definite");
-    return ok();
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "%s: dtype %d unknown", who, (int)dtype);
+    r = check_solve_args(st, W_out, b_out, dtype, who);
+    if (r) return r;
+    DeviceGuard g(c->device);
+    r = run_ridge(c, &st, 1, lambda, false, 0, dtype == KVMAP_DTYPE_BF16, &W_out, &b_out, nullptr,
+                  (hipStream_t)stream, who);
+    return r ? r : ok();
+}
+
+extern "C" int kvmap_ridge_solve_device_batch(kvmap_ctx* c, const kvmap_gram_state* const* states, int32_t n,
+                                              double lambda, void* const* W_out, void* const* b_out, int32_t dtype,
+                                              void* stream) {
+    const char* who = "kvmap_ridge_solve_device_batch";
+    int r = check_common(c, lambda, who);
+    if (r) return r;
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "%s: dtype %d unknown", who, (int)dtype);
+    if (n < 1 || !states || !W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: empty batch or NULL array", who);
+    const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    for (int i = 0; i < n; ++i) {
+        r = check_solve_args(states[i], W_out[i], b_out[i], dtype, who);
+        if (r) return r;
+        if (states[i]->p != states[0]->p || states[i]->q != states[0]->q)
+            return fail(KVMAP_ERR_SHAPE, "%s: state %d has another (p, q) than state 0", who, i);
+        const size_t wb = (size_t)states[i]->p * states[i]->q * es, bb = (size_t)states[i]->q * es;
+        for (int j = 0; j < i; ++j) {
+            if (ranges_overlap(W_out[i], wb, W_out[j], wb) || ranges_overlap(W_out[i], wb, b_out[j], bb) ||
+                ranges_overlap(b_out[i], bb, W_out[j], wb) || ranges_overlap(b_out[i], bb, b_out[j], bb))
+                return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: outputs of systems %d and %d overlap", who, j, i);
+        }
+    }
+    DeviceGuard g(c->device);
+    r = run_ridge(c, states, n, lambda, false, 0, dtype == KVMAP_DTYPE_BF16, W_out, b_out, nullptr,
+                  (hipStream_t)stream, who);
+    return r ? r : ok();
+}
+
+extern "C" int kvmap_ridge_r2(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, int32_t group,
+                              double* r2_out, void* stream) {
+    const char* who = "kvmap_ridge_r2";
+    int r = check_common(c, lambda, who);
+    if (r) return r;
+    r = check_r2_args(st, group, r2_out, who);
+    if (r) return r;
+    DeviceGuard g(c->device);
+    r = run_ridge(c, &st, 1, lambda, true, group, false, nullptr, nullptr, &r2_out, (hipStream_t)stream, who);
+    return r ? r : ok();
+}
+
+extern "C" int kvmap_ridge_r2_batch(kvmap_ctx* c, const kvmap_gram_state* const* states, int32_t n, double lambda,
+                                    int32_t group, double* const* r2_out, void* stream) {
+    const char* who = "kvmap_ridge_r2_batch";
+    int r = check_common(c, lambda, who);
+    if (r) return r;
+    if (n < 1 || !states || !r2_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: empty batch or NULL array", who);
+    for (int i = 0; i < n; ++i) {
+        r = check_r2_args(states[i], group, r2_out[i], who);
+        if (r) return r;
+        if (states[i]->p != states[0]->p || states[i]->q != states[0]->q)
+            return fail(KVMAP_ERR_SHAPE, "%s: state %d has another (p, q) than state 0", who, i);
+        const size_t ob = (size_t)(states[i]->q / group) * 8;
+        for (int j = 0; j < i; ++j)
+            if (ranges_overlap(r2_out[i], ob, r2_out[j], ob))
+                return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: outputs of systems %d and %d overlap", who, j, i);
+    }
+    DeviceGuard g(c->device);
+    r = run_ridge(c, states, n, lambda, true, group, false, nullptr, nullptr, r2_out, (hipStream_t)stream, who);
+    return r ? r : ok();
 }
 
 extern "C" int kvmap_ridge_solve(kvmap_ctx* c, const kvmap_gram_state* st, double lambda, float* W_out,

@@ -206,11 +206,14 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
     if (f->n_first < 0) f->n_first = f->n_pass;
     if (f->stage == 1) {
         const int H = c.H_kv;
+        std::vector<const kvmap_gram_state*> st;
+        std::vector<double*> out;
         for (int kv = 0; kv < 2; ++kv)
             for (int sl = 0; sl < c.L_src; ++sl) {
-                double* out = f->r2 + (((size_t)kv * c.L_src + sl) * c.L_tgt + f->t0) * H;
-                FIT_TRY(kvmap_ridge_r2(f->ctx, &f->states[kv * c.L_src + sl], c.lambda, c.head_dim, out, s));
+                st.push_back(&f->states[kv * c.L_src + sl]);
+                out.push_back(f->r2 + (((size_t)kv * c.L_src + sl) * c.L_tgt + f->t0) * H);
             }
+        FIT_TRY(kvmap_ridge_r2_batch(f->ctx, st.data(), (int)st.size(), c.lambda, c.head_dim, out.data(), s));
         if (f->pass == f->sel_passes - 1) {
             double* scores = c.scores ? c.scores : f->own_scores;
             FIT_HIP(launch_fit_select(f->r2, c.L_src, c.L_tgt, H, c.k, scores, c.layer_sel, s));
@@ -222,13 +225,16 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
         return KVMAP_OK;
     }
     const size_t es = esize(c.out_dtype);
+    std::vector<const kvmap_gram_state*> st;
+    std::vector<void*> Ws, bs;
     for (int t = f->t0; t < f->t1; ++t)
         for (int kv = 0; kv < 2; ++kv) {
-            char* W = (char*)(kv ? c.W_v : c.W_k) + (size_t)t * f->N * f->F * es;
-            char* b = (char*)(kv ? c.b_v : c.b_k) + (size_t)t * f->N * es;
-            FIT_TRY(kvmap_ridge_solve_device(f->ctx, &f->states[2 * (t - f->t0) + kv], c.lambda, W, b, c.out_dtype,
-                                             s));
+            st.push_back(&f->states[2 * (t - f->t0) + kv]);
+            Ws.push_back((char*)(kv ? c.W_v : c.W_k) + (size_t)t * f->N * f->F * es);
+            bs.push_back((char*)(kv ? c.b_v : c.b_k) + (size_t)t * f->N * es);
         }
+    FIT_TRY(kvmap_ridge_solve_device_batch(f->ctx, st.data(), (int)st.size(), c.lambda, Ws.data(), bs.data(),
+                                           c.out_dtype, s));
     if (f->pass == f->sel_passes + f->map_passes - 1) free_stage(f);
     return KVMAP_OK;
 }

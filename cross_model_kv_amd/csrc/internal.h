@@ -109,13 +109,29 @@ hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // ---- ridge solve on the device (ridge_dev.hip), float64 --------------------------------
-size_t ridge_dev_scratch_bytes(int p, int q);
-hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
-                            const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
-                            void* scratch, int* bad, hipStream_t s);
+// Up to kRidgeMaxBatch independent systems of one (p, q) are solved together: every kernel of
+// the factorisation and the substitutions covers all of them (grid y = system), so the serial
+// chain of 64-wide block steps is paid once per batch.
+constexpr int kRidgeMaxBatch = 16;
+struct RidgeSys {
+    const float* M_xx;
+    const float* M_xy;
+    const float* mean_x;  // solve: b = mean_y - mean_x W
+    const float* mean_y;
+    const float* ss_y;    // R^2: total sums of squares
+    void* W_out;          // solve: [q][p] output-major, bf16 or fp32
+    void* b_out;          // solve: [q]
+    double* r2_out;       // R^2: [q / group]
+};
+// Scratch for n systems (fp64 factor, right-hand sides, residual sums; pivot flags at the end).
+size_t ridge_dev_scratch_bytes(int p, int q, int n);
+// Pivot flags of the n systems (nonzero: not positive definite) inside that scratch.
+int* ridge_dev_flags(void* scratch, int p, int q, int n);
+hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lambda, bool bf16, void* scratch,
+                            hipStream_t s);
 // r2_out[g] = in-sample R^2 of the ridge fit pooled over y columns g*group .. +group-1
-hipError_t launch_ridge_r2(int p, int q, const float* M_xx, const float* M_xy, const float* ss_y, double lambda,
-                           int group, double* r2_out, void* scratch, int* bad, hipStream_t s);
+hipError_t launch_ridge_r2(int n, int p, int q, const RidgeSys* sys, double lambda, int group, void* scratch,
+                           hipStream_t s);
 
 // ---- fit driver's scoring kernel (fit.hip) ----------------------------------------------
 // scores[t][s] = mean over {K, V} and heads of r2[kv][s][t][h]; sel[t] = the k best s, ties to

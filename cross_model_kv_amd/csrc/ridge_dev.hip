@@ -10,9 +10,12 @@
 //   b = mean_y - mean_x W;  W written output-major [q][p] in bf16 or fp32 (the apply's layout),
 //   or, for layer scoring, the in-sample R^2 of the fit pooled over groups of y columns, from
 //   the statistics alone: RSS_c = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2
-// Every update is a 64 x 64 fp64 tile C -= op(A) op(B) with K = 64 on the vector ALUs
-// (fp64 FMA runs at the same rate as the fp64 matrix cores on this chip).  A non-positive or
-// non-finite pivot sets a device flag that the host turns into KVMAP_ERR_NOT_SPD.
+// A batch of up to kRidgeMaxBatch systems of one shape runs through every kernel together
+// (grid y = system): the 64-wide diagonal steps form a serial chain of about 4 P / 64 small
+// launches, which a batch pays once.  The tile updates C -= op(A) op(B) (64 x 64, K = 64) run
+// on the fp64 matrix cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their
+// global orientation.  A non-positive or non-finite pivot sets the system's device flag, which
+// the host turns into KVMAP_ERR_NOT_SPD.
 
 #include "common.h"
 #include "internal.h"
@@ -21,9 +24,28 @@ namespace kvmap {
 
 namespace {
 
-constexpr int RB = 64;  // block size
+constexpr int RB = 64;       // block size
+constexpr int LDW = RB + 2;  // LDS row stride (doubles) of a staged 64 x 64 tile
 
-// Upper-triangle index of the lower-triangle tile list: tile u -> (I >= J)
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// Everything a batched launch needs, passed by value (kernel argument space).
+struct RidgeArgs {
+    RidgeSys s[kRidgeMaxBatch];
+    double* scratch;  // system z: A = scratch + z * stride, B = A + P^2, rss = B + P Q
+    size_t stride;    // doubles per system
+    int* bad;         // [n] pivot flags
+    int p, q, P, Q;
+    double lambda;
+};
+
+__device__ __forceinline__ double* sys_a(const RidgeArgs& g) { return g.scratch + (size_t)blockIdx.y * g.stride; }
+__device__ __forceinline__ double* sys_b(const RidgeArgs& g) { return sys_a(g) + (size_t)g.P * g.P; }
+__device__ __forceinline__ double* sys_rss(const RidgeArgs& g) {
+    return sys_b(g) + (size_t)g.P * g.Q;
+}
+
+// Lower-triangle tile list after a block: tile u -> (I >= J)
 __device__ __forceinline__ void lower_decode(int u, int& I, int& J) {
     int i = (int)((sqrt(8.0 * (double)u + 1.0) - 1.0) * 0.5);
     while ((int64_t)i * (i + 1) / 2 > u) --i;
@@ -35,33 +57,36 @@ __device__ __forceinline__ void lower_decode(int u, int& I, int& J) {
 }  // namespace
 
 // A[i][j] = M_xx[min][max] (+ lambda on the diagonal) for i, j < p; identity padding.
-__global__ __launch_bounds__(256) void ridge_init_a_kernel(const float* __restrict__ M_xx, int p, int P,
-                                                           double lambda, double* __restrict__ A) {
+__global__ __launch_bounds__(256) void ridge_init_a_kernel(const RidgeArgs g) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int P = g.P, p = g.p;
     if (idx >= (int64_t)P * P) return;
+    const float* M_xx = g.s[blockIdx.y].M_xx;
     const int i = (int)(idx / P), j = (int)(idx - (int64_t)i * P);
     double v;
     if (i < p && j < p) {
         v = (double)M_xx[(size_t)min(i, j) * p + max(i, j)];
-        if (i == j) v += lambda;
+        if (i == j) v += g.lambda;
     } else {
         v = (i == j) ? 1.0 : 0.0;
     }
-    A[idx] = v;
+    sys_a(g)[idx] = v;
 }
 
-__global__ __launch_bounds__(256) void ridge_init_b_kernel(const float* __restrict__ M_xy, int p, int q, int P,
-                                                           int Q, double* __restrict__ B) {
+__global__ __launch_bounds__(256) void ridge_init_b_kernel(const RidgeArgs g) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int P = g.P, Q = g.Q, p = g.p, q = g.q;
     if (idx >= (int64_t)P * Q) return;
+    const float* M_xy = g.s[blockIdx.y].M_xy;
     const int i = (int)(idx / Q), c = (int)(idx - (int64_t)i * Q);
-    B[idx] = (i < p && c < q) ? (double)M_xy[(size_t)i * q + c] : 0.0;
+    sys_b(g)[idx] = (i < p && c < q) ? (double)M_xy[(size_t)i * q + c] : 0.0;
 }
 
-// Factor the diagonal block kb in place (lower triangle), one workgroup of 64 threads.
-__global__ __launch_bounds__(64) void ridge_potrf_kernel(double* __restrict__ A, int P, int kb,
-                                                         int* __restrict__ bad) {
+// Factor the diagonal block kb in place (lower triangle), one workgroup of 64 threads per system.
+__global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
     __shared__ double t[RB][RB + 1];
+    double* A = sys_a(g);
+    const int P = g.P;
     const int r = threadIdx.x;
     const int o = kb * RB;
     for (int c = 0; c < RB; ++c) t[r][c] = A[(size_t)(o + r) * P + o + c];
@@ -69,7 +94,7 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(double* __restrict__ A,
     for (int j = 0; j < RB; ++j) {
         double d = t[j][j];
         if (!(d > 0.0) || !isfinite(d)) {
-            if (r == 0) atomicOr(bad, 1);
+            if (r == 0) atomicOr(&g.bad[blockIdx.y], 1);
             d = 1.0;  // keep going with a harmless pivot; the result is refused by the host
         }
         const double ljj = sqrt(d);
@@ -86,9 +111,11 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(double* __restrict__ A,
 
 // Panel: A_ik <- A_ik L_kk^-T for the 64-row blocks i below kb; workgroup = one row block,
 // thread = one row (forward substitution along the row).
-__global__ __launch_bounds__(64) void ridge_trsm_panel_kernel(double* __restrict__ A, int P, int kb) {
+__global__ __launch_bounds__(64) void ridge_trsm_panel_kernel(const RidgeArgs g, int kb) {
     __shared__ double L[RB][RB + 1];
     __shared__ double X[RB][RB + 1];
+    double* A = sys_a(g);
+    const int P = g.P;
     const int r = threadIdx.x;
     const int o = kb * RB;
     const int i0 = o + RB * (1 + (int)blockIdx.x);
@@ -108,10 +135,12 @@ __global__ __launch_bounds__(64) void ridge_trsm_panel_kernel(double* __restrict
 // Right-hand sides, diagonal block kb: forward (Z_kb = L_kk^-1 B_kb) or backward
 // (W_kb = L_kk^-T Z_kb); workgroup = 64 right-hand-side columns, thread = one column.
 template <bool FWD>
-__global__ __launch_bounds__(64) void ridge_trsm_rhs_kernel(const double* __restrict__ A, int P,
-                                                            double* __restrict__ B, int Q, int kb) {
+__global__ __launch_bounds__(64) void ridge_trsm_rhs_kernel(const RidgeArgs g, int kb) {
     __shared__ double L[RB][RB + 1];
     __shared__ double Xs[RB][RB + 1];
+    const double* A = sys_a(g);
+    double* B = sys_b(g);
+    const int P = g.P, Q = g.Q;
     const int c = threadIdx.x;
     const int o = kb * RB, c0 = (int)blockIdx.x * RB;
     for (int rr = 0; rr < RB; ++rr) {
@@ -135,19 +164,26 @@ __global__ __launch_bounds__(64) void ridge_trsm_rhs_kernel(const double* __rest
     for (int rr = 0; rr < RB; ++rr) B[(size_t)(o + rr) * Q + c0 + c] = Xs[rr][c];
 }
 
-// C -= op(A) op(B) on 64 x 64 tiles, K = 64.  op(A)[r][m] = Aop[r * sar + m * sam],
-// op(B)[m][c] = Bop[m * sbm + c * sbc] (one stride of each is 1).  The tile list:
+// C -= op(A) op(B) on 64 x 64 tiles, K = 64, on the fp64 matrix cores.  The tile list:
 //   MODE 0  trailing lower triangle of A after block kb:  C = A_IJ, op(A) = A_I,kb,
 //           op(B) = A_J,kb^T  (I >= J > kb)
 //   MODE 1  forward update of the right-hand sides: C = B_I,J (I > kb), op(A) = L_I,kb,
 //           op(B) = Z_kb,J
 //   MODE 2  backward update: C = Z_I,J (I < kb), op(A) = L_kb,I^T, op(B) = W_kb,J
-// 256 threads; thread (ty, tx) accumulates rows 4 ty .. 4 ty + 3, columns 4 tx .. 4 tx + 3.
+// Operand tiles are copied to LDS as they lie in memory (64 rows of 64 consecutive doubles,
+// coalesced); A_ROWS / B_ROWS say whether an LDS row is an r (resp. c) index or an m index.
+// 4 waves, each a 32 x 32 quarter of C as 2 x 2 blocks of 16 x 16 (v_mfma_f64_16x16x4f64:
+// lane (i, k) = (lane & 15, lane >> 4) supplies A[i][k] and B[k][i]; accumulator element e
+// of lane is C[(lane >> 4) + 4 e][lane & 15], rows interleaved by 4, unlike the fp32 forms).
 template <int MODE>
-__global__ __launch_bounds__(256) void ridge_update_kernel(double* __restrict__ A, int P, double* __restrict__ B,
-                                                           int Q, int kb, int ncol) {
-    __shared__ double As[RB][RB + 4];  // [m][r]
-    __shared__ double Bs[RB][RB + 4];  // [m][c]
+__global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, int kb, int ncol) {
+    constexpr bool A_ROWS = MODE != 2;  // LDS row of A is r (else m)
+    constexpr bool B_ROWS = MODE == 0;  // LDS row of B is c (else m)
+    __shared__ double As[RB * LDW];
+    __shared__ double Bs[RB * LDW];
+    double* A = sys_a(g);
+    double* Bm = sys_b(g);
+    const int P = g.P, Q = g.Q;
     const int tid = threadIdx.x;
     int I, J;
     if (MODE == 0) {
@@ -162,67 +198,78 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(double* __restrict__ 
     const int o = kb * RB;
     double* C;
     int ldc;
-    const double* Ap;
-    int sar, sam;
+    const double* Ap;  // row x of the stored tile: Ap + x * lda
     const double* Bp;
-    int sbm, sbc;
+    int lda, ldb;
     if (MODE == 0) {
         C = A + (size_t)I * RB * P + (size_t)J * RB;
         ldc = P;
-        Ap = A + (size_t)I * RB * P + o; sar = P; sam = 1;
-        Bp = A + (size_t)J * RB * P + o; sbm = 1; sbc = P;
+        Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
+        Bp = A + (size_t)J * RB * P + o; ldb = P;   // rows c, columns m
     } else if (MODE == 1) {
-        C = B + (size_t)I * RB * Q + (size_t)J * RB;
+        C = Bm + (size_t)I * RB * Q + (size_t)J * RB;
         ldc = Q;
-        Ap = A + (size_t)I * RB * P + o; sar = P; sam = 1;
-        Bp = B + (size_t)o * Q + (size_t)J * RB; sbm = Q; sbc = 1;
+        Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
+        Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
     } else {
-        C = B + (size_t)I * RB * Q + (size_t)J * RB;
+        C = Bm + (size_t)I * RB * Q + (size_t)J * RB;
         ldc = Q;
-        Ap = A + (size_t)o * P + (size_t)I * RB; sar = 1; sam = P;
-        Bp = B + (size_t)o * Q + (size_t)J * RB; sbm = Q; sbc = 1;
+        Ap = A + (size_t)o * P + (size_t)I * RB; lda = P;   // rows m, columns r
+        Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
     }
-    // loads: 4096 elements each, 16 per thread, consecutive threads along the unit stride
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int e = u * 256 + tid;
-        const int x = e >> 6, y = e & 63;  // y runs along the unit stride
-        if (sam == 1) As[y][x] = Ap[(size_t)x * sar + y];  // element (r = x, m = y)
-        else As[x][y] = Ap[(size_t)x * sam + y];           // element (m = x, r = y)
-        if (sbc == 1) Bs[x][y] = Bp[(size_t)x * sbm + y];  // element (m = x, c = y)
-        else Bs[y][x] = Bp[(size_t)x * sbc + y];           // element (c = x, m = y)
+        const int x = e >> 6, y = e & 63;
+        As[x * LDW + y] = Ap[(size_t)x * lda + y];
+        Bs[x * LDW + y] = Bp[(size_t)x * ldb + y];
     }
     __syncthreads();
-    const int ty = tid >> 4, tx = tid & 15;
-    double acc[4][4] = {};
-#pragma unroll 8
-    for (int m = 0; m < RB; ++m) {
-        double a[4], b[4];
+    const int lane = tid & 63, w = tid >> 6;
+    const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
+    const int li = lane & 15, lk = lane >> 4;
+    f64x4_t acc[2][2];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            a[v] = As[m][ty * 4 + v];
-            b[v] = Bs[m][tx * 4 + v];
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < RB; k0 += 4) {
+        const int m = k0 + lk;
+        double a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = r0 + 16 * i + li, c = c0 + 16 * i + li;
+            a[i] = A_ROWS ? As[r * LDW + m] : As[m * LDW + r];
+            b[i] = B_ROWS ? Bs[c * LDW + m] : Bs[m * LDW + c];
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) acc[r][cc] = fma(a[r], b[cc], acc[r][cc]);
+            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) C[(size_t)(ty * 4 + r) * ldc + tx * 4 + cc] -= acc[r][cc];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + 16 * i + lk + 4 * e, c = c0 + 16 * j + li;
+                C[(size_t)r * ldc + c] -= acc[i][j][e];
+            }
 }
 
 // b[c] = mean_y[c] - sum_i mean_x[i] W[i][c] (fp64), and W_out[c][i] = W[i][c] in the output
 // dtype (output-major), through a 64 x 64 transpose in LDS.  Workgroup: 64 columns c x all i.
 template <bool BF16>
-__global__ __launch_bounds__(256) void ridge_finalize_kernel(const double* __restrict__ W, int P, int Q, int p,
-                                                             int q, const float* __restrict__ mean_x,
-                                                             const float* __restrict__ mean_y,
-                                                             void* __restrict__ W_out, void* __restrict__ b_out) {
+__global__ __launch_bounds__(256) void ridge_finalize_kernel(const RidgeArgs g) {
     __shared__ double t[RB][RB + 1];
     __shared__ double part[4][RB];
+    const RidgeSys& S = g.s[blockIdx.y];
+    const double* W = sys_b(g);
+    const int Q = g.Q, p = g.p, q = g.q;
+    const float* mean_x = S.mean_x;
+    void* W_out = S.W_out;
     const int tid = threadIdx.x;
     const int c0 = (int)blockIdx.x * RB;
     const int cx = tid & 63, ry = tid >> 6;  // 4 row groups
@@ -249,9 +296,9 @@ __global__ __launch_bounds__(256) void ridge_finalize_kernel(const double* __res
     part[ry][cx] = dot;
     __syncthreads();
     if (ry == 0 && c0 + cx < q) {
-        const double bv = (double)mean_y[c0 + cx] - (part[0][cx] + part[1][cx] + part[2][cx] + part[3][cx]);
-        if (BF16) ((uint16_t*)b_out)[c0 + cx] = (uint16_t)(pack_bf16((float)bv, 0.f) & 0xffffu);
-        else ((float*)b_out)[c0 + cx] = (float)bv;
+        const double bv = (double)S.mean_y[c0 + cx] - (part[0][cx] + part[1][cx] + part[2][cx] + part[3][cx]);
+        if (BF16) ((uint16_t*)S.b_out)[c0 + cx] = (uint16_t)(pack_bf16((float)bv, 0.f) & 0xffffu);
+        else ((float*)S.b_out)[c0 + cx] = (float)bv;
     }
 }
 
@@ -260,12 +307,12 @@ __global__ __launch_bounds__(256) void ridge_finalize_kernel(const double* __res
 //   sum (yc - xc w)^2 = ss_y[c] - 2 w.m + w^T M_xx w = ss_y[c] - w.m - lambda |w|^2,
 // since w^T M_xx w = w^T (m - lambda w).  Workgroup: 64 columns; the 4 row groups are
 // reduced in a fixed order.
-__global__ __launch_bounds__(256) void ridge_rss_kernel(const double* __restrict__ W, int Q, int p, int q,
-                                                        const float* __restrict__ M_xy,
-                                                        const float* __restrict__ ss_y, double lambda,
-                                                        double* __restrict__ rss) {
+__global__ __launch_bounds__(256) void ridge_rss_kernel(const RidgeArgs g) {
     __shared__ double pd[4][RB];
     __shared__ double pn[4][RB];
+    const RidgeSys& S = g.s[blockIdx.y];
+    const double* W = sys_b(g);
+    const int Q = g.Q, p = g.p, q = g.q;
     const int tid = threadIdx.x;
     const int cx = tid & 63, ry = tid >> 6;
     const int c = (int)blockIdx.x * RB + cx;
@@ -273,7 +320,7 @@ __global__ __launch_bounds__(256) void ridge_rss_kernel(const double* __restrict
     if (c < q) {
         for (int i = ry; i < p; i += 4) {
             const double w = W[(size_t)i * Q + c];
-            dot += w * (double)M_xy[(size_t)i * q + c];
+            dot += w * (double)S.M_xy[(size_t)i * q + c];
             nrm += w * w;
         }
     }
@@ -283,91 +330,105 @@ __global__ __launch_bounds__(256) void ridge_rss_kernel(const double* __restrict
     if (ry == 0 && c < q) {
         const double d = ((pd[0][cx] + pd[1][cx]) + pd[2][cx]) + pd[3][cx];
         const double n2 = ((pn[0][cx] + pn[1][cx]) + pn[2][cx]) + pn[3][cx];
-        rss[c] = (double)ss_y[c] - d - lambda * n2;
+        sys_rss(g)[c] = (double)S.ss_y[c] - d - g.lambda * n2;
     }
 }
 
-// R^2 of group g (columns g*group .. g*group + group - 1) pooled over its columns:
+// R^2 of group gi (columns gi*group .. gi*group + group - 1) pooled over its columns:
 // 1 - sum RSS / sum ss_y; NaN when the group's total sum of squares is 0.
-__global__ __launch_bounds__(256) void ridge_r2_group_kernel(const double* __restrict__ rss,
-                                                             const float* __restrict__ ss_y, int groups,
-                                                             int group, double* __restrict__ r2) {
-    const int g = (int)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= groups) return;
+__global__ __launch_bounds__(256) void ridge_r2_group_kernel(const RidgeArgs g, int group) {
+    const int groups = g.q / group;
+    const int gi = (int)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gi >= groups) return;
+    const RidgeSys& S = g.s[blockIdx.y];
+    const double* rss = sys_rss(g);
     double r = 0.0, t = 0.0;
     for (int j = 0; j < group; ++j) {
-        r += rss[(size_t)g * group + j];
-        t += (double)ss_y[(size_t)g * group + j];
+        r += rss[(size_t)gi * group + j];
+        t += (double)S.ss_y[(size_t)gi * group + j];
     }
-    r2[g] = t > 0.0 ? 1.0 - r / t : __builtin_nan("");
+    S.r2_out[gi] = t > 0.0 ? 1.0 - r / t : __builtin_nan("");
 }
 
 // ---------------------------------------------------------------------------------------
 
-size_t ridge_dev_scratch_bytes(int p, int q) {
+namespace {
+
+size_t sys_stride(int p, int q) {
     const size_t P = ((size_t)p + RB - 1) / RB * RB, Q = ((size_t)q + RB - 1) / RB * RB;
-    return (P * P + P * Q + Q) * sizeof(double) + 256;  // A, B (then W), rss, pivot flag
+    return (P * P + P * Q + Q + 31) / 32 * 32;  // A, B (then W), rss; 256-byte aligned
 }
 
-// A = sym(M_xx) + lambda I = L L^T (lower triangle of A), then W = A^-1 M_xy in B = A + P^2,
-// row-major [P][Q].
-static void ridge_dev_solve(int p, int q, const float* M_xx, const float* M_xy, double lambda, void* scratch,
-                            int* bad, hipStream_t s) {
-    const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
+RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, void* scratch) {
+    RidgeArgs g{};
+    for (int i = 0; i < n; ++i) g.s[i] = sys[i];
+    g.scratch = (double*)scratch;
+    g.stride = sys_stride(p, q);
+    g.bad = ridge_dev_flags(scratch, p, q, n);
+    g.p = p;
+    g.q = q;
+    g.P = (p + RB - 1) / RB * RB;
+    g.Q = (q + RB - 1) / RB * RB;
+    g.lambda = lambda;
+    return g;
+}
+
+// A = L L^T (lower triangle of A), then W = A^-1 M_xy in B, row-major [P][Q], every system.
+void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
+    const int P = g.P, Q = g.Q;
     const int nb = P / RB, nq = Q / RB;
-    double* A = (double*)scratch;
-    double* B = A + (size_t)P * P;
-    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256)), dim3(256), 0, s, M_xx, p,
-                       P, lambda, A);
-    hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256)), dim3(256), 0, s, M_xy, p,
-                       q, P, Q, B);
+    const unsigned un = (unsigned)n;
+    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256), un), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), dim3(256), 0, s, g);
     for (int kb = 0; kb < nb; ++kb) {
-        hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1), dim3(RB), 0, s, A, P, kb, bad);
+        hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1, un), dim3(RB), 0, s, g, kb);
         const int below = nb - kb - 1;
         if (below > 0) {
-            hipLaunchKernelGGL(ridge_trsm_panel_kernel, dim3(below), dim3(RB), 0, s, A, P, kb);
-            hipLaunchKernelGGL(ridge_update_kernel<0>, dim3(below * (below + 1) / 2), dim3(256), 0, s, A, P, B, Q,
-                               kb, 0);
+            hipLaunchKernelGGL(ridge_trsm_panel_kernel, dim3(below, un), dim3(RB), 0, s, g, kb);
+            hipLaunchKernelGGL(ridge_update_kernel<0>, dim3(below * (below + 1) / 2, un), dim3(256), 0, s, g, kb, 0);
         }
     }
     for (int kb = 0; kb < nb; ++kb) {
-        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<true>, dim3(nq), dim3(RB), 0, s, A, P, B, Q, kb);
+        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<true>, dim3(nq, un), dim3(RB), 0, s, g, kb);
         const int below = nb - kb - 1;
         if (below > 0)
-            hipLaunchKernelGGL(ridge_update_kernel<1>, dim3(below * nq), dim3(256), 0, s, A, P, B, Q, kb, nq);
+            hipLaunchKernelGGL(ridge_update_kernel<1>, dim3(below * nq, un), dim3(256), 0, s, g, kb, nq);
     }
     for (int kb = nb - 1; kb >= 0; --kb) {
-        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<false>, dim3(nq), dim3(RB), 0, s, A, P, B, Q, kb);
-        if (kb > 0) hipLaunchKernelGGL(ridge_update_kernel<2>, dim3(kb * nq), dim3(256), 0, s, A, P, B, Q, kb, nq);
+        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<false>, dim3(nq, un), dim3(RB), 0, s, g, kb);
+        if (kb > 0) hipLaunchKernelGGL(ridge_update_kernel<2>, dim3(kb * nq, un), dim3(256), 0, s, g, kb, nq);
     }
 }
 
-hipError_t launch_ridge_dev(int p, int q, const float* mean_x, const float* mean_y, const float* M_xx,
-                            const float* M_xy, double lambda, void* W_out, void* b_out, bool bf16,
-                            void* scratch, int* bad, hipStream_t s) {
-    const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
-    const int nq = Q / RB;
-    const double* B = (const double*)scratch + (size_t)P * P;
-    ridge_dev_solve(p, q, M_xx, M_xy, lambda, scratch, bad, s);
+}  // namespace
+
+size_t ridge_dev_scratch_bytes(int p, int q, int n) { return (size_t)n * sys_stride(p, q) * sizeof(double) + 256; }
+
+int* ridge_dev_flags(void* scratch, int p, int q, int n) {
+    return (int*)((char*)scratch + (size_t)n * sys_stride(p, q) * sizeof(double));
+}
+
+hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lambda, bool bf16, void* scratch,
+                            hipStream_t s) {
+    if (n < 1 || n > kRidgeMaxBatch) return hipErrorInvalidValue;
+    const RidgeArgs g = make_args(n, p, q, sys, lambda, scratch);
+    solve_batch(g, n, s);
+    const dim3 grid(g.Q / RB, (unsigned)n);
     if (bf16)
-        hipLaunchKernelGGL(ridge_finalize_kernel<true>, dim3(nq), dim3(256), 0, s, B, P, Q, p, q, mean_x, mean_y,
-                           W_out, b_out);
+        hipLaunchKernelGGL(ridge_finalize_kernel<true>, grid, dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL(ridge_finalize_kernel<false>, dim3(nq), dim3(256), 0, s, B, P, Q, p, q, mean_x, mean_y,
-                           W_out, b_out);
+        hipLaunchKernelGGL(ridge_finalize_kernel<false>, grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
-hipError_t launch_ridge_r2(int p, int q, const float* M_xx, const float* M_xy, const float* ss_y, double lambda,
-                           int group, double* r2_out, void* scratch, int* bad, hipStream_t s) {
-    const int P = (p + RB - 1) / RB * RB, Q = (q + RB - 1) / RB * RB;
-    const double* B = (const double*)scratch + (size_t)P * P;
-    double* rss = (double*)scratch + (size_t)P * P + (size_t)P * Q;
-    ridge_dev_solve(p, q, M_xx, M_xy, lambda, scratch, bad, s);
-    hipLaunchKernelGGL(ridge_rss_kernel, dim3(Q / RB), dim3(256), 0, s, B, Q, p, q, M_xy, ss_y, lambda, rss);
+hipError_t launch_ridge_r2(int n, int p, int q, const RidgeSys* sys, double lambda, int group, void* scratch,
+                           hipStream_t s) {
+    if (n < 1 || n > kRidgeMaxBatch || group < 1 || q % group) return hipErrorInvalidValue;
+    const RidgeArgs g = make_args(n, p, q, sys, lambda, scratch);
+    solve_batch(g, n, s);
+    hipLaunchKernelGGL(ridge_rss_kernel, dim3(g.Q / RB, (unsigned)n), dim3(256), 0, s, g);
     const int groups = q / group;
-    hipLaunchKernelGGL(ridge_r2_group_kernel, dim3((groups + 255) / 256), dim3(256), 0, s, rss, ss_y, groups, group,
-                       r2_out);
+    hipLaunchKernelGGL(ridge_r2_group_kernel, dim3((groups + 255) / 256, (unsigned)n), dim3(256), 0, s, g, group);
     return hipGetLastError();
 }
 

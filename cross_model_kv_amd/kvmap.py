@@ -105,6 +105,12 @@ _SIGS = {
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "kvmap_ridge_r2": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_double, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "kvmap_ridge_solve_device_batch": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.POINTER(GramStateC)),
+                                                      ctypes.c_int32, ctypes.c_double, ctypes.POINTER(ctypes.c_void_p),
+                                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_void_p]),
+    "kvmap_ridge_r2_batch": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.POINTER(GramStateC)), ctypes.c_int32,
+                                            ctypes.c_double, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.c_void_p]),
     "kvmap_fit_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(FitConfigC), ctypes.POINTER(ctypes.c_void_p)]),
     "kvmap_fit_next_pass": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(FitPassC), ctypes.c_void_p]),
     "kvmap_fit_add": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -412,9 +418,38 @@ class Context:
                                     _stream_handle(stream, st.device)), "kvmap_ridge_r2")
         return out
 
+    def ridge_solve_device_batch(self, states, lam: float, dtype=None, stream=None):
+        """kvmap_ridge_solve_device_batch: [(W [q][p] output-major, b [q])] for states of one (p, q),
+        solved together on the device (dtype: bf16 or fp32, default fp32)."""
+        torch = _torch()
+        dtype = dtype if dtype is not None else torch.float32
+        n = len(states)
+        outs = [(torch.empty((st.q, st.p), dtype=dtype, device=st.device),
+                 torch.empty((st.q,), dtype=dtype, device=st.device)) for st in states]
+        sp = (ctypes.POINTER(GramStateC) * n)(*[ctypes.pointer(st.c) for st in states])
+        Wp = (ctypes.c_void_p * n)(*[w.data_ptr() for w, _ in outs])
+        bp = (ctypes.c_void_p * n)(*[b.data_ptr() for _, b in outs])
+        code = BF16 if dtype == torch.bfloat16 else F32
+        _check(lib().kvmap_ridge_solve_device_batch(self._h, sp, n, float(lam), Wp, bp, code,
+                                                    _stream_handle(stream, states[0].device)),
+               "kvmap_ridge_solve_device_batch")
+        return outs
+
+    def ridge_r2_batch(self, states, lam: float, group: int, stream=None):
+        """kvmap_ridge_r2_batch: [R^2 per group of y columns, device float64 [q / group]] per state."""
+        torch = _torch()
+        n = len(states)
+        outs = [torch.empty((max(1, st.q // max(1, int(group))),), dtype=torch.float64, device=st.device)
+                for st in states]
+        sp = (ctypes.POINTER(GramStateC) * n)(*[ctypes.pointer(st.c) for st in states])
+        op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+        _check(lib().kvmap_ridge_r2_batch(self._h, sp, n, float(lam), int(group), op,
+                                          _stream_handle(stream, states[0].device)), "kvmap_ridge_r2_batch")
+        return outs
+
     def fit(self, calibration, *, L_src: int, L_tgt: int, H: int, d: int, k: int, theta_src: float,
             theta_tgt: float, lam: float, out_dtype=None, layer_sel=None, select_block: int = 0,
-            map_block: int = 0, stream=None) -> dict:
+            map_block: int = 0, stream=None, on_pass=None) -> dict:
         """kvmap_fit_*: the two-stage fit (selection, then maps) over re-iterable calibration data.
 
         `calibration` is a callable returning an iterable of (src_k, src_v, tgt_k, tgt_v, pos0):
@@ -422,7 +457,9 @@ class Context:
         and its first position; it is called once per pass and must yield the same sequences
         each time.  layer_sel (device int32 [L_tgt][k]) skips the selection stage.
         Returns dict(layer_sel, scores (None with a given layer_sel), W_k, b_k, W_v, b_v); the maps
-        are output-major [L_tgt][H*d][k*H*d] in out_dtype (default: the caches' dtype)."""
+        are output-major [L_tgt][H*d][k*H*d] in out_dtype (default: the caches' dtype).
+        on_pass(stage, t_begin, t_end, pass_index, passes) is called after each
+        kvmap_fit_next_pass (which returns once the previous pass is solved)."""
         torch = _torch()
         dev = torch.device(f"cuda:{self.device}")
         N, F = H * d, k * H * d
@@ -465,6 +502,8 @@ class Context:
                     it, seqs = iter(calibration()), []
                 sh = _stream_handle(stream, dev)
                 _check(lib().kvmap_fit_next_pass(h, ctypes.byref(info), sh), "kvmap_fit_next_pass")
+                if on_pass is not None:
+                    on_pass(info.stage, info.t_begin, info.t_end, info.pass_, info.passes)
                 if info.stage == 0:
                     break
                 for seq in _chain(seqs, it):

@@ -270,7 +270,7 @@ int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
  *   W_out  device [q][p] output-major (the layout kvmap_apply takes for one target layer),
  *   b_out  device [q], both in `dtype` (bf16: rounded to nearest even; fp32), 4-byte aligned,
  *          not overlapping each other or the state.
- * The context keeps an fp64 scratch of (P^2 + P Q) * 8 bytes, P and Q being p and q rounded
+ * The context keeps an fp64 scratch of (P^2 + P Q + Q) * 8 bytes, P and Q being p and q rounded
  * up to multiples of 64 (576 MiB at p 8192, q 1024), allocated on first use.  Synchronous:
  * returns after the solve, KVMAP_ERR_NOT_SPD if a pivot was not positive and finite (the
  * outputs are then undefined), INVALID_ARGUMENT / UNSUPPORTED on refused arguments (nothing
@@ -290,6 +290,18 @@ int kvmap_ridge_solve_device(kvmap_ctx* ctx, const kvmap_gram_state* st, double 
  * KVMAP_ERR_NOT_SPD as kvmap_ridge_solve_device. */
 int kvmap_ridge_r2(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, int32_t group, double* r2_out,
                    void* stream);
+
+/* Batched forms of the two device solves above: n >= 1 states of one (p, q), host arrays of
+ * n state pointers and n output pointers (the outputs of different systems must not overlap).
+ * The library solves up to 16 systems together: every kernel of the factorisation and the
+ * substitutions covers all of them, so the serial chain of 64-wide block steps is paid once per
+ * batch; the scratch grows to the batch's size (as many systems as fit in about 8 GiB, at least
+ * one).  Synchronous; validation of all n before any device work; KVMAP_ERR_NOT_SPD names the
+ * first system that failed (outputs of systems in earlier batches are then already written). */
+int kvmap_ridge_solve_device_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, int32_t n, double lambda,
+                                   void* const* W_out, void* const* b_out, int32_t dtype, void* stream);
+int kvmap_ridge_r2_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, int32_t n, double lambda,
+                         int32_t group, double* const* r2_out, void* stream);
 
 /* ---- end-to-end fit: layer selection, then the maps (KVBridge README, fitting section
  * headed "Loading": a two-stage, multi-pass fit over re-iterable calibration data that keeps

@@ -331,3 +331,27 @@ def test_fit_refusals(ctx, K):
     with pytest.raises(K.KvmapError) as e:
         ctx.fit(shrinking, **base)
     assert e.value.status == K.ERR_SHAPE
+
+
+def test_ridge_batches_equal_single_solves(ctx, K):
+    """kvmap_ridge_solve_device_batch / kvmap_ridge_r2_batch over 18 states (two batches: at most
+    16 systems share the kernels) give bit for bit the single-system results; a state that is not
+    positive definite is named in the refusal."""
+    states = []
+    for i in range(18):
+        X, Y = _xy(300 + 7 * i, 72, 24, seed=100 + i)
+        st = ctx.gram_state(72, 24, keep_ss_y=True)
+        ctx.gram_reset(st)
+        ctx.gram(st, _dev(X, "f32"), _dev(Y, "f32"))
+        states.append(st)
+    outs = ctx.ridge_solve_device_batch(states, 0.01, dtype=torch.float32)
+    r2s = ctx.ridge_r2_batch(states, 0.01, 8)
+    for st, (W, b), r2 in zip(states, outs, r2s):
+        W1, b1 = ctx.ridge_solve_device(st, 0.01, dtype=torch.float32)
+        assert torch.equal(W, W1) and torch.equal(b, b1)
+        assert torch.equal(r2, ctx.ridge_r2(st, 0.01, 8))
+    empty = ctx.gram_state(72, 24, keep_ss_y=True)
+    ctx.gram_reset(empty)
+    with pytest.raises(K.KvmapError) as e:
+        ctx.ridge_solve_device_batch(states[:3] + [empty], 0.0)
+    assert e.value.status == K.ERR_NOT_SPD and "system 3" in str(e.value)
