@@ -61,9 +61,11 @@ constexpr int kGramMaxSplits = 64;
 
 struct RopeEntry {
     double theta = 0;
+    std::vector<double> freq;  // the model's own frequencies when given (then theta is unused)
     int64_t pos0 = 0;
     bool diff = false;  // recode table of (theta, pos0) -> (theta2, pos0_2)
     double theta2 = 0;
+    std::vector<double> freq2;
     int64_t pos0_2 = 0;
     int d = 0;
     int64_t T_cap = 0;
@@ -201,13 +203,19 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
 // validation
 // ---------------------------------------------------------------------------------------
 
-static int validate_rope(const kvmap_rope* r, const char* which, int64_t T) {
+// d: the head dim, already validated (64 or 128); inv_freq, if given, has d/2 entries.
+static int validate_rope(const kvmap_rope* r, const char* which, int64_t T, int d) {
     if (!r) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE descriptor is NULL", which);
     if (r->style != KVMAP_ROPE_HALF_SPLIT)
         return fail(KVMAP_ERR_UNSUPPORTED, "%s RoPE style %d refused: only the half-split form is mapped",
                     which, (int)r->style);
-    if (!(r->theta > 0.0) || !std::isfinite(r->theta))
+    if (r->inv_freq) {
+        for (int i = 0; i < d / 2; ++i)
+            if (!(r->inv_freq[i] >= 0.0) || !std::isfinite(r->inv_freq[i]))
+                return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE inv_freq[%d] must be finite and >= 0", which, i);
+    } else if (!(r->theta > 0.0) || !std::isfinite(r->theta)) {
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE theta must be finite and > 0", which);
+    }
     if (r->pos0 < 0) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE pos0 must be >= 0", which);
     if (r->pos0 > (int64_t(1) << 31) - T)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s RoPE pos0 + T exceeds 2^31", which);
@@ -238,9 +246,9 @@ extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_se
         return fail(KVMAP_ERR_SHAPE, "T*head_dim must stay below 2^31");
     if ((int64_t)d->L_tgt * d->k >= (int64_t(1) << 24))
         return fail(KVMAP_ERR_SHAPE, "L_tgt*k too large");
-    int st = validate_rope(rs, "source", d->T);
+    int st = validate_rope(rs, "source", d->T, d->head_dim);
     if (st) return st;
-    st = validate_rope(rt, "target", d->T);
+    st = validate_rope(rt, "target", d->T, d->head_dim);
     if (st) return st;
     std::vector<char> seen(d->L_src, 0);
     for (int t = 0; t < d->L_tgt; ++t) {
@@ -263,13 +271,30 @@ extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_se
 
 // Cached fp32 tables built in fp64: a RoPE table of r, or (r2 given) the recode table
 // from r to r2.
+static bool same_freqs(double theta, const std::vector<double>& f, const kvmap_rope* r, int d) {
+    if (r->inv_freq) return (int)f.size() == d / 2 && std::equal(f.begin(), f.end(), r->inv_freq);
+    return f.empty() && theta == r->theta;
+}
+
+static RopeFreqs make_freqs(const kvmap_rope* r, int d) {
+    RopeFreqs fr{};
+    fr.theta = r->theta;
+    fr.given = r->inv_freq != nullptr;
+    for (int i = 0; fr.given && i < d / 2; ++i) fr.f[i] = r->inv_freq[i];
+    return fr;
+}
+
+static std::vector<double> freq_list(const kvmap_rope* r, int d) {
+    return r->inv_freq ? std::vector<double>(r->inv_freq, r->inv_freq + d / 2) : std::vector<double>();
+}
+
 static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, hipStream_t s,
                           float2** out, bool* built, const kvmap_rope* r2 = nullptr) {
     *built = false;
     const bool diff = r2 != nullptr;
     for (auto& e : c->ropes) {
-        if (e.theta == r->theta && e.pos0 == r->pos0 && e.d == d && e.T_cap >= T && e.diff == diff &&
-            (!diff || (e.theta2 == r2->theta && e.pos0_2 == r2->pos0))) {
+        if (same_freqs(e.theta, e.freq, r, d) && e.pos0 == r->pos0 && e.d == d && e.T_cap >= T && e.diff == diff &&
+            (!diff || (same_freqs(e.theta2, e.freq2, r2, d) && e.pos0_2 == r2->pos0))) {
             e.last_use = ++c->clock;
             *out = e.tab;
             return KVMAP_OK;
@@ -285,15 +310,17 @@ static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, h
     }
     RopeEntry e;
     e.theta = r->theta;
+    e.freq = freq_list(r, d);
     e.pos0 = r->pos0;
     e.diff = diff;
     e.theta2 = diff ? r2->theta : 0.0;
+    if (diff) e.freq2 = freq_list(r2, d);
     e.pos0_2 = diff ? r2->pos0 : 0;
     e.d = d;
     e.T_cap = T;
     KVMAP_HIP(hipMalloc((void**)&e.tab, (size_t)T * (d / 2) * sizeof(float2)));
-    hipError_t err = diff ? launch_rope_diff_table(e.tab, T, d, r->theta, r->pos0, r2->theta, r2->pos0, s)
-                          : launch_rope_table(e.tab, T, d, r->theta, r->pos0, s);
+    hipError_t err = diff ? launch_rope_diff_table(e.tab, T, d, make_freqs(r, d), r->pos0, make_freqs(r2, d), r2->pos0, s)
+                          : launch_rope_table(e.tab, T, d, make_freqs(r, d), r->pos0, s);
     if (err != hipSuccess) {
         (void)hipFree(e.tab);
         return fail(KVMAP_ERR_DEVICE, "RoPE table launch: %s", hipGetErrorString(err));
@@ -463,14 +490,14 @@ extern "C" int kvmap_recode(kvmap_ctx* c, int32_t rows, int64_t T, int32_t head_
     if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: ctx is NULL");
     if (rows < 1 || T < 1 || T > (int64_t(1) << 31) || (int64_t)rows * T > (int64_t(1) << 40))
         return fail(KVMAP_ERR_SHAPE, "kvmap_recode: rows=%d, T=%lld out of range", (int)rows, (long long)T);
-    int st = validate_rope(rope_src, "source", T);
-    if (st) return st;
-    st = validate_rope(rope_tgt, "target", T);
-    if (st) return st;
     if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
         return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_recode: dtype %d unknown", (int)dtype);
     if (head_dim != 64 && head_dim != 128)
         return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_recode: head_dim %d (64 or 128 supported)", (int)head_dim);
+    int st = validate_rope(rope_src, "source", T, head_dim);
+    if (st) return st;
+    st = validate_rope(rope_tgt, "target", T, head_dim);
+    if (st) return st;
     if (!src || !dst) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: NULL device pointer");
     if ((((uintptr_t)src) | ((uintptr_t)dst)) & 15)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_recode: pointers must be 16-byte aligned");
@@ -514,7 +541,7 @@ extern "C" int kvmap_cache_rows(kvmap_ctx* c, const void* cache, int32_t L, int3
         rl.l[j] = layers[j];
     }
     if (rope) {
-        int st = validate_rope(rope, "rows", T);
+        int st = validate_rope(rope, "rows", T, head_dim);
         if (st) return st;
     }
     if (!cache || !out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_cache_rows: NULL device pointer");

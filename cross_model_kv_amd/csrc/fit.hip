@@ -91,6 +91,7 @@ struct kvmap_fit {
     int stage = 0, t0 = 0, t1 = 0;
     int64_t n_pass = 0, n_first = -1;  // tokens fed to the open pass / to the first pass
     std::vector<int32_t> sel;          // host copy of layer_sel [L_tgt][k]
+    std::vector<double> freq_src, freq_tgt;  // the models' own rotary frequencies, if given
     std::vector<kvmap_gram_state> states;
     float* state_mem = nullptr;
     double* r2 = nullptr;              // [2][L_src][L_tgt][H]
@@ -270,8 +271,17 @@ extern "C" int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvm
     for (int32_t dt : {c.dtype, c.out_dtype})
         if (dt != KVMAP_DTYPE_BF16 && dt != KVMAP_DTYPE_F32)
             return report(KVMAP_ERR_UNSUPPORTED, "kvmap_fit_create: dtype %d unknown", (int)dt);
-    if (!(c.theta_src > 0.0) || !(c.theta_tgt > 0.0) || !std::isfinite(c.theta_src) || !std::isfinite(c.theta_tgt))
-        return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: RoPE bases must be finite and > 0");
+    for (int side = 0; side < 2; ++side) {
+        const double theta = side ? c.theta_tgt : c.theta_src;
+        const double* f = side ? c.inv_freq_tgt : c.inv_freq_src;
+        if (f) {
+            for (int i = 0; i < c.head_dim / 2; ++i)
+                if (!(f[i] >= 0.0) || !std::isfinite(f[i]))
+                    return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: inv_freq[%d] must be finite and >= 0", i);
+        } else if (!(theta > 0.0) || !std::isfinite(theta)) {
+            return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: RoPE bases must be finite and > 0");
+        }
+    }
     if (!(c.lambda >= 0.0) || !std::isfinite(c.lambda))
         return report(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_fit_create: lambda must be finite and >= 0");
     const int max_sel_block = (int)std::min<int64_t>(kMaxRowLayers, kMaxGramWidth / N);
@@ -293,6 +303,10 @@ extern "C" int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvm
     f->N = (int)N;
     f->F = (int)F;
     f->sel.assign((size_t)c.L_tgt * c.k, 0);
+    if (c.inv_freq_src) f->freq_src.assign(c.inv_freq_src, c.inv_freq_src + c.head_dim / 2);
+    if (c.inv_freq_tgt) f->freq_tgt.assign(c.inv_freq_tgt, c.inv_freq_tgt + c.head_dim / 2);
+    f->cfg.inv_freq_src = nullptr;  // the copies above are used from here on
+    f->cfg.inv_freq_tgt = nullptr;
     f->sel_block = c.select_block ? c.select_block : std::min<int>(c.L_tgt, max_sel_block);
     f->map_block = c.map_block ? std::min<int>(c.map_block, c.L_tgt) : c.L_tgt;
     f->sel_passes = c.given_sel ? 0 : (c.L_tgt + f->sel_block - 1) / f->sel_block;
@@ -360,8 +374,8 @@ extern "C" int kvmap_fit_add(kvmap_fit* f, const void* src_k, const void* src_v,
     hipStream_t s = (hipStream_t)stream;
     const size_t es = esize(c.dtype);
     const int d = c.head_dim, H = c.H_kv;
-    const kvmap_rope rs{c.theta_src, pos0, KVMAP_ROPE_HALF_SPLIT};
-    const kvmap_rope rt{c.theta_tgt, pos0, KVMAP_ROPE_HALF_SPLIT};
+    const kvmap_rope rs{c.theta_src, pos0, KVMAP_ROPE_HALF_SPLIT, f->freq_src.empty() ? nullptr : f->freq_src.data()};
+    const kvmap_rope rt{c.theta_tgt, pos0, KVMAP_ROPE_HALF_SPLIT, f->freq_tgt.empty() ? nullptr : f->freq_tgt.data()};
     const void* src[2] = {src_k, src_v};
     const void* tgt[2] = {tgt_k, tgt_v};
     if (f->stage == 1) {

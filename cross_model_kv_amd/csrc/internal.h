@@ -20,14 +20,21 @@ struct ApplyGeom {
 };
 
 // ---- RoPE tables / key de-rotation (rope.hip) -------------------------------------
-// tab[t][i] = (cos a, sin a), a = (pos0 + t) * theta^(-2i/d), formed in float64.
-hipError_t launch_rope_table(float2* tab, int64_t T, int d, double theta, int64_t pos0,
-                             hipStream_t s);
+// Rotary frequencies of one model: f_i = theta^(-2i/d) (formed on the device), or the given
+// list (the model's own factors); passed by value.
+struct RopeFreqs {
+    double theta;
+    int given;       // nonzero: f[0 .. d/2) are the frequencies
+    double f[64];
+};
 
-// tab[t][i] = (cos A, sin A), A = (pos0_s + t) theta_s^(-2i/d) - (pos0_t + t) theta_t^(-2i/d),
-// formed in float64: rotating by -A re-encodes a source-roped key to the target RoPE.
-hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, double theta_s, int64_t pos0_s,
-                                  double theta_t, int64_t pos0_t, hipStream_t s);
+// tab[t][i] = (cos a, sin a), a = (pos0 + t) * f_i, formed in float64.
+hipError_t launch_rope_table(float2* tab, int64_t T, int d, const RopeFreqs& fr, int64_t pos0, hipStream_t s);
+
+// tab[t][i] = (cos A, sin A), A = (pos0_s + t) f_s,i - (pos0_t + t) f_t,i, formed in float64:
+// rotating by -A re-encodes a source-roped key to the target RoPE.
+hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, const RopeFreqs& fs, int64_t pos0_s,
+                                  const RopeFreqs& ft, int64_t pos0_t, hipStream_t s);
 // ws[l][h][t][:] = every pair of src[l][h][t][:] rotated by -a (a from tab), for every l in
 // layers[0..n_layers).
 hipError_t launch_derope(Elem e, const void* src, void* ws, const int32_t* layers, int n_layers,

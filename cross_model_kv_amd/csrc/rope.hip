@@ -16,15 +16,18 @@
 
 namespace kvmap {
 
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int64_t T,
-                                                          int d, double theta, int64_t pos0) {
+__device__ __forceinline__ double rope_freq(const RopeFreqs& fr, int i, int d) {
+    return fr.given ? fr.f[i] : pow(fr.theta, -2.0 * (double)i / (double)d);
+}
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int64_t T, int d,
+                                                         const RopeFreqs fr, int64_t pos0) {
     const int half = d / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * half) return;
     const int64_t t = idx / half;
     const int i = (int)(idx - t * half);
-    const double f = pow(theta, -2.0 * (double)i / (double)d);
-    const double a = (double)(pos0 + t) * f;
+    const double a = (double)(pos0 + t) * rope_freq(fr, i, d);
     double s, c;
     sincos(a, &s, &c);
     tab[idx] = make_float2((float)c, (float)s);
@@ -36,34 +39,31 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 // target one in a single rotation (VeloxQuant-MLX "Cross-Model KV Transfer", section "Metal
 // kernel": both rotations act on the same pair at the same position).
 __global__ __launch_bounds__(256) void rope_diff_table_kernel(float2* __restrict__ tab, int64_t T, int d,
-                                                               double theta_s, int64_t pos0_s, double theta_t,
-                                                               int64_t pos0_t) {
+                                                              const RopeFreqs fs, int64_t pos0_s,
+                                                              const RopeFreqs ft, int64_t pos0_t) {
     const int half = d / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * half) return;
     const int64_t t = idx / half;
     const int i = (int)(idx - t * half);
-    const double e = -2.0 * (double)i / (double)d;
-    const double a = (double)(pos0_s + t) * pow(theta_s, e) - (double)(pos0_t + t) * pow(theta_t, e);
+    const double a = (double)(pos0_s + t) * rope_freq(fs, i, d) - (double)(pos0_t + t) * rope_freq(ft, i, d);
     double s, c;
     sincos(a, &s, &c);
     tab[idx] = make_float2((float)c, (float)s);
 }
 
-hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, double theta_s, int64_t pos0_s,
-                                  double theta_t, int64_t pos0_t, hipStream_t s) {
+hipError_t launch_rope_diff_table(float2* tab, int64_t T, int d, const RopeFreqs& fs, int64_t pos0_s,
+                                  const RopeFreqs& ft, int64_t pos0_t, hipStream_t s) {
     const int64_t n = T * (d / 2);
     const unsigned blocks = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(rope_diff_table_kernel, dim3(blocks), dim3(256), 0, s, tab, T, d, theta_s, pos0_s, theta_t,
-                       pos0_t);
+    hipLaunchKernelGGL(rope_diff_table_kernel, dim3(blocks), dim3(256), 0, s, tab, T, d, fs, pos0_s, ft, pos0_t);
     return hipGetLastError();
 }
 
-hipError_t launch_rope_table(float2* tab, int64_t T, int d, double theta, int64_t pos0,
-                             hipStream_t s) {
+hipError_t launch_rope_table(float2* tab, int64_t T, int d, const RopeFreqs& fr, int64_t pos0, hipStream_t s) {
     const int64_t n = T * (d / 2);
     const unsigned blocks = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, tab, T, d, theta, pos0);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, tab, T, d, fr, pos0);
     return hipGetLastError();
 }
 

@@ -45,7 +45,19 @@ class Dims(ctypes.Structure):
 
 
 class Rope(ctypes.Structure):
-    _fields_ = [("theta", ctypes.c_double), ("pos0", ctypes.c_int64), ("style", ctypes.c_int32)]
+    _fields_ = [("theta", ctypes.c_double), ("pos0", ctypes.c_int64), ("style", ctypes.c_int32),
+                ("inv_freq", ctypes.c_void_p)]
+
+
+def _rope(theta, pos0, style, inv_freq, keep: list) -> Rope:
+    """A kvmap_rope; inv_freq (host sequence of head_dim/2 frequencies, or None) is kept alive in
+    `keep` for the duration of the call."""
+    ptr = None
+    if inv_freq is not None:
+        a = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float64).reshape(-1))
+        keep.append(a)
+        ptr = a.ctypes.data
+    return Rope(float(theta if theta is not None else 0.0), int(pos0), int(style), ptr)
 
 
 class GramStateC(ctypes.Structure):
@@ -61,7 +73,7 @@ class FitConfigC(ctypes.Structure):
                 ("given_sel", ctypes.c_int32), ("theta_src", ctypes.c_double), ("theta_tgt", ctypes.c_double),
                 ("lambda_", ctypes.c_double), ("layer_sel", ctypes.c_void_p), ("scores", ctypes.c_void_p),
                 ("W_k", ctypes.c_void_p), ("b_k", ctypes.c_void_p), ("W_v", ctypes.c_void_p),
-                ("b_v", ctypes.c_void_p)]
+                ("b_v", ctypes.c_void_p), ("inv_freq_src", ctypes.c_void_p), ("inv_freq_tgt", ctypes.c_void_p)]
 
 
 class FitPassC(ctypes.Structure):
@@ -165,11 +177,14 @@ def _sel_array(layer_sel) -> np.ndarray:
 
 
 def validate_apply(L_src, L_tgt, H, d, k, T, dtype, layer_sel, theta_src, theta_tgt,
-                   pos0_src=0, pos0_tgt=0, style_src=ROPE_HALF_SPLIT, style_tgt=ROPE_HALF_SPLIT) -> int:
+                   pos0_src=0, pos0_tgt=0, style_src=ROPE_HALF_SPLIT, style_tgt=ROPE_HALF_SPLIT,
+                   inv_freq_src=None, inv_freq_tgt=None) -> int:
     """kvmap_validate_apply; returns the status code (host only, needs no GPU)."""
     sel = _sel_array(layer_sel)
     dm = _dims(L_src, L_tgt, H, d, k, T, dtype)
-    rs, rt = Rope(theta_src, pos0_src, style_src), Rope(theta_tgt, pos0_tgt, style_tgt)
+    keep = []
+    rs = _rope(theta_src, pos0_src, style_src, inv_freq_src, keep)
+    rt = _rope(theta_tgt, pos0_tgt, style_tgt, inv_freq_tgt, keep)
     return lib().kvmap_validate_apply(ctypes.byref(dm), sel.ctypes.data, ctypes.byref(rs), ctypes.byref(rt))
 
 
@@ -282,10 +297,12 @@ class Context:
 
     def apply(self, src_k, src_v, layer_sel, W_k, b_k, W_v, b_v, theta_src: float, theta_tgt: float,
               pos0_src: int = 0, pos0_tgt: int | None = None, out_k=None, out_v=None, stream=None,
-              flags: int = 0, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT):
+              flags: int = 0, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT,
+              inv_freq_src=None, inv_freq_tgt=None):
         """kvmap_apply.  src_k/src_v [L_src][H][T][d], W_k/W_v [L_tgt][N][F] (output-major),
         b_k/b_v [L_tgt][N] device tensors of one dtype (bf16 or fp32); layer_sel host
-        int [L_tgt][k].  Returns (tgt_k, tgt_v) [L_tgt][H][T][d] (allocated if not given)."""
+        int [L_tgt][k].  inv_freq_src/tgt: optional host [d/2] rotary frequencies of each model
+        (instead of theta).  Returns (tgt_k, tgt_v) [L_tgt][H][T][d] (allocated if not given)."""
         torch = _torch()
         sel = _sel_array(layer_sel)
         L_src, H, T, d = src_k.shape
@@ -309,8 +326,9 @@ class Context:
             if tuple(t.shape) != (L_tgt, H, T, d) or t.dtype != src_k.dtype:
                 raise ValueError(f"{name} must be [L_tgt][H][T][d] of the input dtype")
         dm = _dims(L_src, L_tgt, H, d, k, T, dt)
-        rs = Rope(float(theta_src), int(pos0_src), int(style_src))
-        rt = Rope(float(theta_tgt), int(pos0_src if pos0_tgt is None else pos0_tgt), int(style_tgt))
+        keep = []
+        rs = _rope(theta_src, pos0_src, style_src, inv_freq_src, keep)
+        rt = _rope(theta_tgt, pos0_src if pos0_tgt is None else pos0_tgt, style_tgt, inv_freq_tgt, keep)
         st = lib().kvmap_apply(self._h, ctypes.byref(dm), _dev_ptr(src_k, "src_k"), _dev_ptr(src_v, "src_v"),
                                sel.ctypes.data, _dev_ptr(W_k, "W_k"), _dev_ptr(b_k, "b_k"),
                                _dev_ptr(W_v, "W_v"), _dev_ptr(b_v, "b_v"), ctypes.byref(rs), ctypes.byref(rt),
@@ -326,10 +344,11 @@ class Context:
         return float(ms[0]), float(ms[1]), float(ms[2])
 
     def recode(self, src, theta_src: float, theta_tgt: float, pos0_src: int = 0, pos0_tgt: int | None = None,
-               out=None, stream=None, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT):
+               out=None, stream=None, style_src: int = ROPE_HALF_SPLIT, style_tgt: int = ROPE_HALF_SPLIT,
+               inv_freq_src=None, inv_freq_tgt=None):
         """kvmap_recode: re-encode keys src [..., T, d] (device, bf16 or fp32; leading dims
-        are the rows) from RoPE (theta_src, pos0_src) to (theta_tgt, pos0_tgt).  Returns out
-        (allocated if not given), of src's shape and dtype."""
+        are the rows) from RoPE (theta_src, pos0_src) to (theta_tgt, pos0_tgt) (or the given
+        frequency lists).  Returns out (allocated if not given), of src's shape and dtype."""
         torch = _torch()
         if src.dim() < 2:
             raise ValueError("src must be [..., T, d]")
@@ -339,8 +358,9 @@ class Context:
             out = torch.empty_like(src)
         if tuple(out.shape) != tuple(src.shape) or out.dtype != src.dtype:
             raise ValueError("out must match src's shape and dtype")
-        rs = Rope(float(theta_src), int(pos0_src), int(style_src))
-        rt = Rope(float(theta_tgt), int(pos0_src if pos0_tgt is None else pos0_tgt), int(style_tgt))
+        keep = []
+        rs = _rope(theta_src, pos0_src, style_src, inv_freq_src, keep)
+        rt = _rope(theta_tgt, pos0_src if pos0_tgt is None else pos0_tgt, style_tgt, inv_freq_tgt, keep)
         _check(lib().kvmap_recode(self._h, rows, T, d, _dtype_code(src), _dev_ptr(src, "src"), _dev_ptr(out, "out"),
                                   ctypes.byref(rs), ctypes.byref(rt), _stream_handle(stream, src.device)),
                "kvmap_recode")
@@ -348,9 +368,9 @@ class Context:
 
     # ---- fit-side statistics ---------------------------------------------------------
     def cache_rows(self, cache, layers, theta: float | None = None, pos0: int = 0, out=None, stream=None,
-                   style: int = ROPE_HALF_SPLIT):
+                   style: int = ROPE_HALF_SPLIT, inv_freq=None):
         """kvmap_cache_rows: rows [T][len(layers) * H * d] of the layers of cache [L][H][T][d]
-        (device, bf16 or fp32), RoPE stripped at (theta, pos0) unless theta is None."""
+        (device, bf16 or fp32), RoPE stripped at (theta or inv_freq, pos0) unless both are None."""
         torch = _torch()
         L, H, T, d = (int(x) for x in cache.shape)
         lay = np.ascontiguousarray(np.asarray(layers, dtype=np.int32).reshape(-1))
@@ -359,7 +379,9 @@ class Context:
             out = torch.empty((T, width), dtype=cache.dtype, device=cache.device)
         if tuple(out.shape) != (T, width) or out.dtype != cache.dtype:
             raise ValueError(f"out must be [T={T}][{width}] of the cache dtype")
-        rope = None if theta is None else ctypes.byref(Rope(float(theta), int(pos0), int(style)))
+        keep = []
+        rope = (None if theta is None and inv_freq is None
+                else ctypes.byref(_rope(theta, pos0, style, inv_freq, keep)))
         _check(lib().kvmap_cache_rows(self._h, _dev_ptr(cache, "cache"), L, H, T, d, _dtype_code(cache),
                                       lay.ctypes.data, len(lay), rope, _dev_ptr(out, "out"),
                                       _stream_handle(stream, cache.device)), "kvmap_cache_rows")
@@ -449,7 +471,7 @@ class Context:
 
     def fit(self, calibration, *, L_src: int, L_tgt: int, H: int, d: int, k: int, theta_src: float,
             theta_tgt: float, lam: float, out_dtype=None, layer_sel=None, select_block: int = 0,
-            map_block: int = 0, stream=None, on_pass=None) -> dict:
+            map_block: int = 0, stream=None, on_pass=None, inv_freq_src=None, inv_freq_tgt=None) -> dict:
         """kvmap_fit_*: the two-stage fit (selection, then maps) over re-iterable calibration data.
 
         `calibration` is a callable returning an iterable of (src_k, src_v, tgt_k, tgt_v, pos0):
@@ -459,7 +481,8 @@ class Context:
         Returns dict(layer_sel, scores (None with a given layer_sel), W_k, b_k, W_v, b_v); the maps
         are output-major [L_tgt][H*d][k*H*d] in out_dtype (default: the caches' dtype).
         on_pass(stage, t_begin, t_end, pass_index, passes) is called after each
-        kvmap_fit_next_pass (which returns once the previous pass is solved)."""
+        kvmap_fit_next_pass (which returns once the previous pass is solved).
+        inv_freq_src/tgt: optional host [d/2] rotary frequencies of each model."""
         torch = _torch()
         dev = torch.device(f"cuda:{self.device}")
         N, F = H * d, k * H * d
@@ -490,11 +513,15 @@ class Context:
                     for name, shape in (("W_k", (L_tgt, N, F)), ("b_k", (L_tgt, N)), ("W_v", (L_tgt, N, F)),
                                         ("b_v", (L_tgt, N))):
                         maps[name] = torch.empty(shape, dtype=odt, device=dev)
+                    fq = [None if f is None else np.ascontiguousarray(np.asarray(f, dtype=np.float64).reshape(-1))
+                          for f in (inv_freq_src, inv_freq_tgt)]
                     cfg = FitConfigC(int(L_src), int(L_tgt), int(H), int(d), int(k), _dtype_code(seq[0]),
                                      _dtype_code(maps["W_k"]), int(select_block), int(map_block), int(given),
-                                     float(theta_src), float(theta_tgt), float(lam), layer_sel.data_ptr(),
-                                     scores.data_ptr() if scores is not None else None,
-                                     *(maps[n].data_ptr() for n in ("W_k", "b_k", "W_v", "b_v")))
+                                     float(theta_src if theta_src is not None else 0.0),
+                                     float(theta_tgt if theta_tgt is not None else 0.0), float(lam),
+                                     layer_sel.data_ptr(), scores.data_ptr() if scores is not None else None,
+                                     *(maps[n].data_ptr() for n in ("W_k", "b_k", "W_v", "b_v")),
+                                     *(None if f is None else f.ctypes.data for f in fq))
                     _check(lib().kvmap_fit_create(self._h, ctypes.byref(cfg), ctypes.byref(h)), "kvmap_fit_create")
                     seqs = [seq]
                     first = False

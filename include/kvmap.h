@@ -92,9 +92,14 @@ typedef struct {
 } kvmap_dims;
 
 typedef struct {
-    double theta;  /* RoPE base of the model, > 0                     */
-    int64_t pos0;  /* absolute position of token 0 (>= 0)             */
-    int32_t style; /* kvmap_rope_style; only KVMAP_ROPE_HALF_SPLIT     */
+    double theta;            /* RoPE base of the model, > 0 (not read when inv_freq is given) */
+    int64_t pos0;            /* absolute position of token 0 (>= 0)                          */
+    int32_t style;           /* kvmap_rope_style; only KVMAP_ROPE_HALF_SPLIT                  */
+    const double* inv_freq;  /* optional host [head_dim/2]: the model's own rotary frequencies
+                                f_i (finite, >= 0), angle (pos0 + t) * f_i, instead of
+                                theta^(-2i/d) (KVBridge README "What ships": exact RoPE from the
+                                factors each model emits).  NULL = theta^(-2i/d).  Read during
+                                the call only.                                                 */
 } kvmap_rope;
 
 /* ---- status / version ------------------------------------------------------------ */
@@ -332,7 +337,8 @@ typedef struct {
                               (block*H*d <= 65536, <= 128 layers)                              */
     int32_t map_block;     /* target layers per map pass; 0 = all                             */
     int32_t given_sel;     /* nonzero: layer_sel is an input and there is no selection stage  */
-    double theta_src;      /* RoPE bases of the two models (> 0)                              */
+    double theta_src;      /* RoPE bases of the two models (> 0; not read where the matching
+                              inv_freq is given)                                               */
     double theta_tgt;
     double lambda;         /* ridge penalty on the unnormalised centered Gram (>= 0)          */
     int32_t* layer_sel;    /* device [L_tgt][k] int32: written by stage 1, or read (given_sel) */
@@ -341,6 +347,9 @@ typedef struct {
     void* b_k;             /* device [L_tgt][H*d], out_dtype                                   */
     void* W_v;
     void* b_v;
+    const double* inv_freq_src;  /* optional host [head_dim/2] rotary frequencies of each model
+                                    (see kvmap_rope); copied by kvmap_fit_create; NULL = theta  */
+    const double* inv_freq_tgt;
 } kvmap_fit_config;
 
 typedef struct {

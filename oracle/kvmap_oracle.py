@@ -37,7 +37,7 @@ from fractions import Fraction
 import numpy as np
 
 __all__ = [
-    "inv_freq", "angles", "rope", "strip_rope", "feature_rows", "affine",
+    "inv_freq", "model_freqs", "angles", "rope", "strip_rope", "feature_rows", "affine",
     "apply_layer", "apply", "apply_rows",
     "stats_empty", "stats_two_pass", "chan_merge", "stats_streamed", "stats_exact",
     "ridge", "r2_pooled", "select_layers", "fit_mapper", "holdout_r2",
@@ -56,9 +56,22 @@ def inv_freq(theta: float, d: int) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * i / d)
 
 
-def angles(pos: np.ndarray, theta: float, d: int) -> np.ndarray:
-    """a[t, i] = pos[t] * f_i in float64, shape [len(pos)][d/2]."""
-    return np.asarray(pos, dtype=np.float64)[:, None] * inv_freq(theta, d)[None, :]
+def model_freqs(theta, d: int) -> np.ndarray:
+    """A model's rotary frequencies: theta^(-2i/d) for a base theta, or theta itself when it is
+    the list of d/2 frequencies the model emits ([KVB] "What ships": exact inverse/forward RoPE
+    from each model's own factors)."""
+    if np.ndim(theta) == 0:
+        return inv_freq(float(theta), d)
+    f = np.asarray(theta, dtype=np.float64).reshape(-1)
+    if f.shape[0] != d // 2:
+        raise ValueError(f"{f.shape[0]} frequencies for head dim {d}")
+    return f
+
+
+def angles(pos: np.ndarray, theta, d: int) -> np.ndarray:
+    """a[t, i] = pos[t] * f_i in float64, shape [len(pos)][d/2]; theta is a base or a
+    frequency list (model_freqs)."""
+    return np.asarray(pos, dtype=np.float64)[:, None] * model_freqs(theta, d)[None, :]
 
 
 def _rotate(x: np.ndarray, a: np.ndarray) -> np.ndarray:
@@ -69,13 +82,14 @@ def _rotate(x: np.ndarray, a: np.ndarray) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
-def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
-    """Apply half-split RoPE at positions pos to x [..., T, d] (float64)."""
+def rope(x: np.ndarray, pos: np.ndarray, theta) -> np.ndarray:
+    """Apply half-split RoPE at positions pos to x [..., T, d] (float64); theta is the base or
+    the model's frequency list."""
     x = np.asarray(x, dtype=np.float64)
     return _rotate(x, angles(pos, theta, x.shape[-1]))
 
 
-def strip_rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+def strip_rope(x: np.ndarray, pos: np.ndarray, theta) -> np.ndarray:
     """Exact inverse of rope(): rotate every pair by the negative angle."""
     x = np.asarray(x, dtype=np.float64)
     return _rotate(x, -angles(pos, theta, x.shape[-1]))

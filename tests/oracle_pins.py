@@ -52,6 +52,25 @@ def pin_rope_matches_complex_rotation():
             assert abs(got[t, i] - z.real) < 1e-12 and abs(got[t, i + d // 2] - z.imag) < 1e-12
 
 
+def pin_rope_with_model_frequencies():
+    """A model's own frequency list (here scaled, uneven frequencies such as a long-context
+    model emits) rotates each pair z = x_i + i x_{i+d/2} by exp(i p f_i); the list
+    theta^(-2i/d) is the base-theta rotation; strip inverts rope for any list."""
+    rng = np.random.default_rng(17)
+    d, T = 16, 4
+    f = np.sort(rng.uniform(0.0, 1.0, d // 2))[::-1] * np.array([1, 1, 1, 0.5, 0.25, 0.125, 0.1, 0.0])
+    x = rng.standard_normal((T, d))
+    pos = np.array([0, 5, 999, 32767])
+    got = oracle.rope(x, pos, f)
+    for t in range(T):
+        for i in range(d // 2):
+            z = complex(x[t, i], x[t, i + d // 2]) * cmath.exp(1j * pos[t] * f[i])
+            assert abs(got[t, i] - z.real) < 1e-11 and abs(got[t, i + d // 2] - z.imag) < 1e-11
+    base_list = [1.0e4 ** (-2.0 * i / d) for i in range(d // 2)]
+    assert np.max(np.abs(oracle.rope(x, pos, base_list) - oracle.rope(x, pos, 1.0e4))) < 1e-12
+    assert np.max(np.abs(oracle.strip_rope(oracle.rope(x, pos, f), pos, f) - x)) < 1e-13
+
+
 def pin_strip_inverts_rope():
     """strip(rope(x)) = x at equal bases (to fp64 rounding), for positions up to 32K."""
     rng = np.random.default_rng(1)
@@ -378,7 +397,8 @@ def pin_fitcheck_recovers_hidden_map(cfg=FITCHECK):
 
 
 ALL_PINS = [
-    pin_rope_frequencies, pin_rope_matches_complex_rotation, pin_strip_inverts_rope,
+    pin_rope_frequencies, pin_rope_matches_complex_rotation, pin_rope_with_model_frequencies,
+    pin_strip_inverts_rope,
     pin_rope_identity_at_zero_and_norm, pin_recode_single_rotation, pin_identity_map_copies_cache,
     pin_identity_map_recodes_keys, pin_apply_brute_force, pin_apply_rows_and_content_space,
     pin_planner_shape_arithmetic, pin_stats_exact_rational, pin_chan_streaming_equals_two_pass,
