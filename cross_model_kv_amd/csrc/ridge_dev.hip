@@ -4,9 +4,11 @@
 //
 //   A = sym(M_xx) + lambda I  (read from M_xx's upper triangle, like the host solver), padded to a
 //       multiple of 64 with an identity block;  B = M_xy, padded with zero rows/columns
-//   A = L L^T    right-looking blocked Cholesky, 64-wide blocks: factor the diagonal block in
-//                one workgroup, solve the panel below it, update the trailing lower triangle
-//   L Z = B, L^T W = Z   blocked forward / back substitution over all right-hand sides
+//   A = L L^T    right-looking blocked Cholesky, 64-wide blocks: factor the diagonal block and
+//                invert its factor in one workgroup, multiply the panel below it by that
+//                inverse, update the trailing lower triangle (once per panel of 4 blocks)
+//   L Z = B, L^T W = Z   blocked forward / back substitution over all right-hand sides, each
+//                diagonal step a product with the block's inverse
 //   b = mean_y - mean_x W;  W written output-major [q][p] in bf16 or fp32 (the apply's layout),
 //   or, for layer scoring, the in-sample R^2 of the fit pooled over groups of y columns, from
 //   the statistics alone: RSS_c = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2
@@ -16,6 +18,8 @@
 // on the fp64 matrix cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their
 // global orientation.  A non-positive or non-finite pivot sets the system's device flag, which
 // the host turns into KVMAP_ERR_NOT_SPD.
+
+#include <algorithm>
 
 #include "common.h"
 #include "internal.h"
@@ -32,7 +36,7 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 // Everything a batched launch needs, passed by value (kernel argument space).
 struct RidgeArgs {
     RidgeSys s[kRidgeMaxBatch];
-    double* scratch;  // system z: A = scratch + z * stride, B = A + P^2, rss = B + P Q
+    double* scratch;  // system z: A = scratch + z * stride, B = A + P^2, rss = B + P Q, Li = rss + Q
     size_t stride;    // doubles per system
     int* bad;         // [n] pivot flags
     int p, q, P, Q;
@@ -44,6 +48,8 @@ __device__ __forceinline__ double* sys_b(const RidgeArgs& g) { return sys_a(g) +
 __device__ __forceinline__ double* sys_rss(const RidgeArgs& g) {
     return sys_b(g) + (size_t)g.P * g.Q;
 }
+// Inverses of the 64 x 64 diagonal blocks of L, [P / 64][64][64]
+__device__ __forceinline__ double* sys_li(const RidgeArgs& g) { return sys_rss(g) + g.Q; }
 
 // Lower-triangle tile list after a block: tile u -> (I >= J)
 __device__ __forceinline__ void lower_decode(int u, int& I, int& J) {
@@ -82,9 +88,13 @@ __global__ __launch_bounds__(256) void ridge_init_b_kernel(const RidgeArgs g) {
     sys_b(g)[idx] = (i < p && c < q) ? (double)M_xy[(size_t)i * q + c] : 0.0;
 }
 
-// Factor the diagonal block kb in place (lower triangle), one workgroup of 64 threads per system.
+// Factor the diagonal block kb in place (lower triangle) and write the inverse of the factor to
+// Li[kb]; one workgroup of 64 threads per system.  The inverse turns every triangular solve
+// with this block (the panel below it and both substitutions) into a 64 x 64 tile product on
+// the matrix cores.
 __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
     __shared__ double t[RB][RB + 1];
+    __shared__ double x[RB][RB + 1];
     double* A = sys_a(g);
     const int P = g.P;
     const int r = threadIdx.x;
@@ -107,124 +117,71 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
         __syncthreads();
     }
     for (int c = 0; c < RB; ++c) A[(size_t)(o + r) * P + o + c] = (c <= r) ? t[r][c] : 0.0;
-}
-
-// Panel: A_ik <- A_ik L_kk^-T for the 64-row blocks i below kb; workgroup = one row block,
-// thread = one row (forward substitution along the row).
-__global__ __launch_bounds__(64) void ridge_trsm_panel_kernel(const RidgeArgs g, int kb) {
-    __shared__ double L[RB][RB + 1];
-    __shared__ double X[RB][RB + 1];
-    double* A = sys_a(g);
-    const int P = g.P;
-    const int r = threadIdx.x;
-    const int o = kb * RB;
-    const int i0 = o + RB * (1 + (int)blockIdx.x);
-    for (int c = 0; c < RB; ++c) {
-        L[r][c] = A[(size_t)(o + r) * P + o + c];
-        X[r][c] = A[(size_t)(i0 + r) * P + o + c];
-    }
-    __syncthreads();
-    for (int j = 0; j < RB; ++j) {
-        double s = X[r][j];
-        for (int m = 0; m < j; ++m) s -= X[r][m] * L[j][m];
-        X[r][j] = s / L[j][j];
-    }
-    for (int c = 0; c < RB; ++c) A[(size_t)(i0 + r) * P + o + c] = X[r][c];
-}
-
-// Right-hand sides, diagonal block kb: forward (Z_kb = L_kk^-1 B_kb) or backward
-// (W_kb = L_kk^-T Z_kb); workgroup = 64 right-hand-side columns, thread = one column.
-template <bool FWD>
-__global__ __launch_bounds__(64) void ridge_trsm_rhs_kernel(const RidgeArgs g, int kb) {
-    __shared__ double L[RB][RB + 1];
-    __shared__ double Xs[RB][RB + 1];
-    const double* A = sys_a(g);
-    double* B = sys_b(g);
-    const int P = g.P, Q = g.Q;
-    const int c = threadIdx.x;
-    const int o = kb * RB, c0 = (int)blockIdx.x * RB;
-    for (int rr = 0; rr < RB; ++rr) {
-        L[rr][c] = A[(size_t)(o + rr) * P + o + c];
-        Xs[rr][c] = B[(size_t)(o + rr) * Q + c0 + c];
-    }
-    __syncthreads();
-    if (FWD) {
-        for (int rr = 0; rr < RB; ++rr) {
-            double s = Xs[rr][c];
-            for (int m = 0; m < rr; ++m) s -= L[rr][m] * Xs[m][c];
-            Xs[rr][c] = s / L[rr][rr];
+    // X = L^-1 by forward substitution, thread r = column r of X:
+    //   X[i][r] = (delta_ir - sum_{m = r}^{i-1} L[i][m] X[m][r]) / L[i][i],  i >= r
+    for (int i = 0; i < RB; ++i) {
+        double v = 0.0;
+        if (i >= r) {
+            double acc = (i == r) ? 1.0 : 0.0;
+            for (int m = r; m < i; ++m) acc -= t[i][m] * x[m][r];
+            v = acc / t[i][i];
         }
-    } else {
-        for (int rr = RB - 1; rr >= 0; --rr) {
-            double s = Xs[rr][c];
-            for (int m = rr + 1; m < RB; ++m) s -= L[m][rr] * Xs[m][c];
-            Xs[rr][c] = s / L[rr][rr];
-        }
+        x[i][r] = v;
     }
-    for (int rr = 0; rr < RB; ++rr) B[(size_t)(o + rr) * Q + c0 + c] = Xs[rr][c];
+    double* Li = sys_li(g) + (size_t)kb * RB * RB;
+    for (int i = 0; i < RB; ++i) Li[(size_t)i * RB + r] = x[i][r];
 }
 
-// C -= op(A) op(B) on 64 x 64 tiles, K = 64, on the fp64 matrix cores.  The tile list:
-//   MODE 0  trailing lower triangle of A after block kb:  C = A_IJ, op(A) = A_I,kb,
-//           op(B) = A_J,kb^T  (I >= J > kb)
-//   MODE 1  forward update of the right-hand sides: C = B_I,J (I > kb), op(A) = L_I,kb,
-//           op(B) = Z_kb,J
-//   MODE 2  backward update: C = Z_I,J (I < kb), op(A) = L_kb,I^T, op(B) = W_kb,J
+// C -= sum over K blocks kb = k0 .. k0 + nk - 1 of op(A) op(B), on 64 x 64 tiles with K = 64
+// per block, on the fp64 matrix cores (MODE 3..5: C = op(A) op(B), one block, C in place).
+// The tile list (i0: first row block; j0, ncol: first column block and count):
+//   MODE 0  lower triangle of A:  C = A_IJ (I >= J), op(A) = A_I,kb, op(B) = A_J,kb^T.  TRI: the
+//           whole lower triangle from block j0 on (lower_decode); else the rectangle
+//           I in [i0, ..) x J in [j0, j0 + ncol), tiles with I < J skipped
+//   MODE 1  forward update of the right-hand sides: C = B_I,J, op(A) = L_I,kb, op(B) = Z_kb,J
+//   MODE 2  backward update: C = Z_I,J, op(A) = L_kb,I^T, op(B) = W_kb,J
+//   MODE 3  panel below block kb: C = A_I,kb (I > kb) = A_I,kb Li_kb^T
+//   MODE 4  forward diagonal step: C = B_kb,J = Li_kb B_kb,J
+//   MODE 5  backward diagonal step: C = B_kb,J = Li_kb^T B_kb,J
 // Operand tiles are copied to LDS as they lie in memory (64 rows of 64 consecutive doubles,
 // coalesced); A_ROWS / B_ROWS say whether an LDS row is an r (resp. c) index or an m index.
 // 4 waves, each a 32 x 32 quarter of C as 2 x 2 blocks of 16 x 16 (v_mfma_f64_16x16x4f64:
 // lane (i, k) = (lane & 15, lane >> 4) supplies A[i][k] and B[k][i]; accumulator element e
 // of lane is C[(lane >> 4) + 4 e][lane & 15], rows interleaved by 4, unlike the fp32 forms).
-template <int MODE>
-__global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, int kb, int ncol) {
-    constexpr bool A_ROWS = MODE != 2;  // LDS row of A is r (else m)
-    constexpr bool B_ROWS = MODE == 0;  // LDS row of B is c (else m)
+// C is read and written once per launch, so a launch over a panel of nk blocks moves nk times
+// fewer C bytes per FLOP than one launch per block.
+template <int MODE, bool TRI>
+__global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, int i0, int j0, int ncol, int k0,
+                                                           int nk) {
+    constexpr bool A_ROWS = MODE != 2 && MODE != 5;  // LDS row of A is r (else m)
+    constexpr bool B_ROWS = MODE == 0 || MODE == 3;  // LDS row of B is c (else m)
+    constexpr bool OVERWRITE = MODE >= 3;
     __shared__ double As[RB * LDW];
     __shared__ double Bs[RB * LDW];
     double* A = sys_a(g);
+    const double* Li = sys_li(g);
     double* Bm = sys_b(g);
     const int P = g.P, Q = g.Q;
     const int tid = threadIdx.x;
     int I, J;
-    if (MODE == 0) {
+    if (MODE == 0 && TRI) {
         lower_decode(blockIdx.x, I, J);
-        I += kb + 1;
-        J += kb + 1;
+        I += j0;
+        J += j0;
     } else {
-        I = (int)blockIdx.x / ncol;
-        J = (int)blockIdx.x - I * ncol;
-        if (MODE == 1) I += kb + 1;
+        I = i0 + (int)blockIdx.x / ncol;
+        J = j0 + (int)blockIdx.x % ncol;
+        if (MODE == 0 && I < J) return;
     }
-    const int o = kb * RB;
     double* C;
     int ldc;
-    const double* Ap;  // row x of the stored tile: Ap + x * lda
-    const double* Bp;
-    int lda, ldb;
-    if (MODE == 0) {
+    if (MODE == 0 || MODE == 3) {
         C = A + (size_t)I * RB * P + (size_t)J * RB;
         ldc = P;
-        Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
-        Bp = A + (size_t)J * RB * P + o; ldb = P;   // rows c, columns m
-    } else if (MODE == 1) {
-        C = Bm + (size_t)I * RB * Q + (size_t)J * RB;
-        ldc = Q;
-        Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
-        Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
     } else {
         C = Bm + (size_t)I * RB * Q + (size_t)J * RB;
         ldc = Q;
-        Ap = A + (size_t)o * P + (size_t)I * RB; lda = P;   // rows m, columns r
-        Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
     }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int e = u * 256 + tid;
-        const int x = e >> 6, y = e & 63;
-        As[x * LDW + y] = Ap[(size_t)x * lda + y];
-        Bs[x * LDW + y] = Bp[(size_t)x * ldb + y];
-    }
-    __syncthreads();
     const int lane = tid & 63, w = tid >> 6;
     const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
     const int li = lane & 15, lk = lane >> 4;
@@ -233,20 +190,52 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int k0 = 0; k0 < RB; k0 += 4) {
-        const int m = k0 + lk;
-        double a[2], b[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = r0 + 16 * i + li, c = c0 + 16 * i + li;
-            a[i] = A_ROWS ? As[r * LDW + m] : As[m * LDW + r];
-            b[i] = B_ROWS ? Bs[c * LDW + m] : Bs[m * LDW + c];
+    for (int kc = 0; kc < nk; ++kc) {
+        const int o = (k0 + kc) * RB;
+        const double* Ap;  // row x of the stored tile: Ap + x * lda
+        const double* Bp;
+        int lda, ldb;
+        if (MODE == 0) {
+            Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
+            Bp = A + (size_t)J * RB * P + o; ldb = P;   // rows c, columns m
+        } else if (MODE == 1) {
+            Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
+            Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
+        } else if (MODE == 2) {
+            Ap = A + (size_t)o * P + (size_t)I * RB; lda = P;   // rows m, columns r
+            Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
+        } else if (MODE == 3) {
+            Ap = C; lda = P;                                    // rows r, columns m
+            Bp = Li + (size_t)(k0 + kc) * RB * RB; ldb = RB;    // Li rows c, columns m
+        } else {
+            Ap = Li + (size_t)(k0 + kc) * RB * RB; lda = RB;    // MODE 4: rows r, cols m; 5: rows m, cols r
+            Bp = C; ldb = Q;                                    // rows m, columns c
         }
+        if (kc) __syncthreads();  // every wave is done with the previous block's tiles
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int u = 0; u < 16; ++u) {
+            const int e = u * 256 + tid;
+            const int x = e >> 6, y = e & 63;
+            As[x * LDW + y] = Ap[(size_t)x * lda + y];
+            Bs[x * LDW + y] = Bp[(size_t)x * ldb + y];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < RB; kk += 4) {
+            const int m = kk + lk;
+            double a[2], b[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 2; ++i) {
+                const int r = r0 + 16 * i + li, c = c0 + 16 * i + li;
+                a[i] = A_ROWS ? As[r * LDW + m] : As[m * LDW + r];
+                b[i] = B_ROWS ? Bs[c * LDW + m] : Bs[m * LDW + c];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -255,7 +244,8 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + 16 * i + lk + 4 * e, c = c0 + 16 * j + li;
-                C[(size_t)r * ldc + c] -= acc[i][j][e];
+                if (OVERWRITE) C[(size_t)r * ldc + c] = acc[i][j][e];
+                else C[(size_t)r * ldc + c] -= acc[i][j][e];
             }
 }
 
@@ -356,7 +346,7 @@ namespace {
 
 size_t sys_stride(int p, int q) {
     const size_t P = ((size_t)p + RB - 1) / RB * RB, Q = ((size_t)q + RB - 1) / RB * RB;
-    return (P * P + P * Q + Q + 31) / 32 * 32;  // A, B (then W), rss; 256-byte aligned
+    return (P * P + P * Q + Q + P * RB + 31) / 32 * 32;  // A, B (then W), rss, Li; 256-byte aligned
 }
 
 RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, void* scratch) {
@@ -374,29 +364,60 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
 }
 
 // A = L L^T (lower triangle of A), then W = A^-1 M_xy in B, row-major [P][Q], every system.
+// The 64-wide blocks are taken in panels of kPanel: inside a panel each block is factored and
+// applied to the panel's own columns (and, in the substitutions, its own rows) at once; the
+// rest of the matrix (or of the right-hand sides) is updated once per panel with K = 64 kPanel.
+constexpr int kPanel = 4;
+
 void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
     const int P = g.P, Q = g.Q;
     const int nb = P / RB, nq = Q / RB;
     const unsigned un = (unsigned)n;
-    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256), un), dim3(256), 0, s, g);
-    hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), dim3(256), 0, s, g);
-    for (int kb = 0; kb < nb; ++kb) {
-        hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1, un), dim3(RB), 0, s, g, kb);
-        const int below = nb - kb - 1;
-        if (below > 0) {
-            hipLaunchKernelGGL(ridge_trsm_panel_kernel, dim3(below, un), dim3(RB), 0, s, g, kb);
-            hipLaunchKernelGGL(ridge_update_kernel<0>, dim3(below * (below + 1) / 2, un), dim3(256), 0, s, g, kb, 0);
+    const dim3 blk(256);
+    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256), un), blk, 0, s, g);
+    hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), blk, 0, s, g);
+    // factorisation
+    for (int b0 = 0; b0 < nb; b0 += kPanel) {
+        const int b1 = std::min(nb, b0 + kPanel);
+        for (int kb = b0; kb < b1; ++kb) {
+            hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1, un), dim3(RB), 0, s, g, kb);
+            const int below = nb - kb - 1;
+            if (below == 0) continue;
+            hipLaunchKernelGGL((ridge_update_kernel<3, false>), dim3(below, un), blk, 0, s, g, kb + 1, kb, 1, kb, 1);
+            const int w = b1 - kb - 1;  // the panel's columns right of kb, every row below
+            if (w > 0)
+                hipLaunchKernelGGL((ridge_update_kernel<0, false>), dim3(below * w, un), blk, 0, s, g, kb + 1, kb + 1,
+                                   w, kb, 1);
         }
+        const int m = nb - b1;  // trailing lower triangle
+        if (m > 0)
+            hipLaunchKernelGGL((ridge_update_kernel<0, true>), dim3(m * (m + 1) / 2, un), blk, 0, s, g, b1, b1, 0, b0,
+                               b1 - b0);
     }
-    for (int kb = 0; kb < nb; ++kb) {
-        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<true>, dim3(nq, un), dim3(RB), 0, s, g, kb);
-        const int below = nb - kb - 1;
-        if (below > 0)
-            hipLaunchKernelGGL(ridge_update_kernel<1>, dim3(below * nq, un), dim3(256), 0, s, g, kb, nq);
+    // L Z = B
+    for (int b0 = 0; b0 < nb; b0 += kPanel) {
+        const int b1 = std::min(nb, b0 + kPanel);
+        for (int kb = b0; kb < b1; ++kb) {
+            hipLaunchKernelGGL((ridge_update_kernel<4, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
+            const int h = b1 - kb - 1;
+            if (h > 0)
+                hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3(h * nq, un), blk, 0, s, g, kb + 1, 0, nq, kb, 1);
+        }
+        if (nb > b1)
+            hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3((nb - b1) * nq, un), blk, 0, s, g, b1, 0, nq, b0,
+                               b1 - b0);
     }
-    for (int kb = nb - 1; kb >= 0; --kb) {
-        hipLaunchKernelGGL(ridge_trsm_rhs_kernel<false>, dim3(nq, un), dim3(RB), 0, s, g, kb);
-        if (kb > 0) hipLaunchKernelGGL(ridge_update_kernel<2>, dim3(kb * nq, un), dim3(256), 0, s, g, kb, nq);
+    // L^T W = Z, panels from the last
+    for (int b1 = nb; b1 > 0; b1 -= kPanel) {
+        const int b0 = std::max(0, b1 - kPanel);
+        for (int kb = b1 - 1; kb >= b0; --kb) {
+            hipLaunchKernelGGL((ridge_update_kernel<5, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
+            const int h = kb - b0;
+            if (h > 0)
+                hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3(h * nq, un), blk, 0, s, g, b0, 0, nq, kb, 1);
+        }
+        if (b0 > 0)
+            hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3(b0 * nq, un), blk, 0, s, g, 0, 0, nq, b0, b1 - b0);
     }
 }
 
