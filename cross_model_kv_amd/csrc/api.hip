@@ -591,6 +591,9 @@ static int validate_state(const kvmap_gram_state* st, const char* which) {
         return fail(KVMAP_ERR_SHAPE, "%s state: p=%d, q=%d must be multiples of 4 in [4, 65536]", which,
                     (int)st->p, (int)st->q);
     if (st->n < 0) return fail(KVMAP_ERR_SHAPE, "%s state: n < 0", which);
+    if (st->xx_block < 0 || (st->xx_block && ((st->xx_block & 3) || st->p % st->xx_block)))
+        return fail(KVMAP_ERR_SHAPE, "%s state: xx_block=%d must be 0 or a multiple of 4 dividing p=%d", which,
+                    (int)st->xx_block, (int)st->p);
     if (!st->mean_x || !st->mean_y || !st->M_xx || !st->M_xy)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s state: NULL array", which);
     const void* arr[5] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy, st->ss_y};
@@ -648,7 +651,7 @@ extern "C" int kvmap_gram_reset(kvmap_ctx* c, kvmap_gram_state* st, void* stream
     hipStream_t s = (hipStream_t)stream;
     KVMAP_HIP(launch_fill_zero(st->mean_x, st->p, s));
     KVMAP_HIP(launch_fill_zero(st->mean_y, st->q, s));
-    KVMAP_HIP(launch_fill_zero(st->M_xx, (int64_t)st->p * st->p, s));
+    KVMAP_HIP(launch_fill_zero(st->M_xx, (int64_t)st->p * (st->xx_block ? st->xx_block : st->p), s));
     KVMAP_HIP(launch_fill_zero(st->M_xy, (int64_t)st->p * st->q, s));
     if (st->ss_y) KVMAP_HIP(launch_fill_zero(st->ss_y, st->q, s));
     st->n = 0;
@@ -681,7 +684,7 @@ extern "C" int kvmap_gram(kvmap_ctx* c, const void* X, const void* Y, int64_t n_
         const char* xb = (const char*)X + (size_t)r0 * st->p * esz;
         const char* yb = (const char*)Y + (size_t)r0 * st->q * esz;
         KVMAP_HIP(launch_gram_batch(e, xb, yb, nr, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
-                                    st->M_xy, st->ss_y, sc, (hipStream_t)stream));
+                                    st->M_xy, st->ss_y, st->xx_block, sc, (hipStream_t)stream));
         st->n += nr;
     }
     return ok();
@@ -699,6 +702,8 @@ extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap
     if (dst->M_xx == src->M_xx) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src alias");
     if (!dst->ss_y != !src->ss_y)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: ss_y kept by one state only");
+    if (dst->xx_block != src->xx_block)
+        return fail(KVMAP_ERR_SHAPE, "kvmap_gram_merge: xx_block differs");
     if (src->n == 0) return ok();
     DeviceGuard g(c->device);
     r = ensure_gram_scratch(c, dst->p, dst->q, 0);
@@ -706,7 +711,7 @@ extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap
     const GramScratch sc = gram_scratch(c, dst->p, dst->q, 1);
     KVMAP_HIP(launch_gram_merge(dst->p, dst->q, dst->n, src->n, dst->mean_x, dst->mean_y, dst->M_xx,
                                 dst->M_xy, dst->ss_y, src->mean_x, src->mean_y, src->M_xx, src->M_xy,
-                                src->ss_y, sc,
+                                src->ss_y, dst->xx_block, sc,
                                 (hipStream_t)stream));
     dst->n += src->n;
     return ok();
@@ -782,6 +787,7 @@ static int check_solve_args(const kvmap_gram_state* st, const void* W_out, const
                             const char* who) {
     int r = validate_state(st, who);
     if (r) return r;
+    if (st->xx_block) return fail(KVMAP_ERR_UNSUPPORTED, "%s: a block-diagonal state (solve its blocks' views)", who);
     if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL output", who);
     const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
     const size_t wb = (size_t)st->p * st->q * es, bb = (size_t)st->q * es;
@@ -799,6 +805,7 @@ static int check_solve_args(const kvmap_gram_state* st, const void* W_out, const
 static int check_r2_args(const kvmap_gram_state* st, int32_t group, const double* r2_out, const char* who) {
     int r = validate_state(st, who);
     if (r) return r;
+    if (st->xx_block) return fail(KVMAP_ERR_UNSUPPORTED, "%s: a block-diagonal state (solve its blocks' views)", who);
     if (!st->ss_y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: the state keeps no ss_y", who);
     if (!r2_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL output", who);
     if (group < 1 || st->q % group)
@@ -902,6 +909,7 @@ extern "C" int kvmap_ridge_solve(kvmap_ctx* c, const kvmap_gram_state* st, doubl
     if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve: ctx is NULL");
     int r = validate_state(st, "kvmap_ridge_solve");
     if (r) return r;
+    if (st->xx_block) return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_ridge_solve: a block-diagonal state");
     if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve: NULL output");
     DeviceGuard g(c->device);
     const size_t p = st->p, q = st->q;

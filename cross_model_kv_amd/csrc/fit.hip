@@ -6,9 +6,15 @@
 //
 // The driver owns the statistics of one stage at a time and calls the library's own entry
 // points for every step: kvmap_cache_rows (gather + strip RoPE into token rows), kvmap_gram
-// (Chan-merged centered statistics), kvmap_ridge_r2 (stage-1 scores per target head) and
-// kvmap_ridge_solve_device (stage-2 maps).  The selection itself (average over heads and
+// (Chan-merged centered statistics), kvmap_ridge_r2_batch (stage-1 scores per target head) and
+// kvmap_ridge_solve_device_batch (stage-2 maps).  The selection itself (average over heads and
 // {K, V}, top-k) is the one kernel of this file.
+//
+// Stage 1 feeds a group of source layers (as many as fit 65,536 features) as ONE Gram state per
+// K/V whose M_xx is kept block-diagonal, one block per layer: every layer's M_xx and M_xy come
+// out of one launch per batch, the target rows are split once per batch rather than once per
+// source layer, and the launch has enough tiles to fill the chip.  Each layer's block is then a
+// state of its own for the R^2 solves.
 
 #include "../../include/kvmap.h"
 
@@ -86,6 +92,7 @@ struct kvmap_fit {
     int device = 0;
     int N = 0, F = 0;                  // H*d, k*H*d
     int sel_block = 0, map_block = 0;  // target layers per pass of each stage
+    int group = 0, groups = 0;         // stage 1: source layers per Gram state, states per K/V
     int sel_passes = 0, map_passes = 0;
     int pass = -1;                     // index of the open pass, -1 before the first
     int stage = 0, t0 = 0, t1 = 0;
@@ -141,26 +148,35 @@ void free_stage(kvmap_fit* f) {
 
 // Lay out n states of (p, q) in one allocation; every array starts 16-byte aligned since p, q
 // are multiples of 64.
-int alloc_states(kvmap_fit* f, int n, int p, int q, bool keep_ss_y) {
+// Lay out states of widths ps[i] (all of one q) in one allocation; every array starts 16-byte
+// aligned since p, q and the block are multiples of 64.  xx_block > 0: M_xx block-diagonal.
+int alloc_states(kvmap_fit* f, const std::vector<int>& ps, int q, bool keep_ss_y, int xx_block) {
     free_stage(f);
-    const size_t per = (size_t)p + q + (size_t)p * p + (size_t)p * q + (keep_ss_y ? q : 0);
-    FIT_HIP(hipMalloc((void**)&f->state_mem, per * n * sizeof(float)));
-    f->states.resize(n);
+    size_t total = 0;
+    for (int p : ps)
+        total += (size_t)p + q + (size_t)p * (xx_block ? xx_block : p) + (size_t)p * q + (keep_ss_y ? q : 0);
+    FIT_HIP(hipMalloc((void**)&f->state_mem, total * sizeof(float)));
+    f->states.assign(ps.size(), kvmap_gram_state{});
     float* b = f->state_mem;
-    for (int i = 0; i < n; ++i) {
+    for (size_t i = 0; i < ps.size(); ++i) {
+        const int p = ps[i];
         kvmap_gram_state& st = f->states[i];
         st.n = 0;
         st.p = p;
         st.q = q;
+        st.xx_block = xx_block;
         st.mean_x = b; b += p;
         st.mean_y = b; b += q;
-        st.M_xx = b; b += (size_t)p * p;
+        st.M_xx = b; b += (size_t)p * (xx_block ? xx_block : p);
         st.M_xy = b; b += (size_t)p * q;
         st.ss_y = keep_ss_y ? b : nullptr;
         b += keep_ss_y ? q : 0;
     }
     return KVMAP_OK;
 }
+
+// Source layers of stage-1 group g: [g * group, min(L_src, (g + 1) * group))
+int group_layers(const kvmap_fit* f, int g) { return std::min(f->cfg.L_src, (g + 1) * f->group) - g * f->group; }
 
 int ensure_rows(void** buf, size_t* cap, size_t need, hipStream_t s) {
     if (need <= *cap) return KVMAP_OK;
@@ -181,7 +197,12 @@ int open_pass(kvmap_fit* f, hipStream_t s) {
         f->stage = 1;
         f->t0 = f->pass * f->sel_block;
         f->t1 = std::min(c.L_tgt, f->t0 + f->sel_block);
-        if (f->pass == 0) FIT_TRY(alloc_states(f, 2 * c.L_src, f->N, f->sel_block * f->N, true));
+        if (f->pass == 0) {
+            std::vector<int> ps;
+            for (int kv = 0; kv < 2; ++kv)
+                for (int g = 0; g < f->groups; ++g) ps.push_back(group_layers(f, g) * f->N);
+            FIT_TRY(alloc_states(f, ps, f->sel_block * f->N, true, f->N));
+        }
         for (auto& st : f->states) {
             st.q = (f->t1 - f->t0) * f->N;
             FIT_TRY(kvmap_gram_reset(f->ctx, &st, s));
@@ -192,7 +213,7 @@ int open_pass(kvmap_fit* f, hipStream_t s) {
     f->stage = 2;
     f->t0 = b * f->map_block;
     f->t1 = std::min(c.L_tgt, f->t0 + f->map_block);
-    if (b == 0) FIT_TRY(alloc_states(f, 2 * f->map_block, f->F, f->N, false));
+    if (b == 0) FIT_TRY(alloc_states(f, std::vector<int>(2 * f->map_block, f->F), f->N, false, 0));
     for (int i = 0; i < 2 * (f->t1 - f->t0); ++i) FIT_TRY(kvmap_gram_reset(f->ctx, &f->states[i], s));
     return KVMAP_OK;
 }
@@ -207,13 +228,25 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
     if (f->n_first < 0) f->n_first = f->n_pass;
     if (f->stage == 1) {
         const int H = c.H_kv;
-        std::vector<const kvmap_gram_state*> st;
+        // one view per (K/V, source layer): the layer's diagonal block of its group's state
+        const int N = f->N;
+        std::vector<kvmap_gram_state> views;
         std::vector<double*> out;
         for (int kv = 0; kv < 2; ++kv)
             for (int sl = 0; sl < c.L_src; ++sl) {
-                st.push_back(&f->states[kv * c.L_src + sl]);
+                const kvmap_gram_state& G = f->states[kv * f->groups + sl / f->group];
+                const int j = sl % f->group;
+                kvmap_gram_state v = G;
+                v.p = N;
+                v.xx_block = 0;
+                v.mean_x = G.mean_x + (size_t)j * N;
+                v.M_xx = G.M_xx + (size_t)j * N * N;
+                v.M_xy = G.M_xy + (size_t)j * N * G.q;
+                views.push_back(v);
                 out.push_back(f->r2 + (((size_t)kv * c.L_src + sl) * c.L_tgt + f->t0) * H);
             }
+        std::vector<const kvmap_gram_state*> st;
+        for (const auto& v : views) st.push_back(&v);
         FIT_TRY(kvmap_ridge_r2_batch(f->ctx, st.data(), (int)st.size(), c.lambda, c.head_dim, out.data(), s));
         if (f->pass == f->sel_passes - 1) {
             double* scores = c.scores ? c.scores : f->own_scores;
@@ -311,6 +344,8 @@ extern "C" int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvm
     f->map_block = c.map_block ? std::min<int>(c.map_block, c.L_tgt) : c.L_tgt;
     f->sel_passes = c.given_sel ? 0 : (c.L_tgt + f->sel_block - 1) / f->sel_block;
     f->map_passes = (c.L_tgt + f->map_block - 1) / f->map_block;
+    f->group = (int)std::min<int64_t>(std::min<int64_t>(c.L_src, kMaxGramWidth / N), kMaxRowLayers);
+    f->groups = (c.L_src + f->group - 1) / f->group;
     int st = KVMAP_OK;
     if (c.given_sel) {
         hipError_t e = hipMemcpy(f->sel.data(), c.layer_sel, f->sel.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
@@ -380,17 +415,20 @@ extern "C" int kvmap_fit_add(kvmap_fit* f, const void* src_k, const void* src_v,
     const void* tgt[2] = {tgt_k, tgt_v};
     if (f->stage == 1) {
         const int nb = f->t1 - f->t0;
-        FIT_TRY(ensure_rows(&f->xrows, &f->xcap, (size_t)T * f->N * es, s));
+        FIT_TRY(ensure_rows(&f->xrows, &f->xcap, (size_t)T * f->group * f->N * es, s));
         FIT_TRY(ensure_rows(&f->yrows, &f->ycap, (size_t)T * nb * f->N * es, s));
         std::vector<int32_t> block(nb);
         for (int j = 0; j < nb; ++j) block[j] = f->t0 + j;
         for (int kv = 0; kv < 2; ++kv) {
             FIT_TRY(kvmap_cache_rows(f->ctx, tgt[kv], c.L_tgt, H, T, d, c.dtype, block.data(), nb, kv ? nullptr : &rt,
                                      f->yrows, s));
-            for (int32_t sl = 0; sl < c.L_src; ++sl) {
-                FIT_TRY(kvmap_cache_rows(f->ctx, src[kv], c.L_src, H, T, d, c.dtype, &sl, 1, kv ? nullptr : &rs,
-                                         f->xrows, s));
-                FIT_TRY(kvmap_gram(f->ctx, f->xrows, f->yrows, T, c.dtype, &f->states[kv * c.L_src + sl], s));
+            for (int g = 0; g < f->groups; ++g) {
+                const int gl = group_layers(f, g);
+                std::vector<int32_t> layers(gl);
+                for (int j = 0; j < gl; ++j) layers[j] = g * f->group + j;
+                FIT_TRY(kvmap_cache_rows(f->ctx, src[kv], c.L_src, H, T, d, c.dtype, layers.data(), gl,
+                                         kv ? nullptr : &rs, f->xrows, s));
+                FIT_TRY(kvmap_gram(f->ctx, f->xrows, f->yrows, T, c.dtype, &f->states[kv * f->groups + g], s));
             }
         }
     } else {

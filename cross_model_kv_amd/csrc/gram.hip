@@ -166,14 +166,22 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
     const void* __restrict__ X, const void* __restrict__ Y, int64_t n_b, int p, int q,
     const float* __restrict__ cx, const float* __restrict__ cy, const float* __restrict__ mx,
     const float* __restrict__ my, const float* __restrict__ dx, const float* __restrict__ dy,
-    float coef, int fresh, float* __restrict__ M_xx, float* __restrict__ M_xy, int nTx, int nXX) {
+    float coef, int fresh, float* __restrict__ M_xx, float* __restrict__ M_xy, int nTx, int nXX, int bd,
+    int nTb) {
     __shared__ float4 lds[2][2][GK * GLD / 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int I, J;
+    // bd > 0: M_xx kept as p / bd compact diagonal blocks (see the bf16 co-moment kernel)
+    int I, J, blk = 0;
     bool xy;
     if ((int)blockIdx.x < nXX) {
-        tri_decode(blockIdx.x, nTx, I, J);
+        if (bd) {
+            const int per = nTb * (nTb + 1) / 2;
+            blk = (int)blockIdx.x / per;
+            tri_decode((int)blockIdx.x - blk * per, nTb, I, J);
+        } else {
+            tri_decode(blockIdx.x, nTx, I, J);
+        }
         xy = false;
     } else {
         const int u = blockIdx.x - nXX;
@@ -181,7 +189,8 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
         J = u / nTx;
         xy = true;
     }
-    const int i0 = I * GT, j0 = J * GT;
+    const int b0 = blk * bd;
+    const int i0 = b0 + I * GT, j0 = b0 + J * GT;
     const void* B = xy ? Y : X;
     const int ldb = xy ? q : p;
     const float* cb = xy ? cy : cx;
@@ -255,8 +264,12 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
 
     // Epilogue: lane holds G[i][j] for column j = lane & 31 of each 32x32 block and rows
     // i = 8*(r/4) + 4*(lane/32) + r%4.
-    float* M = xy ? M_xy : M_xx;
-    const int ldm = xy ? q : p;
+    const bool blocked = !xy && bd;
+    float* M = xy ? M_xy : (blocked ? M_xx + (size_t)blk * bd * bd : M_xx);
+    const int ldm = xy ? q : (blocked ? bd : p);
+    const int moff = blocked ? b0 : 0;
+    const int lim = xy ? q : (blocked ? b0 + bd : p);  // column limit
+    const int rlim = blocked ? b0 + bd : p;            // row limit
     const float* mb = xy ? my : mx;
     const float* db = xy ? dy : dx;
     const float nbf = (float)n_b;
@@ -264,14 +277,14 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int j = j0 + wj * 64 + b * 32 + (lane & 31);
-        const bool jok = j < ldm;
+        const bool jok = j < lim;
         const float mj = jok ? mb[j] : 0.f, dj = jok ? db[j] : 0.f;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int ib = i0 + wi * 64 + a * 32 + g * 8 + (lane >> 5) * 4;
-                if (ib >= p || !jok) continue;
+                if (ib >= rlim || !jok) continue;
                 const float4 mi = *(const float4*)(mx + ib);
                 const float4 di = *(const float4*)(dx + ib);
                 float v[4];
@@ -282,11 +295,11 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
                     v[r] = acc[a][b][g * 4 + r] - nbf * mia[r] * mj + coef * dia[r] * dj;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float* dst = M + (size_t)(ib + r) * ldm + j;
+                    float* dst = M + (size_t)(ib - moff + r) * ldm + (j - moff);
                     *dst = fresh ? v[r] : *dst + v[r];
                 }
                 if (mirror) {
-                    float4* dst = (float4*)(M + (size_t)j * ldm + ib);
+                    float4* dst = (float4*)(M + (size_t)(j - moff) * ldm + (ib - moff));
                     float4 o = fresh ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
                     o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
                     *dst = o;
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
 
 hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
                              int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
-                             float* M_xy, float* ss_y, const GramScratch& sc, hipStream_t s) {
+                             float* M_xy, float* ss_y, int bd, const GramScratch& sc, hipStream_t s) {
     const bool bf = (e == Elem::BF16);
     const dim3 gx((p + CS_TILE - 1) / CS_TILE, sc.splits), gy((q + CS_TILE - 1) / CS_TILE, sc.splits);
     const int stride = p + q;
@@ -324,7 +337,7 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, ss, p, q, n_b, n_old, 1, 0,
                            sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, sc.part2, ss_y);
-        return launch_gram_x3(Sx, Sy, n_b, p, q, sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, s);
+        return launch_gram_x3(Sx, Sy, n_b, p, q, sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, bd, s);
     }
     for (int phase = 0; phase < 2; ++phase) {
         const float* shx = phase ? sc.cx : nullptr;
@@ -338,10 +351,11 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
                            sc.part2, phase == 1 ? ss_y : nullptr);
     }
     const int nTx = (p + GT - 1) / GT, nTy = (q + GT - 1) / GT;
-    const int nXX = nTx * (nTx + 1) / 2;
+    const int nTb = bd ? (bd + GT - 1) / GT : 0;
+    const int nXX = bd ? (p / bd) * (nTb * (nTb + 1) / 2) : nTx * (nTx + 1) / 2;
     const int blocks = nXX + nTx * nTy;
     hipLaunchKernelGGL(gram_kernel<false>, dim3(blocks), dim3(256), 0, s, X, Y, n_b, p, q, sc.cx, sc.cy,
-                       sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX);
+                       sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, nTx, nXX, bd, nTb);
     return hipGetLastError();
 }
 
@@ -390,15 +404,22 @@ __global__ __launch_bounds__(256) void merge_moments_kernel(int rows, int cols, 
 hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
                              float* mean_y, float* M_xx, float* M_xy, float* ss_y, const float* s_mean_x,
                              const float* s_mean_y, const float* s_M_xx, const float* s_M_xy, const float* s_ss_y,
-                             const GramScratch& sc, hipStream_t s) {
+                             int bd, const GramScratch& sc, hipStream_t s) {
     const double n = (double)n_dst + (double)n_src;
     const int fresh = (n_dst == 0);
     const float coef = (float)((double)n_dst * (double)n_src / n);
     hipLaunchKernelGGL(merge_delta_kernel, dim3((p + q + 255) / 256), dim3(256), 0, s, p, q,
                        (double)n_src / n, fresh, mean_x, mean_y, s_mean_x, s_mean_y, sc.dx, sc.dy, ss_y, s_ss_y,
                        (double)n_dst * (double)n_src / n);
-    hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, p, coef, fresh, M_xx, s_M_xx,
-                       sc.dx, sc.dx);
+    if (bd) {
+        for (int b = 0; b < p / bd; ++b)
+            hipLaunchKernelGGL(merge_moments_kernel, dim3(1024), dim3(256), 0, s, bd, bd, coef, fresh,
+                               M_xx + (size_t)b * bd * bd, s_M_xx + (size_t)b * bd * bd, sc.dx + (size_t)b * bd,
+                               sc.dx + (size_t)b * bd);
+    } else {
+        hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, p, coef, fresh, M_xx, s_M_xx,
+                           sc.dx, sc.dx);
+    }
     hipLaunchKernelGGL(merge_moments_kernel, dim3(4096), dim3(256), 0, s, p, q, coef, fresh, M_xy, s_M_xy,
                        sc.dx, sc.dy);
     return hipGetLastError();

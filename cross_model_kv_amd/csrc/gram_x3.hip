@@ -13,11 +13,12 @@
 //      transposed as S [column][token block][hi of 32 tokens | lo of 32 tokens] (one
 //      128-byte line per column and block), plus partial column sums of d (the tiny mean
 //      of the shifted batch).
-//   2. gram_x3_kernel: the upper triangle of 256 x 256 tiles of S_x S_x^T and all tiles of
-//      S_x S_y^T, K = tokens, with the map GEMM's direct-to-LDS pipeline; the epilogue
-//      turns co-moments about c into co-moments about the batch mean and merges them
-//      into the running state (M += G - n_b m m^T + coef delta delta^T), writing
-//      off-diagonal tiles of M_xx to both triangles.
+//   2. gram_x3_kernel: the upper triangle of 256 x 256 tiles of S_x S_x^T (or, for a state
+//      that keeps M_xx block-diagonal, of each diagonal block) and all tiles of S_x S_y^T,
+//      K = tokens, with the map GEMM's direct-to-LDS pipeline; the epilogue turns co-moments
+//      about c into co-moments about the batch mean and merges them into the running state
+//      (M += G - n_b m m^T + coef delta delta^T), writing off-diagonal tiles of M_xx to both
+//      triangles.
 
 #include "common.h"
 #include "internal.h"
@@ -160,17 +161,25 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ dx,
                                                       const float* __restrict__ dy, float coef, float nbf,
                                                       int fresh, float* __restrict__ M_xx,
-                                                      float* __restrict__ M_xy) {
+                                                      float* __restrict__ M_xy, int bd, int nTb) {
     constexpr int NW = 8, LPO = 4, TW = 64, JB = 4, IB = 8;
     constexpr int TILE = GSTAGE * 16;  // 32 KB
     constexpr int NA = 2, NB = 3;
     __shared__ __attribute__((aligned(16))) char smem[(NA + NB) * TILE];
     uint4* lds = (uint4*)smem;
 
-    int I, J;
+    // bd > 0: M_xx is kept as p / bd diagonal blocks of bd x bd (compact); blk is the block,
+    // I, J count tiles from the matrix origin, b0 is the block's first feature
+    int I, J, blk = 0;
     bool xy;
     if ((int)blockIdx.x < nXX) {
-        tri_decode256(blockIdx.x, nTx, I, J);
+        if (bd) {
+            const int per = nTb * (nTb + 1) / 2;
+            blk = (int)blockIdx.x / per;
+            tri_decode256((int)blockIdx.x - blk * per, nTb, I, J);
+        } else {
+            tri_decode256(blockIdx.x, nTx, I, J);
+        }
         xy = false;
     } else {
         const int u = blockIdx.x - nXX;
@@ -178,7 +187,8 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
         J = u / nTx;
         xy = true;
     }
-    const int i0 = I * GB, j0 = J * GB;
+    const int b0 = blk * bd;  // 0 unless blocked
+    const int i0 = b0 + I * GB, j0 = b0 + J * GB;
     const int ldb = xy ? q : p;
     const uint16_t* __restrict__ Bs = xy ? Sy : Sx;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -311,19 +321,24 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
 
     // Epilogue: lane holds G[i][j] for j = column (lane & 15) and i = 4 (lane / 16) + r of
     // each 16 x 16 block.
-    float* __restrict__ M = xy ? M_xy : M_xx;
+    // M_xx of a blocked state: block blk at M_xx + blk bd^2, local row/column, leading dim bd
+    const bool blocked = !xy && bd;
+    float* __restrict__ M = xy ? M_xy : (blocked ? M_xx + (size_t)blk * bd * bd : M_xx);
+    const int ldm = xy ? q : (blocked ? bd : p);
+    const int moff = blocked ? b0 : 0;
+    const int lim = blocked ? b0 + bd : p;  // rows and columns of M_xx's block (or of M_xx)
     const float* __restrict__ mb = xy ? my : mx;
     const float* __restrict__ db = xy ? dy : dx;
     const bool mirror = !xy && I != J;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
         const int j = j0 + wp * TW + jb * 16 + (lane & 15);
-        const bool jok = j < ldb;
+        const bool jok = j < (xy ? ldb : lim);
         const float mj = jok ? mb[j] : 0.f, dj = jok ? db[j] : 0.f;
 #pragma unroll
         for (int ib = 0; ib < IB; ++ib) {
             const int i = i0 + wn * 128 + ib * 16 + kq * 4;
-            if (!jok || i >= p) continue;  // p is a multiple of 4: all 4 rows valid
+            if (!jok || i >= lim) continue;  // p and bd are multiples of 4: all 4 rows valid
             const float4 mi = *(const float4*)(mx + i);
             const float4 di = *(const float4*)(dx + i);
             const float mia[4] = {mi.x, mi.y, mi.z, mi.w};
@@ -333,11 +348,11 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
             for (int r = 0; r < 4; ++r) v[r] = acc[ib][jb][r] - nbf * mia[r] * mj + coef * dia[r] * dj;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float* dst = M + (size_t)(i + r) * ldb + j;
+                float* dst = M + (size_t)(i - moff + r) * ldm + (j - moff);
                 *dst = fresh ? v[r] : *dst + v[r];
             }
             if (mirror) {
-                float4* dst = (float4*)(M + (size_t)j * p + i);
+                float4* dst = (float4*)(M + (size_t)(j - moff) * ldm + (i - moff));
                 float4 o = fresh ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
                 o.x += v[0];
                 o.y += v[1];
@@ -372,13 +387,14 @@ hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* 
 
 hipError_t launch_gram_x3(const uint16_t* Sx, const uint16_t* Sy, int64_t n_b, int p, int q, const float* mx,
                           const float* my, const float* dx, const float* dy, float coef, int fresh,
-                          float* M_xx, float* M_xy, hipStream_t s) {
+                          float* M_xx, float* M_xy, int bd, hipStream_t s) {
     const int nkb = (int)((n_b + SP_TOK - 1) / SP_TOK);
     const int nTx = (p + GB - 1) / GB, nTy = (q + GB - 1) / GB;
-    const int nXX = nTx * (nTx + 1) / 2;
+    const int nTb = bd ? (bd + GB - 1) / GB : 0;
+    const int nXX = bd ? (p / bd) * (nTb * (nTb + 1) / 2) : nTx * (nTx + 1) / 2;
     const int blocks = nXX + nTx * nTy;
     hipLaunchKernelGGL(gram_x3_kernel, dim3(blocks), dim3(512), 0, s, Sx, Sy, nkb, p, q, nTx, nXX, mx, my, dx,
-                       dy, coef, (float)n_b, fresh, M_xx, M_xy);
+                       dy, coef, (float)n_b, fresh, M_xx, M_xy, bd, nTb);
     return hipGetLastError();
 }
 

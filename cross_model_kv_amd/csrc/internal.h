@@ -96,9 +96,11 @@ struct GramScratch {
 };
 // Sizes (floats) of the scratch for p, q.
 size_t gram_scratch_floats(int p, int q, int splits);
+// bd > 0: M_xx is kept only on its p / bd diagonal blocks of bd x bd, stored compactly
+// ([p / bd][bd][bd]); 0: the whole p x p matrix.
 hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, int p, int q,
                              int64_t n_old, float* mean_x, float* mean_y, float* M_xx,
-                             float* M_xy, float* ss_y, const GramScratch& sc, hipStream_t s);
+                             float* M_xy, float* ss_y, int bd, const GramScratch& sc, hipStream_t s);
 // Rows per kvmap_gram sub-batch: larger batches are merged in pieces of at most this many
 // rows (the split operands' scratch and 32-bit tile offsets are sized for it).
 constexpr int64_t kGramSubBatch = 16384;
@@ -108,11 +110,11 @@ hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* 
                              float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s);
 hipError_t launch_gram_x3(const uint16_t* Sx, const uint16_t* Sy, int64_t n_b, int p, int q, const float* mx,
                           const float* my, const float* dx, const float* dy, float coef, int fresh,
-                          float* M_xx, float* M_xy, hipStream_t s);
+                          float* M_xx, float* M_xy, int bd, hipStream_t s);
 hipError_t launch_gram_merge(int p, int q, int64_t n_dst, int64_t n_src, float* mean_x,
                              float* mean_y, float* M_xx, float* M_xy, float* ss_y, const float* s_mean_x,
                              const float* s_mean_y, const float* s_M_xx, const float* s_M_xy, const float* s_ss_y,
-                             const GramScratch& sc, hipStream_t s);
+                             int bd, const GramScratch& sc, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // ---- ridge solve on the device (ridge_dev.hip), float64 --------------------------------

@@ -63,7 +63,8 @@ def _rope(theta, pos0, style, inv_freq, keep: list) -> Rope:
 class GramStateC(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("p", ctypes.c_int32), ("q", ctypes.c_int32),
                 ("mean_x", ctypes.c_void_p), ("mean_y", ctypes.c_void_p),
-                ("M_xx", ctypes.c_void_p), ("M_xy", ctypes.c_void_p), ("ss_y", ctypes.c_void_p)]
+                ("M_xx", ctypes.c_void_p), ("M_xy", ctypes.c_void_p), ("ss_y", ctypes.c_void_p),
+                ("xx_block", ctypes.c_int32)]
 
 
 class FitConfigC(ctypes.Structure):
@@ -246,18 +247,21 @@ class GramState:
     """Device-resident centered statistics (n, mean_x, mean_y, M_xx, M_xy and, with
     keep_ss_y, the per-column centered sum of squares ss_y) of kvmap_gram."""
 
-    def __init__(self, p: int, q: int, device, keep_ss_y: bool = False):
+    def __init__(self, p: int, q: int, device, keep_ss_y: bool = False, xx_block: int = 0):
         torch = _torch()
         self.p, self.q, self.device = int(p), int(q), torch.device(device)
+        self.xx_block = int(xx_block)
         kw = dict(dtype=torch.float32, device=self.device)
         self.mean_x = torch.zeros(p, **kw)
         self.mean_y = torch.zeros(q, **kw)
-        self.M_xx = torch.zeros(p, p, **kw)
+        # blocked: [p / b][b][b] diagonal blocks only
+        self.M_xx = (torch.zeros(p // self.xx_block, self.xx_block, self.xx_block, **kw) if self.xx_block
+                     else torch.zeros(p, p, **kw))
         self.M_xy = torch.zeros(p, q, **kw)
         self.ss_y = torch.zeros(q, **kw) if keep_ss_y else None
         self.c = GramStateC(0, self.p, self.q, self.mean_x.data_ptr(), self.mean_y.data_ptr(),
                             self.M_xx.data_ptr(), self.M_xy.data_ptr(),
-                            self.ss_y.data_ptr() if keep_ss_y else None)
+                            self.ss_y.data_ptr() if keep_ss_y else None, self.xx_block)
 
     @property
     def n(self) -> int:
@@ -387,8 +391,8 @@ class Context:
                                       _stream_handle(stream, cache.device)), "kvmap_cache_rows")
         return out
 
-    def gram_state(self, p: int, q: int, keep_ss_y: bool = False) -> GramState:
-        return GramState(p, q, f"cuda:{self.device}", keep_ss_y)
+    def gram_state(self, p: int, q: int, keep_ss_y: bool = False, xx_block: int = 0) -> GramState:
+        return GramState(p, q, f"cuda:{self.device}", keep_ss_y, xx_block)
 
     def gram_reset(self, st: GramState, stream=None):
         _check(lib().kvmap_gram_reset(self._h, ctypes.byref(st.c), _stream_handle(stream, st.device)),

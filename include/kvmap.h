@@ -226,6 +226,13 @@ typedef struct {
     float* M_xx;
     float* M_xy;
     float* ss_y;
+    int32_t xx_block;  /* 0: M_xx is the whole [p][p].  b > 0 (a multiple of 4 dividing p): only
+                          the p / b diagonal blocks of b x b features are kept, compactly as
+                          [p / b][b][b]; for features split into groups (the layers of a
+                          selection stage) that need their own co-moments but share Y.  Block g
+                          is then a whole state of its own, viewed as p = b, mean_x + g b,
+                          M_xx + g b^2, M_xy + g b q (same mean_y, ss_y, n, q) -- the form the
+                          ridge calls take (they refuse a blocked state).                    */
 } kvmap_gram_state;
 
 /* Zero the state's device arrays on `stream` and set n = 0. */
@@ -317,8 +324,9 @@ int kvmap_ridge_r2_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, 
  *   for V; the in-sample R^2 pooled per target head, averaged over heads and {K, V}, scores
  *   the pair; the k best s per t win (ties to the lower index), kept ascending ("What ships":
  *   head-averaged single-source R^2, then top-k cross-layer features).  One Gram state per
- *   (source layer, K/V) against the rows of a block of target layers (X = the source layer's
- *   rows, p = H*d; Y = the block's rows, q = block*H*d), so M_xx is shared by the block.
+ *   (group of source layers, K/V) against the rows of a block of target layers: X = the
+ *   group's rows (as many layers as fit 65,536 features), Y = the block's rows
+ *   (q = block*H*d), M_xx block-diagonal with one H*d block per source layer (xx_block).
  * Stage 2, maps: per (target layer, K/V) the statistics of the selected layers' rows
  *   (p = k*H*d) against the target layer's rows (q = H*d), solved on the device in fp64 into
  *   the apply's layout.
@@ -363,9 +371,10 @@ typedef struct {
 typedef struct kvmap_fit kvmap_fit;
 
 /* Validate cfg and create a fit on ctx (the fit uses ctx's scratch: one fit per context at a
- * time).  Device memory is allocated per stage: stage 1 holds 2*L_src states of
- * 4*(p + 2q + p^2 + p*q) bytes (p = H*d, q = block*H*d), stage 2 holds 2*block states of
- * 4*(F + N + F^2 + F*N) bytes (F = k*H*d, N = H*d), plus row buffers of T rows.  With
+ * time).  Device memory is allocated per stage: stage 1 holds, per K/V and source group,
+ * 4*(p + 2q + p*N + p*q) bytes (p = group layers * N, N = H*d, q = block*N), stage 2 holds
+ * 2*block states of 4*(F + N + F^2 + F*N) bytes (F = k*N), plus row buffers of T rows.
+ * After a failed call the fit is not usable: destroy it.  With
  * given_sel the selection is copied to the host and checked (distinct, in range) here.
  * Synchronous. */
 int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvmap_fit** out);

@@ -227,3 +227,34 @@ def test_ridge_solve_device_not_spd(ctx):
     with pytest.raises(K.KvmapError) as e:
         ctx.ridge_solve_device(st, 0.0)
     assert e.value.status == K.ERR_NOT_SPD
+
+
+@pytest.mark.parametrize("dtype,bd", [("bf16", 64), ("bf16", 256), ("f32", 64), ("f32", 128)])
+def test_gram_block_diagonal_state(ctx, dtype, bd):
+    """A state that keeps M_xx only on its diagonal blocks (xx_block): each block equals the
+    oracle's M_xx block of the full two-pass statistics, M_xy, the means and ss_y are those of
+    the full state; a merge of two blocked states too.  p = 512 in blocks of 64 (not a tile
+    multiple: tiles reach past a block and are masked) or of 128 / 256."""
+    cfg = FIT_STATS_CONFIG.replace(cid=403, p=512, q=72, n_tokens=1500, batch=700)
+    parts = _batches(cfg, [700, 800])
+    a = ctx.gram_state(cfg.p, cfg.q, keep_ss_y=True, xx_block=bd)
+    b = ctx.gram_state(cfg.p, cfg.q, keep_ss_y=True, xx_block=bd)
+    ctx.gram_reset(a)
+    ctx.gram_reset(b)
+    ctx.gram(a, _dev(parts[0][0], dtype), _dev(parts[0][1], dtype))
+    ctx.gram(b, _dev(parts[1][0], dtype), _dev(parts[1][1], dtype))
+    ctx.gram_merge(a, b)
+    torch.cuda.synchronize()
+    ref = oracle.stats_two_pass(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    f = lambda t: t.double().cpu().numpy()
+    Mxx = f(a.M_xx)
+    assert Mxx.shape == (cfg.p // bd, bd, bd)
+    worst = 0.0
+    for g in range(cfg.p // bd):
+        blk = ref["Mxx"][g * bd:(g + 1) * bd, g * bd:(g + 1) * bd]
+        worst = max(worst, _rel(Mxx[g], blk))
+    r_xy = _rel(f(a.M_xy), ref["Mxy"])
+    r_ss = _rel(f(a.ss_y), ref["ssy"])
+    print(f"[gram] blocked {dtype} bd {bd}: worst block rel {worst:.2e}, M_xy {r_xy:.2e}, ss_y {r_ss:.2e}", flush=True)
+    assert worst <= GRAM_REL and r_xy <= GRAM_REL and r_ss <= GRAM_REL
+    assert np.max(np.abs(f(a.mean_x) - ref["mx"])) <= GRAM_REL * np.max(np.abs(ref["mx"]))
