@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
     const int P = g.P;
     const int r = threadIdx.x;
     const int o = kb * RB;
-    for (int c = 0; c < RB; ++c) t[r][c] = A[(size_t)(o + r) * P + o + c];
+    for (int i = 0; i < RB; ++i) t[i][r] = A[(size_t)(o + i) * P + o + r];  // coalesced rows
     __syncthreads();
     for (int j = 0; j < RB; ++j) {
         double d = t[j][j];
@@ -116,15 +116,24 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
             for (int m = j + 1; m <= r; ++m) t[r][m] -= t[r][j] * t[m][j];
         __syncthreads();
     }
-    for (int c = 0; c < RB; ++c) A[(size_t)(o + r) * P + o + c] = (c <= r) ? t[r][c] : 0.0;
+    __syncthreads();
+    for (int i = 0; i < RB; ++i) A[(size_t)(o + i) * P + o + r] = (r <= i) ? t[i][r] : 0.0;
     // X = L^-1 by forward substitution, thread r = column r of X:
     //   X[i][r] = (delta_ir - sum_{m = r}^{i-1} L[i][m] X[m][r]) / L[i][i],  i >= r
+    // (four partial sums: the LDS reads of one row pipeline instead of waiting on one chain)
     for (int i = 0; i < RB; ++i) {
         double v = 0.0;
         if (i >= r) {
-            double acc = (i == r) ? 1.0 : 0.0;
-            for (int m = r; m < i; ++m) acc -= t[i][m] * x[m][r];
-            v = acc / t[i][i];
+            double a0 = (i == r) ? 1.0 : 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+            int m = r;
+            for (; m + 3 < i; m += 4) {
+                a0 -= t[i][m] * x[m][r];
+                a1 -= t[i][m + 1] * x[m + 1][r];
+                a2 -= t[i][m + 2] * x[m + 2][r];
+                a3 -= t[i][m + 3] * x[m + 3][r];
+            }
+            for (; m < i; ++m) a0 -= t[i][m] * x[m][r];
+            v = ((a0 + a1) + (a2 + a3)) / t[i][i];
         }
         x[i][r] = v;
     }
