@@ -19,8 +19,8 @@ fit        the fit side on its own workload (262,144 calibration tokens, p 8192,
            4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
            with HIP events on its stream; one ridge solve of the merged state on the host and one
            on the device (fp64, W written in bf16 output-major)
-fit_driver the complete two-stage fit (layer selection, then the maps) at the 14B->32B model shape
-           over --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per stage
+fit_driver the complete fit (layer selection, then the maps) at the 14B->32B model shape over
+           --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per pass
 """
 
 from __future__ import annotations
@@ -231,7 +231,8 @@ def fit_driver_leg(K, n_seqs=8, T=4096, cpu=True):
     target layers, H 8, d 128, k 8, lambda 0.01, over n_seqs seeded bf16 calibration sequences
     of T tokens resident in HBM.  Stage 1 scores all 2560 (target, source) pairs for K and V;
     stage 2 fits and solves 128 maps of 8192 x 1024.  Wall time per pass from the pass callbacks
-    (each kvmap_fit_next_pass returns after the solves of the pass it closes)."""
+    (each kvmap_fit_next_pass returns after the solves of the pass it closes).  At this shape the
+    fit runs in one pass (the full source Gram; the maps gathered from it)."""
     import torch
     L_src, L_tgt, H, d, k, lam = 40, 64, 8, 128, 8, 0.01
     dev = "cuda:0"
@@ -257,17 +258,20 @@ def fit_driver_leg(K, n_seqs=8, T=4096, cpu=True):
     torch.cuda.synchronize()
     total = time.perf_counter() - t_start
     ctx.close()
-    # stamps[i] opens pass i; the last one marks the end of the last pass
-    sel_s = sum(stamps[i + 1][0] - stamps[i][0] for i in range(len(stamps) - 1) if stamps[i][1] == 1)
-    map_s = sum(stamps[i + 1][0] - stamps[i][0] for i in range(len(stamps) - 1) if stamps[i][1] == 2)
+    # stamps[i] opens pass i (its stage); the last one marks the end of the last pass, which
+    # includes that pass's solves (in one-pass mode: the selection and all maps)
+    pass_s = [stamps[i + 1][0] - stamps[i][0] for i in range(len(stamps) - 1)]
+    stages = [stamps[i][1] for i in range(len(stamps) - 1)]
     n_tok = n_seqs * T
     del seqs, res
     torch.cuda.empty_cache()
-    log(f"fit driver: {total:.2f} s ({sel_s:.2f} s selection, {map_s:.2f} s maps) over {n_tok} calibration tokens")
+    log(f"fit driver: {total:.2f} s in {len(pass_s)} pass(es) {['%.2f' % x for x in pass_s]} over {n_tok} "
+        f"calibration tokens")
     base = fit_driver_cpu_baseline(n_tok, L_src, L_tgt, H, d, k, lam) if cpu else None
     return {"workload": f"qwen3-14b-to-32b fit: L {L_src}->{L_tgt}, H {H}, d {d}, k {k}, {n_seqs} x {T} bf16 "
                         f"calibration tokens, lambda {lam}",
-            "seconds": total, "selection_s": sel_s, "maps_s": map_s, "calibration_tokens": n_tok,
+            "seconds": total, "passes": len(pass_s), "pass_stages": stages, "pass_s": pass_s,
+            "calibration_tokens": n_tok,
             "calibration_tokens_per_s": n_tok / total, "cpu_baseline": base}
 
 

@@ -750,7 +750,7 @@ static int ensure_ridge_scratch(kvmap_ctx* c, size_t need) {
 // share one scratch of at most about kRidgeScratchBudget bytes (at least one system).  Each
 // batch is checked for non-positive pivots before the next starts.  r2: R^2 per group of y
 // columns into r2o[i]; else W[i], b[i] in bf16 or fp32.
-constexpr size_t kRidgeScratchBudget = size_t(8) << 30;
+constexpr size_t kRidgeScratchBudget = size_t(16) << 30;
 
 static int run_ridge(kvmap_ctx* c, const kvmap_gram_state* const* st, int n, double lambda, bool r2, int group,
                      bool bf16, void* const* W, void* const* b, double* const* r2o, hipStream_t s, const char* who) {

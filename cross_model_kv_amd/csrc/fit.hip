@@ -11,10 +11,19 @@
 // {K, V}, top-k) is the one kernel of this file.
 //
 // Stage 1 feeds a group of source layers (as many as fit 65,536 features) as ONE Gram state per
-// K/V whose M_xx is kept block-diagonal, one block per layer: every layer's M_xx and M_xy come
-// out of one launch per batch, the target rows are split once per batch rather than once per
-// source layer, and the launch has enough tiles to fill the chip.  Each layer's block is then a
-// state of its own for the R^2 solves.
+// K/V against the rows of a block of target layers: every layer's co-moments come out of one
+// launch per batch, the target rows are split once per batch rather than once per source
+// layer, and the launch has enough tiles to fill the chip.
+//
+// One pass, when every source layer fits one state and every target layer one block (the
+// 14B->32B shape: 40 x 1024 source features, 64 x 1024 target features): the state keeps the
+// FULL source Gram (all pairs of source layers; 6.7 GB per K/V at that shape, which HBM holds).
+// Every statistic a map needs is then a block of it: target t's M_xx is the blocks of its
+// selected layers, its M_xy the rows of those layers and the columns of t.  Selection and all
+// maps come from this one pass over the calibration data -- no second pass, and fewer co-moment
+// FLOPs than per-target states, since target layers that share source layers share blocks.
+// Otherwise M_xx is kept block-diagonal (one block per source layer) for the selection and a
+// second stage of passes accumulates per-target statistics.
 
 #include "../../include/kvmap.h"
 
@@ -93,6 +102,9 @@ struct kvmap_fit {
     int N = 0, F = 0;                  // H*d, k*H*d
     int sel_block = 0, map_block = 0;  // target layers per pass of each stage
     int group = 0, groups = 0;         // stage 1: source layers per Gram state, states per K/V
+    bool one_pass = false;             // full source Gram in stage 1, maps gathered from it
+    float* gbuf = nullptr;             // one-pass mode: gathered blocks (diagonal blocks, then maps)
+    size_t gbuf_floats = 0;
     int sel_passes = 0, map_passes = 0;
     int pass = -1;                     // index of the open pass, -1 before the first
     int stage = 0, t0 = 0, t1 = 0;
@@ -175,6 +187,104 @@ int alloc_states(kvmap_fit* f, const std::vector<int>& ps, int q, bool keep_ss_y
     return KVMAP_OK;
 }
 
+// Blocks of a gathered matrix: block i of the output is block b[i] of the input.
+struct BlockList {
+    int n;
+    int b[kMaxRowLayers];
+};
+
+// out[(bi NR + r) ldo + bj NC + c] = in[(rows.b[bi] NR + r) ldi + cols.b[bj] NC + c]; NC and the
+// leading dimensions are multiples of 4 (float4 copies).
+__global__ __launch_bounds__(256) void gather_blocks_kernel(float* __restrict__ out, int64_t ldo,
+                                                            const float* __restrict__ in, int64_t ldi,
+                                                            const BlockList rows, const BlockList cols, int NR,
+                                                            int NC) {
+    const int64_t nrow = (int64_t)rows.n * NR;
+    const int64_t row4 = (int64_t)cols.n * NC / 4;
+    const int64_t total = nrow * row4;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t R = idx / row4;
+        const int C = (int)(idx - R * row4) * 4;
+        const int bi = (int)(R / NR), r = (int)(R - (int64_t)bi * NR);
+        const int bj = C / NC, c = C - bj * NC;
+        const float4 v = *(const float4*)(in + ((int64_t)rows.b[bi] * NR + r) * ldi + (int64_t)cols.b[bj] * NC + c);
+        *(float4*)(out + R * ldo + C) = v;
+    }
+}
+
+hipError_t gather_blocks(float* out, int64_t ldo, const float* in, int64_t ldi, const BlockList& rows,
+                         const BlockList& cols, int NR, int NC, hipStream_t s) {
+    const int64_t total = (int64_t)rows.n * NR * cols.n * NC / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 16384);
+    hipLaunchKernelGGL(gather_blocks_kernel, dim3(std::max(1u, blocks)), dim3(256), 0, s, out, ldo, in, ldi, rows,
+                       cols, NR, NC);
+    return hipGetLastError();
+}
+
+BlockList one_block(int b) {
+    BlockList l{};
+    l.n = 1;
+    l.b[0] = b;
+    return l;
+}
+
+int ensure_gbuf(kvmap_fit* f, size_t floats, hipStream_t s) {
+    if (floats <= f->gbuf_floats) return KVMAP_OK;
+    FIT_HIP(hipStreamSynchronize(s));
+    (void)hipFree(f->gbuf);
+    f->gbuf = nullptr;
+    f->gbuf_floats = 0;
+    FIT_HIP(hipMalloc((void**)&f->gbuf, floats * sizeof(float)));
+    f->gbuf_floats = floats;
+    return KVMAP_OK;
+}
+
+// One-pass mode, after the selection: the maps of all target layers from the stage-1 states
+// (state kv: p = L_src N, full M_xx, q = L_tgt N), gathered a few systems at a time into
+// per-target states and solved in batches.
+int solve_maps_from_full(kvmap_fit* f, hipStream_t s) {
+    const kvmap_fit_config& c = f->cfg;
+    const int N = f->N, F = f->F, k = c.k;
+    const size_t per = (size_t)F * F + (size_t)F * N + F;  // M_xx, M_xy, mean_x of one system
+    const int chunk_t = 8;                                  // target layers (x K, V) per batch
+    FIT_TRY(ensure_gbuf(f, per * 2 * chunk_t, s));
+    const size_t es = esize(c.out_dtype);
+    for (int t0 = 0; t0 < c.L_tgt; t0 += chunk_t) {
+        const int t1 = std::min(c.L_tgt, t0 + chunk_t);
+        std::vector<kvmap_gram_state> sys;
+        std::vector<void*> Ws, bs;
+        float* g = f->gbuf;
+        for (int t = t0; t < t1; ++t) {
+            BlockList sel{};
+            sel.n = k;
+            for (int j = 0; j < k; ++j) sel.b[j] = f->sel[(size_t)t * k + j];
+            for (int kv = 0; kv < 2; ++kv) {
+                const kvmap_gram_state& G = f->states[kv];
+                kvmap_gram_state v{};
+                v.n = G.n;
+                v.p = F;
+                v.q = N;
+                v.M_xx = g; g += (size_t)F * F;
+                v.M_xy = g; g += (size_t)F * N;
+                v.mean_x = g; g += F;
+                v.mean_y = G.mean_y + (size_t)t * N;
+                FIT_HIP(gather_blocks(v.M_xx, F, G.M_xx, G.p, sel, sel, N, N, s));
+                FIT_HIP(gather_blocks(v.M_xy, N, G.M_xy, G.q, sel, one_block(t), N, N, s));
+                FIT_HIP(gather_blocks(v.mean_x, F, G.mean_x, 0, one_block(0), sel, 1, N, s));
+                sys.push_back(v);
+                Ws.push_back((char*)(kv ? c.W_v : c.W_k) + (size_t)t * N * F * es);
+                bs.push_back((char*)(kv ? c.b_v : c.b_k) + (size_t)t * N * es);
+            }
+        }
+        std::vector<const kvmap_gram_state*> st;
+        for (const auto& v : sys) st.push_back(&v);
+        FIT_TRY(kvmap_ridge_solve_device_batch(f->ctx, st.data(), (int)st.size(), c.lambda, Ws.data(), bs.data(),
+                                               c.out_dtype, s));
+    }
+    return KVMAP_OK;
+}
+
 // Source layers of stage-1 group g: [g * group, min(L_src, (g + 1) * group))
 int group_layers(const kvmap_fit* f, int g) { return std::min(f->cfg.L_src, (g + 1) * f->group) - g * f->group; }
 
@@ -201,7 +311,7 @@ int open_pass(kvmap_fit* f, hipStream_t s) {
             std::vector<int> ps;
             for (int kv = 0; kv < 2; ++kv)
                 for (int g = 0; g < f->groups; ++g) ps.push_back(group_layers(f, g) * f->N);
-            FIT_TRY(alloc_states(f, ps, f->sel_block * f->N, true, f->N));
+            FIT_TRY(alloc_states(f, ps, f->sel_block * f->N, true, f->one_pass ? 0 : f->N));
         }
         for (auto& st : f->states) {
             st.q = (f->t1 - f->t0) * f->N;
@@ -228,8 +338,16 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
     if (f->n_first < 0) f->n_first = f->n_pass;
     if (f->stage == 1) {
         const int H = c.H_kv;
-        // one view per (K/V, source layer): the layer's diagonal block of its group's state
+        // one view per (K/V, source layer): the layer's diagonal block of its group's state (in
+        // one-pass mode copied out of the full M_xx, which the views cannot address)
         const int N = f->N;
+        if (f->one_pass) {
+            FIT_TRY(ensure_gbuf(f, (size_t)2 * c.L_src * N * N, s));
+            for (int kv = 0; kv < 2; ++kv)
+                for (int sl = 0; sl < c.L_src; ++sl)
+                    FIT_HIP(gather_blocks(f->gbuf + ((size_t)kv * c.L_src + sl) * N * N, N, f->states[kv].M_xx,
+                                          f->states[kv].p, one_block(sl), one_block(sl), N, N, s));
+        }
         std::vector<kvmap_gram_state> views;
         std::vector<double*> out;
         for (int kv = 0; kv < 2; ++kv)
@@ -240,7 +358,7 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
                 v.p = N;
                 v.xx_block = 0;
                 v.mean_x = G.mean_x + (size_t)j * N;
-                v.M_xx = G.M_xx + (size_t)j * N * N;
+                v.M_xx = f->one_pass ? f->gbuf + ((size_t)kv * c.L_src + sl) * N * N : G.M_xx + (size_t)j * N * N;
                 v.M_xy = G.M_xy + (size_t)j * N * G.q;
                 views.push_back(v);
                 out.push_back(f->r2 + (((size_t)kv * c.L_src + sl) * c.L_tgt + f->t0) * H);
@@ -254,6 +372,7 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
             FIT_HIP(hipMemcpyAsync(f->sel.data(), c.layer_sel, f->sel.size() * sizeof(int32_t),
                                    hipMemcpyDeviceToHost, s));
             FIT_HIP(hipStreamSynchronize(s));
+            if (f->one_pass) FIT_TRY(solve_maps_from_full(f, s));
             free_stage(f);
         }
         return KVMAP_OK;
@@ -282,6 +401,7 @@ void destroy(kvmap_fit* f) {
     (void)hipFree(f->own_scores);
     (void)hipFree(f->xrows);
     (void)hipFree(f->yrows);
+    (void)hipFree(f->gbuf);
     delete f;
 }
 
@@ -346,6 +466,9 @@ extern "C" int kvmap_fit_create(kvmap_ctx* ctx, const kvmap_fit_config* cfg, kvm
     f->map_passes = (c.L_tgt + f->map_block - 1) / f->map_block;
     f->group = (int)std::min<int64_t>(std::min<int64_t>(c.L_src, kMaxGramWidth / N), kMaxRowLayers);
     f->groups = (c.L_src + f->group - 1) / f->group;
+    // one pass: one source group, one target block, and the choice not forced off
+    f->one_pass = !c.given_sel && f->groups == 1 && f->sel_passes == 1 && !c.two_pass;
+    if (f->one_pass) f->map_passes = 0;
     int st = KVMAP_OK;
     if (c.given_sel) {
         hipError_t e = hipMemcpy(f->sel.data(), c.layer_sel, f->sel.size() * sizeof(int32_t), hipMemcpyDeviceToHost);

@@ -71,7 +71,8 @@ class FitConfigC(ctypes.Structure):
     _fields_ = [("L_src", ctypes.c_int32), ("L_tgt", ctypes.c_int32), ("H_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("select_block", ctypes.c_int32), ("map_block", ctypes.c_int32),
-                ("given_sel", ctypes.c_int32), ("theta_src", ctypes.c_double), ("theta_tgt", ctypes.c_double),
+                ("given_sel", ctypes.c_int32), ("two_pass", ctypes.c_int32), ("theta_src", ctypes.c_double),
+                ("theta_tgt", ctypes.c_double),
                 ("lambda_", ctypes.c_double), ("layer_sel", ctypes.c_void_p), ("scores", ctypes.c_void_p),
                 ("W_k", ctypes.c_void_p), ("b_k", ctypes.c_void_p), ("W_v", ctypes.c_void_p),
                 ("b_v", ctypes.c_void_p), ("inv_freq_src", ctypes.c_void_p), ("inv_freq_tgt", ctypes.c_void_p)]
@@ -475,7 +476,8 @@ class Context:
 
     def fit(self, calibration, *, L_src: int, L_tgt: int, H: int, d: int, k: int, theta_src: float,
             theta_tgt: float, lam: float, out_dtype=None, layer_sel=None, select_block: int = 0,
-            map_block: int = 0, stream=None, on_pass=None, inv_freq_src=None, inv_freq_tgt=None) -> dict:
+            map_block: int = 0, stream=None, on_pass=None, inv_freq_src=None, inv_freq_tgt=None,
+            two_pass: bool = False) -> dict:
         """kvmap_fit_*: the two-stage fit (selection, then maps) over re-iterable calibration data.
 
         `calibration` is a callable returning an iterable of (src_k, src_v, tgt_k, tgt_v, pos0):
@@ -521,22 +523,22 @@ class Context:
                           for f in (inv_freq_src, inv_freq_tgt)]
                     cfg = FitConfigC(int(L_src), int(L_tgt), int(H), int(d), int(k), _dtype_code(seq[0]),
                                      _dtype_code(maps["W_k"]), int(select_block), int(map_block), int(given),
+                                     int(bool(two_pass)),
                                      float(theta_src if theta_src is not None else 0.0),
                                      float(theta_tgt if theta_tgt is not None else 0.0), float(lam),
                                      layer_sel.data_ptr(), scores.data_ptr() if scores is not None else None,
                                      *(maps[n].data_ptr() for n in ("W_k", "b_k", "W_v", "b_v")),
                                      *(None if f is None else f.ctypes.data for f in fq))
                     _check(lib().kvmap_fit_create(self._h, ctypes.byref(cfg), ctypes.byref(h)), "kvmap_fit_create")
-                    seqs = [seq]
-                    first = False
-                else:
-                    it, seqs = iter(calibration()), []
                 sh = _stream_handle(stream, dev)
                 _check(lib().kvmap_fit_next_pass(h, ctypes.byref(info), sh), "kvmap_fit_next_pass")
                 if on_pass is not None:
                     on_pass(info.stage, info.t_begin, info.t_end, info.pass_, info.passes)
                 if info.stage == 0:
                     break
+                # the first pass continues the peeked iterator; each later pass asks for a new one
+                seqs, it = ([seq], it) if first else ([], iter(calibration()))
+                first = False
                 for seq in _chain(seqs, it):
                     sk, sv, tk, tv, pos0 = seq
                     if (tuple(sk.shape) != (L_src, H, sk.shape[2], d) or tuple(sv.shape) != tuple(sk.shape)

@@ -307,7 +307,7 @@ int kvmap_ridge_r2(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, in
  * n state pointers and n output pointers (the outputs of different systems must not overlap).
  * The library solves up to 16 systems together: every kernel of the factorisation and the
  * substitutions covers all of them, so the serial chain of 64-wide block steps is paid once per
- * batch; the scratch grows to the batch's size (as many systems as fit in about 8 GiB, at least
+ * batch; the scratch grows to the batch's size (as many systems as fit in about 16 GiB, at least
  * one).  Synchronous; validation of all n before any device work; KVMAP_ERR_NOT_SPD names the
  * first system that failed (outputs of systems in earlier batches are then already written). */
 int kvmap_ridge_solve_device_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, int32_t n, double lambda,
@@ -330,6 +330,11 @@ int kvmap_ridge_r2_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, 
  * Stage 2, maps: per (target layer, K/V) the statistics of the selected layers' rows
  *   (p = k*H*d) against the target layer's rows (q = H*d), solved on the device in fp64 into
  *   the apply's layout.
+ * One-pass mode (the default when L_src*H*d <= 65,536 and L_tgt*H*d <= 65,536, select_block
+ *   covering every target layer, no given selection, two_pass = 0): the stage-1 state keeps the
+ *   FULL source Gram (all pairs of source layers) instead of its diagonal blocks, so every map's
+ *   statistics are blocks of the stage-1 statistics; the maps are gathered and solved right
+ *   after the selection, at the end of the single pass -- one pass over the calibration data.
  * Keys enter every statistic in content space: each model's own RoPE is stripped first
  * (VeloxQuant-MLX "The mapping").  Rows are tokens; columns follow kvmap_cache_rows.
  *
@@ -344,7 +349,9 @@ typedef struct {
     int32_t select_block;  /* target layers per selection pass; 0 = as many as fit one state
                               (block*H*d <= 65536, <= 128 layers)                              */
     int32_t map_block;     /* target layers per map pass; 0 = all                             */
-    int32_t given_sel;     /* nonzero: layer_sel is an input and there is no selection stage  */
+    int32_t given_sel;     /* nonzero: layer_sel is an input and there is no selection stage;
+                              it is read (synchronously) by kvmap_fit_create                   */
+    int32_t two_pass;      /* nonzero: never the one-pass mode (see below)                      */
     double theta_src;      /* RoPE bases of the two models (> 0; not read where the matching
                               inv_freq is given)                                               */
     double theta_tgt;

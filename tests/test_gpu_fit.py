@@ -257,15 +257,23 @@ def test_fit_fitcheck_matches_oracle(ctx, K):
             r2 = np.concatenate([oracle.holdout_r2(pr["tgt_k_content"][s, t], kc),
                                  oracle.holdout_r2(pr["tgt_v"][s, t], gv[t])])
             assert r2.min() > 0.99999, (s, t, r2)
+    # The default run is the one-pass mode (maps gathered from the full source Gram); the same
+    # fit in two passes (forced, or by blocks of target layers) and from a given selection
+    # computes every co-moment from the same products, so it agrees to fp32 rounding of the
+    # merges; blocked and unblocked two-pass runs are bit-identical.
+    two = _run_fit(ctx, cfg, seqs, two_pass=True)
     blocked = _run_fit(ctx, cfg, seqs, select_block=4, map_block=4)
-    assert np.array_equal(blocked["layer_sel"], got["layer_sel"])
-    assert np.max(np.abs(blocked["scores"] - got["scores"])) <= 1e-9
-    for n in ("W_k", "b_k", "W_v", "b_v"):
-        assert np.array_equal(blocked[n], got[n]), n
     given = _run_fit(ctx, cfg, seqs, layer_sel=torch.from_numpy(got["layer_sel"]), map_block=5)
     assert given["scores"] is None
+    for run in (two, blocked):
+        assert np.array_equal(run["layer_sel"], got["layer_sel"])
+        assert np.max(np.abs(run["scores"] - got["scores"])) <= 1e-9
     for n in ("W_k", "b_k", "W_v", "b_v"):
-        assert np.array_equal(given[n], got[n]), n
+        assert np.array_equal(blocked[n], two[n]), n
+        assert np.array_equal(given[n], two[n]), n
+        rel = max(np.linalg.norm(two[n][t] - got[n][t]) / np.linalg.norm(got[n][t]) for t in range(cfg.L_tgt))
+        print(f"[fit] one pass vs two passes {n}: rel {rel:.2e}", flush=True)
+        assert rel <= 1e-5, n
 
 
 def test_fit_bf16_matches_oracle(ctx):
@@ -321,7 +329,7 @@ def test_fit_refusals(ctx, K):
     with pytest.raises(K.KvmapError) as e:
         ctx.fit(lambda: seqs, layer_sel=sel, **base)
     assert e.value.status == K.ERR_SHAPE
-    # a pass that sees fewer tokens than the first
+    # a pass that sees fewer tokens than the first (two passes: the one-pass mode has no second)
     calls = []
 
     def shrinking():
@@ -329,8 +337,9 @@ def test_fit_refusals(ctx, K):
         return seqs if len(calls) == 1 else seqs[:-1]
 
     with pytest.raises(K.KvmapError) as e:
-        ctx.fit(shrinking, **base)
+        ctx.fit(shrinking, two_pass=True, **base)
     assert e.value.status == K.ERR_SHAPE
+    assert len(calls) == 2
 
 
 def test_ridge_batches_equal_single_solves(ctx, K):
