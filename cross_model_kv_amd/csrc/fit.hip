@@ -1,8 +1,8 @@
 // End-to-end fit driver over the C-ABI (KVBridge README, fitting section headed "Loading":
 // a two-stage, multi-pass fit over re-iterable calibration data that keeps only centered
-// statistics, with target-layer blocks bounding memory; "What ships": head-averaged
-// single-source R^2 selects the top-k source layers per target layer, then per-target-layer
-// ridge maps for K and V).
+// statistics, with target-layer blocks bounding memory; "What ships": source layers scored one
+// at a time by R^2 averaged over target heads, the best k per target layer kept, then
+// per-target-layer ridge maps for K and V).
 //
 // The driver owns the statistics of one stage at a time and calls the library's own entry
 // points for every step: kvmap_cache_rows (gather + strip RoPE into token rows), kvmap_gram

@@ -292,7 +292,7 @@ int kvmap_ridge_solve_device(kvmap_ctx* ctx, const kvmap_gram_state* st, double 
 
 /* In-sample R^2 of that ridge fit, pooled over groups of `group` consecutive y columns
  * (one target KV head's head_dim outputs: the per-head score of the layer selection, KVBridge
- * README "What ships": head-averaged single-source R^2).  For group g
+ * README "What ships": each source layer is scored alone, by R^2 averaged over heads).  For group g
  *   R^2_g = 1 - sum_c RSS_c / sum_c ss_y[c]   over its columns c,
  *   RSS_c = sum_rows (y_c - yhat_c)^2 = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2,
  * the last form following from (M_xx + lambda I) w_c = M_xy[:, c]; it needs the state's
@@ -323,7 +323,7 @@ int kvmap_ridge_r2_batch(kvmap_ctx* ctx, const kvmap_gram_state* const* states, 
  *   from all H*d features of source layer s to all H*d outputs of target layer t, for K and
  *   for V; the in-sample R^2 pooled per target head, averaged over heads and {K, V}, scores
  *   the pair; the k best s per t win (ties to the lower index), kept ascending ("What ships":
- *   head-averaged single-source R^2, then top-k cross-layer features).  One Gram state per
+ *   the k best-scoring source layers become the concatenated features).  One Gram state per
  *   (group of source layers, K/V) against the rows of a block of target layers: X = the
  *   group's rows (as many layers as fit 65,536 features), Y = the block's rows
  *   (q = block*H*d), M_xx block-diagonal with one H*d block per source layer (xx_block).

@@ -284,8 +284,8 @@ def r2_pooled(y: np.ndarray, yhat: np.ndarray) -> float:
 
 
 # ---------------------------------------------------------------------------
-# Layer selection and the full fit ([KVB] "What ships": head-averaged
-# single-source R^2, then top-k cross-layer features; [VQ] "The mapping" item 1)
+# Layer selection and the full fit ([KVB] "What ships": each source layer scored alone by R^2
+# averaged over target heads, the best k concatenated as features; [VQ] "The mapping" item 1)
 # ---------------------------------------------------------------------------
 
 def _rows_of_layer(layer_seq) -> np.ndarray:
