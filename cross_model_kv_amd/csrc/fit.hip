@@ -2,7 +2,7 @@
 // a two-stage, multi-pass fit over re-iterable calibration data that keeps only centered
 // statistics, with target-layer blocks bounding memory; "What ships": source layers scored one
 // at a time by R^2 averaged over target heads, the best k per target layer kept, then
-// per-target-layer ridge maps for K and V).
+// one ridge map per target layer for keys and one for values).
 //
 // The driver owns the statistics of one stage at a time and calls the library's own entry
 // points for every step: kvmap_cache_rows (gather + strip RoPE into token rows), kvmap_gram

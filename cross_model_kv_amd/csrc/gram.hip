@@ -1,7 +1,6 @@
 // Fit-side statistics: centered co-moments of a batch, merged into a running state with
-// the Chan/Welford pairwise update (KVBridge README, fitting section headed "Loading":
-// batchwise Chan/Welford updates accumulate centered covariance directly instead of
-// subtracting large raw moments).
+// the Chan/Welford pairwise update (KVBridge README, fitting section headed "Loading": the
+// statistics stay centered batch by batch, so no large raw moments are ever subtracted).
 //
 // Per batch of n_b rows (x in R^p, y in R^q):
 //   1. column sums (wavefront/LDS reduced)  -> shift c = fp32 column mean

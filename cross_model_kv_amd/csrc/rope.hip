@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 // float64 (the two products reach ~3e4 rad at 32K positions; their difference in fp32 would
 // be off by ~1e-3).  Rotating a source-roped key by -A strips the source RoPE and applies the
 // target one in a single rotation (VeloxQuant-MLX "Cross-Model KV Transfer", section "Metal
-// kernel": both rotations act on the same pair at the same position).
+// kernel": the strip and the target rotation turn one pair at one position, so they compose).
 __global__ __launch_bounds__(256) void rope_diff_table_kernel(float2* __restrict__ tab, int64_t T, int d,
                                                               const RopeFreqs fs, int64_t pos0_s,
                                                               const RopeFreqs ft, int64_t pos0_t) {

@@ -176,8 +176,8 @@ int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
  * for every row r (layers x heads flattened), which is one rotation of every pair
  * (e, e + d/2) by (pos0_t + t) f_t,e - (pos0_s + t) f_s,e, f_e = theta^(-2e/d)
  * (VeloxQuant-MLX "Cross-Model KV Transfer", section "Metal kernel": the strip and the
- * target rotation act on the same pair at the same position and compose into one rotation
- * by the per-dimension angle difference).  The angle is formed in float64 into a cached fp32
+ * target rotation turn one pair at one position, so one rotation by the difference of the
+ * two angles does both).  The angle is formed in float64 into a cached fp32
  * cos/sin table [T][d/2] (built on first use of the (theta, pos0) pair, like the apply's
  * tables); the rotation runs in fp32 and is rounded once to `dtype`.
  *   src, dst  device [rows][T][head_dim], row-major, bf16 or fp32, 16-byte aligned, not

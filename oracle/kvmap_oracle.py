@@ -262,7 +262,7 @@ def stats_exact(X, Y) -> dict:
 # ---------------------------------------------------------------------------
 # Ridge ([KVB] fitting section: W = (X^T X + lambda I)^-1 X^T Y, b = Ybar - Xbar W;
 # [RA] ridge demo: centre x and y, solve with lambda = 0.01, intercept from means;
-# [VQ] "The mapping": solved on centered data so the intercept escapes the penalty)
+# [VQ] "The mapping": the fit runs on centered data, which leaves the intercept unpenalised)
 # ---------------------------------------------------------------------------
 
 def ridge(st: dict, lam: float):

@@ -1,9 +1,9 @@
 """Assemble fit-check cache pairs from raw seeded draws, using the oracle's arithmetic.
 
 The hidden map is the data-generating process of the KVBridge README's synthetic
-demo ("Thirty-second proof"): two model-family members with different depths and
-RoPE bases, a hidden cross-layer affine map, cache pairs over the same tokens,
-and holdout sequences never seen by the fit.
+demo ("Thirty-second proof"): a source and a target model of one family that differ in
+layer count and RoPE base, an affine map across layers hidden in the data, cache pairs
+over the same tokens, and holdout sequences the fit never sees.
 """
 
 import numpy as np
