@@ -199,11 +199,9 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-    for (int kc = 0; kc < nk; ++kc) {
+    // The operand tiles of K block k0 + kc: row x of a stored tile is at base + x * ld.
+    auto tiles = [&](int kc, const double*& Ap, int& lda, const double*& Bp, int& ldb) {
         const int o = (k0 + kc) * RB;
-        const double* Ap;  // row x of the stored tile: Ap + x * lda
-        const double* Bp;
-        int lda, ldb;
         if (MODE == 0) {
             Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
             Bp = A + (size_t)J * RB * P + o; ldb = P;   // rows c, columns m
@@ -220,15 +218,35 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
             Ap = Li + (size_t)(k0 + kc) * RB * RB; lda = RB;    // MODE 4: rows r, cols m; 5: rows m, cols r
             Bp = C; ldb = Q;                                    // rows m, columns c
         }
+    };
+    // Each thread moves 16 elements of each tile, consecutive threads along the unit stride;
+    // the next K block's elements are loaded into registers while this one is multiplied.
+    double ra[16], rb[16];
+    auto fetch = [&](int kc) {
+        const double* Ap;
+        const double* Bp;
+        int lda, ldb;
+        tiles(kc, Ap, lda, Bp, ldb);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = u * 256 + tid;
+            const int x = e >> 6, y = e & 63;
+            ra[u] = Ap[(size_t)x * lda + y];
+            rb[u] = Bp[(size_t)x * ldb + y];
+        }
+    };
+    fetch(0);
+    for (int kc = 0; kc < nk; ++kc) {
         if (kc) __syncthreads();  // every wave is done with the previous block's tiles
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int e = u * 256 + tid;
             const int x = e >> 6, y = e & 63;
-            As[x * LDW + y] = Ap[(size_t)x * lda + y];
-            Bs[x * LDW + y] = Bp[(size_t)x * ldb + y];
+            As[x * LDW + y] = ra[u];
+            Bs[x * LDW + y] = rb[u];
         }
         __syncthreads();
+        if (kc + 1 < nk) fetch(kc + 1);
 #pragma unroll 4
         for (int kk = 0; kk < RB; kk += 4) {
             const int m = kk + lk;

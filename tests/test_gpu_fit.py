@@ -364,3 +364,26 @@ def test_ridge_batches_equal_single_solves(ctx, K):
     with pytest.raises(K.KvmapError) as e:
         ctx.ridge_solve_device_batch(states[:3] + [empty], 0.0)
     assert e.value.status == K.ERR_NOT_SPD and "system 3" in str(e.value)
+
+
+def test_fit_two_source_groups(ctx):
+    """130 source layers of H 2 x d 64 exceed one selection state's 128 row layers: two groups
+    of source layers (128 + 2), so the fit runs in two passes (block-diagonal selection states,
+    then per-target statistics).  Selection and maps against the oracle at the fp32 bounds."""
+    cfg = FITCHECK.replace(cid=13, L_src=130, L_tgt=3, holdout_pos0=())
+    pr, st, seqs = _pairs(cfg, "f32")
+    passes = []
+    res = ctx.fit(lambda: seqs, L_src=cfg.L_src, L_tgt=cfg.L_tgt, H=cfg.H, d=cfg.d, k=cfg.k,
+                  theta_src=cfg.theta_src, theta_tgt=cfg.theta_tgt, lam=cfg.lam,
+                  on_pass=lambda *a: passes.append(a))
+    torch.cuda.synchronize()
+    assert [p_[0] for p_ in passes] == [1, 2, 0], passes
+    ref = _oracle_fit(cfg, pr, st)
+    assert np.array_equal(res["layer_sel"].cpu().numpy(), ref["layer_sel"])
+    assert np.array_equal(ref["layer_sel"], pr["draws"]["true_sel"])
+    ref_scores = _oracle_scores(cfg, pr, st, list(range(cfg.L_tgt)))
+    serr = np.max(np.abs(res["scores"].cpu().numpy() - ref_scores))
+    got = {n: res[n].cpu().numpy() for n in ("W_k", "b_k", "W_v", "b_v")}
+    print(f"[fit] two source groups: scores max |err| {serr:.2e}", flush=True)
+    assert serr <= 1e-4
+    _check_maps(got, ref, 2e-4, "two source groups")
