@@ -19,6 +19,8 @@ fit        the fit side on its own workload (262,144 calibration tokens, p 8192,
            4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
            with HIP events on its stream; one ridge solve of the merged state on the host and one
            on the device (fp64, W written in bf16 output-major)
+short      kvmap_apply on the first T tokens (T = 1 .. 256) with the workload's maps: ms against the
+           HBM roofline of reading W and the rows
 fit_driver the complete fit (layer selection, then the maps) at the 14B->32B model shape over
            --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per pass
 """
@@ -119,6 +121,46 @@ def recode_leg(K, ctx, cfg, src, iters=10, warmup=2):
                         f"theta {cfg.theta_src:g} -> {cfg.theta_tgt:g}",
             "ms": ms, "bytes": nbytes, "GBps": nbytes / (ms / 1e3) / 1e9,
             "frac_hbm": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+
+
+def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=3):
+    """Short caches (the short-prefix regime): kvmap_apply of the workload's first T tokens for a
+    few T, with all of the workload's maps.  At these lengths the apply reads all of W (2 x L_tgt
+    x N x F bf16) for little arithmetic, so the bound is HBM: W + the gathered source rows +
+    the written target rows over 8 TB/s.  Caches of up to 64 tokens take the split-K kernel."""
+    import torch
+    stream = torch.cuda.current_stream()
+    w_bytes = 2 * cfg.L_tgt * cfg.N * cfg.F * 2
+    rows = []
+    for T in lengths:
+        sk = inp["src_k"][:, :, :T, :].contiguous()
+        sv = inp["src_v"][:, :, :T, :].contiguous()
+        ok_ = torch.empty((cfg.L_tgt, cfg.H, T, cfg.d), dtype=sk.dtype, device=sk.device)
+        ov_ = torch.empty_like(ok_)
+
+        def run():
+            ctx.apply(sk, sv, inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"], cfg.theta_src,
+                      cfg.theta_tgt, pos0_src=cfg.pos0, out_k=ok_, out_v=ov_, stream=stream)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        x_bytes = 2 * cfg.L_tgt * cfg.k * cfg.H * T * cfg.d * 2   # gathered per target layer, K and V
+        o_bytes = 2 * cfg.L_tgt * cfg.H * T * cfg.d * 2
+        roof_ms = (w_bytes + x_bytes + o_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3
+        rows.append({"T": T, "ms": ms, "W_GBps": w_bytes / (ms / 1e3) / 1e9, "hbm_roofline_ms": roof_ms,
+                     "frac_hbm": roof_ms / ms, "kernel": "map_bf16_small" if T <= 64 else "map_bf16"})
+        log(f"short T={T}: {ms:.3f} ms ({w_bytes / (ms / 1e3) / 1e12:.2f} TB/s of W; HBM roofline {roof_ms:.3f} ms)")
+        del sk, sv, ok_, ov_
+    return {"workload": f"{cfg.name} maps (W {w_bytes / 1e9:.2f} GB bf16) on the first T tokens of the cache",
+            "lengths": rows}
 
 
 def fit_cpu_baseline(C, X, Y, budget_s=10.0):
@@ -285,6 +327,7 @@ def main():
     ap.add_argument("--no-fit", action="store_true", help="skip the fit-side measurement")
     ap.add_argument("--no-recode", action="store_true", help="skip the RoPE-recode measurement")
     ap.add_argument("--no-fit-driver", action="store_true", help="skip the end-to-end fit measurement")
+    ap.add_argument("--no-short", action="store_true", help="skip the short-cache measurement")
     ap.add_argument("--fit-seqs", type=int, default=8, help="calibration sequences of 4096 tokens for the fit driver")
     ap.add_argument("--fit-driver-only", action="store_true",
                     help="run only the end-to-end fit measurement and print its object as the JSON line")
@@ -384,6 +427,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     if not args.no_recode:
         result["recode"] = recode_leg(K, ctx, cfg, inp["src_k"])
+    if not args.no_short:
+        result["short"] = short_leg(K, ctx, cfg, inp)
     ctx.close()
     if not args.no_fit:
         del inp, out_k, out_v
