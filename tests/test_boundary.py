@@ -58,7 +58,8 @@ def _validate(**over):
     return K.validate_apply(args["L_src"], args["L_tgt"], args["H"], args["d"], args["k"], args["T"],
                             args["dtype"], sel, args["theta_src"], args["theta_tgt"],
                             args.get("pos0_src", 0), args.get("pos0_tgt", 0),
-                            args.get("style_src", 0), args.get("style_tgt", 0))
+                            args.get("style_src", 0), args.get("style_tgt", 0),
+                            args.get("inv_freq_src"), args.get("inv_freq_tgt"))
 
 
 def test_validate_accepts_good_call():
@@ -88,6 +89,37 @@ def test_validate_accepts_good_call():
 def test_validate_refusals(over, status):
     assert _validate(**over) == status
     assert K.last_error() != ""
+
+
+def test_validate_frequency_lists():
+    """A model's own frequency list replaces theta (which is then not read); entries must be
+    finite and >= 0 (0: a pair that never turns)."""
+    f = np.power(1.0e4, -2.0 * np.arange(64) / 128)
+    assert _validate(theta_src=0.0, inv_freq_src=f) == K.OK
+    assert _validate(theta_tgt=float("nan"), inv_freq_tgt=np.zeros(64)) == K.OK
+    for bad in (-1e-3, float("nan"), float("inf")):
+        g = f.copy()
+        g[17] = bad
+        assert _validate(inv_freq_src=g) == K.ERR_INVALID_ARGUMENT
+        assert "inv_freq[17]" in K.last_error()
+
+
+def test_fit_and_ridge_refuse_null_handles():
+    """Host-side refusals of the fit driver and device ridge entry points (no GPU needed)."""
+    L = K.lib()
+    import ctypes
+    h = ctypes.c_void_p()
+    cfg = K.FitConfigC()
+    assert L.kvmap_fit_create(None, ctypes.byref(cfg), ctypes.byref(h)) == K.ERR_INVALID_ARGUMENT
+    assert h.value is None
+    info = K.FitPassC()
+    assert L.kvmap_fit_next_pass(None, ctypes.byref(info), None) == K.ERR_INVALID_ARGUMENT
+    assert L.kvmap_fit_add(None, None, None, None, None, 16, 0, None) == K.ERR_INVALID_ARGUMENT
+    assert L.kvmap_fit_destroy(None) == K.OK
+    st = K.GramStateC()
+    assert L.kvmap_ridge_r2(None, ctypes.byref(st), 0.01, 64, None, None) == K.ERR_INVALID_ARGUMENT
+    assert L.kvmap_ridge_solve_device(None, ctypes.byref(st), 0.01, None, None, K.F32, None) == \
+        K.ERR_INVALID_ARGUMENT
 
 
 def test_validate_accepts_repeats_across_rows():
