@@ -118,6 +118,12 @@ struct kvmap_fit {
     void* xrows = nullptr;
     void* yrows = nullptr;
     size_t xcap = 0, ycap = 0;
+    // Stage 1 with one source group: the rows of consecutive sequences are gathered per K/V
+    // into these buffers and merged together, up to kAccRows rows per kvmap_gram call.
+    void* accx[2] = {nullptr, nullptr};
+    void* accy[2] = {nullptr, nullptr};
+    size_t accx_cap = 0, accy_cap = 0;
+    int64_t n_acc = 0;
 };
 
 namespace {
@@ -285,6 +291,20 @@ int solve_maps_from_full(kvmap_fit* f, hipStream_t s) {
     return KVMAP_OK;
 }
 
+// Rows per accumulated stage-1 batch (the statistics' sub-batch size): short calibration
+// sequences are merged in batches of this many rows, so each co-moment launch has a long
+// reduction and the per-launch costs (column sums, split, epilogue merge) are shared.
+constexpr int64_t kAccRows = 16384;
+
+// Merge the accumulated stage-1 rows into the states (one source group).
+int flush_rows(kvmap_fit* f, hipStream_t s) {
+    if (f->n_acc == 0) return KVMAP_OK;
+    for (int kv = 0; kv < 2; ++kv)
+        FIT_TRY(kvmap_gram(f->ctx, f->accx[kv], f->accy[kv], f->n_acc, f->cfg.dtype, &f->states[kv], s));
+    f->n_acc = 0;
+    return KVMAP_OK;
+}
+
 // Source layers of stage-1 group g: [g * group, min(L_src, (g + 1) * group))
 int group_layers(const kvmap_fit* f, int g) { return std::min(f->cfg.L_src, (g + 1) * f->group) - g * f->group; }
 
@@ -337,6 +357,7 @@ int close_pass(kvmap_fit* f, hipStream_t s) {
                       (long long)f->n_pass, (long long)f->n_first);
     if (f->n_first < 0) f->n_first = f->n_pass;
     if (f->stage == 1) {
+        FIT_TRY(flush_rows(f, s));
         const int H = c.H_kv;
         // one view per (K/V, source layer): the layer's diagonal block of its group's state (in
         // one-pass mode copied out of the full M_xx, which the views cannot address)
@@ -401,6 +422,10 @@ void destroy(kvmap_fit* f) {
     (void)hipFree(f->own_scores);
     (void)hipFree(f->xrows);
     (void)hipFree(f->yrows);
+    for (int kv = 0; kv < 2; ++kv) {
+        (void)hipFree(f->accx[kv]);
+        (void)hipFree(f->accy[kv]);
+    }
     (void)hipFree(f->gbuf);
     delete f;
 }
@@ -536,7 +561,35 @@ extern "C" int kvmap_fit_add(kvmap_fit* f, const void* src_k, const void* src_v,
     const kvmap_rope rt{c.theta_tgt, pos0, KVMAP_ROPE_HALF_SPLIT, f->freq_tgt.empty() ? nullptr : f->freq_tgt.data()};
     const void* src[2] = {src_k, src_v};
     const void* tgt[2] = {tgt_k, tgt_v};
-    if (f->stage == 1) {
+    if (f->stage == 1 && f->groups == 1 && T <= kAccRows) {
+        // gather this sequence's rows behind the ones already accumulated; merge when full
+        const int nb = f->t1 - f->t0;
+        const size_t xrow = (size_t)f->group * f->N * es, yrow = (size_t)nb * f->N * es;
+        if (f->accx_cap < (size_t)kAccRows * xrow || f->accy_cap < (size_t)kAccRows * yrow) {
+            FIT_TRY(flush_rows(f, s));
+            FIT_HIP(hipStreamSynchronize(s));
+            size_t cx = 0, cy = 0;
+            for (int kv = 0; kv < 2; ++kv) {
+                cx = f->accx_cap;
+                cy = f->accy_cap;
+                FIT_TRY(ensure_rows(&f->accx[kv], &cx, (size_t)kAccRows * xrow, s));
+                FIT_TRY(ensure_rows(&f->accy[kv], &cy, (size_t)kAccRows * yrow, s));
+            }
+            f->accx_cap = cx;
+            f->accy_cap = cy;
+        }
+        if (f->n_acc + T > kAccRows) FIT_TRY(flush_rows(f, s));
+        std::vector<int32_t> block(nb), layers(c.L_src);
+        for (int j = 0; j < nb; ++j) block[j] = f->t0 + j;
+        for (int j = 0; j < c.L_src; ++j) layers[j] = j;
+        for (int kv = 0; kv < 2; ++kv) {
+            FIT_TRY(kvmap_cache_rows(f->ctx, tgt[kv], c.L_tgt, H, T, d, c.dtype, block.data(), nb, kv ? nullptr : &rt,
+                                     (char*)f->accy[kv] + (size_t)f->n_acc * yrow, s));
+            FIT_TRY(kvmap_cache_rows(f->ctx, src[kv], c.L_src, H, T, d, c.dtype, layers.data(), c.L_src,
+                                     kv ? nullptr : &rs, (char*)f->accx[kv] + (size_t)f->n_acc * xrow, s));
+        }
+        f->n_acc += T;
+    } else if (f->stage == 1) {
         const int nb = f->t1 - f->t0;
         FIT_TRY(ensure_rows(&f->xrows, &f->xcap, (size_t)T * f->group * f->N * es, s));
         FIT_TRY(ensure_rows(&f->yrows, &f->ycap, (size_t)T * nb * f->N * es, s));

@@ -279,7 +279,8 @@ def test_fit_fitcheck_matches_oracle(ctx, K):
 def test_fit_bf16_matches_oracle(ctx):
     """bf16 caches (H = 4, d = 128, 6 source and 4 target layers, k = 2, 4 x 1024 calibration
     tokens at theta 1e6 -> 5e5): selection equal, scores and maps within the bf16 bounds;
-    maps written in fp32 and in bf16 (the latter the fp32 maps rounded once)."""
+    maps written in fp32 and in bf16 from the same statistics (the latter the fp32 maps
+    rounded once)."""
     cfg = FITCHECK.replace(cid=11, L_src=6, L_tgt=4, H=4, d=128, k=2, T=1024, n_calib=4, holdout_pos0=(),
                            theta_src=1.0e6, theta_tgt=5.0e5, noise_sd=1e-2)
     pr, st, seqs = _pairs(cfg, "bf16")
@@ -291,9 +292,12 @@ def test_fit_bf16_matches_oracle(ctx):
     print(f"[fit] bf16 scores: max |err| {serr:.2e}", flush=True)
     assert serr <= 1e-3
     _check_maps(got, ref, 5e-3, "bf16 caches, fp32 maps")
-    gb = _run_fit(ctx, cfg, seqs, out_dtype=torch.bfloat16, layer_sel=torch.from_numpy(got["layer_sel"]))
+    # the same fit (given selection: same statistics) with maps written in fp32 and in bf16
+    sel_t = torch.from_numpy(got["layer_sel"])
+    g32 = _run_fit(ctx, cfg, seqs, out_dtype=torch.float32, layer_sel=sel_t)
+    gb = _run_fit(ctx, cfg, seqs, out_dtype=torch.bfloat16, layer_sel=sel_t)
     for n in ("W_k", "b_k", "W_v", "b_v"):
-        w32 = got[n].astype(np.float64)
+        w32 = g32[n].astype(np.float64)
         assert np.all(np.abs(gb[n] - w32) <= 2.0 ** -8 * np.abs(w32) + 1e-30), n
 
 
