@@ -5,7 +5,8 @@
 // long-cache kernel's 256-token tiles would be mostly padding here and would leave only a
 // few hundred workgroups to stream W, so this path
 //   * tiles 256 features x 64 tokens, and splits the reduction over KS groups of K-steps,
-//     so that about 2048 workgroups stream disjoint parts of W;
+//     so that enough workgroups stream disjoint parts of W (about 4096 for caches of up to
+//     16 tokens; longer ones do not split, the partial sums would cost more than they gain);
 //   * writes each split's fp32 partial sums, and a second kernel adds them in a fixed order
 //     (deterministic), adds the bias and applies the target RoPE (keys), rounding once to
 //     bf16 into the target cache layout [t][h][p][e].
@@ -235,7 +236,12 @@ SmallPlan map_bf16_small_plan(const ApplyGeom& g) {
     pl.nP = (int)((g.T + SBN - 1) / SBN);
     const int nk_all = g.F() / SBK;
     const int tiles = g.L_tgt * 2 * pl.nN * pl.nP;
-    int ks = (2048 + tiles - 1) / tiles;
+    // Splits trade parallel W streams against the partial sums' traffic (KS x T x N fp32 per
+    // target layer and K/V, written and read back by the reduce).  Measured at the 14B->32B maps
+    // (512 tiles): about 4096 workgroups are best up to 16 tokens (0.394 ms at T = 1 against
+    // 0.430 with 2048), about 512 -- no split -- from 32 on (0.493 ms at T = 64 against 0.538).
+    const int target = g.T <= 16 ? 4096 : 512;
+    int ks = (target + tiles - 1) / tiles;
     ks = std::max(1, std::min(ks, nk_all));
     pl.kps = (nk_all + ks - 1) / ks;
     pl.KS = (nk_all + pl.kps - 1) / pl.kps;  // every split non-empty
