@@ -93,6 +93,7 @@ int kvmap::report(int status, const char* fmt, ...) {
 
 struct kvmap_ctx {
     int device = 0;
+    int cus = 0;                  // compute units of the device (persistent launches)
     std::vector<RopeEntry> ropes;
     uint64_t clock = 0;
     void* ws = nullptr;
@@ -160,6 +161,7 @@ extern "C" int kvmap_create(kvmap_ctx** out, int device) {
     if (!g.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipSetDevice(%d) failed", device);
     kvmap_ctx* c = new kvmap_ctx();
     c->device = device;
+    c->cus = prop.multiProcessorCount;
     for (auto& e : c->ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             kvmap_destroy(c);
@@ -385,11 +387,11 @@ static size_t derope_bytes(const kvmap_dims* d) {
 
 static bool small_path(const kvmap_dims* d) { return d->dtype == KVMAP_DTYPE_BF16 && d->T <= kSmallT; }
 
-static size_t workspace_bytes(const kvmap_dims* d) {
+static size_t workspace_bytes(const kvmap_ctx* c, const kvmap_dims* d) {
     size_t b = derope_bytes(d);
     if (small_path(d)) {
         const ApplyGeom g{d->L_src, d->L_tgt, d->H_kv, d->head_dim, d->k, d->T};
-        b += map_bf16_small_plan(g).part_bytes;
+        b += map_bf16_small_plan(g, c->cus).part_bytes;
     }
     return b;
 }
@@ -397,7 +399,7 @@ static size_t workspace_bytes(const kvmap_dims* d) {
 extern "C" int kvmap_reserve(kvmap_ctx* c, const kvmap_dims* d) {
     if (!c || !d) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_reserve: NULL argument");
     DeviceGuard g(c->device);
-    int st = ensure_workspace(c, workspace_bytes(d));
+    int st = ensure_workspace(c, workspace_bytes(c, d));
     if (st) return st;
     return ok();
 }
@@ -447,7 +449,7 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     int n_used = 0;
     st = upload_selection(c, d, layer_sel, s, &n_used);
     if (st) return st;
-    st = ensure_workspace(c, workspace_bytes(d));
+    st = ensure_workspace(c, workspace_bytes(c, d));
     if (st) return st;
 
     const Elem e = d->dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
@@ -456,7 +458,7 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     if (timing) KVMAP_HIP(hipEventRecord(c->ev[2], s));
     MapArgs a{c->ws, src_v, c->d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
     if (small_path(d))
-        KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g), (float*)((char*)c->ws + derope_bytes(d)), s));
+        KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g, c->cus), (float*)((char*)c->ws + derope_bytes(d)), s));
     else if (e == Elem::BF16)
         KVMAP_HIP(launch_map_bf16(a, g, s));
     else

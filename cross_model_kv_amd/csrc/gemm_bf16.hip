@@ -56,9 +56,20 @@ __device__ __forceinline__ bool decode_tile(int bid, int L_tgt, int nP, int nN, 
     const int s = (local / tps) * 8 + xcd;
     const int w = local - (local / tps) * tps;
     if (s >= S) return false;
+    // (t, K|V) pairs.  With fewer than 8 super-tiles per pair (caches of up to 14,336 tokens)
+    // the 8 XCDs work on different pairs at once: then every target layer's keys come first,
+    // then every target layer's values, so that the pairs in flight read one contiguous span of
+    // one map tensor (alternating the K and V maps, two allocations read at the same offsets in
+    // lockstep, streams W up to 25 % slower).  With 8 or more, all XCDs share one pair at a
+    // time, and t-major order (K then V of each target layer) measured 2 % faster.
     const int tkv = s / spk, sg = s - (s / spk) * spk;
-    o.t = tkv >> 1;
-    o.kv = tkv & 1;
+    if (spk < 8) {
+        o.kv = tkv / L_tgt;
+        o.t = tkv - o.kv * L_tgt;
+    } else {
+        o.t = tkv >> 1;
+        o.kv = tkv & 1;
+    }
     o.pb = sg * pg + w / nN;
     o.nb = w - (w / nN) * nN;
     return o.pb < nP;

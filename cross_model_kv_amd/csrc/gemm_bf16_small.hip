@@ -1,13 +1,16 @@
-// The map GEMM for short caches (T up to a few hundred tokens), bf16.  At these lengths the
-// apply moves the whole of W (F x N per target layer, K and V) for little arithmetic, so it
-// is bound by reading W from HBM (VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping":
-// one ridge map per target head; the same Y = X W + b, then bias and target RoPE).  The
-// long-cache kernel's 256-token tiles would be mostly padding here and would leave only a
-// few hundred workgroups to stream W, so this path
-//   * tiles 256 features x 64 tokens, and splits the reduction over KS groups of K-steps,
-//     so that enough workgroups stream disjoint parts of W (about 4096 for caches of up to
-//     16 tokens; longer ones do not split, the partial sums would cost more than they gain);
-//   * writes each split's fp32 partial sums, and a second kernel adds them in a fixed order
+// The map GEMM for short caches (up to 64 tokens), bf16.  At these lengths the apply moves the
+// whole of W (F x N per target layer, K and V) for little arithmetic, so it is bound by reading
+// W from HBM (VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping": one ridge map per target
+// head; the same Y = X W + b, then bias and target RoPE).  The long-cache kernel's 256-token
+// tiles would be mostly padding here and its one-tile workgroups would drain and refill their
+// load pipeline per tile, so this path
+//   * tiles 256 features x 16, 32 or 64 tokens and runs one persistent workgroup per compute
+//     unit; each streams its share of the work items (a tile, or a split of a tile's K
+//     reduction when the tiles do not divide evenly over the compute units) through one ring
+//     of LDS stages that runs on from item to item;
+//   * loads W, which is read exactly once, with the non-temporal hint (7.2 against 5.9 TB/s
+//     for a plain stream on gfx950);
+//   * writes each item's fp32 partial sums, and a second kernel adds them in a fixed order
 //     (deterministic), adds the bias and applies the target RoPE (keys), rounding once to
 //     bf16 into the target cache layout [t][h][p][e].
 // The gather is the long-cache kernel's: one K-step of 64 features lies in one (selected
@@ -23,162 +26,239 @@ namespace kvmap {
 
 namespace {
 
-constexpr int SBM = 256;                          // features per tile
-constexpr int SBN = 64;                           // tokens per tile
-constexpr int SBK = 64;                           // features (reduction) per K-step
-constexpr int NRING = 4;                          // stages in flight + the one computed
-constexpr int W_CHUNKS = SBM * SBK / 8;           // 16-byte chunks of W per stage (2048)
-constexpr int X_CHUNKS = SBN * SBK / 8;           // ... of X (512)
-constexpr int STAGE = (W_CHUNKS + X_CHUNKS) * 16;  // 40 KB
-constexpr int LW = W_CHUNKS / 512, LX = X_CHUNKS / 512;  // loads per thread per stage (4, 1)
-constexpr int LPS = LW + LX;
+constexpr int SBM = 256;                 // features per tile
+constexpr int SBN = 64;                  // most tokens per tile (the path takes T <= SBN)
+constexpr int SBK = 64;                  // features (reduction) per K-step
+constexpr int NRING = 4;                 // stages in flight + the one computed
+constexpr int W_CHUNKS = SBM * SBK / 8;  // 16-byte chunks of W per stage (2048)
+constexpr int LW = W_CHUNKS / 512;       // W loads per thread per stage (4)
+
+#ifndef KVMAP_SMALL_NT
+#define KVMAP_SMALL_NT true
+#endif
 
 }  // namespace
 
-// Workgroup b: split ks = b % KS, then feature tile, token tile, (t, K|V).  8 waves: wave w
-// computes features (w & 1) * 128 .. + 127 (whole heads) of tokens (w >> 1) * 16 .. + 15,
-// as 8 blocks of v_mfma_f32_16x16x32_bf16.  Ring of 4 stages (W tile + X tile), each filled
-// by buffer_load_dwordx4 ... lds three K-steps ahead of its use.
-template <int D>
-__global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
-                                                             int nN, int nP, int KS, int kps,
-                                                             float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) char smem[NRING * STAGE];
-    uint4* lds = (uint4*)smem;
+// Work item i of n_items = tiles x KS: split i % KS (K-steps kt0 .. kt0 + nk - 1) of feature
+// tile (i / KS) % nN of target layer (i / (KS nN)) % L_tgt, keys for the first L_tgt KS nN
+// items, values after them.  Uniform scalars.  The items in flight at one time (consecutive
+// indices) thus read one contiguous span of one map tensor: interleaving the K and V maps,
+// two allocations about a gigabyte apart read at the same offsets in lockstep, measured 25 %
+// slower at the 14B->32B maps.
+struct ShortItem {
+    int t, kv, n0, ks, kt0, nk;
+};
 
-    int b = blockIdx.x;
-    const int ks = b % KS;
-    b /= KS;
-    const int nb = b % nN;
-    b /= nN;
-    const int pb = b % nP;
-    b /= nP;
-    const int kv = b & 1, t = b >> 1;
-    if (t >= L_tgt) return;
+__device__ __forceinline__ ShortItem short_item(int i, int KS, int nN, int L_tgt, int kps, int nk_all) {
+    ShortItem it;
+    it.ks = i % KS;
+    i /= KS;
+    it.n0 = (i % nN) * SBM;
+    i /= nN;
+    it.t = i % L_tgt;
+    it.kv = i / L_tgt;
+    it.kt0 = it.ks * kps;
+    it.nk = min(kps, nk_all - it.kt0);
+    return it;
+}
+
+// Persistent: workgroup g (one per compute unit) takes items g, g + G, g + 2G, ... and streams
+// them through ONE ring of 4 stages (W tile + X tile), each filled by buffer_load_dwordx4 ...
+// lds three K-steps ahead of its use.  The ring runs on across items: the loads of an item's
+// first K-steps go out while the previous item's last ones are computed, so W streams without
+// a drain and refill per tile.  At the end of an item its fp32 partial sums are stored and the
+// accumulators cleared.  8 waves: wave w computes features (w & 1) * 128 .. + 127 (whole
+// heads) of tokens (w >> 1) * 16 .. + 15 of its item's tile, as 8 blocks of
+// v_mfma_f32_16x16x32_bf16.  TOK (16, 32 or 64, at least T) tokens per tile: 128 / TOK waves
+// side by side along the features, each 2 TOK features (whole 16-feature blocks) x 16 tokens,
+// so that short caches spend no MFMAs and fragment reads on padding tokens; only the first
+// TOK / 8 waves load the X tile.  NT: W (read exactly once) is loaded with the non-temporal
+// hint.
+template <int D, int TOK, bool NT>
+__global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
+                                                             int nN, int KS, int kps, int n_items,
+                                                             float* __restrict__ part) {
+    constexpr int X_CHUNKS = TOK * SBK / 8;           // 16-byte chunks of X per stage
+    constexpr int XW = X_CHUNKS / 64;                 // waves that load X, one chunk per lane
+    constexpr int STAGE = (W_CHUNKS + X_CHUNKS) * 16;  // 34, 36 or 40 KB
+    constexpr int WN = 128 / TOK;                     // waves along the features
+    constexpr int FW = SBM / WN;                      // features per wave
+    constexpr int IB = FW / 16;                       // 16-feature MFMA blocks per wave
+    static_assert(TOK == 16 || TOK == 32 || TOK == 64, "tokens per tile");
+    __shared__ __attribute__((aligned(16))) char smem[NRING * STAGE];
+    const uint4* lds = (const uint4*)smem;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    if (g >= n_items) return;  // (the host launches at most n_items workgroups)
 
     const int N = H * D, F = k * N;
     const int nk_all = F / SBK;
-    const int kt0 = ks * kps;
-    const int nk = min(kps, nk_all - kt0);  // >= 1 (the host sizes KS so)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = nb * SBM, p0 = pb * SBN;
-    const uint16_t* __restrict__ X = (const uint16_t*)(kv ? a.xv : a.xk);
-    const uint16_t* __restrict__ W = (const uint16_t*)(kv ? a.Wv : a.Wk) + (size_t)t * N * F;
     const size_t slab = (size_t)T * D;
     const uint32_t slab_bytes = (uint32_t)(slab * 2);
-    const uint64_t lbase = (uint64_t)(uintptr_t)(X + (size_t)(lane < k ? a.sel[t * k + lane] : 0) * H * slab);
-    const int lb_lo = (int)(uint32_t)lbase, lb_hi = (int)(uint32_t)(lbase >> 32);
-    const i32x4_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
     // Loads: W slot u = i*512 + tid holds row u/8, chunk (u%8) ^ slot_xor(row); X slot tid
-    // holds row tid/8 likewise.  Rows past N or T repeat the last one (never stored).
-    int aoff[LW], boff;
+    // (tid < X_CHUNKS) holds row tid/8 likewise.  Rows past N or T repeat the last one (never
+    // stored).
+    int arow[LW], acol[LW];
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
-        const int r = i * 64 + wave * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ slot_xor(r);
-        aoff[i] = (min(n0 + r, N - 1) * F + c * 8) * 2;
+        arow[i] = i * 64 + wave * 8 + (lane >> 3);
+        acol[i] = ((lane & 7) ^ slot_xor(arow[i])) * 8;
     }
+    int boff;
     {
         const int r = wave * 8 + (lane >> 3);
         const int c = (lane & 7) ^ slot_xor(r);
-        boff = ((int)(min((int64_t)(p0 + r), T - 1) * D) + c * 8) * 2;
+        boff = ((int)(min((int64_t)r, T - 1) * D) + c * 8) * 2;
     }
-    // Issue state: W byte offset of the next K-step; gathered slab (head h of selected layer
-    // j) and feature offset in its rows; all stop at the split's last K-step (the extra
-    // stages the pipeline loads at the end repeat it and are never read).
-    const int w_last = (kt0 + nk - 1) * SBK * 2;
-    int w_soff = kt0 * SBK * 2;
-    const int per = H * D;
-    // (divisions by the runtime H*D are vector code: read the uniform results back into SGPRs)
-    int x_j = __builtin_amdgcn_readfirstlane((kt0 * SBK) / per);
-    int x_h = __builtin_amdgcn_readfirstlane(((kt0 * SBK) % per) / D);
-    int x_eb = __builtin_amdgcn_readfirstlane(((kt0 * SBK) % D) * 2);
-    int x_left = nk;  // K-steps of the split not yet issued
-    const uint64_t x0 = (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane(lb_lo, x_j)) +
-                        (uint64_t)x_h * slab_bytes;
-    uint32_t x_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x0);
-    uint32_t x_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x0 >> 32));
+
+    // ---- issue side: the item whose stages are being loaded, and its position ----
+    // W: descriptor of W[t] (K or V), per-lane row offsets, byte offset of the next K-step.
+    // X: the gathered slab (head x_h of selected layer x_j) and the K-step's byte offset in
+    // its rows.  x_left = K-steps of the item not yet issued; past the last K-step of the
+    // last item the issue repeats that K-step (in bounds, never read).
+    int is_item = g, is_t = 0, x_left = 0, x_j = 0, x_h = 0, x_eb = 0, w_soff = 0;
+    int aoff[LW];
+    i32x4_t wr;
+    const uint16_t* is_x = nullptr;  // K or V cache (de-rotated keys or values)
+    uint64_t x_addr = 0;             // address of the current slab
+    auto x_slab = [&](int j, int h) {
+        const int layer = scalar_load_dword(a.sel + is_t * k + j);
+        return (uint64_t)(uintptr_t)is_x + ((uint64_t)layer * H + h) * slab_bytes;
+    };
+    auto begin_item = [&](int item) {
+        const ShortItem it = short_item(item, KS, nN, L_tgt, kps, nk_all);
+        is_t = __builtin_amdgcn_readfirstlane(it.t);
+        const int kv = __builtin_amdgcn_readfirstlane(it.kv);
+        const int n0 = __builtin_amdgcn_readfirstlane(it.n0);
+        const int kt0 = __builtin_amdgcn_readfirstlane(it.kt0);
+        const uint16_t* W = (const uint16_t*)(kv ? a.Wv : a.Wk) + (size_t)is_t * N * F;
+        wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
+        is_x = (const uint16_t*)(kv ? a.xv : a.xk);
+#pragma unroll
+        for (int i = 0; i < LW; ++i) aoff[i] = (min(n0 + arow[i], N - 1) * F + acol[i]) * 2;
+        w_soff = kt0 * SBK * 2;
+        const int f0 = kt0 * SBK, per = H * D;
+        x_j = __builtin_amdgcn_readfirstlane(f0 / per);
+        x_h = __builtin_amdgcn_readfirstlane((f0 % per) / D);
+        x_eb = __builtin_amdgcn_readfirstlane((f0 % D) * 2);
+        x_left = __builtin_amdgcn_readfirstlane(it.nk);
+        x_addr = x_slab(x_j, x_h);
+    };
     int s_buf = 0;
     auto issue = [&]() {
         const uint32_t la = lds_base + (uint32_t)s_buf * STAGE + wave_s * 1024u;
-        const i32x4_t xr = {(int)x_lo, (int)x_hi, (int)slab_bytes, 0x00020000};
+        const i32x4_t xr = {(int)(uint32_t)x_addr, (int)(uint32_t)(x_addr >> 32), (int)slab_bytes, 0x00020000};
 #pragma unroll
-        for (int i = 0; i < LW; ++i) lds_dma16(wr, la + i * 8192u, aoff[i], w_soff);
-        lds_dma16(xr, la + (uint32_t)(W_CHUNKS * 16), boff, x_eb);
+        for (int i = 0; i < LW; ++i) {
+            if constexpr (NT)
+                lds_dma16_nt(wr, la + i * 8192u, aoff[i], w_soff);
+            else
+                lds_dma16(wr, la + i * 8192u, aoff[i], w_soff);
+        }
+        if (wave_s < XW) lds_dma16(xr, la + (uint32_t)(W_CHUNKS * 16), boff, x_eb);
         s_buf = (s_buf + 1 == NRING) ? 0 : s_buf + 1;
-        // advance (held at the split's last K-step once it has been issued)
-        const int adv = x_left > 1;
-        x_left -= adv;
-        w_soff = min(w_soff + adv * SBK * 2, w_last);
-        const int eb = x_eb + adv * SBK * 2;
-        const int we = (eb == D * 2);
-        x_eb = we ? 0 : eb;
-        const int hh = x_h + we;
-        const int wh = (hh == H);
-        x_h = wh ? 0 : hh;
-        x_j = min(x_j + wh, k - 1);
-        const uint32_t a_lo = x_lo + (we ? slab_bytes : 0u);
-        const uint32_t a_hi = x_hi + (a_lo < x_lo ? 1u : 0u);
-        x_lo = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_lo, x_j), a_lo);
-        x_hi = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j), a_hi);
+        if (x_left > 1) {  // next K-step of the item
+            --x_left;
+            w_soff += SBK * 2;
+            x_eb += SBK * 2;
+            if (x_eb == D * 2) {  // next head
+                x_eb = 0;
+                if (++x_h == H) {  // next selected layer
+                    x_h = 0;
+                    ++x_j;
+                    x_addr = x_slab(x_j, 0);
+                } else {
+                    x_addr += slab_bytes;
+                }
+            }
+        } else if (is_item + G < n_items) {  // first K-step of the next item
+            is_item += G;
+            begin_item(is_item);
+        }
     };
 
-    constexpr int IB = 8;
     f32x4_t acc[IB];
 #pragma unroll
     for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
-    const int wn = wave & 1, wp = wave >> 1;
+    const int wn = wave % WN, wp = wave / WN;
     const int kq = lane >> 4;
     const int fx = slot_xor(lane & 15);
-    const int arow = (wn * 128 + (lane & 15)) * 8;
-    const int brow = W_CHUNKS + (wp * 16 + (lane & 15)) * 8;
+    const int arow0 = (wn * FW + (lane & 15)) * 8;
+    const int brow0 = W_CHUNKS + (wp * 16 + (lane & 15)) * 8;
 
+    begin_item(g);
 #pragma unroll
     for (int s = 0; s < NRING; ++s) issue();
-    wait_vmcnt<(NRING - 1) * LPS>();
+    // this wave's loads per stage: LW, plus one X load in the first XW waves
+    if (wave_s < XW)
+        wait_vmcnt<(NRING - 1) * (LW + 1)>();
+    else
+        wait_vmcnt<(NRING - 1) * LW>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    for (int kk = 0; kk < nk; ++kk) {
-        const uint4* st = lds + (kk % NRING) * (STAGE / 16);
+
+    int c_item = g;                                                       // item being computed
+    int c_left = short_item(g, KS, nN, L_tgt, kps, nk_all).nk;                   // its K-steps left
+    int c_buf = 0;
+    for (;;) {
+        const uint4* st = lds + c_buf * (STAGE / 16);
         bf16x8_t fa[2][IB], fb[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int slot = (h * 4 + kq) ^ fx;
 #pragma unroll
-            for (int i = 0; i < IB; ++i) fa[h][i] = __builtin_bit_cast(bf16x8_t, st[arow + i * 128 + slot]);
-            fb[h] = __builtin_bit_cast(bf16x8_t, st[brow + slot]);
+            for (int i = 0; i < IB; ++i) fa[h][i] = __builtin_bit_cast(bf16x8_t, st[arow0 + i * 128 + slot]);
+            fb[h] = __builtin_bit_cast(bf16x8_t, st[brow0 + slot]);
         }
+        // all fragment reads in flight before the first MFMA waits for one
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < IB; ++i)
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][i], fb[h], acc[i], 0, 0, 0);
-        // every read of stage kk returned, stage kk+1 landed (kk+2 and kk+3 may be in flight);
-        // after the barrier its buffer takes stage kk+4
+        // every read of this stage returned, the next one landed (the two after it may be in
+        // flight); after the barrier this buffer takes the stage three K-steps ahead.  Vector
+        // stores of an item's partial sums below only add younger operations to the count, so
+        // they can only make this wait stricter, never let it pass early.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        wait_vmcnt<(NRING - 2) * LPS>();
+        if (wave_s < XW)
+            wait_vmcnt<(NRING - 2) * (LW + 1)>();
+        else
+            wait_vmcnt<(NRING - 2) * LW>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         issue();
-    }
-    wait_vmcnt<0>();
-
-    // partial sums: lane holds features 4 (lane / 16) + r of each 16 x 16 block, token lane % 16
-    const int p = p0 + wp * 16 + (lane & 15);
-    if (p < T) {
-        float* dst = part + ((((size_t)ks * L_tgt + t) * 2 + kv) * (size_t)T + p) * N;
+        c_buf = (c_buf + 1 == NRING) ? 0 : c_buf + 1;
+        if (--c_left == 0) {
+            // partial sums of the item: lane holds features 4 (lane / 16) + r of each 16 x 16
+            // block, token lane % 16
+            const ShortItem it = short_item(c_item, KS, nN, L_tgt, kps, nk_all);
+            const int p = wp * 16 + (lane & 15);
+            if (p < T) {
+                float* dst = part + ((((size_t)it.ks * L_tgt + it.t) * 2 + it.kv) * (size_t)T + p) * N;
 #pragma unroll
-        for (int i = 0; i < IB; ++i) {
-            const int n = n0 + wn * 128 + i * 16 + kq * 4;
-            if (n < N) *(float4*)(dst + n) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                for (int i = 0; i < IB; ++i) {
+                    const int n = it.n0 + wn * FW + i * 16 + kq * 4;
+                    if (n < N) *(float4*)(dst + n) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < IB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+            c_item += G;
+            if (c_item >= n_items) break;
+            c_left = short_item(c_item, KS, nN, L_tgt, kps, nk_all).nk;
         }
     }
+    wait_vmcnt<0>();  // the repeated tail stages must land before the workgroup's LDS is released
 }
 
 // Sum of the KS partials in split order, + bias, target RoPE on keys, bf16 into [t][h][p][e].
@@ -230,38 +310,65 @@ __global__ __launch_bounds__(256) void map_small_reduce_kernel(MapArgs a, const 
 
 // ---------------------------------------------------------------------------------------
 
-SmallPlan map_bf16_small_plan(const ApplyGeom& g) {
+SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus) {
     SmallPlan pl;
     pl.nN = (g.N() + SBM - 1) / SBM;
-    pl.nP = (int)((g.T + SBN - 1) / SBN);
+    pl.nP = (int)((g.T + SBN - 1) / SBN);  // 1: the path takes T <= SBN
     const int nk_all = g.F() / SBK;
     const int tiles = g.L_tgt * 2 * pl.nN * pl.nP;
-    // Splits trade parallel W streams against the partial sums' traffic (KS x T x N fp32 per
-    // target layer and K/V, written and read back by the reduce).  Measured at the 14B->32B maps
-    // (512 tiles): about 4096 workgroups are best up to 16 tokens (0.394 ms at T = 1 against
-    // 0.430 with 2048), about 512 -- no split -- from 32 on (0.493 ms at T = 64 against 0.538).
-    const int target = g.T <= 16 ? 4096 : 512;
-    int ks = (target + tiles - 1) / tiles;
-    ks = std::max(1, std::min(ks, nk_all));
-    pl.kps = (nk_all + ks - 1) / ks;
+    cus = std::max(1, cus);
+    // The persistent kernel needs no split for parallelism; a split only evens out the work
+    // when the tiles do not divide over the compute units.  Take the split count that
+    // minimises the K-steps of the busiest workgroup (fewest splits on a tie: every split
+    // adds T x N fp32 partial sums per tile).
+    int best = 1;
+    int64_t best_steps = -1;
+    for (int ks = 1; ks <= std::min(16, nk_all); ++ks) {
+        const int kps = (nk_all + ks - 1) / ks;
+        const int KS = (nk_all + kps - 1) / kps;
+        const int64_t items = (int64_t)tiles * KS;
+        const int64_t grid = std::min<int64_t>(items, cus);
+        const int64_t steps = (items + grid - 1) / grid * kps;
+        if (best_steps < 0 || steps < best_steps) {
+            best_steps = steps;
+            best = ks;
+        }
+    }
+    pl.kps = (nk_all + best - 1) / best;
     pl.KS = (nk_all + pl.kps - 1) / pl.kps;  // every split non-empty
+    pl.n_items = tiles * pl.KS;
+    pl.grid = std::min(pl.n_items, cus);
     pl.part_bytes = (size_t)pl.KS * g.L_tgt * 2 * (size_t)g.T * g.N() * sizeof(float);
     return pl;
 }
 
+template <int D, int TOK>
+static void launch_short(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part, hipStream_t s) {
+    hipLaunchKernelGGL((map_bf16_small_kernel<D, TOK, KVMAP_SMALL_NT>), dim3(pl.grid), dim3(512), 0, s, a, g.L_tgt,
+                       g.H, g.k, g.T, pl.nN, pl.KS, pl.kps, pl.n_items, part);
+}
+
+template <int D>
+static void launch_short_d(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part, hipStream_t s) {
+    if (g.T <= 16)
+        launch_short<D, 16>(a, g, pl, part, s);
+    else if (g.T <= 32)
+        launch_short<D, 32>(a, g, pl, part, s);
+    else
+        launch_short<D, 64>(a, g, pl, part, s);
+}
+
 hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,
                                  hipStream_t s) {
-    const unsigned blocks = (unsigned)(g.L_tgt * 2 * pl.nN * pl.nP * pl.KS);
+    if (g.T < 1 || g.T > SBN) return hipErrorInvalidValue;
     const int64_t rthreads = (int64_t)g.L_tgt * 2 * g.T * g.H * (g.d / 8);
     const unsigned rblocks = (unsigned)((rthreads + 255) / 256);
     if (g.d == 128) {
-        hipLaunchKernelGGL((map_bf16_small_kernel<128>), dim3(blocks), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T,
-                           pl.nN, pl.nP, pl.KS, pl.kps, part);
+        launch_short_d<128>(a, g, pl, part, s);
         hipLaunchKernelGGL((map_small_reduce_kernel<128>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
                            g.T, pl.KS);
     } else {
-        hipLaunchKernelGGL((map_bf16_small_kernel<64>), dim3(blocks), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T,
-                           pl.nN, pl.nP, pl.KS, pl.kps, part);
+        launch_short_d<64>(a, g, pl, part, s);
         hipLaunchKernelGGL((map_small_reduce_kernel<64>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
                            g.T, pl.KS);
     }

@@ -70,9 +70,10 @@ hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 constexpr int64_t kSmallT = KVMAP_SMALL_T;
 struct SmallPlan {
     int nN, nP, KS, kps;  // feature tiles, token tiles, K splits, K-steps per split
+    int n_items, grid;    // work items (tiles x splits), persistent workgroups
     size_t part_bytes;    // fp32 partial sums [KS][L_tgt][2][T][N]
 };
-SmallPlan map_bf16_small_plan(const ApplyGeom& g);
+SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus);
 hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,
                                  hipStream_t s);
 

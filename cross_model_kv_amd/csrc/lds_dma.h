@@ -38,6 +38,22 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds_addr, int v
                  :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
+// The same load with the non-temporal hint: for data read exactly once (a stream of map
+// weights), so that it does not displace lines that other workgroups will read again.
+__device__ __forceinline__ void lds_dma16_nt(i32x4_t rsrc, uint32_t lds_addr, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+// One dword at a wave-uniform address through the scalar cache (a read; the wait for it is
+// part of the statement, so the result is ready when it ends).  For small tables read inside
+// a pipeline whose vector-memory counter must only count the pipeline's own loads.
+__device__ __forceinline__ int scalar_load_dword(const int32_t* p) {
+    int r;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(r) : "s"(p) : "memory");
+    return r;
+}
+
 // c ? a : b on uniform values, as one s_cselect.  Written out because the compiler turns a
 // select between a v_readlane result and an add into a branch, which would split the loop.
 __device__ __forceinline__ uint32_t uniform_select(uint32_t c, uint32_t a, uint32_t b) {

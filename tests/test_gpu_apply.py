@@ -195,7 +195,7 @@ def test_full_size_sampled(ctx, cid):
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
 
 
-# ---- short caches (T <= 256: the split-K path with a separate reduce) -------------------
+# ---- short caches (T <= 64: the persistent short-cache kernel with a separate reduce) ----
 
 SHORT = [
     # 1.5 feature tiles (H=3), 64 tokens exactly one token tile, L_tgt > L_src
@@ -206,6 +206,13 @@ SHORT = [
     ApplyConfig(223, "short-T256-H8", 4, 2, 8, 128, 256, 2, 1.0e6, 1.0e6, "bf16", 0.5),
     # one head of d = 64 (N = 64, a partial feature tile), k = 5 (320 features: 5 K-steps)
     ApplyConfig(224, "short-H1-d64-k5-T129", 6, 2, 1, 64, 129, 5, 1.0e4, 1.0e4, "bf16", 0.5),
+    # 320 tiles (80 target layers x K/V x 2 feature tiles) on a 256-CU device: the K reduction
+    # is split 4 ways and every workgroup streams 5 work items (tiles of different target
+    # layers, K/V and splits) through one ring
+    ApplyConfig(226, "short-many-items-T16", 3, 80, 4, 128, 16, 1, 1.0e4, 1.0e6, "bf16", 0.5),
+    # head dim 64, 3 selected layers, T = 5: 12 splits of one K-step each, so consecutive
+    # items of a workgroup read different (selected layer, head) slabs
+    ApplyConfig(227, "short-many-items-k3-T5", 4, 48, 4, 64, 5, 3, 1.0e6, 5.0e5, "bf16", 0.5, pos0=7),
 ]
 
 
@@ -214,12 +221,13 @@ def test_short_caches(ctx, cfg):
     _full_check(ctx, cfg)
 
 
-def test_short_cache_full_layer_shape(ctx):
-    """The Qwen3 14B->32B layer shape (L 40->64, H 8, d 128, k 8) at T = 64, where the K
-    reduction is split across workgroups: every row of sampled target layers against the
-    oracle, and bit-identical outputs on a second call (the partial sums are added in a
-    fixed order)."""
-    cfg = APPLY_CONFIGS[3].replace(cid=225, name="qwen3-14b-to-32b-T64", T=64)
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_short_cache_full_layer_shape(ctx, T):
+    """The Qwen3 14B->32B layer shape (L 40->64, H 8, d 128, k 8) at T = 1, 16 and 64, where
+    every workgroup streams two whole tiles through its ring: every row of sampled target
+    layers against the oracle, and bit-identical outputs on a second call (the partial sums
+    are added in a fixed order)."""
+    cfg = APPLY_CONFIGS[3].replace(cid=225, name=f"qwen3-14b-to-32b-T{T}", T=T)
     inp = apply_inputs(cfg, "cuda:0")
     ok_, ov_ = _run(ctx, cfg, inp)
     targets = [0, 21, 42, 63]
