@@ -88,57 +88,71 @@ __global__ __launch_bounds__(256) void ridge_init_b_kernel(const RidgeArgs g) {
     sys_b(g)[idx] = (i < p && c < q) ? (double)M_xy[(size_t)i * q + c] : 0.0;
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Factor the diagonal block kb in place (lower triangle) and write the inverse of the factor to
-// Li[kb]; one workgroup of 64 threads per system.  The inverse turns every triangular solve
-// with this block (the panel below it and both substitutions) into a 64 x 64 tile product on
-// the matrix cores.
+// Li[kb]; one wave of 64 lanes per system.  The inverse turns every triangular solve with this
+// block (the panel below it and both substitutions) into a 64 x 64 tile product on the matrix
+// cores.  The block lives in registers, lane r holding row r (64 doubles), so that the only
+// LDS traffic is one broadcast column per step:
+//   step j: l_jj = sqrt(a_jj) (lane j's, read with v_readlane); lane r > j: l_rj = a_rj / l_jj,
+//   published in col[r]; then every lane r: a_rm -= l_rj l_mj for m > j (col[m] = l_mj is a
+//   broadcast LDS read).  Elements above a lane's diagonal are updated too and never used.
+// The inverse X = L^-1 by forward substitution, lane r holding column r:
+//   X_ir = (delta_ir - sum_{m < i} L_im X_mr) / L_ii, with L_im broadcast from LDS; the terms
+//   with m < r vanish because X is lower triangular.
 __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
-    __shared__ double t[RB][RB + 1];
-    __shared__ double x[RB][RB + 1];
+    __shared__ double Ls[RB][RB + 1];
+    __shared__ double col[RB];
     double* A = sys_a(g);
     const int P = g.P;
     const int r = threadIdx.x;
     const int o = kb * RB;
-    for (int i = 0; i < RB; ++i) t[i][r] = A[(size_t)(o + i) * P + o + r];  // coalesced rows
+    for (int i = 0; i < RB; ++i) Ls[i][r] = A[(size_t)(o + i) * P + o + r];  // coalesced rows
     __syncthreads();
+    double a[RB];
+#pragma unroll
+    for (int c = 0; c < RB; ++c) a[c] = Ls[r][c];
+    bool bad = false;
+#pragma unroll
     for (int j = 0; j < RB; ++j) {
-        double d = t[j][j];
+        double d = readlane_f64(a[j], j);
         if (!(d > 0.0) || !isfinite(d)) {
-            if (r == 0) atomicOr(&g.bad[blockIdx.y], 1);
+            bad = true;
             d = 1.0;  // keep going with a harmless pivot; the result is refused by the host
         }
         const double ljj = sqrt(d);
+        const double lrj = (r == j) ? ljj : a[j] / ljj;
+        a[j] = lrj;
+        col[r] = lrj;
         __syncthreads();
-        if (r == j) t[j][j] = ljj;
-        if (r > j) t[r][j] /= ljj;
-        __syncthreads();
-        if (r > j)
-            for (int m = j + 1; m <= r; ++m) t[r][m] -= t[r][j] * t[m][j];
-        __syncthreads();
+#pragma unroll
+        for (int m = j + 1; m < RB; ++m) a[m] -= lrj * col[m];
+        __syncthreads();  // every read of col done before the next step writes it
     }
+    if (bad && r == 0) atomicOr(&g.bad[blockIdx.y], 1);
+    // the factor, zero above the diagonal: back to A (coalesced rows, through LDS) and kept in
+    // LDS for the inverse
+#pragma unroll
+    for (int c = 0; c < RB; ++c) Ls[r][c] = (c <= r) ? a[c] : 0.0;
     __syncthreads();
-    for (int i = 0; i < RB; ++i) A[(size_t)(o + i) * P + o + r] = (r <= i) ? t[i][r] : 0.0;
-    // X = L^-1 by forward substitution, thread r = column r of X:
-    //   X[i][r] = (delta_ir - sum_{m = r}^{i-1} L[i][m] X[m][r]) / L[i][i],  i >= r
-    // (four partial sums: the LDS reads of one row pipeline instead of waiting on one chain)
+    for (int i = 0; i < RB; ++i) A[(size_t)(o + i) * P + o + r] = Ls[i][r];
+    double x[RB];
+#pragma unroll
     for (int i = 0; i < RB; ++i) {
-        double v = 0.0;
-        if (i >= r) {
-            double a0 = (i == r) ? 1.0 : 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-            int m = r;
-            for (; m + 3 < i; m += 4) {
-                a0 -= t[i][m] * x[m][r];
-                a1 -= t[i][m + 1] * x[m + 1][r];
-                a2 -= t[i][m + 2] * x[m + 2][r];
-                a3 -= t[i][m + 3] * x[m + 3][r];
-            }
-            for (; m < i; ++m) a0 -= t[i][m] * x[m][r];
-            v = ((a0 + a1) + (a2 + a3)) / t[i][i];
-        }
-        x[i][r] = v;
+        double v = (i == r) ? 1.0 : 0.0;
+#pragma unroll
+        for (int m = 0; m < i; ++m) v -= Ls[i][m] * x[m];
+        x[i] = v / Ls[i][i];
     }
     double* Li = sys_li(g) + (size_t)kb * RB * RB;
-    for (int i = 0; i < RB; ++i) Li[(size_t)i * RB + r] = x[i][r];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) Li[(size_t)i * RB + r] = x[i];
 }
 
 // C -= sum over K blocks kb = k0 .. k0 + nk - 1 of op(A) op(B), on 64 x 64 tiles with K = 64
