@@ -14,9 +14,10 @@
 //   the statistics alone: RSS_c = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2
 // A batch of up to kRidgeMaxBatch systems of one shape runs through every kernel together
 // (grid y = system): the 64-wide diagonal steps form a serial chain of about 4 P / 64 small
-// launches, which a batch pays once.  The tile updates C -= op(A) op(B) (64 x 64, K = 64) run
-// on the fp64 matrix cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their
-// global orientation.  A non-positive or non-finite pivot sets the system's device flag, which
+// launches, which a batch pays once.  The tile updates C -= op(A) op(B) run on the fp64 matrix
+// cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their global orientation: 64 x
+// 64 tiles inside a panel, 128 x 128 tiles for the once-per-panel updates of the trailing matrix
+// and of the right-hand sides (P and Q padded to multiples of 128 for them).  A non-positive or non-finite pivot sets the system's device flag, which
 // the host turns into KVMAP_ERR_NOT_SPD.
 
 #include <algorithm>
@@ -29,7 +30,15 @@ namespace kvmap {
 namespace {
 
 constexpr int RB = 64;       // block size
-constexpr int LDW = RB + 2;  // LDS row stride (doubles) of a staged 64 x 64 tile
+// LDS row strides (doubles) of staged tiles, odd: a 16-lane group of a fragment read (one
+// double per lane, lanes 16 rows apart by one row each) then covers 16 distinct bank pairs of
+// the 32 banks; with an even stride of 66, rows 8 apart shared a pair (the counters showed 40 %
+// of the LDS cycles of the trailing update in bank conflicts)
+constexpr int LDW = RB + 1;  // 64 x 64 tile
+constexpr int TB = 128;      // C tile of the large updates (the trailing matrix, the right-hand sides)
+constexpr int KB = 32;       // K per LDS stage of the large updates
+constexpr int LD_R = KB + 1;  // LDS row stride of a stage stored with the tile's rows (128 x 32)
+constexpr int LD_M = TB + 2;  // ... with its K index as rows (32 x 128)
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -261,22 +270,42 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
         }
         __syncthreads();
         if (kc + 1 < nk) fetch(kc + 1);
-#pragma unroll 4
-        for (int kk = 0; kk < RB; kk += 4) {
+        // fragments of k-step kk + 4 are read while the MFMAs of k-step kk run
+        double a[2][2], b[2][2];
+        auto frags = [&](int kk, int h) {
             const int m = kk + lk;
-            double a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = r0 + 16 * i + li, c = c0 + 16 * i + li;
-                a[i] = A_ROWS ? As[r * LDW + m] : As[m * LDW + r];
-                b[i] = B_ROWS ? Bs[c * LDW + m] : Bs[m * LDW + c];
+                a[h][i] = A_ROWS ? As[r * LDW + m] : As[m * LDW + r];
+                b[h][i] = B_ROWS ? Bs[c * LDW + m] : Bs[m * LDW + c];
             }
+        };
+        frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < RB; kk += 4) {
+            const int h = (kk >> 2) & 1;
+            if (kk + 4 < RB) frags(kk + 4, h ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    // C: every element of the thread read first, then written (written element by element
+    // as load-subtract-store, each load would wait for the previous store: 16 serial round trips)
+    double cv[2][2][4];
+    if (!OVERWRITE) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cv[i][j][e] = C[(size_t)(r0 + 16 * i + lk + 4 * e) * ldc + c0 + 16 * j + li];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -285,8 +314,146 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + 16 * i + lk + 4 * e, c = c0 + 16 * j + li;
-                if (OVERWRITE) C[(size_t)r * ldc + c] = acc[i][j][e];
-                else C[(size_t)r * ldc + c] -= acc[i][j][e];
+                C[(size_t)r * ldc + c] = OVERWRITE ? acc[i][j][e] : cv[i][j][e] - acc[i][j][e];
+            }
+}
+
+// The large updates of MODE 0 (TRI), 1 and 2 of ridge_update_kernel on 128 x 128 tiles of C, K
+// = 64 nk from block k0 (i0, j0: first row and column tile, in tiles of 128; ncol: column tiles;
+// MODE 0 takes the lower triangle of tiles from tile j0 on, and computes the diagonal tiles
+// whole: their upper 64 x 64 quarter is never read).  Twice the arithmetic per operand byte of
+// the 64 x 64 kernel.  4 waves, each a 64 x 64 quarter of C as 4 x 4 blocks of 16 x 16
+// (v_mfma_f64_16x16x4f64).  The operands go through LDS in stages of K = 32, two stages
+// deep: the registers holding stage kc + 1 are written to LDS, and stage kc + 2 is requested,
+// before the MFMAs of stage kc, so neither waits on the other.
+template <int MODE>
+__global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i0, int j0, int ncol, int k0,
+                                                        int nk) {
+    static_assert(MODE == 0 || MODE == 1 || MODE == 2, "large-update modes");
+    constexpr bool A_ROWS = MODE != 2;  // A stage stored with the rows r (else with m as rows)
+    constexpr bool B_ROWS = MODE == 0;  // B stage stored with the columns c as rows (else m)
+    constexpr int A_LDS = A_ROWS ? TB * LD_R : KB * LD_M;
+    constexpr int B_LDS = B_ROWS ? TB * LD_R : KB * LD_M;
+    __shared__ double As[2][A_LDS];
+    __shared__ double Bs[2][B_LDS];
+    double* A = sys_a(g);
+    double* Bm = sys_b(g);
+    const int P = g.P, Q = g.Q;
+    const int tid = threadIdx.x;
+    int I, J;
+    if (MODE == 0) {
+        lower_decode(blockIdx.x, I, J);
+        I += j0;
+        J += j0;
+    } else {
+        I = i0 + (int)blockIdx.x / ncol;
+        J = j0 + (int)blockIdx.x % ncol;
+    }
+    double* C;
+    int ldc;
+    if (MODE == 0) {
+        C = A + (size_t)I * TB * P + (size_t)J * TB;
+        ldc = P;
+    } else {
+        C = Bm + (size_t)I * TB * Q + (size_t)J * TB;
+        ldc = Q;
+    }
+    // stage kc: element (x, y) of the stored A (B) stage is Ap[x * lda + y] (Bp[x * ldb + y])
+    auto stage = [&](int kc, const double*& Ap, int& lda, const double*& Bp, int& ldb) {
+        const int ko = k0 * RB + kc * KB;
+        if (MODE == 0) {
+            Ap = A + (size_t)I * TB * P + ko; lda = P;  // rows r, columns m
+            Bp = A + (size_t)J * TB * P + ko; ldb = P;  // rows c, columns m
+        } else if (MODE == 1) {
+            Ap = A + (size_t)I * TB * P + ko; lda = P;  // rows r, columns m
+            Bp = Bm + (size_t)ko * Q + (size_t)J * TB; ldb = Q;  // rows m, columns c
+        } else {
+            Ap = A + (size_t)ko * P + (size_t)I * TB; lda = P;  // rows m, columns r
+            Bp = Bm + (size_t)ko * Q + (size_t)J * TB; ldb = Q;  // rows m, columns c
+        }
+    };
+    constexpr int PER = TB * KB / 512;  // elements of each stage per thread (8)
+    double ra[PER], rb[PER];
+    auto fetch = [&](int kc) {
+        const double* Ap;
+        const double* Bp;
+        int lda, ldb;
+        stage(kc, Ap, lda, Bp, ldb);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = u * 512 + tid;
+            const int xa = A_ROWS ? e / KB : e / TB, ya = A_ROWS ? e % KB : e % TB;
+            const int xb = B_ROWS ? e / KB : e / TB, yb = B_ROWS ? e % KB : e % TB;
+            ra[u] = Ap[(size_t)xa * lda + ya];
+            rb[u] = Bp[(size_t)xb * ldb + yb];
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = u * 512 + tid;
+            const int xa = A_ROWS ? e / KB : e / TB, ya = A_ROWS ? e % KB : e % TB;
+            const int xb = B_ROWS ? e / KB : e / TB, yb = B_ROWS ? e % KB : e % TB;
+            As[buf][xa * (A_ROWS ? LD_R : LD_M) + ya] = ra[u];
+            Bs[buf][xb * (B_ROWS ? LD_R : LD_M) + yb] = rb[u];
+        }
+    };
+    const int lane = tid & 63, w = tid >> 6;
+    const int wr0 = (w >> 2) * 64, wc0 = (w & 3) * 32;
+    const int li = lane & 15, lk = lane >> 4;
+    f64x4_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    const int nkb = nk * (RB / KB);
+    fetch(0);
+    stash(0);
+    if (nkb > 1) fetch(1);
+    __syncthreads();
+    for (int kc = 0; kc < nkb; ++kc) {
+        const int cur = kc & 1;
+        if (kc + 1 < nkb) stash(cur ^ 1);  // that buffer's last reader was stage kc - 1
+        if (kc + 2 < nkb) fetch(kc + 2);
+        const double* as = As[cur];
+        const double* bs = Bs[cur];
+#pragma unroll 2
+        for (int kk = 0; kk < KB; kk += 4) {
+            const int m = kk + lk;
+            double a[4], b[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wr0 + 16 * i + li;
+                a[i] = A_ROWS ? as[r * LD_R + m] : as[m * LD_M + r];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = wc0 + 16 * j + li;
+                b[j] = B_ROWS ? bs[c * LD_R + m] : bs[m * LD_M + c];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();  // stage kc read by every wave before its buffer is refilled
+    }
+    double cv[4][2][4];  // C read whole before any store (see ridge_update_kernel)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cv[i][j][e] = C[(size_t)(wr0 + 16 * i + lk + 4 * e) * ldc + wc0 + 16 * j + li];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = wr0 + 16 * i + lk + 4 * e, c = wc0 + 16 * j + li;
+                C[(size_t)r * ldc + c] = cv[i][j][e] - acc[i][j][e];
             }
 }
 
@@ -385,8 +552,12 @@ __global__ __launch_bounds__(256) void ridge_r2_group_kernel(const RidgeArgs g, 
 
 namespace {
 
+// P, Q: p and q padded to a multiple of the 128-wide tiles of the large updates (so that every
+// panel boundary, a multiple of 4 blocks of 64, is a tile boundary).
+int pad_dim(int n) { return (n + TB - 1) / TB * TB; }
+
 size_t sys_stride(int p, int q) {
-    const size_t P = ((size_t)p + RB - 1) / RB * RB, Q = ((size_t)q + RB - 1) / RB * RB;
+    const size_t P = (size_t)pad_dim(p), Q = (size_t)pad_dim(q);
     return (P * P + P * Q + Q + P * RB + 31) / 32 * 32;  // A, B (then W), rss, Li; 256-byte aligned
 }
 
@@ -398,8 +569,8 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
     g.bad = ridge_dev_flags(scratch, p, q, n);
     g.p = p;
     g.q = q;
-    g.P = (p + RB - 1) / RB * RB;
-    g.Q = (q + RB - 1) / RB * RB;
+    g.P = pad_dim(p);
+    g.Q = pad_dim(q);
     g.lambda = lambda;
     return g;
 }
@@ -412,7 +583,8 @@ constexpr int kPanel = 4;
 
 void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
     const int P = g.P, Q = g.Q;
-    const int nb = P / RB, nq = Q / RB;
+    const int nb = P / RB, nq = Q / RB, nq2 = Q / TB;  // (P, Q: multiples of 128, so nb is even and every
+                                                        // panel boundary, a multiple of 4 blocks, is even)
     const unsigned un = (unsigned)n;
     const dim3 blk(256);
     hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256), un), blk, 0, s, g);
@@ -430,9 +602,9 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
                 hipLaunchKernelGGL((ridge_update_kernel<0, false>), dim3(below * w, un), blk, 0, s, g, kb + 1, kb + 1,
                                    w, kb, 1);
         }
-        const int m = nb - b1;  // trailing lower triangle
+        const int m = (nb - b1) / 2;  // trailing lower triangle, in tiles of 128
         if (m > 0)
-            hipLaunchKernelGGL((ridge_update_kernel<0, true>), dim3(m * (m + 1) / 2, un), blk, 0, s, g, b1, b1, 0, b0,
+            hipLaunchKernelGGL(ridge_big_kernel<0>, dim3(m * (m + 1) / 2, un), dim3(512), 0, s, g, 0, b1 / 2, 0, b0,
                                b1 - b0);
     }
     // L Z = B
@@ -445,7 +617,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
                 hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3(h * nq, un), blk, 0, s, g, kb + 1, 0, nq, kb, 1);
         }
         if (nb > b1)
-            hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3((nb - b1) * nq, un), blk, 0, s, g, b1, 0, nq, b0,
+            hipLaunchKernelGGL(ridge_big_kernel<1>, dim3((nb - b1) / 2 * nq2, un), dim3(512), 0, s, g, b1 / 2, 0, nq2, b0,
                                b1 - b0);
     }
     // L^T W = Z, panels from the last
@@ -458,7 +630,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
                 hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3(h * nq, un), blk, 0, s, g, b0, 0, nq, kb, 1);
         }
         if (b0 > 0)
-            hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3(b0 * nq, un), blk, 0, s, g, 0, 0, nq, b0, b1 - b0);
+            hipLaunchKernelGGL(ridge_big_kernel<2>, dim3(b0 / 2 * nq2, un), dim3(512), 0, s, g, 0, 0, nq2, b0, b1 - b0);
     }
 }
 

@@ -196,9 +196,10 @@ def test_fit_stats_full_size(ctx):
 
 
 def test_ridge_solve_device_matches_oracle(ctx):
-    """kvmap_ridge_solve_device on a GPU-built state (p = 520, q = 68: both padded to multiples
-    of 64 inside), against the oracle's fp64 ridge on the same (fp32) statistics and against
-    the host solver; lambda = 0.01 and a larger lambda."""
+    """kvmap_ridge_solve_device on a GPU-built state (p = 520, q = 68: padded to multiples of
+    128 inside, 10 blocks of 64 in 3 panels, so the 128-tile updates of the trailing matrix and
+    of the right-hand sides run on partial panels), against the oracle's fp64 ridge on the same
+    (fp32) statistics and against the host solver; lambda = 0.01 and a larger lambda."""
     from cross_model_kv_amd import kvmap as K
     parts = _batches(SMALL, [700, 1300])
     st = ctx.gram_state(SMALL.p, SMALL.q)
