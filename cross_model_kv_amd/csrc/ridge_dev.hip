@@ -17,8 +17,8 @@
 // launches, which a batch pays once.  The tile updates C -= op(A) op(B) run on the fp64 matrix
 // cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their global orientation: 64 x
 // 64 tiles inside a panel, 128 x 128 tiles for the once-per-panel updates of the trailing matrix
-// and of the right-hand sides (P and Q padded to multiples of 128 for them).  A non-positive or non-finite pivot sets the system's device flag, which
-// the host turns into KVMAP_ERR_NOT_SPD.
+// and of the right-hand sides (P and Q padded to multiples of 128 for them).  A non-positive or
+// non-finite pivot sets the system's device flag, which the host turns into KVMAP_ERR_NOT_SPD.
 
 #include <algorithm>
 
