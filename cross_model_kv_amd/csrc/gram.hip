@@ -278,8 +278,28 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
         const int j = j0 + wj * 64 + b * 32 + (lane & 31);
         const bool jok = j < lim;
         const float mj = jok ? mb[j] : 0.f, dj = jok ? db[j] : 0.f;
+        // per (column block, row half): the old values are read before any store of the group
+        // (element-wise load-add-store would make each load wait for the previous store)
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
+            float old[4][4], oldm[4][4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) old[g][r] = oldm[g][r] = 0.f;
+            if (!fresh) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ib = i0 + wi * 64 + a * 32 + g * 8 + (lane >> 5) * 4;
+                    if (ib >= rlim || !jok) continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) old[g][r] = M[(size_t)(ib - moff + r) * ldm + (j - moff)];
+                    if (mirror) {
+                        const float4 o = *(const float4*)(M + (size_t)(j - moff) * ldm + (ib - moff));
+                        oldm[g][0] = o.x; oldm[g][1] = o.y; oldm[g][2] = o.z; oldm[g][3] = o.w;
+                    }
+                }
+            }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int ib = i0 + wi * 64 + a * 32 + g * 8 + (lane >> 5) * 4;
@@ -293,16 +313,10 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(
                 for (int r = 0; r < 4; ++r)
                     v[r] = acc[a][b][g * 4 + r] - nbf * mia[r] * mj + coef * dia[r] * dj;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* dst = M + (size_t)(ib - moff + r) * ldm + (j - moff);
-                    *dst = fresh ? v[r] : *dst + v[r];
-                }
-                if (mirror) {
-                    float4* dst = (float4*)(M + (size_t)(j - moff) * ldm + (ib - moff));
-                    float4 o = fresh ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
-                    o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-                    *dst = o;
-                }
+                for (int r = 0; r < 4; ++r) M[(size_t)(ib - moff + r) * ldm + (j - moff)] = old[g][r] + v[r];
+                if (mirror)
+                    *(float4*)(M + (size_t)(j - moff) * ldm + (ib - moff)) =
+                        make_float4(oldm[g][0] + v[0], oldm[g][1] + v[1], oldm[g][2] + v[2], oldm[g][3] + v[3]);
             }
         }
     }

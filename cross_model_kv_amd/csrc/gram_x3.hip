@@ -330,35 +330,55 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
     const float* __restrict__ mb = xy ? my : mx;
     const float* __restrict__ db = xy ? dy : dx;
     const bool mirror = !xy && I != J;
+    // Per 16-column block and half of the row blocks: every old value of the state is read
+    // before any store of the group (as load-add-store element by element, each load would
+    // wait for the previous store).
+    constexpr int IH = IB / 2;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
         const int j = j0 + wp * TW + jb * 16 + (lane & 15);
         const bool jok = j < (xy ? ldb : lim);
         const float mj = jok ? mb[j] : 0.f, dj = jok ? db[j] : 0.f;
 #pragma unroll
-        for (int ib = 0; ib < IB; ++ib) {
-            const int i = i0 + wn * 128 + ib * 16 + kq * 4;
-            if (!jok || i >= lim) continue;  // p and bd are multiples of 4: all 4 rows valid
-            const float4 mi = *(const float4*)(mx + i);
-            const float4 di = *(const float4*)(dx + i);
-            const float mia[4] = {mi.x, mi.y, mi.z, mi.w};
-            const float dia[4] = {di.x, di.y, di.z, di.w};
-            float v[4];
+        for (int h = 0; h < 2; ++h) {
+            float old[IH][4], oldm[IH][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[ib][jb][r] - nbf * mia[r] * mj + coef * dia[r] * dj;
+            for (int u = 0; u < IH; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* dst = M + (size_t)(i - moff + r) * ldm + (j - moff);
-                *dst = fresh ? v[r] : *dst + v[r];
+                for (int r = 0; r < 4; ++r) old[u][r] = oldm[u][r] = 0.f;
+            if (!fresh) {
+#pragma unroll
+                for (int u = 0; u < IH; ++u) {
+                    const int i = i0 + wn * 128 + (h * IH + u) * 16 + kq * 4;
+                    if (!jok || i >= lim) continue;  // p and bd are multiples of 4: all 4 rows valid
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) old[u][r] = M[(size_t)(i - moff + r) * ldm + (j - moff)];
+                    if (mirror) {
+                        const float4 o = *(const float4*)(M + (size_t)(j - moff) * ldm + (i - moff));
+                        oldm[u][0] = o.x;
+                        oldm[u][1] = o.y;
+                        oldm[u][2] = o.z;
+                        oldm[u][3] = o.w;
+                    }
+                }
             }
-            if (mirror) {
-                float4* dst = (float4*)(M + (size_t)(j - moff) * ldm + (i - moff));
-                float4 o = fresh ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
-                o.x += v[0];
-                o.y += v[1];
-                o.z += v[2];
-                o.w += v[3];
-                *dst = o;
+#pragma unroll
+            for (int u = 0; u < IH; ++u) {
+                const int ib = h * IH + u;
+                const int i = i0 + wn * 128 + ib * 16 + kq * 4;
+                if (!jok || i >= lim) continue;
+                const float4 mi = *(const float4*)(mx + i);
+                const float4 di = *(const float4*)(dx + i);
+                const float mia[4] = {mi.x, mi.y, mi.z, mi.w};
+                const float dia[4] = {di.x, di.y, di.z, di.w};
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[ib][jb][r] - nbf * mia[r] * mj + coef * dia[r] * dj;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) M[(size_t)(i - moff + r) * ldm + (j - moff)] = old[u][r] + v[r];
+                if (mirror)
+                    *(float4*)(M + (size_t)(j - moff) * ldm + (i - moff)) =
+                        make_float4(oldm[u][0] + v[0], oldm[u][1] + v[1], oldm[u][2] + v[2], oldm[u][3] + v[3]);
             }
         }
     }
