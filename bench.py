@@ -127,7 +127,8 @@ def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=
     """Short caches (the short-prefix regime): kvmap_apply of the workload's first T tokens for a
     few T, with all of the workload's maps.  At these lengths the apply reads all of W (2 x L_tgt
     x N x F bf16) for little arithmetic, so the bound is HBM: W + the gathered source rows +
-    the written target rows over 8 TB/s.  Caches of up to 64 tokens take the split-K kernel."""
+    the written target rows over 8 TB/s.  Caches of up to 128 tokens take the persistent
+    short-cache kernel."""
     import torch
     stream = torch.cuda.current_stream()
     w_bytes = 2 * cfg.L_tgt * cfg.N * cfg.F * 2
@@ -156,7 +157,7 @@ def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=
         o_bytes = 2 * cfg.L_tgt * cfg.H * T * cfg.d * 2
         roof_ms = (w_bytes + x_bytes + o_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3
         rows.append({"T": T, "ms": ms, "W_GBps": w_bytes / (ms / 1e3) / 1e9, "hbm_roofline_ms": roof_ms,
-                     "frac_hbm": roof_ms / ms, "kernel": "map_bf16_small" if T <= 64 else "map_bf16"})
+                     "frac_hbm": roof_ms / ms, "kernel": "map_bf16_small" if T <= 128 else "map_bf16"})
         log(f"short T={T}: {ms:.3f} ms ({w_bytes / (ms / 1e3) / 1e12:.2f} TB/s of W; HBM roofline {roof_ms:.3f} ms)")
         del sk, sv, ok_, ov_
     return {"workload": f"{cfg.name} maps (W {w_bytes / 1e9:.2f} GB bf16) on the first T tokens of the cache",

@@ -1,10 +1,10 @@
-// The map GEMM for short caches (up to 64 tokens), bf16.  At these lengths the apply moves the
+// The map GEMM for short caches (up to 128 tokens), bf16.  At these lengths the apply moves the
 // whole of W (F x N per target layer, K and V) for little arithmetic, so it is bound by reading
 // W from HBM (VeloxQuant-MLX "Cross-Model KV Transfer", "The mapping": one ridge map per target
 // head; the same Y = X W + b, then bias and target RoPE).  The long-cache kernel's 256-token
 // tiles would be mostly padding here and its one-tile workgroups would drain and refill their
 // load pipeline per tile, so this path
-//   * tiles 256 features x 16, 32 or 64 tokens and runs one persistent workgroup per compute
+//   * tiles 256 features x 16, 32, 64 or 128 tokens and runs one persistent workgroup per compute
 //     unit; each streams its share of the work items (a tile, or a split of a tile's K
 //     reduction when the tiles do not divide evenly over the compute units) through one ring
 //     of LDS stages that runs on from item to item;
@@ -27,9 +27,8 @@ namespace kvmap {
 namespace {
 
 constexpr int SBM = 256;                 // features per tile
-constexpr int SBN = 64;                  // most tokens per tile (the path takes T <= SBN)
+constexpr int SBN = 128;                 // most tokens per tile (the path takes T <= SBN)
 constexpr int SBK = 64;                  // features (reduction) per K-step
-constexpr int NRING = 4;                 // stages in flight + the one computed
 constexpr int W_CHUNKS = SBM * SBK / 8;  // 16-byte chunks of W per stage (2048)
 constexpr int LW = W_CHUNKS / 512;       // W loads per thread per stage (4)
 
@@ -63,28 +62,32 @@ __device__ __forceinline__ ShortItem short_item(int i, int KS, int nN, int L_tgt
 }
 
 // Persistent: workgroup g (one per compute unit) takes items g, g + G, g + 2G, ... and streams
-// them through ONE ring of 4 stages (W tile + X tile), each filled by buffer_load_dwordx4 ...
-// lds three K-steps ahead of its use.  The ring runs on across items: the loads of an item's
-// first K-steps go out while the previous item's last ones are computed, so W streams without
-// a drain and refill per tile.  At the end of an item its fp32 partial sums are stored and the
-// accumulators cleared.  8 waves: wave w computes features (w & 1) * 128 .. + 127 (whole
-// heads) of tokens (w >> 1) * 16 .. + 15 of its item's tile, as 8 blocks of
-// v_mfma_f32_16x16x32_bf16.  TOK (16, 32 or 64, at least T) tokens per tile: 128 / TOK waves
-// side by side along the features, each 2 TOK features (whole 16-feature blocks) x 16 tokens,
-// so that short caches spend no MFMAs and fragment reads on padding tokens; only the first
-// TOK / 8 waves load the X tile.  NT: W (read exactly once) is loaded with the non-temporal
-// hint.
+// them through ONE ring of NRING stages (W tile + X tile), each filled by buffer_load_dwordx4
+// ... lds NRING - 1 K-steps ahead of its use.  The ring runs on across items: the loads of an
+// item's first K-steps go out while the previous item's last ones are computed, so W streams
+// without a drain and refill per tile.  At the end of an item its fp32 partial sums are stored
+// and the accumulators cleared.  TOK (16, 32, 64 or 128, at least T) tokens per tile, 8 waves:
+// WN waves side by side along the features, each FW features (whole 16-feature blocks) x TW
+// tokens as IB x JB blocks of v_mfma_f32_16x16x32_bf16 -- 8 x 1 waves of 32 x 16 at TOK 16,
+// 4 x 2 of 64 x 16 at 32, 2 x 4 of 128 x 16 at 64, 2 x 4 of 128 x 32 at 128 -- so that short
+// caches spend no MFMAs and fragment reads on padding tokens.  The ring has 4 stages (34 to 40
+// KB) up to 64 tokens and 3 (48 KB) at 128.  NT: W (read exactly once) is loaded with the
+// non-temporal hint.
 template <int D, int TOK, bool NT>
 __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
                                                              int nN, int KS, int kps, int n_items,
                                                              float* __restrict__ part) {
-    constexpr int X_CHUNKS = TOK * SBK / 8;           // 16-byte chunks of X per stage
-    constexpr int XW = X_CHUNKS / 64;                 // waves that load X, one chunk per lane
-    constexpr int STAGE = (W_CHUNKS + X_CHUNKS) * 16;  // 34, 36 or 40 KB
-    constexpr int WN = 128 / TOK;                     // waves along the features
-    constexpr int FW = SBM / WN;                      // features per wave
-    constexpr int IB = FW / 16;                       // 16-feature MFMA blocks per wave
-    static_assert(TOK == 16 || TOK == 32 || TOK == 64, "tokens per tile");
+    static_assert(TOK == 16 || TOK == 32 || TOK == 64 || TOK == 128, "tokens per tile");
+    constexpr int X_CHUNKS = TOK * SBK / 8;            // 16-byte chunks of X per stage
+    constexpr int LX = X_CHUNKS > 512 ? X_CHUNKS / 512 : 1;  // X loads per loading lane
+    constexpr int XW = X_CHUNKS / (64 * LX);           // waves that load X
+    constexpr int STAGE = (W_CHUNKS + X_CHUNKS) * 16;  // 34, 36, 40 or 48 KB
+    constexpr int NRING = TOK == 128 ? 3 : 4;          // stages in the ring (LDS: 136 - 160 KB)
+    constexpr int WN = TOK <= 64 ? 128 / TOK : 2;      // waves along the features
+    constexpr int TW = TOK / (8 / WN);                 // tokens per wave
+    constexpr int FW = SBM / WN;                       // features per wave
+    constexpr int IB = FW / 16;                        // 16-feature MFMA blocks per wave
+    constexpr int JB = TW / 16;                        // 16-token MFMA blocks per wave
     __shared__ __attribute__((aligned(16))) char smem[NRING * STAGE];
     const uint4* lds = (const uint4*)smem;
     const int G = gridDim.x;
@@ -99,20 +102,21 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-    // Loads: W slot u = i*512 + tid holds row u/8, chunk (u%8) ^ slot_xor(row); X slot tid
-    // (tid < X_CHUNKS) holds row tid/8 likewise.  Rows past N or T repeat the last one (never
-    // stored).
+    // Loads: W slot u = i*512 + tid holds row u/8, chunk (u%8) ^ slot_xor(row); X slot u =
+    // i*512 + tid (u < X_CHUNKS) holds row u/8 likewise.  Rows past N or T repeat the last one
+    // (never stored).
     int arow[LW], acol[LW];
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         arow[i] = i * 64 + wave * 8 + (lane >> 3);
         acol[i] = ((lane & 7) ^ slot_xor(arow[i])) * 8;
     }
-    int boff;
-    {
-        const int r = wave * 8 + (lane >> 3);
+    int boff[LX];
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+        const int r = i * 64 + wave * 8 + (lane >> 3);
         const int c = (lane & 7) ^ slot_xor(r);
-        boff = ((int)(min((int64_t)r, T - 1) * D) + c * 8) * 2;
+        boff[i] = ((int)(min((int64_t)r, T - 1) * D) + c * 8) * 2;
     }
 
     // ---- issue side: the item whose stages are being loaded, and its position ----
@@ -159,7 +163,10 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
             else
                 lds_dma16(wr, la + i * 8192u, aoff[i], w_soff);
         }
-        if (wave_s < XW) lds_dma16(xr, la + (uint32_t)(W_CHUNKS * 16), boff, x_eb);
+        if (wave_s < XW) {
+#pragma unroll
+            for (int i = 0; i < LX; ++i) lds_dma16(xr, la + (uint32_t)(W_CHUNKS * 16) + i * 8192u, boff[i], x_eb);
+        }
         s_buf = (s_buf + 1 == NRING) ? 0 : s_buf + 1;
         if (x_left > 1) {  // next K-step of the item
             --x_left;
@@ -181,23 +188,25 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
         }
     };
 
-    f32x4_t acc[IB];
+    f32x4_t acc[IB][JB];
 #pragma unroll
     for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
     const int wn = wave % WN, wp = wave / WN;
     const int kq = lane >> 4;
     const int fx = slot_xor(lane & 15);
     const int arow0 = (wn * FW + (lane & 15)) * 8;
-    const int brow0 = W_CHUNKS + (wp * 16 + (lane & 15)) * 8;
+    const int brow0 = W_CHUNKS + (wp * TW + (lane & 15)) * 8;
 
     begin_item(g);
 #pragma unroll
     for (int s = 0; s < NRING; ++s) issue();
-    // this wave's loads per stage: LW, plus one X load in the first XW waves
+    // this wave's loads per stage: LW, plus LX X loads in the first XW waves
     if (wave_s < XW)
-        wait_vmcnt<(NRING - 1) * (LW + 1)>();
+        wait_vmcnt<(NRING - 1) * (LW + LX)>();
     else
         wait_vmcnt<(NRING - 1) * LW>();
     __builtin_amdgcn_s_barrier();
@@ -208,13 +217,14 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
     int c_buf = 0;
     for (;;) {
         const uint4* st = lds + c_buf * (STAGE / 16);
-        bf16x8_t fa[2][IB], fb[2];
+        bf16x8_t fa[2][IB], fb[2][JB];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int slot = (h * 4 + kq) ^ fx;
 #pragma unroll
             for (int i = 0; i < IB; ++i) fa[h][i] = __builtin_bit_cast(bf16x8_t, st[arow0 + i * 128 + slot]);
-            fb[h] = __builtin_bit_cast(bf16x8_t, st[brow0 + slot]);
+#pragma unroll
+            for (int j = 0; j < JB; ++j) fb[h][j] = __builtin_bit_cast(bf16x8_t, st[brow0 + j * 128 + slot]);
         }
         // all fragment reads in flight before the first MFMA waits for one
         __builtin_amdgcn_sched_barrier(0);
@@ -222,14 +232,16 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < IB; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][i], fb[h], acc[i], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < JB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][i], fb[h][j], acc[i][j], 0, 0, 0);
         // every read of this stage returned, the next one landed (the two after it may be in
         // flight); after the barrier this buffer takes the stage three K-steps ahead.  Vector
         // stores of an item's partial sums below only add younger operations to the count, so
         // they can only make this wait stricter, never let it pass early.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (wave_s < XW)
-            wait_vmcnt<(NRING - 2) * (LW + 1)>();
+            wait_vmcnt<(NRING - 2) * (LW + LX)>();
         else
             wait_vmcnt<(NRING - 2) * LW>();
         __builtin_amdgcn_s_barrier();
@@ -240,19 +252,24 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
             // partial sums of the item: lane holds features 4 (lane / 16) + r of each 16 x 16
             // block, token lane % 16
             const ShortItem it = short_item(c_item, KS, nN, L_tgt, kps, nk_all);
-            const int p = wp * 16 + (lane & 15);
-            if (p < T) {
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                const int p = wp * TW + j * 16 + (lane & 15);
+                if (p >= T) continue;
                 float* dst = part + ((((size_t)it.ks * L_tgt + it.t) * 2 + it.kv) * (size_t)T + p) * N;
 #pragma unroll
                 for (int i = 0; i < IB; ++i) {
                     const int n = it.n0 + wn * FW + i * 16 + kq * 4;
-                    if (n < N) *(float4*)(dst + n) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+                    if (n < N)
+                        *(float4*)(dst + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
                 }
             }
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+                for (int j = 0; j < JB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
             c_item += G;
             if (c_item >= n_items) break;
             c_left = short_item(c_item, KS, nN, L_tgt, kps, nk_all).nk;
@@ -354,8 +371,10 @@ static void launch_short_d(const MapArgs& a, const ApplyGeom& g, const SmallPlan
         launch_short<D, 16>(a, g, pl, part, s);
     else if (g.T <= 32)
         launch_short<D, 32>(a, g, pl, part, s);
-    else
+    else if (g.T <= 64)
         launch_short<D, 64>(a, g, pl, part, s);
+    else
+        launch_short<D, 128>(a, g, pl, part, s);
 }
 
 hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,

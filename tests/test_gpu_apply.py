@@ -195,15 +195,19 @@ def test_full_size_sampled(ctx, cid):
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
 
 
-# ---- short caches (T <= 64: the persistent short-cache kernel with a separate reduce) ----
+# ---- short caches (T <= 128: the persistent short-cache kernel with a separate reduce) ---
 
 SHORT = [
     # 1.5 feature tiles (H=3), 64 tokens exactly one token tile, L_tgt > L_src
     ApplyConfig(221, "short-T64-H3", 5, 7, 3, 128, 64, 2, 1.0e4, 1.0e6, "bf16", 0.5),
     # d = 64, ragged 37 tokens, continuation offset, k = 3
     ApplyConfig(222, "short-d64-T37-pos0", 4, 3, 2, 64, 37, 3, 1.0e6, 5.0e5, "bf16", 0.5, pos0=1000),
-    # 256 tokens (the largest short cache): four token tiles, K split 1
+    # 256 tokens (past the short path: the long-cache kernel), H = 8
     ApplyConfig(223, "short-T256-H8", 4, 2, 8, 128, 256, 2, 1.0e6, 1.0e6, "bf16", 0.5),
+    # ragged 100 tokens in one 128-token tile (the 3-stage ring, 2 token blocks per wave)
+    ApplyConfig(228, "short-T100-H3", 5, 7, 3, 128, 100, 2, 1.0e4, 1.0e6, "bf16", 0.5, pos0=33),
+    # exactly 128 tokens, head dim 64, k = 3
+    ApplyConfig(229, "short-T128-d64", 4, 5, 2, 64, 128, 3, 1.0e6, 5.0e5, "bf16", 0.5),
     # one head of d = 64 (N = 64, a partial feature tile), k = 5 (320 features: 5 K-steps)
     ApplyConfig(224, "short-H1-d64-k5-T129", 6, 2, 1, 64, 129, 5, 1.0e4, 1.0e4, "bf16", 0.5),
     # 320 tiles (80 target layers x K/V x 2 feature tiles) on a 256-CU device: the K reduction
@@ -221,9 +225,9 @@ def test_short_caches(ctx, cfg):
     _full_check(ctx, cfg)
 
 
-@pytest.mark.parametrize("T", [1, 16, 64])
+@pytest.mark.parametrize("T", [1, 16, 64, 128])
 def test_short_cache_full_layer_shape(ctx, T):
-    """The Qwen3 14B->32B layer shape (L 40->64, H 8, d 128, k 8) at T = 1, 16 and 64, where
+    """The Qwen3 14B->32B layer shape (L 40->64, H 8, d 128, k 8) at T = 1, 16, 64 and 128, where
     every workgroup streams two whole tiles through its ring: every row of sampled target
     layers against the oracle, and bit-identical outputs on a second call (the partial sums
     are added in a fixed order)."""
