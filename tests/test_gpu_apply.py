@@ -208,6 +208,8 @@ SHORT = [
     ApplyConfig(228, "short-T100-H3", 5, 7, 3, 128, 100, 2, 1.0e4, 1.0e6, "bf16", 0.5, pos0=33),
     # exactly 128 tokens, head dim 64, k = 3
     ApplyConfig(229, "short-T128-d64", 4, 5, 2, 64, 128, 3, 1.0e6, 5.0e5, "bf16", 0.5),
+    # 128-token tiles with 4 splits and 5 work items per workgroup (as short-many-items-T16)
+    ApplyConfig(230, "short-many-items-T100", 3, 80, 4, 128, 100, 1, 1.0e4, 1.0e6, "bf16", 0.5),
     # one head of d = 64 (N = 64, a partial feature tile), k = 5 (320 features: 5 K-steps)
     ApplyConfig(224, "short-H1-d64-k5-T129", 6, 2, 1, 64, 129, 5, 1.0e4, 1.0e4, "bf16", 0.5),
     # 320 tiles (80 target layers x K/V x 2 feature tiles) on a 256-CU device: the K reduction
