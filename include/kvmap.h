@@ -155,7 +155,10 @@ int kvmap_validate_apply(const kvmap_dims* dims, const int32_t* layer_sel,
  * Inputs must not overlap outputs; all pointers 16-byte aligned.  Asynchronous on
  * `stream` (except KVMAP_FLAG_CHECK_FINITE).  Allocates only when the context's
  * workspace or RoPE-table cache must grow (see kvmap_reserve).  In bf16 the de-rotated
- * keys are rounded to bf16 before the map (fp32 accumulation, bf16 output). */
+ * keys are rounded to bf16 before the map (fp32 accumulation, bf16 output).  bf16 caches of
+ * up to 128 tokens take a kernel that streams the maps (the apply is bound by reading W
+ * there); its fp32 partial sums live in the workspace and are added in a fixed order, so
+ * repeated calls give identical outputs. */
 int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
                 const void* src_k, const void* src_v, const int32_t* layer_sel,
                 const void* W_k, const void* b_k, const void* W_v, const void* b_v,
@@ -165,7 +168,8 @@ int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
 /* Durations (ms) of the kernels the last KVMAP_FLAG_TIMING apply on this context
  * launched, measured with HIP events recorded on the apply's stream:
  *   ms[0] RoPE-table build (0 if cached), ms[1] key de-rotation producer,
- *   ms[2] map GEMM (K and V of all target layers, one launch).
+ *   ms[2] map GEMM (K and V of all target layers: one launch; for bf16 caches of up to 128
+ *         tokens the short-cache kernel and the reduce that adds its partial sums).
  * Synchronises on the events.  n_ms must be >= 3. */
 int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
 
