@@ -71,21 +71,37 @@ __device__ __forceinline__ void lower_decode(int u, int& I, int& J) {
 
 }  // namespace
 
-// A[i][j] = M_xx[min][max] (+ lambda on the diagonal) for i, j < p; identity padding.
+// A[i][j] = M_xx[min][max] (+ lambda on the diagonal) for i, j < p; identity padding.  One
+// 64 x 64 tile (I, J) of A per workgroup: the tile is read from M_xx's upper triangle as tile
+// (min, max) -- rows of 64 consecutive floats either way -- through LDS, so that the tiles below
+// the diagonal, which are transposes, are read and written with whole rows too.
 __global__ __launch_bounds__(256) void ridge_init_a_kernel(const RidgeArgs g) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ float t[RB][RB + 1];
     const int P = g.P, p = g.p;
-    if (idx >= (int64_t)P * P) return;
+    const int nb = P / RB;
+    const int I = (int)blockIdx.x / nb, J = (int)blockIdx.x % nb;
     const float* M_xx = g.s[blockIdx.y].M_xx;
-    const int i = (int)(idx / P), j = (int)(idx - (int64_t)i * P);
-    double v;
-    if (i < p && j < p) {
-        v = (double)M_xx[(size_t)min(i, j) * p + max(i, j)];
-        if (i == j) v += g.lambda;
-    } else {
-        v = (i == j) ? 1.0 : 0.0;
+    const int tr = min(I, J) * RB, tc = max(I, J) * RB;  // source tile in the upper triangle
+    const int tid = threadIdx.x, c = tid & 63;
+    for (int r = tid >> 6; r < RB; r += 4) {
+        const int i = tr + r, j = tc + c;
+        t[r][c] = (i < p && j < p) ? M_xx[(size_t)i * p + j] : 0.f;
     }
-    sys_a(g)[idx] = v;
+    __syncthreads();
+    double* A = sys_a(g);
+    for (int r = tid >> 6; r < RB; r += 4) {
+        const int i = I * RB + r, j = J * RB + c;
+        double v;
+        if (i < p && j < p) {
+            // element (i, j) = M_xx[min][max]: in the staged tile at (i - tr, j - tc) when i <= j
+            // (the tile is (I, J) itself, or the diagonal tile's upper part), else at (j - tr, i - tc)
+            v = (i <= j) ? (double)t[i - tr][j - tc] : (double)t[j - tr][i - tc];
+            if (i == j) v += g.lambda;
+        } else {
+            v = (i == j) ? 1.0 : 0.0;
+        }
+        A[(size_t)i * P + j] = v;
+    }
 }
 
 __global__ __launch_bounds__(256) void ridge_init_b_kernel(const RidgeArgs g) {
@@ -587,7 +603,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
                                                         // panel boundary, a multiple of 4 blocks, is even)
     const unsigned un = (unsigned)n;
     const dim3 blk(256);
-    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(((int64_t)P * P + 255) / 256), un), blk, 0, s, g);
+    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(nb * nb), un), blk, 0, s, g);
     hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), blk, 0, s, g);
     // factorisation
     for (int b0 = 0; b0 < nb; b0 += kPanel) {
