@@ -151,8 +151,9 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         const int c = (lane & 7) ^ slot_xor(r);
         const int n = min(n0 + r, N - 1);
         const int64_t p = min((int64_t)(p0 + r), T - 1);
-        aoff[i] = (n * F + c * 8) * 2;
-        boff[i] = ((int)(p * D) + c * 8) * 2;
+        // byte offsets below 2^32 (N F < 2^31 and T d < 2^31 are validated): unsigned arithmetic
+        aoff[i] = (int)(((uint32_t)n * (uint32_t)F + (uint32_t)c * 8u) * 2u);
+        boff[i] = (int)(((uint32_t)p * (uint32_t)D + (uint32_t)c * 8u) * 2u);
     }
     const int nk = F / BK;
 

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
     for (int i = 0; i < LX; ++i) {
         const int r = i * 64 + wave * 8 + (lane >> 3);
         const int c = (lane & 7) ^ slot_xor(r);
-        boff[i] = ((int)(min((int64_t)r, T - 1) * D) + c * 8) * 2;
+        boff[i] = (int)(((uint32_t)min((int64_t)r, T - 1) * (uint32_t)D + (uint32_t)c * 8u) * 2u);
     }
 
     // ---- issue side: the item whose stages are being loaded, and its position ----
@@ -143,7 +143,8 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
         wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
         is_x = (const uint16_t*)(kv ? a.xv : a.xk);
 #pragma unroll
-        for (int i = 0; i < LW; ++i) aoff[i] = (min(n0 + arow[i], N - 1) * F + acol[i]) * 2;
+        for (int i = 0; i < LW; ++i)  // byte offsets below 2^32 (N F < 2^31 is validated)
+            aoff[i] = (int)(((uint32_t)min(n0 + arow[i], N - 1) * (uint32_t)F + (uint32_t)acol[i]) * 2u);
         w_soff = kt0 * SBK * 2;
         const int f0 = kt0 * SBK, per = H * D;
         x_j = __builtin_amdgcn_readfirstlane(f0 / per);
