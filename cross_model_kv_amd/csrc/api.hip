@@ -379,7 +379,7 @@ static int ensure_workspace(kvmap_ctx* c, size_t bytes) {
     return KVMAP_OK;
 }
 
-// De-rotated source keys, then (short bf16 caches) the split-K partial sums.
+// De-rotated source keys, then (short bf16 caches) the short-cache kernel's fp32 partial sums.
 static size_t derope_bytes(const kvmap_dims* d) {
     const size_t es = d->dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
     return ((size_t)d->L_src * d->H_kv * (size_t)d->T * d->head_dim * es + 255) & ~(size_t)255;

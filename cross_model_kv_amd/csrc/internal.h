@@ -61,9 +61,9 @@ struct MapArgs {
 hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 
-// Short caches (gemm_bf16_small.hip): bf16 applies with T <= kSmallT tokens take the split-K
-// path (fp32 partial sums in `part`, then a deterministic reduce with bias and target RoPE);
-// measured faster than the long-cache kernel up to 128 tokens.
+// Short caches (gemm_bf16_small.hip): bf16 applies with T <= kSmallT tokens take the persistent
+// short-cache kernel (fp32 partial sums in `part`, then a deterministic reduce with bias and
+// target RoPE); measured faster than the long-cache kernel up to 128 tokens.
 #ifndef KVMAP_SMALL_T
 #define KVMAP_SMALL_T 128
 #endif

@@ -198,7 +198,7 @@ def test_full_size_sampled(ctx, cid):
 # ---- short caches (T <= 128: the persistent short-cache kernel with a separate reduce) ---
 
 SHORT = [
-    # 1.5 feature tiles (H=3), 64 tokens exactly one token tile, L_tgt > L_src
+    # 1.5 feature tiles (H=3), 64 tokens: exactly one 64-token tile, L_tgt > L_src
     ApplyConfig(221, "short-T64-H3", 5, 7, 3, 128, 64, 2, 1.0e4, 1.0e6, "bf16", 0.5),
     # d = 64, ragged 37 tokens, continuation offset, k = 3
     ApplyConfig(222, "short-d64-T37-pos0", 4, 3, 2, 64, 37, 3, 1.0e6, 5.0e5, "bf16", 0.5, pos0=1000),
