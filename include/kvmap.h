@@ -267,7 +267,8 @@ int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_sta
 
 /* Closed-form ridge from statistics held in host memory (fp32 as kept on the device):
  *   W = (M_xx + lambda I)^-1 M_xy,  b = mean_y - mean_x W
- * solved by blocked Cholesky in float64 on `n_threads` host threads (0 = all cores).
+ * solved by blocked Cholesky in float64 on `n_threads` host threads (0 = all cores; at most one
+ * per 64 rows of p, so small systems run on fewer).
  * W_out is written OUTPUT-major [q][p] (the layout kvmap_apply takes), b_out [q], both
  * fp32 host.  M_xx is read from its upper triangle.  Returns KVMAP_ERR_NOT_SPD if the
  * factorisation meets a non-positive pivot, INVALID_ARGUMENT for lambda < 0 or NULLs. */
@@ -286,8 +287,8 @@ int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
  *   W_out  device [q][p] output-major (the layout kvmap_apply takes for one target layer),
  *   b_out  device [q], both in `dtype` (bf16: rounded to nearest even; fp32), 4-byte aligned,
  *          not overlapping each other or the state.
- * The context keeps an fp64 scratch of (P^2 + P Q + Q) * 8 bytes, P and Q being p and q rounded
- * up to multiples of 64 (576 MiB at p 8192, q 1024), allocated on first use.  Synchronous:
+ * The context keeps an fp64 scratch of (P^2 + P Q + Q + 64 P) * 8 bytes, P and Q being p and q
+ * rounded up to multiples of 128 (580 MiB at p 8192, q 1024), allocated on first use.  Synchronous:
  * returns after the solve, KVMAP_ERR_NOT_SPD if a pivot was not positive and finite (the
  * outputs are then undefined), INVALID_ARGUMENT / UNSUPPORTED on refused arguments (nothing
  * written). */
