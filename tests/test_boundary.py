@@ -134,7 +134,7 @@ def _random_stats(p, q, n, seed):
     return oracle.stats_two_pass(X, Y)
 
 
-@pytest.mark.parametrize("p,q,n", [(8, 4, 50), (64, 16, 500), (300, 40, 1000)])
+@pytest.mark.parametrize("p,q,n", [(8, 4, 50), (64, 16, 500), (300, 40, 1000), (389, 37, 1200)])
 def test_ridge_solve_host_matches_oracle(p, q, n):
     st = _random_stats(p, q, n, seed=p)
     lam = 0.01
@@ -146,6 +146,23 @@ def test_ridge_solve_host_matches_oracle(p, q, n):
     assert W.shape == (q, p)
     assert np.max(np.abs(W.T - Wr)) <= 1e-5 * max(1.0, np.max(np.abs(Wr)))
     assert np.max(np.abs(b - br)) <= 1e-5 * max(1.0, np.max(np.abs(br)))
+
+
+def test_ridge_solve_host_thread_count_and_lower_triangle():
+    # p = 3 * 128 + 5 and q = 4 * 8 + 5: ragged panel, ragged 6 x 8 register blocks on both sides.
+    # The tiles do not depend on the thread count and each is summed by one thread, so any
+    # thread count gives the same bits; only M_xx's upper triangle is read, so NaN below the
+    # diagonal changes nothing.
+    p, q, n = 389, 37, 1200
+    st = _random_stats(p, q, n, seed=7)
+    f32 = {k: (v.astype(np.float32) if isinstance(v, np.ndarray) else v) for k, v in st.items()}
+    Mxx = np.triu(f32["Mxx"])
+    W1, b1 = K.ridge_solve_host(f32["mx"], f32["my"], Mxx, f32["Mxy"], 0.01, n_threads=1)
+    Mxx_nan = Mxx.copy()
+    Mxx_nan[np.tril_indices(p, -1)] = np.nan
+    for nt in (2, 3, 8):
+        W, b = K.ridge_solve_host(f32["mx"], f32["my"], Mxx_nan, f32["Mxy"], 0.01, n_threads=nt)
+        assert np.array_equal(W, W1) and np.array_equal(b, b1), nt
 
 
 def test_ridge_solve_host_refusals():
