@@ -336,8 +336,9 @@ def main():
                     help="first run one plain 1 GiB device copy (the reference dispatch for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the mapper needs no exchange between GPUs and this build "
-              "runs on one MI355X only (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the apply shards by target layer or by tokens with no "
+              "exchange between GPUs; runs on several GPUs are not measured here",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
