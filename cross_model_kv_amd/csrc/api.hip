@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <new>
 #include <vector>
 
 #include "internal.h"
@@ -731,8 +732,13 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_host: NULL pointer");
     if (!(lambda >= 0.0) || !std::isfinite(lambda))
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve_host: lambda must be finite and >= 0");
-    if (ridge_solve_f64(p, q, mean_x, mean_y, M_xx, M_xy, lambda, W_out, b_out, n_threads))
-        return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_host: M_xx + lambda I is not positive definite");
+    int r;
+    try {  // the fp64 system takes p^2 * 8 bytes of host memory (32 GiB at p 65,536)
+        r = ridge_solve_f64(p, q, mean_x, mean_y, M_xx, M_xy, lambda, W_out, b_out, n_threads);
+    } catch (const std::bad_alloc&) {
+        return fail(KVMAP_ERR_OUT_OF_MEMORY, "kvmap_ridge_solve_host: no host memory for the fp64 system");
+    }
+    if (r) return fail(KVMAP_ERR_NOT_SPD, "kvmap_ridge_solve_host: M_xx + lambda I is not positive definite");
     return ok();
 }
 
@@ -915,7 +921,15 @@ extern "C" int kvmap_ridge_solve(kvmap_ctx* c, const kvmap_gram_state* st, doubl
     if (!W_out || !b_out) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_ridge_solve: NULL output");
     DeviceGuard g(c->device);
     const size_t p = st->p, q = st->q;
-    std::vector<float> mx(p), my(q), Mxx(p * p), Mxy(p * q);
+    std::vector<float> mx, my, Mxx, Mxy;
+    try {
+        mx.resize(p);
+        my.resize(q);
+        Mxx.resize(p * p);
+        Mxy.resize(p * q);
+    } catch (const std::bad_alloc&) {
+        return fail(KVMAP_ERR_OUT_OF_MEMORY, "kvmap_ridge_solve: no host memory for the statistics");
+    }
     hipStream_t s = (hipStream_t)stream;
     KVMAP_HIP(hipMemcpyAsync(mx.data(), st->mean_x, p * 4, hipMemcpyDeviceToHost, s));
     KVMAP_HIP(hipMemcpyAsync(my.data(), st->mean_y, q * 4, hipMemcpyDeviceToHost, s));

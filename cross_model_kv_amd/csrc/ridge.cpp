@@ -30,6 +30,7 @@
 #include <functional>
 #include <memory>
 #include <mutex>
+#include <system_error>
 #include <thread>
 #include <vector>
 
@@ -42,8 +43,15 @@ namespace {
 // (Starting threads per parallel step cost more than the small steps themselves.)
 class Pool {
   public:
-    explicit Pool(int n_threads) : n_(std::max(1, n_threads)) {
-        for (int t = 1; t < n_; ++t) workers_.emplace_back([this] { loop(); });
+    explicit Pool(int n_threads) {
+        for (int t = 1; t < n_threads; ++t) {
+            try {
+                workers_.emplace_back([this] { loop(); });
+            } catch (const std::system_error&) {
+                break;  // the system refused another thread: run on those that did start
+            }
+        }
+        n_ = (int)workers_.size() + 1;
     }
     ~Pool() {
         {
@@ -94,7 +102,7 @@ class Pool {
             if (--pending_ == 0) done_.notify_one();
         }
     }
-    const int n_;
+    int n_ = 1;
     std::vector<std::thread> workers_;
     std::mutex mu_;
     std::condition_variable start_, done_;

@@ -271,13 +271,16 @@ int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_sta
  * per 64 rows of p, so small systems run on fewer).
  * W_out is written OUTPUT-major [q][p] (the layout kvmap_apply takes), b_out [q], both
  * fp32 host.  M_xx is read from its upper triangle.  Returns KVMAP_ERR_NOT_SPD if the
- * factorisation meets a non-positive pivot, INVALID_ARGUMENT for lambda < 0 or NULLs. */
+ * factorisation meets a non-positive pivot, INVALID_ARGUMENT for lambda < 0 or NULLs,
+ * OUT_OF_MEMORY if the host cannot hold the fp64 system (p^2 + p q doubles); if the system
+ * refuses threads, the solve runs on those that did start. */
 int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x, const float* mean_y,
                            const float* M_xx, const float* M_xy, double lambda,
                            float* W_out, float* b_out, int n_threads);
 
 /* Same, from a device state: copies mean_x, mean_y, M_xx, M_xy to the host on `stream`,
- * synchronises, and solves.  Synchronous. */
+ * synchronises, and solves on all host cores.  Synchronous; OUT_OF_MEMORY also when the host
+ * cannot hold the fp32 copy of the statistics. */
 int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
                       float* W_out, float* b_out, void* stream);
 
