@@ -3,7 +3,7 @@
 // b = mean_y - mean_x W).
 //
 //   A = sym(M_xx) + lambda I  (read from M_xx's upper triangle, like the host solver), padded to a
-//       multiple of 64 with an identity block;  B = M_xy, padded with zero rows/columns
+//       multiple of 128 with an identity block;  B = M_xy, padded with zero rows/columns
 //   A = L L^T    right-looking blocked Cholesky, 64-wide blocks: factor the diagonal block and
 //                invert its factor in one workgroup, multiply the panel below it by that
 //                inverse, update the trailing lower triangle (once per panel of 4 blocks)
@@ -13,11 +13,11 @@
 //   or, for layer scoring, the in-sample R^2 of the fit pooled over groups of y columns, from
 //   the statistics alone: RSS_c = ss_y[c] - w_c . M_xy[:, c] - lambda |w_c|^2
 // A batch of up to kRidgeMaxBatch systems of one shape runs through every kernel together
-// (grid y = system): the 64-wide diagonal steps form a serial chain of about 4 P / 64 small
-// launches, which a batch pays once.  The tile updates C -= op(A) op(B) run on the fp64 matrix
-// cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their global orientation: 64 x
-// 64 tiles inside a panel, 128 x 128 tiles for the once-per-panel updates of the trailing matrix
-// and of the right-hand sides (P and Q padded to multiples of 128 for them).  A non-positive or
+// (the last grid dimension = system): the 64-wide diagonal steps form a serial chain of about
+// 4 P / 64 small launches, which a batch pays once.  The tile updates C -= op(A) op(B) run on the
+// fp64 matrix cores (v_mfma_f64_16x16x4f64), operands staged through LDS in their global
+// orientation: 64 x 64 tiles inside a panel, 128 x 128 tiles for the once-per-panel updates of
+// the trailing matrix and of the right-hand sides.  A non-positive or
 // non-finite pivot sets the system's device flag, which the host turns into KVMAP_ERR_NOT_SPD.
 
 #include <algorithm>
@@ -52,6 +52,7 @@ struct RidgeArgs {
     double lambda;
 };
 
+// Every kernel of the solve takes its system from grid y: these helpers index the scratch by blockIdx.y.
 __device__ __forceinline__ double* sys_a(const RidgeArgs& g) { return g.scratch + (size_t)blockIdx.y * g.stride; }
 __device__ __forceinline__ double* sys_b(const RidgeArgs& g) { return sys_a(g) + (size_t)g.P * g.P; }
 __device__ __forceinline__ double* sys_rss(const RidgeArgs& g) {
@@ -473,46 +474,56 @@ __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i
             }
 }
 
-// b[c] = mean_y[c] - sum_i mean_x[i] W[i][c] (fp64), and W_out[c][i] = W[i][c] in the output
-// dtype (output-major), through a 64 x 64 transpose in LDS.  Workgroup: 64 columns c x all i.
+// W_out[c][i] = W[i][c] in the output dtype (output-major): one 64 x 64 tile per workgroup,
+// through LDS, so rows of W are read and rows of W_out written as coalesced runs.
 template <bool BF16>
-__global__ __launch_bounds__(256) void ridge_finalize_kernel(const RidgeArgs g) {
+__global__ __launch_bounds__(256) void ridge_out_kernel(const RidgeArgs g) {
     __shared__ double t[RB][RB + 1];
-    __shared__ double part[4][RB];
     const RidgeSys& S = g.s[blockIdx.y];
     const double* W = sys_b(g);
     const int Q = g.Q, p = g.p, q = g.q;
-    const float* mean_x = S.mean_x;
-    void* W_out = S.W_out;
-    const int tid = threadIdx.x;
-    const int c0 = (int)blockIdx.x * RB;
-    const int cx = tid & 63, ry = tid >> 6;  // 4 row groups
+    const int i0 = (int)blockIdx.x * RB, c0 = (int)blockIdx.z * RB;  // grid: (row tiles, system, column tiles)
+    const int tid = threadIdx.x, cx = tid & 63, ry = tid >> 6;
+    for (int rr = ry; rr < RB; rr += 4) {
+        const int i = i0 + rr;
+        t[rr][cx] = (i < p) ? W[(size_t)i * Q + c0 + cx] : 0.0;
+    }
+    __syncthreads();
+    for (int cc = ry; cc < RB; cc += 4) {
+        const int c = c0 + cc, i = i0 + cx;
+        if (c < q && i < p) {
+            const double v = t[cx][cc];
+            if (BF16) ((uint16_t*)S.W_out)[(size_t)c * p + i] = (uint16_t)(pack_bf16((float)v, 0.f) & 0xffffu);
+            else ((float*)S.W_out)[(size_t)c * p + i] = (float)v;
+        }
+    }
+}
+
+// b[c] = mean_y[c] - sum_i mean_x[i] W[i][c] (fp64).  Workgroup: 16 columns x 16 row groups
+// (a wave reads 4 rows of 16 consecutive doubles, whole 128-byte lines); the row groups are
+// added in a fixed order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void ridge_bias_kernel(const RidgeArgs g) {
+    constexpr int BC = 16, RG = 16;
+    __shared__ double part[RG][BC + 1];
+    const RidgeSys& S = g.s[blockIdx.y];
+    const double* W = sys_b(g);
+    const int Q = g.Q, p = g.p, q = g.q;
+    const int tid = threadIdx.x, cx = tid % BC, ry = tid / BC;
+    const int c = (int)blockIdx.x * BC + cx;
     double dot = 0.0;
-    for (int i0 = 0; i0 < p; i0 += RB) {
-        for (int rr = ry; rr < RB; rr += 4) {
-            const int i = i0 + rr;
-            const double w = (i < p) ? W[(size_t)i * Q + c0 + cx] : 0.0;
-            t[rr][cx] = w;
-            if (i < p) dot += (double)mean_x[i] * w;
-        }
-        __syncthreads();
-        // write rows c of W_out: thread (ry, cx) writes element i0 + cx of columns c0 + ry + 4k
-        for (int cc = ry; cc < RB; cc += 4) {
-            const int c = c0 + cc, i = i0 + cx;
-            if (c < q && i < p) {
-                const double v = t[cx][cc];
-                if (BF16) ((uint16_t*)W_out)[(size_t)c * p + i] = (uint16_t)(pack_bf16((float)v, 0.f) & 0xffffu);
-                else ((float*)W_out)[(size_t)c * p + i] = (float)v;
-            }
-        }
-        __syncthreads();
+    if (c < q) {
+#pragma unroll 8
+        for (int i = ry; i < p; i += RG) dot += (double)S.mean_x[i] * W[(size_t)i * Q + c];
     }
     part[ry][cx] = dot;
     __syncthreads();
-    if (ry == 0 && c0 + cx < q) {
-        const double bv = (double)S.mean_y[c0 + cx] - (part[0][cx] + part[1][cx] + part[2][cx] + part[3][cx]);
-        if (BF16) ((uint16_t*)S.b_out)[c0 + cx] = (uint16_t)(pack_bf16((float)bv, 0.f) & 0xffffu);
-        else ((float*)S.b_out)[c0 + cx] = (float)bv;
+    if (ry == 0 && c < q) {
+        double sum = 0.0;
+        for (int r = 0; r < RG; ++r) sum += part[r][cx];
+        const double bv = (double)S.mean_y[c] - sum;
+        if (BF16) ((uint16_t*)S.b_out)[c] = (uint16_t)(pack_bf16((float)bv, 0.f) & 0xffffu);
+        else ((float*)S.b_out)[c] = (float)bv;
     }
 }
 
@@ -663,11 +674,15 @@ hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lam
     if (n < 1 || n > kRidgeMaxBatch) return hipErrorInvalidValue;
     const RidgeArgs g = make_args(n, p, q, sys, lambda, scratch);
     solve_batch(g, n, s);
-    const dim3 grid(g.Q / RB, (unsigned)n);
-    if (bf16)
-        hipLaunchKernelGGL(ridge_finalize_kernel<true>, grid, dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL(ridge_finalize_kernel<false>, grid, dim3(256), 0, s, g);
+    const dim3 tiles((unsigned)((p + RB - 1) / RB), (unsigned)n, (unsigned)(g.Q / RB));  // system on grid y
+    const dim3 cols((unsigned)((q + 15) / 16), (unsigned)n);
+    if (bf16) {
+        hipLaunchKernelGGL(ridge_out_kernel<true>, tiles, dim3(256), 0, s, g);
+        hipLaunchKernelGGL(ridge_bias_kernel<true>, cols, dim3(256), 0, s, g);
+    } else {
+        hipLaunchKernelGGL(ridge_out_kernel<false>, tiles, dim3(256), 0, s, g);
+        hipLaunchKernelGGL(ridge_bias_kernel<false>, cols, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 
