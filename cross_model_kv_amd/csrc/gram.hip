@@ -83,6 +83,22 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const void* __restri
     }
 }
 
+// sum_y part[y * stride + col] over y = 0 .. splits - 1 in float64, in that order; the loads go
+// out 16 at a time (one dependent load per split had made the finalize latency-bound).
+__device__ __forceinline__ double sum_splits(const float* __restrict__ part, int splits, int stride, int col) {
+    double s = 0.0;
+    int y = 0;
+    for (; y + 16 <= splits; y += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = part[(size_t)(y + u) * stride + col];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += (double)v[u];
+    }
+    for (; y < splits; ++y) s += (double)part[(size_t)y * stride + col];
+    return s;
+}
+
 // Reduce the split partial sums (float64, fixed order) and derive the phase's outputs.
 //   phase 0: c = sum / n_b (rounded to bf16 when round_c: the split co-moment path shifts
 //            bf16 data by a bf16 value, so that x - c is exact)
@@ -99,8 +115,7 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     const int col = blockIdx.x * blockDim.x + threadIdx.x;
     const int stride = p + q;
     if (col >= stride) return;
-    double s = 0.0;
-    for (int y = 0; y < splits; ++y) s += (double)part[(size_t)y * stride + col];
+    const double s = sum_splits(part, splits, stride, col);
     const double mean_b = s / (double)n_b;
     const bool isx = col < p;
     const int c = isx ? col : col - p;
@@ -131,8 +146,7 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(
         mean[c] = (float)(old + delta * ((double)n_b / (double)(n_old + n_b)));
     }
     if (!isx && ss_y) {
-        double s2 = 0.0;
-        for (int y = 0; y < splits; ++y) s2 += (double)part2[(size_t)y * stride + col];
+        const double s2 = sum_splits(part2, splits, stride, col);
         const double ssb = s2 - (double)n_b * mean_b * mean_b;
         const double coef = (double)n_old * (double)n_b / (double)(n_old + n_b);
         ss_y[c] = (float)((n_old == 0 ? 0.0 : (double)ss_y[c]) + ssb + coef * delta * delta);
