@@ -181,3 +181,14 @@ def test_ridge_solve_host_refusals():
         K.ridge_solve_host(mx, my, Z, Mxy, 0.0)
     W, b = K.ridge_solve_host(mx, my, Z, Mxy, 0.5)
     assert np.allclose(W, 2.0)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so, before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
