@@ -396,11 +396,99 @@ def pin_fitcheck_recovers_hidden_map(cfg=FITCHECK):
     assert 1e-7 < 1.0 - r2.mean() < 1e-5, r2.mean()
 
 
+# ---------------------------------------------------------------------------
+# Layer-selection score (KVBridge README "What ships": every source layer is scored alone by
+# the R^2 of its ridge map, averaged over target heads; the k best become the features)
+# ---------------------------------------------------------------------------
+
+def _walsh(n):
+    """Sylvester-Hadamard matrix of order n (a power of 2): its columns are +-1 Walsh functions,
+    mutually orthogonal with squared norm n; every column but the first sums to zero."""
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def _walsh_selection_case():
+    """Content caches whose scores follow by hand.  T = 16 tokens, H = 2 heads of d = 2.  Source
+    layer s (K and V alike) holds Walsh columns w[1 + 4s .. 4 + 4s] (s = 0, 1, 2); layer 3 is a
+    copy of layer 2.  One target layer:
+      K head 0: (3 w1 + w13, w2)    K head 1: (w5, w14)
+      V head 0: (w9, w15)           V head 1: (w11, w12)
+    The columns are orthogonal and centred, so at lambda -> 0 a map explains exactly the energy of
+    the target columns that lie in the source layer's span.  Per-head pooled R^2, averaged over
+    heads and then over {K, V}:
+      s0: K (10/11 + 0)/2 = 5/11, V 0      -> 5/22
+      s1: K (0 + 1/2)/2 = 1/4,    V 0      -> 1/8
+      s2: K 0, V (1/2 + 1)/2 = 3/4          -> 3/8   (= s3, an exact tie)"""
+    w = _walsh(16)
+    T, H, d = 16, 2, 2
+    src = np.zeros((1, 4, H, T, d))
+    for s in range(3):
+        for h in range(H):
+            for e in range(d):
+                src[0, s, h, :, e] = w[:, 1 + 4 * s + 2 * h + e]
+    src[0, 3] = src[0, 2]
+    tk = np.zeros((1, 1, H, T, d))
+    tv = np.zeros((1, 1, H, T, d))
+    tk[0, 0, 0, :, 0] = 3 * w[:, 1] + w[:, 13]
+    tk[0, 0, 0, :, 1] = w[:, 2]
+    tk[0, 0, 1, :, 0] = w[:, 5]
+    tk[0, 0, 1, :, 1] = w[:, 14]
+    tv[0, 0, 0, :, 0] = w[:, 9]
+    tv[0, 0, 0, :, 1] = w[:, 15]
+    tv[0, 0, 1, :, 0] = w[:, 11]
+    tv[0, 0, 1, :, 1] = w[:, 12]
+    return src, tk, tv
+
+
+def pin_selection_scores_by_hand():
+    """The selection score is the per-head pooled R^2 averaged over target heads and over {K, V}
+    (a K-only score, R^2 pooled over a whole layer or averaged per column give other numbers and
+    other choices); an exact tie goes to the lower source index; each row is kept ascending."""
+    src, tk, tv = _walsh_selection_case()
+    sel, scores = oracle.select_layers(src, src.copy(), tk, tv, 1, 1e-9)
+    want = np.array([[5 / 22, 1 / 8, 3 / 8, 3 / 8]])
+    assert np.max(np.abs(scores - want)) < 1e-8, scores
+    assert scores[0, 2] == scores[0, 3]
+    assert sel.tolist() == [[2]]
+    sel, _ = oracle.select_layers(src, src.copy(), tk, tv, 2, 1e-9)
+    assert sel.tolist() == [[2, 3]]
+    sel, _ = oracle.select_layers(src, src.copy(), tk, tv, 3, 1e-9)
+    assert sel.tolist() == [[0, 2, 3]]
+
+
+# ---------------------------------------------------------------------------
+# Comparison fields of one (layer, head, K/V) block (voidwest.dev "Before Mapping KV Caches,
+# Make Them Measurable", "measurement before mapping": cosine, MSE and max abs error per block)
+# ---------------------------------------------------------------------------
+
+def pin_block_metrics_hand_values():
+    """Fields worked out by hand on tiny blocks.  Relative errors divide by the reference (never
+    by the value compared), the MSE is a mean over elements, and the cosine keeps its sign."""
+    m = oracle.block_metrics(np.array([[3.0, 4.0], [0.0, 1.0]]), np.array([[3.0, 4.0], [0.0, 0.0]]))
+    assert m["rel_fro"] == 1.0 / 5.0       # |diff| 1 over |ref| 5
+    assert m["max_abs"] == 1.0
+    assert m["max_rel"] == 1.0 / 4.0       # over max |ref| = 4
+    assert abs(m["cosine"] - 5.0 / math.sqrt(26.0)) < 1e-15  # 25 / (sqrt(26) * 5)
+    assert m["mse"] == 1.0 / 4.0           # one unit error over 4 elements
+    ref = np.array([1.0, -2.0, 2.0])
+    m = oracle.block_metrics(2.0 * ref, ref)  # the error is ref itself
+    assert m["rel_fro"] == 1.0 and m["max_abs"] == 2.0 and m["max_rel"] == 1.0
+    assert abs(m["cosine"] - 1.0) < 1e-15 and abs(m["mse"] - 3.0) < 1e-15
+    m = oracle.block_metrics(-ref, ref)
+    assert abs(m["cosine"] + 1.0) < 1e-15 and abs(m["rel_fro"] - 2.0) < 1e-15
+    m = oracle.block_metrics(np.array([0.0, 10.0]), np.array([0.0, 1.0]))
+    assert m["rel_fro"] == 9.0 and m["max_rel"] == 9.0 and m["max_abs"] == 9.0
+
+
 ALL_PINS = [
     pin_rope_frequencies, pin_rope_matches_complex_rotation, pin_rope_with_model_frequencies,
     pin_strip_inverts_rope,
     pin_rope_identity_at_zero_and_norm, pin_recode_single_rotation, pin_identity_map_copies_cache,
     pin_identity_map_recodes_keys, pin_apply_brute_force, pin_apply_rows_and_content_space,
     pin_planner_shape_arithmetic, pin_stats_exact_rational, pin_chan_streaming_equals_two_pass,
-    pin_ridge_limits, pin_ridge_recovers_hidden_map, pin_r2_textbook, pin_fitcheck_recovers_hidden_map,
+    pin_ridge_limits, pin_ridge_recovers_hidden_map, pin_r2_textbook, pin_block_metrics_hand_values,
+    pin_selection_scores_by_hand, pin_fitcheck_recovers_hidden_map,
 ]

@@ -111,6 +111,55 @@ def _strip_same_direction(x, pos, theta):
     return K._rotate(x, K.angles(pos, theta, x.shape[-1]))
 
 
+def _select_variant(score, tie_to_higher=False, ascending=True):
+    """select_layers with one step changed: score(per-(K|V) list of (ys, yhat, H, d)) -> number."""
+    def sel_fn(src_k_c, src_v_c, tgt_k_c, tgt_v_c, k, lam):
+        L_src, H, d = src_k_c.shape[1], src_k_c.shape[2], src_k_c.shape[4]
+        L_tgt = tgt_k_c.shape[1]
+        scores = np.zeros((L_tgt, L_src))
+        for t in range(L_tgt):
+            yk, yv = K._rows_of_layer(tgt_k_c[:, t]), K._rows_of_layer(tgt_v_c[:, t])
+            for s in range(L_src):
+                fits = []
+                for xs, ys in ((K._rows_of_layer(src_k_c[:, s]), yk), (K._rows_of_layer(src_v_c[:, s]), yv)):
+                    W, b = K.ridge(K.stats_two_pass(xs, ys), lam)
+                    fits.append((ys, xs @ W + b))
+                scores[t, s] = score(fits, H, d)
+        sel = np.empty((L_tgt, k), dtype=np.int32)
+        for t in range(L_tgt):
+            key = (lambda s: (-scores[t, s], -s)) if tie_to_higher else (lambda s: (-scores[t, s], s))
+            top = sorted(range(L_src), key=key)[:k]
+            sel[t] = np.sort(top) if ascending else top
+        return sel, scores
+    return sel_fn
+
+
+def _heads_r2(ys, yh, H, d):
+    return [K.r2_pooled(ys[:, h * d:(h + 1) * d], yh[:, h * d:(h + 1) * d]) for h in range(H)]
+
+
+_score_mean = lambda fits, H, d: np.mean([r for ys, yh in fits for r in _heads_r2(ys, yh, H, d)])
+_score_k_only = lambda fits, H, d: np.mean(_heads_r2(fits[0][0], fits[0][1], H, d))
+_score_layer_pooled = lambda fits, H, d: np.mean([K.r2_pooled(ys, yh) for ys, yh in fits])
+_score_per_column = lambda fits, H, d: np.mean([K.r2_pooled(ys[:, c:c + 1], yh[:, c:c + 1])
+                                                for ys, yh in fits for c in range(ys.shape[1])])
+
+
+def _metrics_variant(rel_by_got=False, max_rel_by_got=False, mse_sum=False, cos_abs=False):
+    def fn(got, ref):
+        g = np.asarray(got, dtype=np.float64).ravel()
+        r = np.asarray(ref, dtype=np.float64).ravel()
+        diff = g - r
+        nr, ng = np.linalg.norm(r), np.linalg.norm(g)
+        cos = g @ r / (ng * nr)
+        return dict(rel_fro=float(np.linalg.norm(diff) / (ng if rel_by_got else nr)),
+                    max_abs=float(np.max(np.abs(diff))),
+                    max_rel=float(np.max(np.abs(diff)) / np.max(np.abs(g if max_rel_by_got else r))),
+                    cosine=float(abs(cos) if cos_abs else cos),
+                    mse=float(np.sum(diff ** 2) if mse_sum else np.mean(diff ** 2)))
+    return fn
+
+
 MUTANTS = {
     "rotation-sign": ("_rotate", _rotate_wrong_sign),
     "rotation-interleaved-pairs": ("_rotate", _rotate_interleaved),
@@ -127,7 +176,30 @@ MUTANTS = {
     "ridge-lambda-times-n": ("ridge", _ridge_penalise_scaled),
     "stats-not-centered": ("stats_two_pass", _two_pass_uncentered),
     "strip-not-inverse": ("strip_rope", _strip_same_direction),
+    "select-k-only-score": ("select_layers", _select_variant(_score_k_only)),
+    "select-r2-pooled-over-layer": ("select_layers", _select_variant(_score_layer_pooled)),
+    "select-r2-per-column-mean": ("select_layers", _select_variant(_score_per_column)),
+    "select-tie-to-higher-index": ("select_layers", _select_variant(_score_mean, tie_to_higher=True)),
+    "select-rows-not-ascending": ("select_layers", _select_variant(_score_mean, ascending=False)),
+    "metrics-rel-fro-over-got": ("block_metrics", _metrics_variant(rel_by_got=True)),
+    "metrics-max-rel-over-got": ("block_metrics", _metrics_variant(max_rel_by_got=True)),
+    "metrics-mse-summed": ("block_metrics", _metrics_variant(mse_sum=True)),
+    "metrics-cosine-unsigned": ("block_metrics", _metrics_variant(cos_abs=True)),
 }
+
+
+def test_select_variant_scaffold_is_faithful():
+    """The scaffold the selection mutants are built on, with the unchanged score, passes the pins
+    (so each mutant differs from the oracle only in the step it names)."""
+    import pytest as _pt
+    mp = _pt.MonkeyPatch()
+    try:
+        _patch(mp, "select_layers", _select_variant(_score_mean))
+        P.pin_selection_scores_by_hand()
+        _patch(mp, "block_metrics", _metrics_variant())
+        P.pin_block_metrics_hand_values()
+    finally:
+        mp.undo()
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
