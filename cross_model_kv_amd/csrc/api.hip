@@ -58,6 +58,19 @@ struct DeviceGuard {
 };
 
 constexpr int kMaxRopeTables = 8;
+constexpr int kSelSlots = 8;
+
+// One uploaded selection: layer_sel [L_tgt*k], the ascending list of the source layers it uses,
+// and L_src as a sentinel.  `copied` is recorded right after the upload from `host`, so the
+// staging buffer is reused only once that copy has run.
+struct SelSlot {
+    int32_t* dev = nullptr;
+    int32_t* host = nullptr;  // pinned
+    hipEvent_t copied = nullptr;
+    bool pending = false;     // `copied` recorded and maybe not yet reached
+    std::vector<int32_t> key;
+    uint64_t last_use = 0;
+};
 constexpr int kGramMaxSplits = 64;
 
 struct RopeEntry {
@@ -99,10 +112,8 @@ struct kvmap_ctx {
     uint64_t clock = 0;
     void* ws = nullptr;
     size_t ws_bytes = 0;
-    int32_t* d_sel = nullptr;     // [L_tgt*k] selection + [L_src] used-layer list
-    size_t sel_cap = 0;           // int32 entries
-    int32_t* h_sel = nullptr;     // pinned staging
-    std::vector<int32_t> sel_cache;
+    SelSlot sel[kSelSlots];       // uploaded selections (see upload_selection)
+    size_t sel_cap = 0;           // int32 entries of every slot
     unsigned int* d_count = nullptr;
     int32_t* d_zero = nullptr;    // the one-entry layer list {0} of kvmap_recode
     void* ridge = nullptr;        // fp64 factor and right-hand sides of the device ridge solve
@@ -189,8 +200,11 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipDeviceSynchronize();
     for (auto& r : c->ropes) (void)hipFree(r.tab);
     (void)hipFree(c->ws);
-    (void)hipFree(c->d_sel);
-    (void)hipHostFree(c->h_sel);
+    for (auto& sl : c->sel) {
+        (void)hipFree(sl.dev);
+        (void)hipHostFree(sl.host);
+        if (sl.copied) (void)hipEventDestroy(sl.copied);
+    }
     (void)hipFree(c->d_count);
     (void)hipFree(c->d_zero);
     (void)hipFree(c->ridge);
@@ -225,10 +239,10 @@ static int validate_rope(const kvmap_rope* r, const char* which, int64_t T, int 
     return KVMAP_OK;
 }
 
-extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_sel,
-                                    const kvmap_rope* rs, const kvmap_rope* rt) {
+// The shape and dtype checks of an apply call (everything but layer_sel and the RoPE
+// descriptors): shared by kvmap_validate_apply and kvmap_reserve.
+static int validate_dims(const kvmap_dims* d) {
     if (!d) return fail(KVMAP_ERR_INVALID_ARGUMENT, "dims is NULL");
-    if (!layer_sel) return fail(KVMAP_ERR_INVALID_ARGUMENT, "layer_sel is NULL");
     if (d->dtype != KVMAP_DTYPE_BF16 && d->dtype != KVMAP_DTYPE_F32)
         return fail(KVMAP_ERR_UNSUPPORTED, "dtype %d unknown", (int)d->dtype);
     if (d->L_src < 1 || d->L_tgt < 1 || d->H_kv < 1 || d->k < 1)
@@ -249,7 +263,15 @@ extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_se
         return fail(KVMAP_ERR_SHAPE, "T*head_dim must stay below 2^31");
     if ((int64_t)d->L_tgt * d->k >= (int64_t(1) << 24))
         return fail(KVMAP_ERR_SHAPE, "L_tgt*k too large");
-    int st = validate_rope(rs, "source", d->T, d->head_dim);
+    return KVMAP_OK;
+}
+
+extern "C" int kvmap_validate_apply(const kvmap_dims* d, const int32_t* layer_sel,
+                                    const kvmap_rope* rs, const kvmap_rope* rt) {
+    int st = validate_dims(d);
+    if (st) return st;
+    if (!layer_sel) return fail(KVMAP_ERR_INVALID_ARGUMENT, "layer_sel is NULL");
+    st = validate_rope(rs, "source", d->T, d->head_dim);
     if (st) return st;
     st = validate_rope(rt, "target", d->T, d->head_dim);
     if (st) return st;
@@ -335,10 +357,40 @@ static int get_rope_table(kvmap_ctx* c, const kvmap_rope* r, int d, int64_t T, h
     return KVMAP_OK;
 }
 
-// Upload layer_sel and the ascending list of source layers it uses; skipped when the
-// context already holds the same selection.
-static int upload_selection(kvmap_ctx* c, const kvmap_dims* d, const int32_t* layer_sel,
-                            hipStream_t s, int* n_used) {
+// Every slot holds `entries` int32 entries; growing them waits for the device (queued kernels
+// may still read the old buffers), like the workspace's growth.
+static int ensure_sel_slots(kvmap_ctx* c, size_t entries) {
+    if (entries <= c->sel_cap) return KVMAP_OK;
+    KVMAP_HIP(hipDeviceSynchronize());
+    for (auto& sl : c->sel) {
+        (void)hipFree(sl.dev);
+        (void)hipHostFree(sl.host);
+        sl.dev = nullptr;
+        sl.host = nullptr;
+        sl.key.clear();
+        sl.pending = false;
+    }
+    c->sel_cap = 0;
+    for (auto& sl : c->sel) {
+        if (!sl.copied) KVMAP_HIP(hipEventCreateWithFlags(&sl.copied, hipEventDisableTiming));
+        KVMAP_HIP(hipMalloc((void**)&sl.dev, entries * sizeof(int32_t)));
+        KVMAP_HIP(hipHostMalloc((void**)&sl.host, entries * sizeof(int32_t), hipHostMallocDefault));
+    }
+    c->sel_cap = entries;
+    return KVMAP_OK;
+}
+
+static size_t sel_entries(const kvmap_dims* d) { return (size_t)d->L_tgt * d->k + d->L_src + 1; }
+
+// The device copy of layer_sel plus the ascending list of the source layers it uses.  A
+// selection already held by a slot is reused as is; a new one goes to the least recently used
+// slot through its pinned staging buffer with an asynchronous copy on `s`, so the host never
+// waits for the stream -- unless that slot's previous upload has not run yet, i.e. the caller has
+// queued kSelSlots applies with other selections behind it.  Queued kernels that still read an
+// overwritten slot are ordered before the copy by the stream (calls sharing a context share
+// one stream, or the caller orders them).
+static int upload_selection(kvmap_ctx* c, const kvmap_dims* d, const int32_t* layer_sel, hipStream_t s,
+                            int* n_used, const int32_t** dev) {
     const size_t nsel = (size_t)d->L_tgt * d->k;
     std::vector<int32_t> want(layer_sel, layer_sel + nsel);
     std::vector<char> used(d->L_src, 0);
@@ -347,25 +399,28 @@ static int upload_selection(kvmap_ctx* c, const kvmap_dims* d, const int32_t* la
         if (used[l]) want.push_back(l);
     *n_used = (int)(want.size() - nsel);
     want.push_back(d->L_src);  // sentinel: distinguishes equal selections over different L_src
-    if (want == c->sel_cache) return KVMAP_OK;
-    if (want.size() > c->sel_cap) {
-        KVMAP_HIP(hipStreamSynchronize(s));
-        (void)hipFree(c->d_sel);
-        (void)hipHostFree(c->h_sel);
-        c->d_sel = nullptr;
-        c->h_sel = nullptr;
-        c->sel_cap = 0;
-        c->sel_cache.clear();
-        KVMAP_HIP(hipMalloc((void**)&c->d_sel, want.size() * sizeof(int32_t)));
-        KVMAP_HIP(hipHostMalloc((void**)&c->h_sel, want.size() * sizeof(int32_t), hipHostMallocDefault));
-        c->sel_cap = want.size();
-    } else {
-        // The staging buffer may still feed an earlier queued copy.
-        KVMAP_HIP(hipStreamSynchronize(s));
+    int st = ensure_sel_slots(c, sel_entries(d));
+    if (st) return st;
+    SelSlot* slot = nullptr;
+    for (auto& sl : c->sel)
+        if (sl.key == want) slot = &sl;
+    if (!slot) {
+        slot = &c->sel[0];
+        for (auto& sl : c->sel)
+            if (sl.last_use < slot->last_use) slot = &sl;
+        if (slot->pending) {
+            KVMAP_HIP(hipEventSynchronize(slot->copied));  // the staging buffer's last copy
+            slot->pending = false;
+        }
+        slot->key.clear();  // invalid until the copy below is queued
+        memcpy(slot->host, want.data(), want.size() * sizeof(int32_t));
+        KVMAP_HIP(hipMemcpyAsync(slot->dev, slot->host, want.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+        KVMAP_HIP(hipEventRecord(slot->copied, s));
+        slot->pending = true;
+        slot->key = want;
     }
-    memcpy(c->h_sel, want.data(), want.size() * sizeof(int32_t));
-    KVMAP_HIP(hipMemcpyAsync(c->d_sel, c->h_sel, want.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
-    c->sel_cache = want;
+    slot->last_use = ++c->clock;
+    *dev = slot->dev;
     return KVMAP_OK;
 }
 
@@ -398,9 +453,14 @@ static size_t workspace_bytes(const kvmap_ctx* c, const kvmap_dims* d) {
 }
 
 extern "C" int kvmap_reserve(kvmap_ctx* c, const kvmap_dims* d) {
-    if (!c || !d) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_reserve: NULL argument");
+    // the dims first: a refused shape never reaches the workspace arithmetic
+    int st = validate_dims(d);
+    if (st) return st;
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_reserve: ctx is NULL");
     DeviceGuard g(c->device);
-    int st = ensure_workspace(c, workspace_bytes(c, d));
+    st = ensure_workspace(c, workspace_bytes(c, d));
+    if (st) return st;
+    st = ensure_sel_slots(c, sel_entries(d));
     if (st) return st;
     return ok();
 }
@@ -448,16 +508,17 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     st = get_rope_table(c, rope_tgt, g.d, g.T, s, &tab_tgt, &b2);
     if (st) return st;
     int n_used = 0;
-    st = upload_selection(c, d, layer_sel, s, &n_used);
+    const int32_t* d_sel = nullptr;
+    st = upload_selection(c, d, layer_sel, s, &n_used, &d_sel);
     if (st) return st;
     st = ensure_workspace(c, workspace_bytes(c, d));
     if (st) return st;
 
     const Elem e = d->dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
     if (timing) KVMAP_HIP(hipEventRecord(c->ev[1], s));
-    KVMAP_HIP(launch_derope(e, src_k, c->ws, c->d_sel + (size_t)g.L_tgt * g.k, n_used, g, tab_src, s));
+    KVMAP_HIP(launch_derope(e, src_k, c->ws, d_sel + (size_t)g.L_tgt * g.k, n_used, g, tab_src, s));
     if (timing) KVMAP_HIP(hipEventRecord(c->ev[2], s));
-    MapArgs a{c->ws, src_v, c->d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
+    MapArgs a{c->ws, src_v, d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
     if (small_path(d))
         KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g, c->cus), (float*)((char*)c->ws + derope_bytes(d)), s));
     else if (e == Elem::BF16)

@@ -332,7 +332,9 @@ SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus) {
     SmallPlan pl;
     pl.nN = (g.N() + SBM - 1) / SBM;
     pl.nP = (int)((g.T + SBN - 1) / SBN);  // 1: the path takes T <= SBN
-    const int nk_all = g.F() / SBK;
+    // validated shapes have F = k H d >= 64, so at least one K-step; the guard keeps the
+    // split arithmetic below free of a division by zero for any other input
+    const int nk_all = std::max(1, g.F() / SBK);
     const int tiles = g.L_tgt * 2 * pl.nN * pl.nP;
     cus = std::max(1, cus);
     // The persistent kernel needs no split for parallelism; a split only evens out the work

@@ -120,8 +120,12 @@ int kvmap_version(void);
 int kvmap_create(kvmap_ctx** out, int device);
 /* Free everything the context owns (synchronises its device first). NULL is a no-op. */
 int kvmap_destroy(kvmap_ctx* ctx);
-/* Pre-allocate the workspace kvmap_apply needs for `dims` so the first apply allocates
- * nothing.  Synchronous. */
+/* Pre-allocate the workspace and the selection buffers kvmap_apply needs for `dims`, so
+ * that applies of those dims (or smaller) allocate nothing and never wait for the device
+ * to grow them.  `dims` is checked first, exactly as kvmap_validate_apply checks it
+ * (SHAPE / UNSUPPORTED / INVALID_ARGUMENT; layer_sel and the RoPE descriptors are not
+ * involved), so a zeroed or otherwise invalid struct is refused before any arithmetic on
+ * it; then a NULL ctx is INVALID_ARGUMENT.  Synchronous. */
 int kvmap_reserve(kvmap_ctx* ctx, const kvmap_dims* dims);
 
 /* ---- apply (the hot path) ---------------------------------------------------------- */
@@ -152,9 +156,17 @@ int kvmap_validate_apply(const kvmap_dims* dims, const int32_t* layer_sel,
  *   X_V[p, (j*H + h')*d + e'] = src_v[layer_sel[t][j]][h'][p][e']
  *   tgt_k[t][h][p] = rope_tgt( (X_K W_k[t]^T + b_k[t])[p, h*d : h*d + d] )
  *   tgt_v[t][h][p][e] = (X_V W_v[t]^T + b_v[t])[p, h*d + e]
- * Inputs must not overlap outputs; all pointers 16-byte aligned.  Asynchronous on
- * `stream` (except KVMAP_FLAG_CHECK_FINITE).  Allocates only when the context's
- * workspace or RoPE-table cache must grow (see kvmap_reserve).  In bf16 the de-rotated
+ * Inputs must not overlap outputs; all pointers 16-byte aligned.
+ * Asynchronous on `stream`: the host returns without waiting for the device, also when
+ * layer_sel differs from the previous call's (the context keeps the last 8 distinct
+ * selections on the device; a new one is uploaded from pinned staging with an
+ * asynchronous copy, and layer_sel is read during the call only).  The host waits only in
+ * these cases: KVMAP_FLAG_CHECK_FINITE (it reads the count back); growth of the workspace
+ * or of the selection buffers (both pre-sized by kvmap_reserve), which waits for the device
+ * before it frees the old buffers; a 9th distinct RoPE table
+ * (theta or frequency list, pos0, head_dim), which evicts the least recently used one
+ * after the device is idle; and a 9th distinct selection queued while the upload of the
+ * selection it replaces has not yet run.  In bf16 the de-rotated
  * keys are rounded to bf16 before the map (fp32 accumulation, bf16 output).  bf16 caches of
  * up to 128 tokens take a kernel that streams the maps (the apply is bound by reading W
  * there); its fp32 partial sums live in the workspace and are added in a fixed order, so
@@ -258,8 +270,15 @@ int kvmap_gram_reset(kvmap_ctx* ctx, kvmap_gram_state* st, void* stream);
 int kvmap_gram(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b, int32_t dtype,
                kvmap_gram_state* st, void* stream);
 
-/* dst <- Chan merge of dst and src (statistics of disjoint samples; same p, q).  Merging
- * an empty state is the identity.  Asynchronous on `stream`. */
+/* dst <- Chan merge of dst and src (statistics of disjoint samples; same p, q, xx_block and
+ * ss_y choice): the pairwise update kvmap_gram applies to each batch, with src as the batch
+ *   n' = n_dst + n_src,  delta = mean_src - mean_dst,  mean_dst += delta * n_src / n',
+ *   M_dst += M_src + (n_dst * n_src / n') delta_x delta_y^T   (likewise M_xx and ss_y)
+ * -- the mergeable form of the centered statistics that lets shards of calibration data be
+ * accumulated apart and combined (KVBridge README, fitting section headed "Loading": only
+ * centered statistics are kept and merged with Chan/Welford updates; "What ships": the
+ * statistics are reduced across workers).  Merging an empty state is the identity.
+ * Asynchronous on `stream`. */
 int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_state* src,
                      void* stream);
 
@@ -267,6 +286,10 @@ int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_sta
 
 /* Closed-form ridge from statistics held in host memory (fp32 as kept on the device):
  *   W = (M_xx + lambda I)^-1 M_xy,  b = mean_y - mean_x W
+ * (KVBridge README, fitting section headed "Loading": the closed-form ridge solve from the
+ * centered statistics; reactapp.top article, section "Eine lineare Bruecke reicht": the
+ * ridge demo centres x and y, adds lambda = 0.01 to the Gram and takes the intercept from the
+ * means, so the intercept is not penalised)
  * solved by blocked Cholesky in float64 on `n_threads` host threads (0 = all cores; at most one
  * per 64 rows of p, so small systems run on fewer).
  * W_out is written OUTPUT-major [q][p] (the layout kvmap_apply takes), b_out [q], both
@@ -278,13 +301,15 @@ int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x, const floa
                            const float* M_xx, const float* M_xy, double lambda,
                            float* W_out, float* b_out, int n_threads);
 
-/* Same, from a device state: copies mean_x, mean_y, M_xx, M_xy to the host on `stream`,
+/* Same solve (same passages), from a device state: copies mean_x, mean_y, M_xx, M_xy to the
+ * host on `stream`,
  * synchronises, and solves on all host cores.  Synchronous; OUT_OF_MEMORY also when the host
  * cannot hold the fp32 copy of the statistics. */
 int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
                       float* W_out, float* b_out, void* stream);
 
-/* Same solve on the device in float64 (no copy of the statistics to the host): blocked
+/* Same solve (same passages) on the device in float64 (no copy of the statistics to the
+ * host): blocked
  * Cholesky of sym(M_xx) + lambda I (read from M_xx's upper triangle) with 64-wide blocks,
  * then forward and back substitution for the q right-hand sides, then b = mean_y - mean_x W.
  *   W_out  device [q][p] output-major (the layout kvmap_apply takes for one target layer),

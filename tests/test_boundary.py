@@ -192,3 +192,21 @@ def test_bench_refuses_several_gpus():
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_reserve_checks_dims_before_anything():
+    """kvmap_reserve refuses a zeroed or unsupported kvmap_dims with a status code (it used to
+    reach the short-cache plan's arithmetic), before it looks at the context."""
+    import ctypes
+    L = K.lib()
+    zero = K.Dims(0, 0, 0, 0, 0, 0, 0)
+    assert L.kvmap_reserve(None, ctypes.byref(zero)) == K.ERR_SHAPE
+    d32 = K.Dims(1, 1, 1, 32, 1, 16, K.BF16)  # head dim 32: not built
+    assert L.kvmap_reserve(None, ctypes.byref(d32)) == K.ERR_UNSUPPORTED
+    neg = K.Dims(4, 4, -2, 128, 2, 64, K.BF16)
+    assert L.kvmap_reserve(None, ctypes.byref(neg)) == K.ERR_SHAPE
+    bad_dtype = K.Dims(4, 4, 2, 128, 2, 64, 7)
+    assert L.kvmap_reserve(None, ctypes.byref(bad_dtype)) == K.ERR_UNSUPPORTED
+    assert L.kvmap_reserve(None, None) == K.ERR_INVALID_ARGUMENT
+    good = K.Dims(4, 4, 2, 128, 2, 64, K.BF16)
+    assert L.kvmap_reserve(None, ctypes.byref(good)) == K.ERR_INVALID_ARGUMENT  # then the NULL ctx
