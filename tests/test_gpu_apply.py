@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_common import compare, to_f64
+from gpu_common import Tally, compare, to_f64
 from synth.device import apply_inputs
 from synth.workloads import APPLY_CONFIGS, ApplyConfig, b_layer, layer_sel, src_layer, to_f64 as s2f, w_layer
 
@@ -99,7 +99,7 @@ def test_qwen3_small_pair_full_layers(ctx):
     _check_sampled(cfg, inp, ok_, ov_, targets=list(range(cfg.L_tgt)), rows=rows)
 
 
-def _check_sampled(cfg, inp, ok_, ov_, targets, rows):
+def _check_sampled(cfg, inp, ok_, ov_, targets, rows, tally=None):
     rows_t = torch.as_tensor(rows, device="cuda:0")
     sel = inp["layer_sel"]
     need = sorted({int(s) for t in targets for s in sel[t]})
@@ -113,7 +113,7 @@ def _check_sampled(cfg, inp, ok_, ov_, targets, rows):
                             targets=targets)
     gk = {t: to_f64(ok_[t][:, rows_t, :]) for t in targets}
     gv = {t: to_f64(ov_[t][:, rows_t, :]) for t in targets}
-    report, worst = compare(gk, gv, ref, cfg.dtype)
+    report, worst = compare(gk, gv, ref, cfg.dtype, tally=tally)
     print(f"[apply] sampled {len(rows)} rows x {len(targets)} layers: worst {worst}", flush=True)
     assert not report, "\n".join(report[:20])
 
@@ -177,22 +177,86 @@ def test_check_finite_flag_and_refusal_leaves_outputs(ctx):
     assert torch.equal(before, ok_)
 
 
+def _block_rows(T, block=256, seed=0):
+    """One row from every 256-token block (the map GEMM's token tile), at a seeded offset inside
+    the block, plus the first and the last row of the cache."""
+    rng = np.random.default_rng([2026, 77, seed])
+    rows = [b + int(rng.integers(0, min(block, T - b))) for b in range(0, T, block)]
+    return np.unique(np.array(rows + [0, T - 1]))
+
+
 @pytest.mark.parametrize("cid", [3, 4])
 def test_full_size_sampled(ctx, cid):
     """The full Qwen3 14B->32B (T=32768) and Llama-3.1 8B->70B (T=16384) shapes, in the launch
-    configuration the bench times, checked on sampled rows of the first, last and two middle
-    target layers (rows from the first, a middle and the last token block)."""
+    configuration the bench times.
+      * Coverage: the outputs are filled with NaN before the apply, and afterwards no element of
+        either cache may be non-finite, so every output tile was written.
+      * Every target layer, K and V, every head, on one row of every 256-token block plus the
+        first and last rows: each (target layer, K|V, token block, feature tile) tile of the GEMM
+        is checked against the oracle on at least one row.
+      * Windows of 24 consecutive rows at the start, middle and end of four target layers.
+      * A second apply gives bit-identical outputs.
+    The elements with |ref| >= 8 are counted and their errors printed per block."""
     cfg = APPLY_CONFIGS[cid]
     print(f"[apply] generating {cfg.name}", flush=True)
     inp = apply_inputs(cfg, "cuda:0")
-    ok_, ov_ = _run(ctx, cfg, inp)
+    shape = (cfg.L_tgt, cfg.H, cfg.T, cfg.d)
+    ok_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    ov_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    _run(ctx, cfg, inp, out_k=ok_, out_v=ov_)
+    assert bool(torch.isfinite(ok_).all()) and bool(torch.isfinite(ov_).all()), "an output tile was not written"
     T = cfg.T
+    tally = Tally()
+    rows = _block_rows(T, seed=cid)
+    print(f"[apply] {len(rows)} rows (one per token block) x all {cfg.L_tgt} target layers", flush=True)
+    for t0 in range(0, cfg.L_tgt, 8):
+        _check_sampled(cfg, inp, ok_, ov_, list(range(t0, min(t0 + 8, cfg.L_tgt))), rows, tally)
     rows = np.unique(np.concatenate([np.arange(0, 24), np.arange(T // 2 - 12, T // 2 + 12), np.arange(T - 24, T)]))
     targets = [0, cfg.L_tgt // 3, (2 * cfg.L_tgt) // 3, cfg.L_tgt - 1]
-    _check_sampled(cfg, inp, ok_, ov_, targets, rows)
+    _check_sampled(cfg, inp, ok_, ov_, targets, rows, tally)
+    print(f"[apply] {cfg.name} total: {tally.summary()}", flush=True)
     # determinism at full size
     ok2, ov2 = _run(ctx, cfg, inp)
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
+
+
+def test_alternating_selections_queue_without_host_wait(ctx):
+    """Applies with selections the context has not seen are queued behind 30 ms of other work on
+    the same stream: the host returns while that work is still running (the selection goes up
+    through pinned staging with an asynchronous copy, not a stream synchronisation), and each
+    queued apply gives the outputs of the same apply run alone."""
+    cfg = EDGE[5]
+    inp = apply_inputs(cfg, "cuda:0")
+    sels = [np.array([[0, 5], [1, 4], [2, 3]], np.int32), np.array([[5, 0], [3, 1], [4, 2]], np.int32),
+            np.array([[1, 2], [0, 3], [5, 4]], np.int32)]
+    args = lambda sel: (inp["src_k"], inp["src_v"], sel, inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"],
+                        cfg.theta_src, cfg.theta_tgt)
+    alone = []
+    for sel in sels:  # warms the tables and the workspace too
+        alone.append(ctx.apply(*args(sel)))
+        torch.cuda.synchronize()
+    # the module's earlier tests filled the context's slots with other selections; these three
+    # must be uploaded again after 8 others have pushed them out
+    rng = np.random.default_rng([2026, 78])
+    others = set()
+    while len(others) < 8:
+        cand = tuple(int(v) for v in rng.permutation(6))
+        if all(cand != tuple(s.ravel()) for s in sels):
+            others.add(cand)
+    for o in sorted(others):
+        ctx.apply(*args(np.array(o, np.int32).reshape(3, 2)))
+    torch.cuda.synchronize()
+    a = torch.randn(8192, 8192, device="cuda:0", dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for _ in range(50):
+        a = a @ a.T.contiguous() * 1e-4  # ~30 ms of queued work ahead of the applies
+    queued = [ctx.apply(*args(sel)) for sel in (sels[0], sels[1], sels[2], sels[0])]
+    still_busy = not stream.query()
+    torch.cuda.synchronize()
+    assert still_busy, "the host waited for the stream inside kvmap_apply"
+    for (gk, gv), (rk, rv) in zip(queued, alone + alone[:1]):
+        assert torch.equal(gk, rk) and torch.equal(gv, rv)
 
 
 # ---- short caches (T <= 128: the persistent short-cache kernel with a separate reduce) ---
