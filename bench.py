@@ -321,8 +321,8 @@ def fit_driver_leg(K, n_seqs=8, T=4096, cpu=True):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fit", action="store_true", help="skip the fit-side measurement")
@@ -379,20 +379,27 @@ def main():
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup}: kernels {ctx.last_timings()} ms")
 
-    gemm_ms, derope_ms = [], []
+    # The timed steps are queued back to back with no host wait between them: one HIP event
+    # before each step on the stream, and the library's own per-launch events (it keeps the
+    # last 128 timed applies), all read after the closing synchronisation.
+    if args.steps > 128:
+        raise SystemExit("--steps is at most 128 (the library holds the events of 128 timed applies)")
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for i in range(args.steps):
+        evs[i].record(stream)
         step()
-        _, dr, gm = ctx.last_timings()  # waits for this step's last event
-        derope_ms.append(dr)
-        gemm_ms.append(gm)
-    ev1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = total_ms / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, gemm {sum(gemm_ms) / len(gemm_ms):.3f} ms, "
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+    kern = [ctx.timings(args.steps - 1 - i) for i in range(args.steps)]
+    derope_ms = [x[1] for x in kern]
+    gemm_ms = [x[2] for x in kern]
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (median {ms_median:.3f}), gemm "
+        f"{sum(gemm_ms) / len(gemm_ms):.3f} ms (median {sorted(gemm_ms)[len(gemm_ms) // 2]:.3f}), "
         f"derope {sum(derope_ms) / len(derope_ms):.3f} ms")
 
     gemm_avg_s = sum(gemm_ms) / len(gemm_ms) / 1e3
@@ -409,6 +416,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -419,7 +427,8 @@ def main():
                    "theta_src": cfg.theta_src, "theta_tgt": cfg.theta_tgt},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "map_bf16_kernel", "kernel_ms": gemm_avg_s * 1e3},
+                     "kernel": "map_bf16_kernel", "kernel_ms": gemm_avg_s * 1e3,
+                     "kernel_ms_median": sorted(gemm_ms)[len(gemm_ms) // 2]},
         "derope": {"ms": derope_avg_s * 1e3, "bytes": derope_bytes,
                    "GBps": derope_bytes / derope_avg_s / 1e9, "frac_hbm": derope_bytes / derope_avg_s / 1e9 / PEAK_HBM_GBPS},
         "cpu_baseline": None,

@@ -59,6 +59,14 @@ struct DeviceGuard {
 
 constexpr int kMaxRopeTables = 8;
 constexpr int kSelSlots = 8;
+constexpr int kTimingRing = 128;
+
+// HIP events of one KVMAP_FLAG_TIMING apply: before the RoPE tables, before the de-rotation,
+// before the map GEMM, after it.  Created on the context's first timed apply.
+struct TimingRec {
+    hipEvent_t ev[4] = {};
+    bool table_built = false;  // a RoPE table was built by that apply (else its table time is 0)
+};
 
 // One uploaded selection: layer_sel [L_tgt*k], the ascending list of the source layers it uses,
 // and L_src as a sentinel.  `copied` is recorded right after the upload from `host`, so the
@@ -122,9 +130,8 @@ struct kvmap_ctx {
     size_t gram_floats = 0;
     uint16_t* gram_split = nullptr;  // bf16 co-moment operands of one sub-batch
     size_t gram_split_elems = 0;
-    hipEvent_t ev[4] = {};
-    bool timed = false;
-    float last_ms[3] = {0, 0, 0};
+    TimingRec timing[kTimingRing];  // events of the last kTimingRing KVMAP_FLAG_TIMING applies
+    int64_t n_timed = 0;
 };
 
 int kvmap::context_device(const kvmap_ctx* c) { return c ? c->device : -1; }
@@ -174,12 +181,6 @@ extern "C" int kvmap_create(kvmap_ctx** out, int device) {
     kvmap_ctx* c = new kvmap_ctx();
     c->device = device;
     c->cus = prop.multiProcessorCount;
-    for (auto& e : c->ev) {
-        if (hipEventCreate(&e) != hipSuccess) {
-            kvmap_destroy(c);
-            return fail(KVMAP_ERR_DEVICE, "kvmap_create: hipEventCreate failed");
-        }
-    }
     const int32_t zero = 0;
     if (hipMalloc((void**)&c->d_count, sizeof(unsigned int)) != hipSuccess ||
         hipMalloc((void**)&c->d_zero, sizeof(int32_t)) != hipSuccess) {
@@ -210,8 +211,9 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipFree(c->ridge);
     (void)hipFree(c->gram);
     (void)hipFree(c->gram_split);
-    for (auto& e : c->ev)
-        if (e) (void)hipEventDestroy(e);
+    for (auto& r : c->timing)
+        for (auto& e : r.ev)
+            if (e) (void)hipEventDestroy(e);
     delete c;
     return ok();
 }
@@ -498,9 +500,13 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     if (!guard.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_apply: hipSetDevice(%d) failed", c->device);
     hipStream_t s = (hipStream_t)stream;
     const bool timing = (flags & KVMAP_FLAG_TIMING) != 0;
-    c->timed = false;
+    TimingRec& tr = c->timing[c->n_timed % kTimingRing];
+    if (timing && !tr.ev[0]) {
+        for (auto& r : c->timing)
+            for (auto& e : r.ev) KVMAP_HIP(hipEventCreate(&e));
+    }
 
-    if (timing) KVMAP_HIP(hipEventRecord(c->ev[0], s));
+    if (timing) KVMAP_HIP(hipEventRecord(tr.ev[0], s));
     float2 *tab_src = nullptr, *tab_tgt = nullptr;
     bool b1 = false, b2 = false;
     st = get_rope_table(c, rope_src, g.d, g.T, s, &tab_src, &b1);
@@ -515,9 +521,9 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     if (st) return st;
 
     const Elem e = d->dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
-    if (timing) KVMAP_HIP(hipEventRecord(c->ev[1], s));
+    if (timing) KVMAP_HIP(hipEventRecord(tr.ev[1], s));
     KVMAP_HIP(launch_derope(e, src_k, c->ws, d_sel + (size_t)g.L_tgt * g.k, n_used, g, tab_src, s));
-    if (timing) KVMAP_HIP(hipEventRecord(c->ev[2], s));
+    if (timing) KVMAP_HIP(hipEventRecord(tr.ev[2], s));
     MapArgs a{c->ws, src_v, d_sel, W_k, b_k, W_v, b_v, tab_tgt, tgt_k, tgt_v};
     if (small_path(d))
         KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g, c->cus), (float*)((char*)c->ws + derope_bytes(d)), s));
@@ -526,9 +532,9 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     else
         KVMAP_HIP(launch_map_f32(a, g, s));
     if (timing) {
-        KVMAP_HIP(hipEventRecord(c->ev[3], s));
-        c->timed = true;
-        c->last_ms[0] = (b1 || b2) ? -1.f : 0.f;  // resolved in kvmap_last_timings
+        KVMAP_HIP(hipEventRecord(tr.ev[3], s));
+        tr.table_built = b1 || b2;
+        ++c->n_timed;
     }
 
     if (flags & KVMAP_FLAG_CHECK_FINITE) {
@@ -630,19 +636,28 @@ extern "C" int kvmap_cache_rows(kvmap_ctx* c, const void* cache, int32_t L, int3
     return ok();
 }
 
-extern "C" int kvmap_last_timings(kvmap_ctx* c, float* ms, int n_ms) {
-    if (!c || !ms || n_ms < 3) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: bad arguments");
-    if (!c->timed) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: no timed apply recorded");
+extern "C" int kvmap_timings(kvmap_ctx* c, int32_t back, float* ms, int n_ms) {
+    if (!c || !ms || n_ms < 3) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_timings: bad arguments");
+    const int64_t held = std::min<int64_t>(c->n_timed, kTimingRing);
+    if (back < 0 || back >= held)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_timings: %d timed applies held, asked for number %d back",
+                    (int)held, (int)back);
     DeviceGuard g(c->device);
-    KVMAP_HIP(hipEventSynchronize(c->ev[3]));
+    const TimingRec& tr = c->timing[(c->n_timed - 1 - back) % kTimingRing];
+    KVMAP_HIP(hipEventSynchronize(tr.ev[3]));
     float t01 = 0, t12 = 0, t23 = 0;
-    KVMAP_HIP(hipEventElapsedTime(&t01, c->ev[0], c->ev[1]));
-    KVMAP_HIP(hipEventElapsedTime(&t12, c->ev[1], c->ev[2]));
-    KVMAP_HIP(hipEventElapsedTime(&t23, c->ev[2], c->ev[3]));
-    ms[0] = c->last_ms[0] < 0 ? t01 : 0.f;
+    KVMAP_HIP(hipEventElapsedTime(&t01, tr.ev[0], tr.ev[1]));
+    KVMAP_HIP(hipEventElapsedTime(&t12, tr.ev[1], tr.ev[2]));
+    KVMAP_HIP(hipEventElapsedTime(&t23, tr.ev[2], tr.ev[3]));
+    ms[0] = tr.table_built ? t01 : 0.f;
     ms[1] = t12;
     ms[2] = t23;
     return ok();
+}
+
+extern "C" int kvmap_last_timings(kvmap_ctx* c, float* ms, int n_ms) {
+    if (c && c->n_timed == 0) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_last_timings: no timed apply recorded");
+    return kvmap_timings(c, 0, ms, n_ms);
 }
 
 // ---------------------------------------------------------------------------------------

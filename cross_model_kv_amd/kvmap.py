@@ -99,6 +99,7 @@ _SIGS = {
                                    ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32]),
     "kvmap_last_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int]),
+    "kvmap_timings": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int]),
     "kvmap_recode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Rope), ctypes.POINTER(Rope),
                                     ctypes.c_void_p]),
@@ -346,6 +347,13 @@ class Context:
         """(rope_table_ms, derope_ms, map_gemm_ms) of the last FLAG_TIMING apply."""
         ms = (ctypes.c_float * 3)()
         _check(lib().kvmap_last_timings(self._h, ms, 3), "kvmap_last_timings")
+        return float(ms[0]), float(ms[1]), float(ms[2])
+
+    def timings(self, back: int):
+        """(rope_table_ms, derope_ms, map_gemm_ms) of the FLAG_TIMING apply `back` calls before the
+        last one (0 = the last; the context holds 128)."""
+        ms = (ctypes.c_float * 3)()
+        _check(lib().kvmap_timings(self._h, int(back), ms, 3), "kvmap_timings")
         return float(ms[0]), float(ms[1]), float(ms[2])
 
     def recode(self, src, theta_src: float, theta_tgt: float, pos0_src: int = 0, pos0_tgt: int | None = None,

@@ -184,6 +184,11 @@ int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
  *         tokens the short-cache kernel and the reduce that adds its partial sums).
  * Synchronises on the events.  n_ms must be >= 3. */
 int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
+/* The same durations for an earlier timed apply: back = 0 is the most recent, up to 127 back
+ * (the context keeps the events of the last 128 KVMAP_FLAG_TIMING applies), so a run of timed
+ * applies can be queued with no host wait between them and read afterwards.  INVALID_ARGUMENT
+ * when that apply is not held.  Synchronises on its events. */
+int kvmap_timings(kvmap_ctx* ctx, int32_t back, float* ms, int n_ms);
 
 /* ---- RoPE recode (identity map) ---------------------------------------------------- */
 
