@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <new>
 #include <vector>
@@ -103,6 +104,39 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------
+// The allocation-free statistics call's scratch: one file-scope device array per GPU, of a
+// fixed size, held for as long as the library is loaded.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from hipGetSymbolAddress,
+// resolved once per device with that device current (at kvmap_create) and kept per device.
+// Every use on the device -- kernel arguments -- takes that resolved address, never the name.
+// ---------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVMAP_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on `device`, which must be the current device.
+int resolve_static_scratch(int device, void** out) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices)
+        return fail(KVMAP_ERR_DEVICE, "static scratch: device %d beyond the %d the library tracks", device, kMaxDevices);
+    if (!g_scratch_dev[device]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(KVMAP_ERR_DEVICE, "static scratch: hipGetSymbolAddress on device %d: %s", device,
+                        hipGetErrorString(e));
+        g_scratch_dev[device] = ptr;
+    }
+    *out = g_scratch_dev[device];
+    return KVMAP_OK;
+}
+}  // namespace
+
 int kvmap::report(int status, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -130,6 +164,7 @@ struct kvmap_ctx {
     size_t gram_floats = 0;
     uint16_t* gram_split = nullptr;  // bf16 co-moment operands of one sub-batch
     size_t gram_split_elems = 0;
+    void* static_scratch = nullptr;  // this device's copy of `scratch` (kvmap_gram_noalloc)
     TimingRec timing[kTimingRing];  // events of the last kTimingRing KVMAP_FLAG_TIMING applies
     int64_t n_timed = 0;
 };
@@ -181,6 +216,14 @@ extern "C" int kvmap_create(kvmap_ctx** out, int device) {
     kvmap_ctx* c = new kvmap_ctx();
     c->device = device;
     c->cus = prop.multiProcessorCount;
+    {
+        const int r = resolve_static_scratch(device, &c->static_scratch);
+        if (r) {
+            const std::string msg = g_err;
+            kvmap_destroy(c);
+            return fail(r, "kvmap_create: %s", msg.c_str());
+        }
+    }
     const int32_t zero = 0;
     if (hipMalloc((void**)&c->d_count, sizeof(unsigned int)) != hipSuccess ||
         hipMalloc((void**)&c->d_zero, sizeof(int32_t)) != hipSuccess) {
@@ -703,9 +746,8 @@ static int ensure_gram_scratch(kvmap_ctx* c, int p, int q, int64_t split_rows) {
     return KVMAP_OK;
 }
 
-static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
+static GramScratch gram_scratch_at(float* base, uint16_t* split, int p, int q, int splits) {
     GramScratch sc;
-    float* base = c->gram;
     sc.part = base;
     base += (size_t)kGramMaxSplits * (p + q);
     sc.part2 = base;
@@ -716,10 +758,52 @@ static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
     sc.my = base; base += q;
     sc.dx = base; base += p;
     sc.dy = base;
-    sc.split = c->gram_split;
+    sc.split = split;
     sc.splits = splits;
     sc.max_splits = kGramMaxSplits;
     return sc;
+}
+
+static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
+    return gram_scratch_at(c->gram, c->gram_split, p, q, splits);
+}
+
+// Checks shared by kvmap_gram and kvmap_gram_noalloc; KVMAP_OK with *empty set for n_b = 0.
+static int check_gram_call(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+                           const kvmap_gram_state* st, const char* who, bool* empty) {
+    *empty = false;
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: ctx is NULL", who);
+    int r = validate_state(st, who);
+    if (r) return r;
+    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
+        return fail(KVMAP_ERR_UNSUPPORTED, "%s: dtype %d unknown", who, (int)dtype);
+    if (n_b < 0 || n_b > (int64_t(1) << 31)) return fail(KVMAP_ERR_SHAPE, "%s: n_b out of range", who);
+    if (n_b == 0) {
+        *empty = true;
+        return KVMAP_OK;
+    }
+    if (!X || !Y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL batch", who);
+    if ((((uintptr_t)X) | ((uintptr_t)Y)) & 15)
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: batch pointers must be 16-byte aligned", who);
+    return KVMAP_OK;
+}
+
+// The batch merged in sub-batches of at most `sub` rows (Chan merges compose exactly), each
+// through the scratch at fbase (floats) and split (bf16 operands).
+static int run_gram(const void* X, const void* Y, int64_t n_b, Elem e, kvmap_gram_state* st, int64_t sub,
+                    float* fbase, uint16_t* split, hipStream_t s) {
+    const size_t esz = e == Elem::BF16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < n_b; r0 += sub) {
+        const int64_t nr = std::min<int64_t>(sub, n_b - r0);
+        const int splits = (int)std::min<int64_t>(kGramMaxSplits, std::max<int64_t>(1, nr / 64));
+        const GramScratch sc = gram_scratch_at(fbase, split, st->p, st->q, splits);
+        const char* xb = (const char*)X + (size_t)r0 * st->p * esz;
+        const char* yb = (const char*)Y + (size_t)r0 * st->q * esz;
+        KVMAP_HIP(launch_gram_batch(e, xb, yb, nr, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx, st->M_xy,
+                                    st->ss_y, st->xx_block, sc, s));
+        st->n += nr;
+    }
+    return KVMAP_OK;
 }
 
 extern "C" int kvmap_gram_reset(kvmap_ctx* c, kvmap_gram_state* st, void* stream) {
@@ -739,34 +823,52 @@ extern "C" int kvmap_gram_reset(kvmap_ctx* c, kvmap_gram_state* st, void* stream
 
 extern "C" int kvmap_gram(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
                           kvmap_gram_state* st, void* stream) {
-    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: ctx is NULL");
-    int r = validate_state(st, "kvmap_gram");
-    if (r) return r;
-    if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
-        return fail(KVMAP_ERR_UNSUPPORTED, "kvmap_gram: dtype %d unknown", (int)dtype);
-    if (n_b < 0 || n_b > (int64_t(1) << 31)) return fail(KVMAP_ERR_SHAPE, "kvmap_gram: n_b out of range");
-    if (n_b == 0) return ok();
-    if (!X || !Y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: NULL batch");
-    if ((((uintptr_t)X) | ((uintptr_t)Y)) & 15)
-        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram: batch pointers must be 16-byte aligned");
+    bool empty = false;
+    int r = check_gram_call(c, X, Y, n_b, dtype, st, "kvmap_gram", &empty);
+    if (r || empty) return r ? r : ok();
     DeviceGuard g(c->device);
     const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
     const int64_t sub = e == Elem::BF16 ? std::min<int64_t>(n_b, kGramSubBatch) : n_b;
     r = ensure_gram_scratch(c, st->p, st->q, e == Elem::BF16 ? sub : 0);
     if (r) return r;
-    // sub-batches of at most kGramSubBatch rows, merged in turn (Chan merges compose exactly)
-    const size_t esz = e == Elem::BF16 ? 2 : 4;
-    for (int64_t r0 = 0; r0 < n_b; r0 += sub) {
-        const int64_t nr = std::min<int64_t>(sub, n_b - r0);
-        const int splits = (int)std::min<int64_t>(kGramMaxSplits, std::max<int64_t>(1, nr / 64));
-        const GramScratch sc = gram_scratch(c, st->p, st->q, splits);
-        const char* xb = (const char*)X + (size_t)r0 * st->p * esz;
-        const char* yb = (const char*)Y + (size_t)r0 * st->q * esz;
-        KVMAP_HIP(launch_gram_batch(e, xb, yb, nr, st->p, st->q, st->n, st->mean_x, st->mean_y, st->M_xx,
-                                    st->M_xy, st->ss_y, st->xx_block, sc, (hipStream_t)stream));
-        st->n += nr;
-    }
-    return ok();
+    r = run_gram(X, Y, n_b, e, st, sub, c->gram, c->gram_split, (hipStream_t)stream);
+    return r ? r : ok();
+}
+
+// Rows of one sub-batch that fit the static scratch next to its fixed part (0: not even 32).
+static int64_t static_scratch_rows(int p, int q, Elem e, int64_t n_b) {
+    const size_t fixed = (gram_scratch_floats(p, q, kGramMaxSplits) * sizeof(float) + 255) & ~(size_t)255;
+    if (fixed > KVMAP_STATIC_SCRATCH_BYTES) return 0;
+    if (e == Elem::F32) return n_b;  // the fp32 path keeps no per-row scratch
+    const size_t per32 = gram_split_elems(p, q, 32) * sizeof(uint16_t);  // one 32-row block
+    const int64_t blocks = (int64_t)((KVMAP_STATIC_SCRATCH_BYTES - fixed) / per32);
+    return std::min<int64_t>(std::min<int64_t>(blocks * 32, kGramSubBatch), n_b);
+}
+
+extern "C" int kvmap_gram_noalloc(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+                                  kvmap_gram_state* st, void* stream) {
+    bool empty = false;
+    int r = check_gram_call(c, X, Y, n_b, dtype, st, "kvmap_gram_noalloc", &empty);
+    if (r || empty) return r ? r : ok();
+    const Elem e = dtype == KVMAP_DTYPE_BF16 ? Elem::BF16 : Elem::F32;
+    const int64_t sub = static_scratch_rows(st->p, st->q, e, n_b);
+    if (sub < 1)
+        return fail(KVMAP_ERR_UNSUPPORTED,
+                    "kvmap_gram_noalloc: p + q = %d needs more than the %zu-byte static scratch (its fixed part is "
+                    "%zu bytes, plus %zu per 32 rows for bf16); use kvmap_gram",
+                    st->p + st->q, (size_t)KVMAP_STATIC_SCRATCH_BYTES,
+                    gram_scratch_floats(st->p, st->q, kGramMaxSplits) * sizeof(float),
+                    gram_split_elems(st->p, st->q, 32) * sizeof(uint16_t));
+    if (!c->static_scratch) return fail(KVMAP_ERR_DEVICE, "kvmap_gram_noalloc: static scratch not resolved");
+    DeviceGuard g(c->device);
+    // [0, fixed): the float scratch (split partial sums, shift, means, deltas); then the bf16
+    // operands of one sub-batch.  Every kernel writes what it reads first (padding rows of the
+    // last 32-row block included), so nothing has to be cleared between calls.
+    float* fbase = (float*)c->static_scratch;
+    const size_t fixed = (gram_scratch_floats(st->p, st->q, kGramMaxSplits) * sizeof(float) + 255) & ~(size_t)255;
+    uint16_t* split = (uint16_t*)((char*)c->static_scratch + fixed);
+    r = run_gram(X, Y, n_b, e, st, sub, fbase, split, (hipStream_t)stream);
+    return r ? r : ok();
 }
 
 extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap_gram_state* src,

@@ -105,6 +105,8 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
 // Rows per kvmap_gram sub-batch: larger batches are merged in pieces of at most this many
 // rows (the split operands' scratch and 32-bit tile offsets are sized for it).
 constexpr int64_t kGramSubBatch = 16384;
+// Bytes of the static device scratch of kvmap_gram_noalloc (one array per GPU).
+#define KVMAP_STATIC_SCRATCH_BYTES (size_t(64) << 20)
 size_t gram_split_elems(int p, int q, int64_t n_b);  // uint16 elements of `split` for n_b rows
 int gram_split_blocks(int64_t n_b, int max_splits);
 hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,

@@ -109,6 +109,8 @@ _SIGS = {
     "kvmap_gram_reset": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
     "kvmap_gram": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
+    "kvmap_gram_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.POINTER(GramStateC), ctypes.c_void_p]),
     "kvmap_gram_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(GramStateC), ctypes.POINTER(GramStateC),
                                         ctypes.c_void_p]),
     "kvmap_ridge_solve_host": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -417,6 +419,19 @@ class Context:
             raise TypeError("X and Y dtypes differ")
         _check(lib().kvmap_gram(self._h, _dev_ptr(X, "X"), _dev_ptr(Y, "Y"), int(X.shape[0]), _dtype_code(X),
                                 ctypes.byref(st.c), _stream_handle(stream, st.device)), "kvmap_gram")
+
+    def gram_noalloc(self, st: GramState, X, Y, stream=None):
+        """kvmap_gram_noalloc: kvmap_gram through the library's static device scratch (no
+        allocation by the library; batches are merged in sub-batches that fit it)."""
+        if X.dim() != 2 or Y.dim() != 2 or X.shape[0] != Y.shape[0]:
+            raise ValueError("X [n_b][p] and Y [n_b][q] must share n_b")
+        if X.shape[1] != st.p or Y.shape[1] != st.q:
+            raise ValueError("batch width does not match the state")
+        if X.dtype != Y.dtype:
+            raise TypeError("X and Y dtypes differ")
+        _check(lib().kvmap_gram_noalloc(self._h, _dev_ptr(X, "X"), _dev_ptr(Y, "Y"), int(X.shape[0]),
+                                        _dtype_code(X), ctypes.byref(st.c), _stream_handle(stream, st.device)),
+               "kvmap_gram_noalloc")
 
     def gram_merge(self, dst: GramState, src: GramState, stream=None):
         _check(lib().kvmap_gram_merge(self._h, ctypes.byref(dst.c), ctypes.byref(src.c),

@@ -275,6 +275,24 @@ int kvmap_gram_reset(kvmap_ctx* ctx, kvmap_gram_state* st, void* stream);
 int kvmap_gram(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b, int32_t dtype,
                kvmap_gram_state* st, void* stream);
 
+/* kvmap_gram for callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, checks and result as kvmap_gram,
+ * but the scratch (split partial sums, shift, means, deltas and the bf16 hi/lo operands of a
+ * sub-batch) is a static device array of KVMAP_STATIC_SCRATCH_BYTES = 64 MiB that the library
+ * holds on every GPU it runs on until the process ends; the call itself allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  bf16 batches are merged in
+ * sub-batches of as many rows (a multiple of 32, at most 16384) as fit next to the fixed part
+ * of (2 * 64 + 3) * (p + q) floats -- 1664 rows at p 8192, q 1024 -- so results match
+ * kvmap_gram bit for bit whenever a batch fits one such sub-batch, and to fp32 rounding of a
+ * different merge order otherwise; fp32 batches need no per-row scratch.  Refused with
+ * KVMAP_ERR_UNSUPPORTED (nothing done) when p + q is too large for even 32 rows (more than
+ * about 100,000 at 64 MiB).  The array is shared by every call on one GPU, from any
+ * context or thread: calls that overlap on one GPU (queued on different streams, or from
+ * two threads) race and give wrong results -- the caller orders them.  Asynchronous on
+ * `stream`; st->n is updated on the host at once. */
+int kvmap_gram_noalloc(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+                       kvmap_gram_state* st, void* stream);
+
 /* dst <- Chan merge of dst and src (statistics of disjoint samples; same p, q, xx_block and
  * ss_y choice): the pairwise update kvmap_gram applies to each batch, with src as the batch
  *   n' = n_dst + n_src,  delta = mean_src - mean_dst,  mean_dst += delta * n_src / n',
