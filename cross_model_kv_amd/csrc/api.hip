@@ -571,7 +571,7 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
     if (small_path(d))
         KVMAP_HIP(launch_map_bf16_small(a, g, map_bf16_small_plan(g, c->cus), (float*)((char*)c->ws + derope_bytes(d)), s));
     else if (e == Elem::BF16)
-        KVMAP_HIP(launch_map_bf16(a, g, s));
+        KVMAP_HIP(launch_map_bf16(a, g, c->cus, s));
     else
         KVMAP_HIP(launch_map_f32(a, g, s));
     if (timing) {

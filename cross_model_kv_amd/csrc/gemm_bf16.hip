@@ -29,6 +29,8 @@
 #include "internal.h"
 #include "lds_dma.h"
 
+#include <algorithm>
+
 namespace kvmap {
 
 namespace {
@@ -98,8 +100,8 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
 // 8 waves (two per SIMD): wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
 // tokens (w >> 1) * 64 .. + 63.
 template <int D>
-__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
-                                                       int nP, int nN) {
+__device__ __forceinline__ void map_tile(const MapArgs& a, int L_tgt, int H, int k, int64_t T,
+                                         const TileId& tl, char* smem, uint32_t lds_base) {
     constexpr int NW = 8;                  // waves
     constexpr int TW = 64;                 // tokens per wave
     constexpr int JB = TW / 16;            // 16-token MFMA blocks per wave
@@ -107,12 +109,7 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     constexpr int NW_BUF = 2, NX_BUF = 3;
     constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
     constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
-    __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
     uint4* lds = (uint4*)smem;  // W buffers 0..1, then X buffers 0..2, 2048 chunks each
-
-    TileId tl;
-    if (!decode_tile(blockIdx.x, L_tgt, nP, nN, tl)) return;
-
     const int N = H * D, F = k * N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = tl.nb * BM, p0 = tl.pb * BN;
@@ -126,7 +123,6 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     const uint64_t lbase = (uint64_t)(uintptr_t)(X + (size_t)(lane < k ? a.sel[tl.t * k + lane] : 0) * H * slab);
     const int lb_lo = (int)(uint32_t)lbase, lb_hi = (int)(uint32_t)(lbase >> 32);
     const i32x4_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
 
     // The 8 waves form two groups of 4, one wave of each group per SIMD (waves 0-3 and 4-7).
     // The groups take turns: while one group issues its 64 MFMAs of a K-step back to back, the
@@ -379,14 +375,44 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
     }
 }
 
-hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s) {
+// Persistent over tiles: workgroup b takes tiles b, b + G, b + 2G, ... of the XCD-aware order
+// (G = gridDim.x, a multiple of 8, so a workgroup's tiles are all on its own XCD and in the same
+// position of successive super-tiles).  The 32 workgroups of an XCD thus start every super-tile
+// together, so the 4 feature tiles that share a token block's X rows stay in step through
+// that XCD's L2, instead of starting whenever a compute unit frees up.
+template <int D>
+__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
+                                                       int nP, int nN, int total) {
+    constexpr int NW = 8;                  // waves
+    constexpr int TW = 64;                 // tokens per wave
+    constexpr int JB = TW / 16;            // 16-token MFMA blocks per wave
+    constexpr int TILE = STAGE_CHUNKS * 16;  // 32 KB: one operand tile of one K-step
+    constexpr int NW_BUF = 2, NX_BUF = 3;
+    constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
+    constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
+    __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
+    for (int bid = blockIdx.x; bid < total; bid += gridDim.x) {
+        TileId tl;
+        if (!decode_tile(bid, L_tgt, nP, nN, tl)) continue;
+        map_tile<D>(a, L_tgt, H, k, T, tl, smem, (uint32_t)(uintptr_t)(lds_ptr_t)smem);
+        __syncthreads();  // the next tile's loads overwrite LDS that this tile's epilogue read
+    }
+}
+
+hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, int cus, hipStream_t s) {
     const int N = g.N();
     const int nP = (int)((g.T + BN - 1) / BN), nN = (N + BM - 1) / BM;
-    const int grid = map_bf16_grid(g.L_tgt, g.T, N);
+    const int total = map_bf16_grid(g.L_tgt, g.T, N);  // a multiple of 8
+    // Persistent (one workgroup per compute unit) only when every super-tile is whole: 32 tiles,
+    // all valid.  Otherwise (caches of a few token blocks, odd head counts) the super-tiles have
+    // empty or missing slots, and a workgroup per tile keeps the work spread over the chip.
+    const int pg = nN >= 32 ? 1 : 32 / nN;
+    const bool whole = pg * nN == 32 && nP % pg == 0;
+    const int grid = whole ? std::max(8, std::min(total, (cus / 8) * 8)) : total;
     if (g.d == 128)
-        hipLaunchKernelGGL((map_bf16_kernel<128>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<128>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN, total);
     else
-        hipLaunchKernelGGL((map_bf16_kernel<64>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
+        hipLaunchKernelGGL((map_bf16_kernel<64>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN, total);
     return hipGetLastError();
 }
 

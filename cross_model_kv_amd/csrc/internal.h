@@ -58,7 +58,7 @@ struct MapArgs {
     const float2* tab_tgt;  // [T][d/2]
     void* outk; void* outv;
 };
-hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
+hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, int cus, hipStream_t s);
 hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 
 // Short caches (gemm_bf16_small.hip): bf16 applies with T <= kSmallT tokens take the persistent

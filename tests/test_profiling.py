@@ -68,3 +68,51 @@ def test_traffic_needs_the_copy_calibration(tmp_path):
     write = _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(3, gemm, 524288, [1.0])])
     with pytest.raises(SystemExit):
         profiling.traffic(fetch, write, "w", str(tmp_path / "t.json"))
+
+
+def test_traffic_of_another_kernel_by_exact_name(tmp_path):
+    """A kernel is picked by its own name (not one that merely contains it), at its largest grid,
+    and its fingerprint covers its own sources."""
+    copy = "__amd_rocclr_copyBuffer"
+    der = "void kvmap::derope_kernel<true, 128>(void const*, void*, int const*, int, int, long, float2 const*)"
+    other = "void kvmap::derope_kernel_probe<true>(void const*)"
+    fetch = _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [
+        (1, copy, 1 << 20, [(1 << 20) / 2]),
+        (2, der, 81920, [3000.0]),
+        (3, der, 2048, [5.0]),          # a short cache: smaller grid
+        (4, other, 81920, [99999.0]),   # another kernel whose name starts the same
+    ])
+    write = _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [
+        (1, copy, 1 << 20, [1 << 20]),
+        (2, der, 81920, [2500.0]),
+    ])
+    out = tmp_path / "d.json"
+    profiling.traffic(fetch, write, "wl", str(out), "derope_kernel")
+    r = json.loads(out.read_text())
+    assert r["kernel"] == "derope_kernel" and r["dispatches"] == 1
+    assert r["fetch_bytes_per_launch"] == pytest.approx(3000.0 * 1024 * 2.0)
+    assert r["write_bytes_per_launch"] == pytest.approx(2500.0 * 1024)
+    assert r["kernel_code_fingerprint"] == profiling.kernel_fingerprint(profiling.KERNEL_SOURCES["derope_kernel"])
+    assert r["kernel_code_fingerprint"] != profiling.kernel_fingerprint()
+
+
+def test_mfma_summary_clock_and_busy_share(tmp_path):
+    """Clock = GRBM_GUI_ACTIVE per XCD over the dispatch's duration; busy share = matrix-pipe busy
+    cycles over (cycles per XCD x 1024 SIMDs); the workload's largest grid only."""
+    k = "void kvmap::gram_x3_kernel(unsigned short const*)"
+    path = tmp_path / "m.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+                               "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d, grid, grbm, busy in ((5, 4096, 8 * 2.0e6, 0.5 * 2.0e6 * 1024), (6, 512, 8 * 10.0, 1.0)):
+            # 1 ms at 2.0 GHz; the small-grid dispatch is left out
+            for name, v in (("GRBM_GUI_ACTIVE", grbm), ("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("SQ_INSTS_MFMA", 77.0)):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Grid_Size": grid, "Counter_Name": name,
+                            "Counter_Value": v, "Start_Timestamp": 1_000_000, "End_Timestamp": 2_000_000})
+    out = tmp_path / "m.json"
+    profiling.mfma(str(path), "wl", str(out), "gram_x3_kernel")
+    r = json.loads(out.read_text())
+    assert r["dispatches"] == 1
+    assert r["clock_GHz"] == pytest.approx(2.0)
+    assert r["mfma_busy_share"] == pytest.approx(0.5)
