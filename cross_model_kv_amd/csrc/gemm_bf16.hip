@@ -16,10 +16,8 @@
 //   * K-steps of 64 features, so every tile row is one whole 128-byte line; the stages are
 //     filled straight from HBM by buffer_load ... lds into two LDS rings, 2 stages for W and
 //     3 for X (5 x 32 KB), with 16-byte chunks XOR-swizzled by row so the MFMA fragment
-//     reads are bank-conflict free;
-//   * the two groups of 4 waves (one wave of each per SIMD) take turns: one issues a K-step's
-//     MFMAs back to back while the other reads its next fragments and issues the loads, so no
-//     memory instruction ever sits between a wave's MFMAs;
+//     reads are bank-conflict free; one barrier per K-step, with W fetched one K-step and
+//     X two K-steps ahead of the step being computed;
 //   * tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD walks
 //     "super-tiles" of 8 token blocks x 4 feature tiles of one (t, K|V), so the A rows and
 //     the W slab each tile needs are shared through that XCD's L2, and the 8 XCDs work on
@@ -28,8 +26,6 @@
 #include "common.h"
 #include "internal.h"
 #include "lds_dma.h"
-
-#include <algorithm>
 
 namespace kvmap {
 
@@ -92,24 +88,44 @@ int map_bf16_grid(int L_tgt, int64_t T, int N) {
 // Software pipeline over K-steps of 64 features (one 128-byte line per tile row, so every
 // 8 lanes of a load cover a whole cache line).  LDS holds two rings of 32 KB tile buffers:
 // a 2-deep ring for the W tile and a 3-deep ring for the gathered X tile (160 KB), filled
-// by buffer_load_dwordx4 ... lds; the schedule is the ping-pong of the two wave groups
-// described in the kernel.  X -- which misses to HBM on its first touch -- is requested
-// about 1.5 K-steps before it is needed and W, which the other token blocks of the
-// super-tile keep in L2, one.
+// by buffer_load_dwordx4 ... lds.  A K-step is two substeps of 32 MFMAs per wave (8 x 4
+// blocks of 16 x 16, 32 features deep), one barrier between them.  Each substep is
+// written as 8 chunks (the 4 MFMAs of one A block, the fragment reads of the other
+// substep's A block and, in 4 of them, of a B block), fenced off from each other, so that
+// single loads can sit between chosen chunks and no burst of loads ever stalls a wave's
+// MFMA issue:
+//   * first substep of K-step kt: MFMAs of its first 32 features; fragment reads of its
+//     second 32; the 4 loads of X(kt+2), one every other chunk, into the X buffer that
+//     K-step kt-1 used (freed at the last barrier).
+//   * wait until this wave's W(kt+1) and X(kt+1) have landed (only X(kt+2) may still be in
+//     flight), barrier: K-step kt+1 is visible everywhere and every read of K-step kt is done.
+//   * second substep: MFMAs of the second 32 features of K-step kt; fragment reads of the
+//     first 32 of K-step kt+1; the 4 loads of W(kt+2), one every other chunk, into the W
+//     buffer of K-step kt.
+// X -- which misses to HBM on its first touch -- is thus requested about 1.5 K-steps before
+// it is needed and W, which the other token blocks of the super-tile keep in L2, one.
+// Every K-step issues exactly one W and one X stage in the same order, so every wait count
+// is a constant.
 //
 // 8 waves (two per SIMD): wave w computes features (w & 1) * 128 .. + 127 (whole heads) of
 // tokens (w >> 1) * 64 .. + 63.
 template <int D>
-__device__ __forceinline__ void map_tile(const MapArgs& a, int L_tgt, int H, int k, int64_t T,
-                                         const TileId& tl, char* smem, uint32_t lds_base) {
+__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
+                                                       int nP, int nN) {
     constexpr int NW = 8;                  // waves
     constexpr int TW = 64;                 // tokens per wave
     constexpr int JB = TW / 16;            // 16-token MFMA blocks per wave
+    constexpr int LPO = 4;                 // loads per wave per operand per stage (2048 chunks / 64 lanes / NW)
     constexpr int TILE = STAGE_CHUNKS * 16;  // 32 KB: one operand tile of one K-step
     constexpr int NW_BUF = 2, NX_BUF = 3;
     constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
     constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
+    __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
     uint4* lds = (uint4*)smem;  // W buffers 0..1, then X buffers 0..2, 2048 chunks each
+
+    TileId tl;
+    if (!decode_tile(blockIdx.x, L_tgt, nP, nN, tl)) return;
+
     const int N = H * D, F = k * N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = tl.nb * BM, p0 = tl.pb * BN;
@@ -123,39 +139,84 @@ __device__ __forceinline__ void map_tile(const MapArgs& a, int L_tgt, int H, int
     const uint64_t lbase = (uint64_t)(uintptr_t)(X + (size_t)(lane < k ? a.sel[tl.t * k + lane] : 0) * H * slab);
     const int lb_lo = (int)(uint32_t)lbase, lb_hi = (int)(uint32_t)(lbase >> 32);
     const i32x4_t wr = make_rsrc(W, (uint32_t)((size_t)N * F * 2));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+    const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-    // The 8 waves form two groups of 4, one wave of each group per SIMD (waves 0-3 and 4-7).
-    // The groups take turns: while one group issues its 64 MFMAs of a K-step back to back, the
-    // other reads its fragments of the next K-step from LDS and issues global loads; one
-    // barrier ends every such phase.  Group 0 runs one phase ahead of group 1:
-    //   phase 2kt     group 0: loads W(kt+1), reads K-step kt    group 1: MFMAs of K-step kt-1
-    //   phase 2kt+1   group 0: MFMAs of K-step kt                 group 1: loads X(kt+2), reads kt
-    // so each SIMD's matrix pipe is fed by one wave's run of independent MFMAs at a time, and
-    // no load or LDS read is ever issued between them.  Group 0 loads the W stages (8 loads per
-    // wave per stage), group 1 the X stages.  Rings: W 2 deep, X 3 deep (160 KB).  W(kt+1)
-    // goes into the buffer that K-step kt-1 used, free once group 1 read it in phase 2kt-1;
-    // X(kt+2) into K-step kt-1's, also free.  Stage kt+1 is complete at the barrier ending
-    // phase 2kt+1: group 0 waits for its W(kt+1) at the end of its MFMA phase, group 1 for its
-    // X(kt+1) at the end of its read phase (only X(kt+2) may still be in flight).  Group 1
-    // passes one extra barrier first (phase 0, when only group 0 works), group 0 one last.
-    constexpr int LPG = 8;  // loads per wave per stage of its group's operand (2048 chunks / 256 lanes)
-    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2), wig = wave & 3;  // uniform per wave
-    const uint32_t wig_s = __builtin_amdgcn_readfirstlane(wig);
-    // Loads: LDS slot u = i*256 + wig*64 + lane of a tile buffer holds row u/8, chunk
+    // Loads: LDS slot u = i*64*NW + wave*64 + lane of a tile buffer holds row u/8, chunk
     // (u%8) ^ slot_xor(row).  Byte offsets within one K-step, fixed for the whole loop.
-    int loff[LPG];
+    int aoff[LPO], boff[LPO];
 #pragma unroll
-    for (int i = 0; i < LPG; ++i) {
-        const int r = i * 32 + wig * 8 + (lane >> 3);
+    for (int i = 0; i < LPO; ++i) {
+        const int r = i * 8 * NW + wave * 8 + (lane >> 3);
         const int c = (lane & 7) ^ slot_xor(r);
         const int n = min(n0 + r, N - 1);
         const int64_t p = min((int64_t)(p0 + r), T - 1);
         // byte offsets below 2^32 (N F < 2^31 and T d < 2^31 are validated): unsigned arithmetic
-        loff[i] = grp == 0 ? (int)(((uint32_t)n * (uint32_t)F + (uint32_t)c * 8u) * 2u)
-                           : (int)(((uint32_t)p * (uint32_t)D + (uint32_t)c * 8u) * 2u);
+        aoff[i] = (int)(((uint32_t)n * (uint32_t)F + (uint32_t)c * 8u) * 2u);
+        boff[i] = (int)(((uint32_t)p * (uint32_t)D + (uint32_t)c * 8u) * 2u);
     }
     const int nk = F / BK;
 
+    // Issue state of each ring: next buffer, and for W the byte offset of the next K-step,
+    // for X the address of the gathered slab (head h of selected layer j, a [T][d] block)
+    // and the byte offset of the K-step's 64 features in its rows.  Advanced with adds and
+    // selects only, so the loop body has no branches.  Past the last K-step the W offset
+    // and j stop at their last values: the extra stages that the branch-free pipeline loads
+    // at the end repeat the last one, stay in bounds and are never read.
+    //
+    // Each stage's issue is planned (buffer, offsets, descriptor: scalar arithmetic only)
+    // in a chunk before the ones that issue its loads.
+    struct WIssue {
+        uint32_t la;
+        int soff;
+    };
+    struct XIssue {
+        i32x4_t rsrc;
+        uint32_t la;
+        int soff;
+    };
+    const int w_last = (nk - 1) * BK * 2;
+    int w_buf = 0, w_soff = 0;
+    int x_buf = 0, x_eb = 0, x_h = 0, x_j = 0;
+    uint32_t x_lo = (uint32_t)__builtin_amdgcn_readlane(lb_lo, 0);  // slab address, two halves
+    uint32_t x_hi = (uint32_t)__builtin_amdgcn_readlane(lb_hi, 0);
+    auto plan_w = [&]() {
+        const WIssue r = {lds_base + (uint32_t)w_buf * TILE + wave_s * 1024u, w_soff};
+        w_buf = (w_buf + 1 == NW_BUF) ? 0 : w_buf + 1;
+        w_soff = min(w_soff + BK * 2, w_last);
+        return r;
+    };
+    auto plan_x = [&]() {
+        const i32x4_t rs = {(int)x_lo, (int)x_hi, (int)slab_bytes, 0x00020000};
+        const XIssue r = {rs, lds_base + (uint32_t)(NW_BUF + x_buf) * TILE + wave_s * 1024u, x_eb};
+        x_buf = (x_buf + 1 == NX_BUF) ? 0 : x_buf + 1;
+        x_eb += BK * 2;
+        const int we = (x_eb == D * 2);  // next head
+        x_eb = we ? 0 : x_eb;
+        x_h += we;
+        const int wh = (x_h == H);  // next selected layer
+        x_h = wh ? 0 : x_h;
+        x_j = min(x_j + wh, k - 1);
+        const uint32_t a_lo = x_lo + (we ? slab_bytes : 0u);
+        const uint32_t a_hi = x_hi + (a_lo < x_lo ? 1u : 0u);
+        x_lo = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_lo, x_j), a_lo);
+        x_hi = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j), a_hi);
+        return r;
+    };
+    // load i (of LPO) of a stage
+    auto issue_w1 = [&](const WIssue& r, int i) { lds_dma16(wr, r.la + i * 1024 * NW, aoff[i], r.soff); };
+    auto issue_x1 = [&](const XIssue& r, int i) { lds_dma16(r.rsrc, r.la + i * 1024 * NW, boff[i], r.soff); };
+    auto issue_w = [&](const WIssue& r) {
+#pragma unroll
+        for (int i = 0; i < LPO; ++i) issue_w1(r, i);
+    };
+    auto issue_x = [&](const XIssue& r) {
+#pragma unroll
+        for (int i = 0; i < LPO; ++i) issue_x1(r, i);
+    };
+
+    // v_mfma_f32_16x16x32_bf16 blocks: IB = 8 blocks of 16 features x JB blocks of 16 tokens.
+    // (Per FLOP it moves half the accumulator registers of the 32 x 32 x 16 form.)
     constexpr int IB = 8;
     f32x4_t acc[IB][JB];
 #pragma unroll
@@ -166,102 +227,77 @@ __device__ __forceinline__ void map_tile(const MapArgs& a, int L_tgt, int H, int
             for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
     const int wn = wave & 1, wp = wave >> 1;
-    const int kq = lane >> 4;
-    const int fx = slot_xor(lane & 15);
-    const int arow = (wn * 128 + (lane & 15)) * 8;
-    const int brow = (wp * TW + (lane & 15)) * 8;
-    bf16x8_t fa[2][IB], fb[2][JB];
-    auto read_stage = [&](int wb, int xb) {
+    const int kq = lane >> 4;                       // which 8-feature quarter of a 32-feature substep
+    const int fx = slot_xor(lane & 15);             // rows read by this lane: r % 16 = lane % 16
+    const int arow = (wn * 128 + (lane & 15)) * 8;  // chunk index of the lane's first A row
+    const int brow = (wp * TW + (lane & 15)) * 8;   // ... and of its first B row
+
+    // Fragments of substep ks (0, 1) of a K-step: lane holds row (lane % 16) + 16 i of A block
+    // i (B block j), features 32 ks + 8 (lane / 16) .. + 7 of the K-step.
+    auto rd_a = [&](int wb, int ks, int i, bf16x8_t* fa) {
         const uint4* la = lds + wb * STAGE_CHUNKS;
+        fa[i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + ((ks * 4 + kq) ^ fx)]);
+    };
+    auto rd_b = [&](int xb, int ks, int j, bf16x8_t* fb) {
         const uint4* lb = lds + (NW_BUF + xb) * STAGE_CHUNKS;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int i = 0; i < IB; ++i) fa[ks][i] = __builtin_bit_cast(bf16x8_t, la[arow + i * 128 + ((ks * 4 + kq) ^ fx)]);
-#pragma unroll
-            for (int j = 0; j < JB; ++j) fb[ks][j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + ((ks * 4 + kq) ^ fx)]);
-        }
+        fb[j] = __builtin_bit_cast(bf16x8_t, lb[brow + j * 128 + ((ks * 4 + kq) ^ fx)]);
     };
-    auto mfma_stage = [&]() {
-        __builtin_amdgcn_s_setprio(1);
+    auto mrow = [&](const bf16x8_t* fa, const bf16x8_t* fb, int i) {  // the MFMAs of A block i
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < IB; ++i)
-#pragma unroll
-                for (int j = 0; j < JB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
+        for (int j = 0; j < JB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
+    // All waves' loads of a stage are visible once each wave has waited for its own (vmcnt
+    // counts the later stages still in flight) and the waves have met at the barrier.  A
+    // plain s_barrier: a release fence would add a vmcnt(0) that drains the pipeline.
     auto sync = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");  // no LDS read moves above the barrier
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (grp == 0) {
-        // W stages: buffer kt % 2, byte offset kt * 128 of every W row (the last K-step's
-        // offset repeated past the end: those stages stay in bounds and are never read)
-        const int w_last = (nk - 1) * BK * 2;
-        auto issue_w = [&](int kt) {
-            const uint32_t la = lds_base + (uint32_t)(kt & 1) * TILE + wig_s * 1024u;
-            const int soff = min(kt * BK * 2, w_last);
+    // prologue: W(0) X(0) W(1) X(1); K-step 0 is complete once only W(1) X(1) remain
+    issue_w(plan_w());
+    issue_x(plan_x());
+    issue_w(plan_w());
+    issue_x(plan_x());
+    XIssue x_next = plan_x();  // X(2), issued during K-step 0
+    WIssue w_next;             // W(kt+2), planned during K-step kt
+    bf16x8_t fa0[IB], fb0[JB], fa1[IB], fb1[JB];
+    wait_vmcnt<2 * LPO>();
+    sync();
+    int cw = 0, cx = 0;  // ring buffers of the K-step being computed
 #pragma unroll
-            for (int i = 0; i < LPG; ++i) lds_dma16(wr, la + i * 4096, loff[i], soff);
-        };
-        issue_w(0);
-        wait_vmcnt<0>();
-        sync();  // stage 0 complete
-        for (int kt = 0; kt < nk; ++kt) {
-            issue_w(kt + 1);
-            read_stage(kt & 1, kt % 3);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            sync();
-            mfma_stage();
-            wait_vmcnt<0>();  // W(kt+1) landed
-            sync();
-        }
-        sync();  // group 1's last MFMA phase
-    } else {
-        // X stages: buffer kt % 3, the gathered slab (head h of selected layer j: a [T][d]
-        // block) and the byte offset of the K-step's 64 features in its rows, advanced with
-        // adds and selects only; past the last K-step j stays at its last value.
-        int x_buf = 0, x_eb = 0, x_h = 0, x_j = 0;
-        uint32_t x_lo = (uint32_t)__builtin_amdgcn_readlane(lb_lo, 0);
-        uint32_t x_hi = (uint32_t)__builtin_amdgcn_readlane(lb_hi, 0);
-        auto issue_x = [&]() {
-            const i32x4_t rs = {(int)x_lo, (int)x_hi, (int)slab_bytes, 0x00020000};
-            const uint32_t la = lds_base + (uint32_t)(NW_BUF + x_buf) * TILE + wig_s * 1024u;
+    for (int i = 0; i < IB; ++i) {
+        rd_a(cw, 0, i, fa0);
+        if (i < JB) rd_b(cx, 0, i, fb0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-            for (int i = 0; i < LPG; ++i) lds_dma16(rs, la + i * 4096, loff[i], x_eb);
-            x_buf = (x_buf + 1 == NX_BUF) ? 0 : x_buf + 1;
-            x_eb += BK * 2;
-            const int we = (x_eb == D * 2);  // next head
-            x_eb = we ? 0 : x_eb;
-            x_h += we;
-            const int wh = (x_h == H);  // next selected layer
-            x_h = wh ? 0 : x_h;
-            x_j = min(x_j + wh, k - 1);
-            const uint32_t a_lo = x_lo + (we ? slab_bytes : 0u);
-            const uint32_t a_hi = x_hi + (a_lo < x_lo ? 1u : 0u);
-            x_lo = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_lo, x_j), a_lo);
-            x_hi = uniform_select(wh, (uint32_t)__builtin_amdgcn_readlane(lb_hi, x_j), a_hi);
-        };
-        issue_x();  // X(0)
-        issue_x();  // X(1)
-        wait_vmcnt<LPG>();
-        sync();  // stage 0 complete
-        sync();  // phase 0: group 0 reads stage 0
-        for (int kt = 0; kt < nk; ++kt) {
-            issue_x();  // X(kt+2)
-            read_stage(kt & 1, kt % 3);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            wait_vmcnt<LPG>();  // X(kt+1) landed
-            sync();
-            mfma_stage();
-            sync();
+        for (int i = 0; i < IB; ++i) {
+            rd_a(cw, 1, i, fa1);
+            if (i < JB) rd_b(cx, 1, i, fb1);
+            mrow(fa0, fb0, i);
+            if (i & 1) issue_x1(x_next, i >> 1);  // X(kt+2) -> X buffer of K-step kt-1
+            if (i == 2) w_next = plan_w();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<LPO>();
+        sync();
+        const int cw1 = (cw + 1 == NW_BUF) ? 0 : cw + 1;
+        const int cx1 = (cx + 1 == NX_BUF) ? 0 : cx + 1;
+        // (after the last K-step this reads buffers that are never used)
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+            if ((i & 1) == 0) issue_w1(w_next, i >> 1);  // W(kt+2) -> W buffer of K-step kt
+            rd_a(cw1, 0, i, fa0);
+            if (i < JB) rd_b(cx1, 0, i, fb0);
+            mrow(fa1, fb1, i);
+            if (i == 3) x_next = plan_x();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        cw = cw1;
+        cx = cx1;
     }
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
     __syncthreads();  // every wave is done reading the pipeline buffers
@@ -375,44 +411,14 @@ __device__ __forceinline__ void map_tile(const MapArgs& a, int L_tgt, int H, int
     }
 }
 
-// Persistent over tiles: workgroup b takes tiles b, b + G, b + 2G, ... of the XCD-aware order
-// (G = gridDim.x, a multiple of 8, so a workgroup's tiles are all on its own XCD and in the same
-// position of successive super-tiles).  The 32 workgroups of an XCD thus start every super-tile
-// together, so the 4 feature tiles that share a token block's X rows stay in step through
-// that XCD's L2, instead of starting whenever a compute unit frees up.
-template <int D>
-__global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int H, int k, int64_t T,
-                                                       int nP, int nN, int total) {
-    constexpr int NW = 8;                  // waves
-    constexpr int TW = 64;                 // tokens per wave
-    constexpr int JB = TW / 16;            // 16-token MFMA blocks per wave
-    constexpr int TILE = STAGE_CHUNKS * 16;  // 32 KB: one operand tile of one K-step
-    constexpr int NW_BUF = 2, NX_BUF = 3;
-    constexpr int MAIN_BYTES = (NW_BUF + NX_BUF) * TILE;
-    constexpr int EPI_BYTES = NW * TW * EPI_ROW * 4;
-    __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
-    for (int bid = blockIdx.x; bid < total; bid += gridDim.x) {
-        TileId tl;
-        if (!decode_tile(bid, L_tgt, nP, nN, tl)) continue;
-        map_tile<D>(a, L_tgt, H, k, T, tl, smem, (uint32_t)(uintptr_t)(lds_ptr_t)smem);
-        __syncthreads();  // the next tile's loads overwrite LDS that this tile's epilogue read
-    }
-}
-
-hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, int cus, hipStream_t s) {
+hipError_t launch_map_bf16(const MapArgs& a, const ApplyGeom& g, int /*cus*/, hipStream_t s) {
     const int N = g.N();
     const int nP = (int)((g.T + BN - 1) / BN), nN = (N + BM - 1) / BM;
-    const int total = map_bf16_grid(g.L_tgt, g.T, N);  // a multiple of 8
-    // Persistent (one workgroup per compute unit) only when every super-tile is whole: 32 tiles,
-    // all valid.  Otherwise (caches of a few token blocks, odd head counts) the super-tiles have
-    // empty or missing slots, and a workgroup per tile keeps the work spread over the chip.
-    const int pg = nN >= 32 ? 1 : 32 / nN;
-    const bool whole = pg * nN == 32 && nP % pg == 0;
-    const int grid = whole ? std::max(8, std::min(total, (cus / 8) * 8)) : total;
+    const int grid = map_bf16_grid(g.L_tgt, g.T, N);
     if (g.d == 128)
-        hipLaunchKernelGGL((map_bf16_kernel<128>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN, total);
+        hipLaunchKernelGGL((map_bf16_kernel<128>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     else
-        hipLaunchKernelGGL((map_bf16_kernel<64>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN, total);
+        hipLaunchKernelGGL((map_bf16_kernel<64>), dim3(grid), dim3(512), 0, s, a, g.L_tgt, g.H, g.k, g.T, nP, nN);
     return hipGetLastError();
 }
 
