@@ -42,22 +42,24 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3                    # dense fp32 matrix peak
 PEAK_FP16_TFLOPS = PEAK_BF16_TFLOPS              # dense fp16 matrix peak (same as bf16)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "map_bf16_traffic.json")
+DEROPE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "derope_traffic.json")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def traffic_entry(cfg_name):
-    """HBM bytes per launch of the map GEMM from the committed counter summary, if that summary
-    was taken on the current kernel code and this workload; else None."""
-    from cross_model_kv_amd.profiling import kernel_fingerprint
+def traffic_entry(cfg_name, path=TRAFFIC_FILE, kernel="map_bf16_kernel"):
+    """HBM bytes per launch of a kernel from its committed counter summary, if that summary was
+    taken on the kernel's current code and this workload; else None."""
+    from cross_model_kv_amd.profiling import KERNEL_SOURCES, kernel_fingerprint
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_code_fingerprint") != kernel_fingerprint() or t.get("workload") != cfg_name:
+    if (t.get("kernel") != kernel or t.get("kernel_code_fingerprint") != kernel_fingerprint(KERNEL_SOURCES[kernel])
+            or t.get("workload") != cfg_name):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -430,7 +432,8 @@ def main():
                      "kernel": "map_bf16_kernel", "kernel_ms": gemm_avg_s * 1e3,
                      "kernel_ms_median": sorted(gemm_ms)[len(gemm_ms) // 2]},
         "derope": {"ms": derope_avg_s * 1e3, "bytes": derope_bytes,
-                   "GBps": derope_bytes / derope_avg_s / 1e9, "frac_hbm": derope_bytes / derope_avg_s / 1e9 / PEAK_HBM_GBPS},
+                   "GBps": derope_bytes / derope_avg_s / 1e9, "frac_hbm": derope_bytes / derope_avg_s / 1e9 / PEAK_HBM_GBPS,
+                   "traffic": traffic_entry(cfg.name, DEROPE_TRAFFIC_FILE, "derope_kernel")},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

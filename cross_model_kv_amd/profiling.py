@@ -2,6 +2,7 @@
 
     python -m cross_model_kv_amd.profiling traffic FETCH_CSV WRITE_CSV WORKLOAD OUT_JSON [KERNEL]
     python -m cross_model_kv_amd.profiling mfma COUNTER_CSV WORKLOAD OUT_JSON KERNEL
+    python -m cross_model_kv_amd.profiling counters COUNTER_CSV KERNEL
 
 traffic: FETCH_CSV / WRITE_CSV are the `*_counter_collection.csv` files of two single-counter
 passes (`rocprofv3 --pmc FETCH_SIZE ...` and `--pmc WRITE_SIZE ...`) of `bench.py
@@ -146,11 +147,30 @@ def mfma(counter_csv, workload, out_json, kernel):
     print(json.dumps({k: v for k, v in out.items() if k != "per_dispatch"}, indent=1))
 
 
+def counters(counter_csv, kernel):
+    """Average of every counter in the file over the kernel's dispatches at its largest grid."""
+    names = set()
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            names.add(r["Counter_Name"])
+    out = {}
+    for c in sorted(names):
+        vals = _workload_launches(_per_dispatch(counter_csv, c), kernel)
+        if vals:
+            out[c] = sum(vals) / len(vals)
+    out["dispatches"] = len(_workload_launches(_per_dispatch(counter_csv, sorted(names)[0]), kernel))
+    print(json.dumps({"kernel": kernel, "kernel_code_fingerprint": kernel_fingerprint(KERNEL_SOURCES[kernel]),
+                      "averages": out}, indent=1))
+    return out
+
+
 if __name__ == "__main__":
     if len(sys.argv) in (6, 7) and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:])
     elif len(sys.argv) == 6 and sys.argv[1] == "mfma":
         mfma(*sys.argv[2:])
+    elif len(sys.argv) == 4 and sys.argv[1] == "counters":
+        counters(*sys.argv[2:])
     else:
         print(__doc__)
         sys.exit(2)
