@@ -159,6 +159,7 @@ struct kvmap_ctx {
     unsigned int* d_count = nullptr;
     int32_t* d_zero = nullptr;    // the one-entry layer list {0} of kvmap_recode
     void* ridge = nullptr;        // fp64 factor and right-hand sides of the device ridge solve
+    RidgeOverlap ridge_ov{};      // side stream and events of the device ridge's lookahead
     size_t ridge_bytes = 0;
     float* gram = nullptr;
     size_t gram_floats = 0;
@@ -252,6 +253,12 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     (void)hipFree(c->d_count);
     (void)hipFree(c->d_zero);
     (void)hipFree(c->ridge);
+    if (c->ridge_ov.side) (void)hipStreamDestroy(c->ridge_ov.side);
+    if (c->ridge_ov.main_ready) (void)hipEventDestroy(c->ridge_ov.main_ready);
+    if (c->ridge_ov.side_done) (void)hipEventDestroy(c->ridge_ov.side_done);
+    if (c->ridge_ov.fwd) (void)hipStreamDestroy(c->ridge_ov.fwd);
+    if (c->ridge_ov.fwd_ready) (void)hipEventDestroy(c->ridge_ov.fwd_ready);
+    if (c->ridge_ov.fwd_done) (void)hipEventDestroy(c->ridge_ov.fwd_done);
     (void)hipFree(c->gram);
     (void)hipFree(c->gram_split);
     for (auto& r : c->timing)
@@ -921,6 +928,14 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
 }
 
 static int ensure_ridge_scratch(kvmap_ctx* c, size_t need) {
+    if (!c->ridge_ov.side) {  // the lookahead's side stream (default priority) and its two events
+        KVMAP_HIP(hipStreamCreateWithFlags(&c->ridge_ov.side, hipStreamNonBlocking));
+        KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.main_ready, hipEventDisableTiming));
+        KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.side_done, hipEventDisableTiming));
+        KVMAP_HIP(hipStreamCreateWithFlags(&c->ridge_ov.fwd, hipStreamNonBlocking));
+        KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.fwd_ready, hipEventDisableTiming));
+        KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.fwd_done, hipEventDisableTiming));
+    }
     if (need > c->ridge_bytes) {
         KVMAP_HIP(hipDeviceSynchronize());
         (void)hipFree(c->ridge);
@@ -957,8 +972,8 @@ static int run_ridge(kvmap_ctx* c, const kvmap_gram_state* const* st, int n, dou
         }
         int* bad = ridge_dev_flags(c->ridge, p, q, m);
         KVMAP_HIP(launch_fill_zero((float*)bad, m, s));
-        if (r2) KVMAP_HIP(launch_ridge_r2(m, p, q, sys, lambda, group, c->ridge, s));
-        else KVMAP_HIP(launch_ridge_dev(m, p, q, sys, lambda, bf16, c->ridge, s));
+        if (r2) KVMAP_HIP(launch_ridge_r2(m, p, q, sys, lambda, group, c->ridge, s, c->ridge_ov));
+        else KVMAP_HIP(launch_ridge_dev(m, p, q, sys, lambda, bf16, c->ridge, s, c->ridge_ov));
         KVMAP_HIP(hipMemcpyAsync(flags, bad, m * sizeof(int), hipMemcpyDeviceToHost, s));
         KVMAP_HIP(hipStreamSynchronize(s));
         for (int j = 0; j < m; ++j)

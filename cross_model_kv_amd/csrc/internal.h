@@ -139,11 +139,23 @@ struct RidgeSys {
 size_t ridge_dev_scratch_bytes(int p, int q, int n);
 // Pivot flags of the n systems (nonzero: not positive definite) inside that scratch.
 int* ridge_dev_flags(void* scratch, int p, int q, int n);
+// A side stream (default priority) and two events for the factorisation's lookahead: the bulk of
+// each panel's trailing update runs there, overlapping the next panel's diagonal chain on the
+// caller's stream.  side NULL: everything on the caller's stream.
+// A second one takes each factored panel's forward substitution.
+struct RidgeOverlap {
+    hipStream_t side;
+    hipEvent_t main_ready;  // recorded on the caller's stream, waited on by the side stream
+    hipEvent_t side_done;   // recorded on the side stream, waited on by the caller's stream
+    hipStream_t fwd;        // NULL: the forward substitution runs after the factorisation
+    hipEvent_t fwd_ready;   // recorded on the caller's stream after each panel, waited on by fwd
+    hipEvent_t fwd_done;    // recorded on fwd after the last panel, waited on by the caller's stream
+};
 hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lambda, bool bf16, void* scratch,
-                            hipStream_t s);
+                            hipStream_t s, const RidgeOverlap& ov);
 // r2_out[g] = in-sample R^2 of the ridge fit pooled over y columns g*group .. +group-1
 hipError_t launch_ridge_r2(int n, int p, int q, const RidgeSys* sys, double lambda, int group, void* scratch,
-                           hipStream_t s);
+                           hipStream_t s, const RidgeOverlap& ov);
 
 // ---- fit driver's scoring kernel (fit.hip) ----------------------------------------------
 // scores[t][s] = mean over {K, V} and heads of r2[kv][s][t][h]; sel[t] = the k best s, ties to

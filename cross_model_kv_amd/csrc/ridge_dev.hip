@@ -126,15 +126,27 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // block (the panel below it and both substitutions) into a 64 x 64 tile product on the matrix
 // cores.  The block lives in registers, lane r holding row r (64 doubles), so that the only
 // LDS traffic is one broadcast column per step:
-//   step j: l_jj = sqrt(a_jj) (lane j's, read with v_readlane); lane r > j: l_rj = a_rj / l_jj,
+//   step j: l_jj = sqrt(a_jj) (lane j's, read with v_readlane) as a_jj rsqrt(a_jj), one reciprocal
+//   square root doing for the root and the division; lane r > j: l_rj = a_rj / l_jj,
 //   published in col[r]; then every lane r: a_rm -= l_rj l_mj for m > j (col[m] = l_mj is a
 //   broadcast LDS read).  Elements above a lane's diagonal are updated too and never used.
 // The inverse X = L^-1 by forward substitution, lane r holding column r:
-//   X_ir = (delta_ir - sum_{m < i} L_im X_mr) / L_ii, with L_im broadcast from LDS; the terms
+//   X_ir = (delta_ir - sum_{m < i} L_im X_mr) / L_ii (times the kept 1 / L_ii), with L_im
+//   broadcast from LDS; the terms
 //   with m < r vanish because X is lower triangular.
+// 1 / sqrt(d) for d > 0 in float64: the hardware estimate refined by two Newton steps
+// y <- y (3 - d y^2) / 2, each of which doubles the correct bits of the estimate.
+__device__ __forceinline__ double rsqrt_f64(double d) {
+    double y = __builtin_amdgcn_rsq(d);
+    y = y * fma(-0.5 * d * y, y, 1.5);
+    y = y * fma(-0.5 * d * y, y, 1.5);
+    return y;
+}
+
 __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
     __shared__ double Ls[RB][RB + 1];
     __shared__ double col[RB];
+    __shared__ double rdiag[RB];  // 1 / l_jj
     double* A = sys_a(g);
     const int P = g.P;
     const int r = threadIdx.x;
@@ -152,10 +164,11 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
             bad = true;
             d = 1.0;  // keep going with a harmless pivot; the result is refused by the host
         }
-        const double ljj = sqrt(d);
-        const double lrj = (r == j) ? ljj : a[j] / ljj;
+        const double rj = rsqrt_f64(d);  // l_jj = d / sqrt(d) = d rj; l_rj = a_rj / l_jj = a_rj rj
+        const double lrj = (r == j) ? d * rj : a[j] * rj;
         a[j] = lrj;
         col[r] = lrj;
+        rdiag[j] = rj;  // the same value from every lane (d is the wave's broadcast pivot)
         __syncthreads();
 #pragma unroll
         for (int m = j + 1; m < RB; ++m) a[m] -= lrj * col[m];
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
         double v = (i == r) ? 1.0 : 0.0;
 #pragma unroll
         for (int m = 0; m < i; ++m) v -= Ls[i][m] * x[m];
-        x[i] = v / Ls[i][i];
+        x[i] = v * rdiag[i];
     }
     double* Li = sys_li(g) + (size_t)kb * RB * RB;
 #pragma unroll
@@ -608,7 +621,26 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
 // rest of the matrix (or of the right-hand sides) is updated once per panel with K = 64 kPanel.
 constexpr int kPanel = 4;
 
-void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
+// Forward substitution over the panel [b0, b1): each diagonal step a product with the block's
+// inverse, then the rows below the panel updated once with K = the panel.  Reads only the
+// factored panel (its columns of L and its blocks' inverses) and writes B.
+static void forward_panel(const RidgeArgs& g, int n, int b0, hipStream_t s) {
+    const int nb = g.P / RB, nq = g.Q / RB, nq2 = g.Q / TB;
+    const unsigned un = (unsigned)n;
+    const dim3 blk(256);
+    const int b1 = std::min(nb, b0 + kPanel);
+    for (int kb = b0; kb < b1; ++kb) {
+        hipLaunchKernelGGL((ridge_update_kernel<4, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
+        const int h = b1 - kb - 1;
+        if (h > 0)
+            hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3(h * nq, un), blk, 0, s, g, kb + 1, 0, nq, kb, 1);
+    }
+    if (nb > b1)
+        hipLaunchKernelGGL(ridge_big_kernel<1>, dim3((nb - b1) / 2 * nq2, un), dim3(512), 0, s, g, b1 / 2, 0, nq2, b0,
+                           b1 - b0);
+}
+
+void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& ov) {
     const int P = g.P, Q = g.Q;
     const int nb = P / RB, nq = Q / RB, nq2 = Q / TB;  // (P, Q: multiples of 128, so nb is even and every
                                                         // panel boundary, a multiple of 4 blocks, is even)
@@ -616,7 +648,15 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
     const dim3 blk(256);
     hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(nb * nb), un), blk, 0, s, g);
     hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), blk, 0, s, g);
-    // factorisation
+    // Factorisation with a one-panel lookahead.  After panel [b0, b1) is factored, its update of
+    // the next panel's columns [b1, b2) (rows b1 ..) runs on `s`, and its update of the rest of
+    // the trailing triangle (rows and columns b2 ..) on the side stream, where it overlaps the
+    // next panel's serial chain of diagonal steps (which touch only columns [b1, b2)).  The next
+    // lookahead update writes columns that the side update writes too, so `s` waits for it first.
+    // Without a side stream (ov.side NULL) the whole trailing update runs on `s`.  With a forward
+    // stream, each factored panel's forward substitution (it reads only that panel's columns of L
+    // and writes B) runs there as soon as the panel is done.
+    bool side_pending = false;
     for (int b0 = 0; b0 < nb; b0 += kPanel) {
         const int b1 = std::min(nb, b0 + kPanel);
         for (int kb = b0; kb < b1; ++kb) {
@@ -629,24 +669,42 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s) {
                 hipLaunchKernelGGL((ridge_update_kernel<0, false>), dim3(below * w, un), blk, 0, s, g, kb + 1, kb + 1,
                                    w, kb, 1);
         }
-        const int m = (nb - b1) / 2;  // trailing lower triangle, in tiles of 128
-        if (m > 0)
+        if (ov.fwd) {  // this panel's forward substitution, on the forward stream
+            (void)hipEventRecord(ov.fwd_ready, s);
+            (void)hipStreamWaitEvent(ov.fwd, ov.fwd_ready, 0);
+            forward_panel(g, n, b0, ov.fwd);
+        }
+        if (b1 == nb) break;
+        if (!ov.side) {
+            const int m = (nb - b1) / 2;  // trailing lower triangle, in tiles of 128
             hipLaunchKernelGGL(ridge_big_kernel<0>, dim3(m * (m + 1) / 2, un), dim3(512), 0, s, g, 0, b1 / 2, 0, b0,
                                b1 - b0);
-    }
-    // L Z = B
-    for (int b0 = 0; b0 < nb; b0 += kPanel) {
-        const int b1 = std::min(nb, b0 + kPanel);
-        for (int kb = b0; kb < b1; ++kb) {
-            hipLaunchKernelGGL((ridge_update_kernel<4, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
-            const int h = b1 - kb - 1;
-            if (h > 0)
-                hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3(h * nq, un), blk, 0, s, g, kb + 1, 0, nq, kb, 1);
+            continue;
         }
-        if (nb > b1)
-            hipLaunchKernelGGL(ridge_big_kernel<1>, dim3((nb - b1) / 2 * nq2, un), dim3(512), 0, s, g, b1 / 2, 0, nq2, b0,
-                               b1 - b0);
+        const int b2 = std::min(nb, b1 + kPanel);
+        if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
+        // lookahead: tiles (I, J) of 64, I in [b1, nb), J in [b1, b2), I >= J, K = the panel
+        hipLaunchKernelGGL((ridge_update_kernel<0, false>), dim3((nb - b1) * (b2 - b1), un), blk, 0, s, g, b1, b1,
+                           b2 - b1, b0, b1 - b0);
+        side_pending = false;
+        if (b2 == nb) continue;
+        const int m = (nb - b2) / 2;  // the rest: lower triangle of 128-tiles from b2
+        (void)hipEventRecord(ov.main_ready, s);
+        (void)hipStreamWaitEvent(ov.side, ov.main_ready, 0);
+        hipLaunchKernelGGL(ridge_big_kernel<0>, dim3(m * (m + 1) / 2, un), dim3(512), 0, ov.side, g, 0, b2 / 2, 0, b0,
+                           b1 - b0);
+        (void)hipEventRecord(ov.side_done, ov.side);
+        side_pending = true;
     }
+    if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
+    if (ov.fwd) {
+        (void)hipEventRecord(ov.fwd_done, ov.fwd);
+        (void)hipStreamWaitEvent(s, ov.fwd_done, 0);
+    }
+    // L Z = B (here only without the forward stream; with it, each panel ran on that stream
+    // right after the panel was factored)
+    if (!ov.fwd)
+        for (int b0 = 0; b0 < nb; b0 += kPanel) forward_panel(g, n, b0, s);
     // L^T W = Z, panels from the last
     for (int b1 = nb; b1 > 0; b1 -= kPanel) {
         const int b0 = std::max(0, b1 - kPanel);
@@ -670,10 +728,10 @@ int* ridge_dev_flags(void* scratch, int p, int q, int n) {
 }
 
 hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lambda, bool bf16, void* scratch,
-                            hipStream_t s) {
+                            hipStream_t s, const RidgeOverlap& ov) {
     if (n < 1 || n > kRidgeMaxBatch) return hipErrorInvalidValue;
     const RidgeArgs g = make_args(n, p, q, sys, lambda, scratch);
-    solve_batch(g, n, s);
+    solve_batch(g, n, s, ov);
     const dim3 tiles((unsigned)((p + RB - 1) / RB), (unsigned)n, (unsigned)(g.Q / RB));  // system on grid y
     const dim3 cols((unsigned)((q + 15) / 16), (unsigned)n);
     if (bf16) {
@@ -687,10 +745,10 @@ hipError_t launch_ridge_dev(int n, int p, int q, const RidgeSys* sys, double lam
 }
 
 hipError_t launch_ridge_r2(int n, int p, int q, const RidgeSys* sys, double lambda, int group, void* scratch,
-                           hipStream_t s) {
+                           hipStream_t s, const RidgeOverlap& ov) {
     if (n < 1 || n > kRidgeMaxBatch || group < 1 || q % group) return hipErrorInvalidValue;
     const RidgeArgs g = make_args(n, p, q, sys, lambda, scratch);
-    solve_batch(g, n, s);
+    solve_batch(g, n, s, ov);
     hipLaunchKernelGGL(ridge_rss_kernel, dim3(g.Q / RB, (unsigned)n), dim3(256), 0, s, g);
     const int groups = q / group;
     hipLaunchKernelGGL(ridge_r2_group_kernel, dim3((groups + 255) / 256, (unsigned)n), dim3(256), 0, s, g, group);
