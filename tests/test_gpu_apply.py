@@ -304,3 +304,24 @@ def test_short_cache_full_layer_shape(ctx, T):
     _check_sampled(cfg, inp, ok_, ov_, targets, np.arange(cfg.T))
     ok2, ov2 = _run(ctx, cfg, inp)
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
+
+
+def test_aliasing_refused_and_outputs_untouched(ctx):
+    """An output that overlaps an input (here the first target layers written over the source
+    cache) or the other output is refused before any device work; nothing is written."""
+    from cross_model_kv_amd import kvmap as K
+    cfg = EDGE[5]  # 6 source layers, 3 target layers: a [3][H][T][d] view of the source fits
+    inp = apply_inputs(cfg, "cuda:0")
+    src_before = inp["src_k"].clone()
+    args = (inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"],
+            cfg.theta_src, cfg.theta_tgt)
+    ov = torch.empty((cfg.L_tgt, cfg.H, cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(K.KvmapError) as e:
+        ctx.apply(*args, out_k=inp["src_k"][: cfg.L_tgt], out_v=ov)
+    assert e.value.status == K.ERR_INVALID_ARGUMENT
+    ok_ = torch.empty_like(ov)
+    with pytest.raises(K.KvmapError) as e:
+        ctx.apply(*args, out_k=ok_, out_v=ok_)
+    assert e.value.status == K.ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+    assert torch.equal(inp["src_k"], src_before)
