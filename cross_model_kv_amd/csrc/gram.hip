@@ -103,6 +103,8 @@ __device__ __forceinline__ double sum_splits(const float* __restrict__ part, int
 //   phase 0: c = sum / n_b (rounded to bf16 when round_c: the split co-moment path shifts
 //            bf16 data by a bf16 value, so that x - c is exact)
 //   phase 1: m = sum / n_b; batch mean = c + m; delta = batch mean - mean; mean updated;
+//            with round_c the shift c was not stored but is the running mean rounded to bf16
+//            (the split path of a merging call), formed here again before the mean moves;
 //            with ss_y (and the partial sums of squares of the shifted y in part2): the
 //            centered sum of squares of y merged the same way (Chan):
 //            ss_y += (sum2 - n_b m^2) + n n_b / n' delta^2
@@ -134,7 +136,13 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(
     float* dd = isx ? dx : dy;
     float* mean = isx ? mean_x : mean_y;
     mm[c] = (float)mean_b;
-    const double bm = (double)cc[c] + mean_b;
+    double shift = (double)cc[c];
+    if (round_c) {
+        uint32_t u = __float_as_uint(mean[c]);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        shift = (double)__uint_as_float(u & 0xffff0000u);
+    }
+    const double bm = shift + mean_b;
     double delta = 0.0;
     if (n_old == 0) {
         dd[c] = 0.f;
@@ -347,23 +355,35 @@ hipError_t launch_gram_batch(Elem e, const void* X, const void* Y, int64_t n_b, 
     const float coef = (float)((double)n_old * (double)n_b / n_new);
     const int fresh = (n_old == 0);
     if (bf) {
-        // column sums -> c = bf16(mean); split (d, hi, lo, transposed) with the sums of d;
-        // m, delta, mean; co-moments on the bf16 matrix cores
-        hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, nullptr, sc.part, stride, 0,
-                           nullptr);
-        hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, nullptr, sc.part, stride, p,
-                           nullptr);
-        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q, n_b, n_old,
-                           0, 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, nullptr, nullptr);
+        // Shift c: a fresh state takes the batch's column means rounded to bf16 (one pass of
+        // column sums first); a merging call takes the running mean rounded to bf16, which is
+        // already on the device, so the batch is read once.  Either way x - c is exact and
+        // the batch's own mean m of x - c is removed in the epilogue, so the shift only sets
+        // how far the split values sit from the batch mean.  Then: split (d, hi, lo,
+        // transposed) with the sums of d; m, delta, mean; co-moments on the bf16 matrix cores.
+        const float* shx = sc.cx;
+        const float* shy = sc.cy;
+        if (fresh) {
+            hipLaunchKernelGGL(colsum_kernel<true>, gx, dim3(CS_THREADS), 0, s, X, n_b, p, nullptr, sc.part, stride,
+                               0, nullptr);
+            hipLaunchKernelGGL(colsum_kernel<true>, gy, dim3(CS_THREADS), 0, s, Y, n_b, q, nullptr, sc.part, stride,
+                               p, nullptr);
+            hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, sc.splits, p, q, n_b,
+                               n_old, 0, 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, nullptr,
+                               nullptr);
+        } else {
+            shx = mean_x;
+            shy = mean_y;
+        }
         const int ss = gram_split_blocks(n_b, sc.max_splits);
         uint16_t* Sx = sc.split;
         uint16_t* Sy = sc.split + gram_split_elems(p, 0, n_b);
-        hipError_t err = launch_gram_split(X, n_b, p, sc.cx, Sx, sc.part, stride, 0, nullptr, ss, s);
+        hipError_t err = launch_gram_split(X, n_b, p, shx, !fresh, Sx, sc.part, stride, 0, nullptr, ss, s);
         if (err != hipSuccess) return err;
-        err = launch_gram_split(Y, n_b, q, sc.cy, Sy, sc.part, stride, p, ss_y ? sc.part2 : nullptr, ss, s);
+        err = launch_gram_split(Y, n_b, q, shy, !fresh, Sy, sc.part, stride, p, ss_y ? sc.part2 : nullptr, ss, s);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, ss, p, q, n_b, n_old, 1, 0,
-                           sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, sc.part2, ss_y);
+        hipLaunchKernelGGL(colsum_finalize_kernel, dim3(fin), dim3(256), 0, s, sc.part, ss, p, q, n_b, n_old, 1,
+                           fresh ? 0 : 1, sc.cx, sc.cy, sc.mx, sc.my, sc.dx, sc.dy, mean_x, mean_y, sc.part2, ss_y);
         return launch_gram_x3(Sx, Sy, n_b, p, q, sc.mx, sc.my, sc.dx, sc.dy, coef, fresh, M_xx, M_xy, bd, s);
     }
     for (int phase = 0; phase < 2; ++phase) {

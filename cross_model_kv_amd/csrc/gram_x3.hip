@@ -1,8 +1,9 @@
 // Co-moments of bf16 batches on the bf16 matrix cores (fit side, KVBridge README fitting
 // section "Loading": centered covariance accumulated batchwise with the Chan/Welford update).
 //
-// For bf16 inputs the batch is shifted by c = its column means rounded to bf16, so that
-// d = x - c is a difference of two bf16 values: exact in fp32 and, whenever the two are
+// For bf16 inputs the batch is shifted by c = its column means rounded to bf16 (a batch into
+// an empty state) or the running mean rounded to bf16 (a merging batch, so the batch is read
+// once), so that d = x - c is a difference of two bf16 values: exact in fp32 and, whenever the two are
 // within a factor 2^7 of each other, exactly the sum hi + lo of two bf16 values
 // (hi = bf16(d), lo = bf16(d - hi)); otherwise hi + lo carries d's leading 16 bits.  The
 // products of the shifted data then come from three bf16 MFMA passes,
@@ -11,7 +12,7 @@
 //
 //   1. gram_split_kernel: per operand (X, then Y) and 32-token block, d, hi and lo, written
 //      transposed as S [column][token block][hi of 32 tokens | lo of 32 tokens] (one
-//      128-byte line per column and block), plus partial column sums of d (the tiny mean
+//      128-byte line per column and block), plus partial column sums of d (the small mean
 //      of the shifted batch).
 //   2. gram_x3_kernel: the upper triangle of 256 x 256 tiles of S_x S_x^T (or, for a state
 //      that keeps M_xx block-diagonal, of each diagonal block) and all tiles of S_x S_y^T,
@@ -50,7 +51,7 @@ __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_fl
 // 8 adjacent columns (two 8-byte halves) of 4 rows per block; the block goes through LDS as
 // (hi | lo << 16) per (column, token) and leaves as whole 128-byte lines, 8 lanes per line.
 __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restrict__ A, int64_t n_b, int cols,
-                                                         int nkb, const float* __restrict__ c,
+                                                         int nkb, const float* __restrict__ c, int round_c,
                                                          uint16_t* __restrict__ S, float* __restrict__ part,
                                                          int part_stride, int col_off, float* __restrict__ part2) {
     __shared__ uint32_t t[SP_COLS * SP_LD];
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         sh[e] = (e < 4 ? cok0 : cok1) ? c[c0 + rc + e] : 0.f;
+        if (round_c) sh[e] = bf16_bits_f32(bf16_rne_bits(sh[e]));
         sum[e] = 0.f;
         sum2[e] = 0.f;
     }
@@ -396,11 +398,11 @@ int gram_split_blocks(int64_t n_b, int max_splits) {
     return (int)std::min<int64_t>(nkb, max_splits);
 }
 
-hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,
+hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, int round_c, uint16_t* S,
                              float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s) {
     const int nkb = (int)((n_b + SP_TOK - 1) / SP_TOK);
     const dim3 grid((cols + SP_COLS - 1) / SP_COLS, splits);
-    hipLaunchKernelGGL(gram_split_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c, S, part,
+    hipLaunchKernelGGL(gram_split_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c, round_c, S, part,
                        part_stride, col_off, part2);
     return hipGetLastError();
 }

@@ -109,7 +109,8 @@ constexpr int64_t kGramSubBatch = 16384;
 #define KVMAP_STATIC_SCRATCH_BYTES (size_t(64) << 20)
 size_t gram_split_elems(int p, int q, int64_t n_b);  // uint16 elements of `split` for n_b rows
 int gram_split_blocks(int64_t n_b, int max_splits);
-hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, uint16_t* S,
+// c: the shift per column (bf16 values), or with round_c any fp32 values rounded to bf16 here.
+hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* c, int round_c, uint16_t* S,
                              float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s);
 hipError_t launch_gram_x3(const uint16_t* Sx, const uint16_t* Sy, int64_t n_b, int p, int q, const float* mx,
                           const float* my, const float* dx, const float* dy, float coef, int fresh,

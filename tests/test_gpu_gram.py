@@ -77,6 +77,20 @@ def test_gram_ragged_batches(ctx, dtype):
     _check_state(st, ref, f"ragged {dtype}")
 
 
+def test_gram_wide_state_every_element(ctx):
+    """p = 6144, q = 1024 (396 co-moment tiles, more than one wave of the compute units), bf16
+    batches of 1000, 300 and 1000 rows: the first shifted by its own column means, the merging
+    ones by the running mean; every element against the oracle's two-pass statistics."""
+    cfg = FIT_STATS_CONFIG.replace(cid=402, p=6144, q=1024, n_tokens=2300, batch=1000)
+    parts = _batches(cfg, [1000, 300, 1000])
+    st = ctx.gram_state(cfg.p, cfg.q)
+    ctx.gram_reset(st)
+    for X, Y in parts:
+        ctx.gram(st, _dev(X, "bf16"), _dev(Y, "bf16"))
+    ref = oracle.stats_two_pass(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    _check_state(st, ref, "wide state")
+
+
 def test_gram_call_larger_than_sub_batch(ctx):
     """One call of 16384 + 1000 + 3 rows (the library merges it in sub-batches of at most
     16384 rows), p = 264, q = 36 (q not a multiple of 8), bf16."""
