@@ -23,6 +23,11 @@ short      kvmap_apply on the first T tokens (T = 1 .. 256) with the workload's 
            HBM roofline of reading W and the rows
 fit_driver the complete fit (layer selection, then the maps) at the 14B->32B model shape over
            --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per pass
+library_gemm  context for the roofline: the vendor BLAS (torch.matmul, hipBLASLt on ROCm) on the
+           plain GEMMs of the same shape and data -- the first target layer's gathered,
+           de-rotated feature rows [T][F] times each of the 2 x L_tgt maps, bf16 in and out with
+           fp32 accumulation, no gather, bias or RoPE -- timed with HIP events, against the same
+           bf16 dense peak
 """
 
 from __future__ import annotations
@@ -164,6 +169,39 @@ def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=
         del sk, sv, ok_, ov_
     return {"workload": f"{cfg.name} maps (W {w_bytes / 1e9:.2f} GB bf16) on the first T tokens of the cache",
             "lengths": rows}
+
+
+def library_gemm_leg(cfg, inp, passes=3):
+    """The vendor library on the plain GEMMs of the apply's shape (see the module docstring)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sel = [int(s) for s in inp["layer_sel"][0]]
+    # X[p][(j H + h) d + e] = src_k[sel[j]][h][p][e] (keys as the apply gathers them; the
+    # de-rotation changes no statistics that matter to the timing)
+    X = inp["src_k"][sel].permute(2, 0, 1, 3).reshape(cfg.T, cfg.F).contiguous()
+    maps = [inp[w][t].t().contiguous() for t in range(cfg.L_tgt) for w in ("W_k", "W_v")]  # [F][N] each
+    out = torch.empty((cfg.T, cfg.N), dtype=X.dtype, device=X.device)
+
+    def one_pass():
+        for Wt in maps:
+            torch.matmul(X, Wt, out=out)
+
+    one_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(passes):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / passes
+    tflops = cfg.flops / (ms / 1e3) / 1e12
+    log(f"library GEMM (torch.matmul) on the same shape: {ms:.3f} ms per pass of {len(maps)} GEMMs, "
+        f"{tflops:.0f} TFLOP/s = {tflops / PEAK_BF16_TFLOPS * 100:.1f} % of the bf16 dense peak")
+    del X, maps, out
+    return {"what": f"torch.matmul [T {cfg.T}][F {cfg.F}] x [F][N {cfg.N}], bf16, {2 * cfg.L_tgt} maps per pass",
+            "ms": ms, "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS}
 
 
 def fit_cpu_baseline(C, X, Y, budget_s=10.0):
@@ -331,6 +369,8 @@ def main():
     ap.add_argument("--no-recode", action="store_true", help="skip the RoPE-recode measurement")
     ap.add_argument("--no-fit-driver", action="store_true", help="skip the end-to-end fit measurement")
     ap.add_argument("--no-short", action="store_true", help="skip the short-cache measurement")
+    ap.add_argument("--no-library-gemm", action="store_true",
+                    help="skip the vendor-library GEMM of the same shape (roofline context)")
     ap.add_argument("--fit-seqs", type=int, default=8, help="calibration sequences of 4096 tokens for the fit driver")
     ap.add_argument("--fit-driver-only", action="store_true",
                     help="run only the end-to-end fit measurement and print its object as the JSON line")
@@ -444,6 +484,8 @@ def main():
     if not args.no_short:
         result["short"] = short_leg(K, ctx, cfg, inp)
     ctx.close()
+    if not args.no_library_gemm and cfg.dtype == "bf16":
+        result["library_gemm"] = library_gemm_leg(cfg, inp)
     if not args.no_fit:
         del inp, out_k, out_v
         torch.cuda.empty_cache()

@@ -48,15 +48,17 @@ __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_fl
 
 // ---- 1: shift, split, transpose -------------------------------------------------------
 // Workgroup: 256 columns; it walks token blocks blockIdx.y, + gridDim.y, ...  A thread reads
-// 8 adjacent columns (two 8-byte halves) of 4 rows per block; the block goes through LDS as
-// (hi | lo << 16) per (column, token) and leaves as whole 128-byte lines, 8 lanes per line.
+// 8 adjacent columns of 4 rows per block (one 16-byte load per row when the rows are 16-byte
+// aligned, else two 8-byte halves), and holds the next block's rows in registers while the
+// current one goes through LDS as (hi | lo << 16) per (column, token) and leaves as whole
+// 128-byte lines, 8 lanes per line.  The column sums are reduced through the same LDS.
+template <bool V16>
 __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restrict__ A, int64_t n_b, int cols,
                                                          int nkb, const float* __restrict__ c, int round_c,
                                                          uint16_t* __restrict__ S, float* __restrict__ part,
                                                          int part_stride, int col_off, float* __restrict__ part2) {
     __shared__ uint32_t t[SP_COLS * SP_LD];
-    __shared__ float red[8][SP_COLS];
-    __shared__ float red2[8][SP_COLS];
+    static_assert(2 * 8 * SP_COLS <= SP_COLS * SP_LD, "the column-sum reduction reuses the transpose buffer");
     const int tid = threadIdx.x;
     const int c0 = blockIdx.x * SP_COLS;
     const int rc = (tid & 31) * 8;  // first of the thread's 8 columns within the workgroup
@@ -71,20 +73,48 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
         sum[e] = 0.f;
         sum2[e] = 0.f;
     }
-    for (int kb = blockIdx.y; kb < nkb; kb += gridDim.y) {
+    // rows tok = 8 pass + rr of block kb, 8 columns each as 4 words.  The loads themselves are
+    // unconditional (rows past the batch and columns past the matrix read a valid element), so
+    // the wait before a block's words are used counts only the loads of the block after it;
+    // what lies outside the batch is zeroed when it is used.
+    const int cl0 = cok0 ? c0 + rc : 0, cl1 = cok1 ? c0 + rc + 4 : 0;
+    auto load = [&](int kb, uint32_t (&w)[4][4]) {
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int64_t row = std::min<int64_t>((int64_t)kb * SP_TOK + pass * 8 + rr, n_b - 1);
+            if (V16) {
+                const uint4 v = *(const uint4*)(A + row * cols + cl0);
+                w[pass][0] = v.x;
+                w[pass][1] = v.y;
+                w[pass][2] = v.z;
+                w[pass][3] = v.w;
+            } else {
+                const uint2 h0 = *(const uint2*)(A + row * cols + cl0);
+                const uint2 h1 = *(const uint2*)(A + row * cols + cl1);
+                w[pass][0] = h0.x;
+                w[pass][1] = h0.y;
+                w[pass][2] = h1.x;
+                w[pass][3] = h1.y;
+            }
+        }
+    };
+    // LDS hand-off between the phases of a block: a plain barrier after this wave's LDS
+    // operations (__syncthreads would also wait for the prefetched global loads)
+    auto lds_sync = [&]() {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // one block through LDS to the split operand
+    auto process = [&](int kb, const uint32_t (&w)[4][4]) {
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
             const int tok = pass * 8 + rr;
-            const int64_t row = (int64_t)kb * SP_TOK + tok;
-            const bool ok0 = cok0 && row < n_b, ok1 = cok1 && row < n_b;
-            uint2 v0 = make_uint2(0, 0), v1 = make_uint2(0, 0);
-            if (ok0) v0 = *(const uint2*)(A + row * cols + c0 + rc);
-            if (ok1) v1 = *(const uint2*)(A + row * cols + c0 + rc + 4);
-            const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
+            const bool inb = (int64_t)kb * SP_TOK + tok < n_b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t bits = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                const float d = (e < 4 ? ok0 : ok1) ? bf16_bits_f32(bits) - sh[e] : 0.f;  // exact
+                const uint32_t bits = (w[pass][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                const float d = ((e < 4 ? cok0 : cok1) && inb) ? bf16_bits_f32(bits) - sh[e] : 0.f;  // exact
                 sum[e] += d;
                 sum2[e] += d * d;
                 const uint32_t hi = bf16_rne_bits(d);
@@ -92,7 +122,7 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
                 t[(rc + e) * SP_LD + tok] = hi | (lo << 16);
             }
         }
-        __syncthreads();
+        lds_sync();
         // line (column, block): chunk ch < 4 = hi of tokens 8ch .. 8ch+7, ch >= 4 = lo of them
         const int ch = tid & 7;
         const int t0 = (ch & 3) * 8;
@@ -109,20 +139,37 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const uint16_t* __restr
                 *(uint4*)(S + ((size_t)(c0 + col) * nkb + kb) * 64 + ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
-        __syncthreads();
+        lds_sync();
+    };
+    // Blocks in pairs of register buffers: the next block's loads (unconditional, a clamped
+    // block past the end repeats the last one) are in flight while the current one is processed.
+    uint32_t wa[4][4], wb[4][4];
+    const int g = gridDim.y;
+    int kb = blockIdx.y;
+    load(kb, wa);
+    while (true) {
+        load(min(kb + g, nkb - 1), wb);
+        process(kb, wa);
+        kb += g;
+        if (kb >= nkb) break;
+        load(min(kb + g, nkb - 1), wa);
+        process(kb, wb);
+        kb += g;
+        if (kb >= nkb) break;
     }
+    float* red = (float*)t;  // [8][SP_COLS] sums, then [8][SP_COLS] sums of squares
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        red[rr][rc + e] = sum[e];
-        red2[rr][rc + e] = sum2[e];
+        red[rr * SP_COLS + rc + e] = sum[e];
+        red[(8 + rr) * SP_COLS + rc + e] = sum2[e];
     }
     __syncthreads();
     if (c0 + tid < cols) {
         float s = 0.f, s2 = 0.f;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
-            s += red[g][tid];
-            s2 += red2[g][tid];
+            s += red[g * SP_COLS + tid];
+            s2 += red[(8 + g) * SP_COLS + tid];
         }
         part[(size_t)blockIdx.y * part_stride + col_off + c0 + tid] = s;
         if (part2) part2[(size_t)blockIdx.y * part_stride + col_off + c0 + tid] = s2;
@@ -402,8 +449,13 @@ hipError_t launch_gram_split(const void* A, int64_t n_b, int cols, const float* 
                              float* part, int part_stride, int col_off, float* part2, int splits, hipStream_t s) {
     const int nkb = (int)((n_b + SP_TOK - 1) / SP_TOK);
     const dim3 grid((cols + SP_COLS - 1) / SP_COLS, splits);
-    hipLaunchKernelGGL(gram_split_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c, round_c, S, part,
-                       part_stride, col_off, part2);
+    // 16-byte row loads when every row starts 16-byte aligned (A itself is)
+    if (cols % 8 == 0 && ((uintptr_t)A & 15) == 0)
+        hipLaunchKernelGGL(gram_split_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c,
+                           round_c, S, part, part_stride, col_off, part2);
+    else
+        hipLaunchKernelGGL(gram_split_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)A, n_b, cols, nkb, c,
+                           round_c, S, part, part_stride, col_off, part2);
     return hipGetLastError();
 }
 
