@@ -16,8 +16,8 @@ cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on the h
 recode     kvmap_recode (identity map: RoPE re-encode, one rotation per pair) of the workload's
            whole source key cache, timed with HIP events; GB/s against the 8 TB/s HBM peak
 fit        the fit side on its own workload (262,144 calibration tokens, p 8192, q 1024, batches of
-           4096): one kvmap_gram call per batch (column sums, shift, co-moments, Chan merge) timed
-           with HIP events on its stream; one ridge solve of the merged state on the host and one
+           4096): one kvmap_gram call per batch (shift, hi/lo split, co-moments, Chan merge), 64
+           calls timed with HIP events on its stream after at least 0.3 s of warm-up calls; one ridge solve of the merged state on the host and one
            on the device (fp64, W written in bf16 output-major)
 short      kvmap_apply on the first T tokens (T = 1 .. 256) with the workload's maps: ms against the
            HBM roofline of reading W and the rows
@@ -228,9 +228,11 @@ def fit_cpu_baseline(C, X, Y, budget_s=10.0):
                       f"statistics + Chan merge, {spent:.1f} s"}
 
 
-def fit_leg(K, batches_timed=16, warmup=2, cpu=True):
+def fit_leg(K, batches_timed=64, warmup_s=0.3, cpu=True):
     """Time kvmap_gram on the fit-statistics workload: a few distinct batches resident in HBM,
-    cycled; then one host ridge solve of the merged state."""
+    cycled, after calls for at least warmup_s seconds (the GPU has idled while the batches were
+    generated on the host, and the first tens of milliseconds of calls run slower); then one host
+    ridge solve of the merged state and one on the device."""
     import torch
     from synth.device import fit_inputs
     from synth.workloads import FIT_STATS_CONFIG as C
@@ -240,10 +242,13 @@ def fit_leg(K, batches_timed=16, warmup=2, cpu=True):
     st = ctx.gram_state(C.p, C.q)
     stream = torch.cuda.current_stream()
     ctx.gram_reset(st, stream)
-    for i in range(warmup):
-        X, Y = resident[i % len(resident)]
-        ctx.gram(st, X, Y, stream)
-    torch.cuda.synchronize()
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < 16 or time.perf_counter() - t_w < warmup_s:
+        for _ in range(16):
+            X, Y = resident[n_w % len(resident)]
+            ctx.gram(st, X, Y, stream)
+            n_w += 1
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(batches_timed):

@@ -517,21 +517,16 @@ extern "C" int kvmap_reserve(kvmap_ctx* c, const kvmap_dims* d) {
     return ok();
 }
 
-extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k, const void* src_v,
-                           const int32_t* layer_sel, const void* W_k, const void* b_k, const void* W_v,
-                           const void* b_v, const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
-                           void* tgt_k, void* tgt_v, void* stream, uint32_t flags) {
-    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: ctx is NULL");
-    int st = kvmap_validate_apply(d, layer_sel, rope_src, rope_tgt);
+extern "C" int kvmap_validate_apply_buffers(const kvmap_dims* d, const void* src_k, const void* src_v,
+                                            const void* W_k, const void* b_k, const void* W_v, const void* b_v,
+                                            const void* tgt_k, const void* tgt_v) {
+    int st = validate_dims(d);
     if (st) return st;
     if (!src_k || !src_v || !W_k || !b_k || !W_v || !b_v || !tgt_k || !tgt_v)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: NULL device pointer");
-    if (flags & ~(KVMAP_FLAG_CHECK_FINITE | KVMAP_FLAG_TIMING))
-        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: unknown flag bits 0x%x", flags);
     const void* ptrs[8] = {src_k, src_v, W_k, b_k, W_v, b_v, tgt_k, tgt_v};
     for (const void* p : ptrs)
         if (((uintptr_t)p) & 15) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: pointers must be 16-byte aligned");
-
     const ApplyGeom g{d->L_src, d->L_tgt, d->H_kv, d->head_dim, d->k, d->T};
     const size_t es = d->dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
     const size_t src_bytes = (size_t)g.L_src * g.H * g.T * g.d * es;
@@ -545,6 +540,21 @@ extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k,
             return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: an input overlaps an output");
     if (ranges_overlap(tgt_k, tgt_bytes, tgt_v, tgt_bytes))
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: tgt_k and tgt_v overlap");
+    return ok();
+}
+
+extern "C" int kvmap_apply(kvmap_ctx* c, const kvmap_dims* d, const void* src_k, const void* src_v,
+                           const int32_t* layer_sel, const void* W_k, const void* b_k, const void* W_v,
+                           const void* b_v, const kvmap_rope* rope_src, const kvmap_rope* rope_tgt,
+                           void* tgt_k, void* tgt_v, void* stream, uint32_t flags) {
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: ctx is NULL");
+    int st = kvmap_validate_apply(d, layer_sel, rope_src, rope_tgt);
+    if (st) return st;
+    st = kvmap_validate_apply_buffers(d, src_k, src_v, W_k, b_k, W_v, b_v, tgt_k, tgt_v);
+    if (st) return st;
+    if (flags & ~(KVMAP_FLAG_CHECK_FINITE | KVMAP_FLAG_TIMING))
+        return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_apply: unknown flag bits 0x%x", flags);
+    const ApplyGeom g{d->L_src, d->L_tgt, d->H_kv, d->head_dim, d->k, d->T};
 
     DeviceGuard guard(c->device);
     if (!guard.okay) return fail(KVMAP_ERR_DEVICE, "kvmap_apply: hipSetDevice(%d) failed", c->device);

@@ -92,6 +92,7 @@ _SIGS = {
     "kvmap_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]),
     "kvmap_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "kvmap_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims)]),
+    "kvmap_validate_apply_buffers": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 8),
     "kvmap_validate_apply": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Rope),
                                             ctypes.POINTER(Rope)]),
     "kvmap_apply": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p,
@@ -191,6 +192,15 @@ def validate_apply(L_src, L_tgt, H, d, k, T, dtype, layer_sel, theta_src, theta_
     rs = _rope(theta_src, pos0_src, style_src, inv_freq_src, keep)
     rt = _rope(theta_tgt, pos0_tgt, style_tgt, inv_freq_tgt, keep)
     return lib().kvmap_validate_apply(ctypes.byref(dm), sel.ctypes.data, ctypes.byref(rs), ctypes.byref(rt))
+
+
+def validate_apply_buffers(L_src, L_tgt, H, d, k, T, dtype, src_k, src_v, W_k, b_k, W_v, b_v,
+                           tgt_k, tgt_v) -> int:
+    """kvmap_validate_apply_buffers on buffer addresses given as integers (nothing is read);
+    returns the status code (host only, needs no GPU)."""
+    dm = _dims(L_src, L_tgt, H, d, k, T, dtype)
+    addrs = [ctypes.c_void_p(int(a)) if a else None for a in (src_k, src_v, W_k, b_k, W_v, b_v, tgt_k, tgt_v)]
+    return lib().kvmap_validate_apply_buffers(ctypes.byref(dm), *addrs)
 
 
 def ridge_solve_host(mean_x, mean_y, M_xx, M_xy, lam: float, n_threads: int = 0):

@@ -142,6 +142,14 @@ int kvmap_reserve(kvmap_ctx* ctx, const kvmap_dims* dims);
  * Needs no device. */
 int kvmap_validate_apply(const kvmap_dims* dims, const int32_t* layer_sel,
                          const kvmap_rope* rope_src, const kvmap_rope* rope_tgt);
+/* Host-only checks of the buffers of an apply call, taken as addresses (nothing is read):
+ * dims as in kvmap_validate_apply; then INVALID_ARGUMENT for a NULL pointer, a pointer not
+ * 16-byte aligned, an output range overlapping an input range, or tgt_k overlapping tgt_v
+ * (ranges from the layouts and sizes of kvmap_apply).  kvmap_apply runs exactly these checks
+ * before any device work.  Needs no device. */
+int kvmap_validate_apply_buffers(const kvmap_dims* dims, const void* src_k, const void* src_v,
+                                 const void* W_k, const void* b_k, const void* W_v, const void* b_v,
+                                 const void* tgt_k, const void* tgt_v);
 
 /* Map a source KV cache into the target model's cache (the whole apply step).
  *   src_k, src_v  device [L_src][H][T][d]   stored source cache (keys rotated by the

@@ -5,6 +5,7 @@
 #include "../../include/kvmap.h"
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <random>
@@ -50,6 +51,25 @@ static void validation() {
     kvmap_dims big = d;
     big.T = int64_t(1) << 40;
     CHECK(kvmap_validate_apply(&big, sel, &rs, &rt) == KVMAP_ERR_SHAPE, "huge T accepted");
+    // buffer addresses (never read): disjoint and aligned, then each refusal
+    {
+        char* base = reinterpret_cast<char*>(uintptr_t(1) << 40);
+        const size_t src = 6 * 2 * 100 * 128 * 2, w = 4 * 256 * 768 * 2, b = 4 * 256 * 2, tgt = 4 * 2 * 100 * 128 * 2;
+        const void *sk = base, *sv = base + src, *wk = base + 2 * src, *bk = base + 2 * src + w;
+        const void *wv = base + 2 * src + w + 4096, *bv = base + 2 * src + 2 * w + 4096;
+        void* tk = base + 2 * src + 2 * w + 8192;
+        void* tv = static_cast<char*>(tk) + tgt;
+        CHECK(kvmap_validate_apply_buffers(&d, sk, sv, wk, bk, wv, bv, tk, tv) == KVMAP_OK, "good buffers refused: %s",
+              kvmap_last_error());
+        CHECK(kvmap_validate_apply_buffers(&d, sk, sv, wk, bk, wv, bv, tk, tk) == KVMAP_ERR_INVALID_ARGUMENT,
+              "tgt_k == tgt_v accepted");
+        CHECK(kvmap_validate_apply_buffers(&d, sk, sv, wk, bk, wv, bv, const_cast<void*>(sv), tv) ==
+                  KVMAP_ERR_INVALID_ARGUMENT, "output over an input accepted");
+        CHECK(kvmap_validate_apply_buffers(&d, sk, sv, wk, bk, wv, bv, static_cast<char*>(tk) + 8, tv) ==
+                  KVMAP_ERR_INVALID_ARGUMENT, "misaligned output accepted");
+        CHECK(kvmap_validate_apply_buffers(&d, nullptr, sv, wk, bk, wv, bv, tk, tv) == KVMAP_ERR_INVALID_ARGUMENT,
+              "NULL input accepted");
+    }
     // kvmap_reserve checks the dims before the context
     kvmap_dims zero{};
     CHECK(kvmap_reserve(nullptr, &zero) == KVMAP_ERR_SHAPE, "zero dims reached the workspace arithmetic");

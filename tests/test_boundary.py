@@ -91,6 +91,52 @@ def test_validate_refusals(over, status):
     assert K.last_error() != ""
 
 
+def _buffers(dtype=K.BF16, **over):
+    """Addresses of a well-placed apply call at GOOD's shape (L 6 -> 4, H 2, d 128, k 3, T 100):
+    every buffer in its own region, 16-byte aligned.  Nothing is ever read at them."""
+    es = 2 if dtype == K.BF16 else 4
+    H, d, T, k, Ls, Lt = GOOD["H"], GOOD["d"], GOOD["T"], GOOD["k"], GOOD["L_src"], GOOD["L_tgt"]
+    N = H * d
+    sizes = dict(src_k=Ls * H * T * d * es, src_v=Ls * H * T * d * es, W_k=Lt * N * N * k * es, b_k=Lt * N * es,
+                 W_v=Lt * N * N * k * es, b_v=Lt * N * es, tgt_k=Lt * H * T * d * es, tgt_v=Lt * H * T * d * es)
+    addr, base = {}, 1 << 40
+    for name, n in sizes.items():
+        addr[name] = base
+        base += (n + 4095) // 4096 * 4096
+    addr.update(over)
+    return addr, sizes
+
+
+def _validate_buffers(dtype=K.BF16, **over):
+    a, _ = _buffers(dtype, **over)
+    return K.validate_apply_buffers(GOOD["L_src"], GOOD["L_tgt"], GOOD["H"], GOOD["d"], GOOD["k"], GOOD["T"],
+                                    dtype, a["src_k"], a["src_v"], a["W_k"], a["b_k"], a["W_v"], a["b_v"],
+                                    a["tgt_k"], a["tgt_v"])
+
+
+def test_validate_buffers_accepts_disjoint_aligned():
+    assert _validate_buffers() == K.OK
+    assert _validate_buffers(K.F32) == K.OK
+
+
+def test_validate_buffers_refusals():
+    """kvmap_apply's own buffer checks, run before any device work: NULL, misaligned, an output
+    over an input (anywhere inside it, or straddling its end), the two outputs overlapping."""
+    a, sz = _buffers()
+    assert _validate_buffers(src_k=0) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_v=0) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(W_k=a["W_k"] + 8) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_k=a["src_k"]) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_k=a["src_v"] + sz["src_v"] - 16) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_v=a["W_v"] + 4096) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_v=a["b_k"]) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_v=a["tgt_k"] + sz["tgt_k"] - 16) == K.ERR_INVALID_ARGUMENT
+    assert _validate_buffers(tgt_v=a["tgt_k"]) == K.ERR_INVALID_ARGUMENT
+    assert K.last_error() != ""
+    # exactly adjacent ranges do not overlap
+    assert _validate_buffers(tgt_v=a["tgt_k"] + sz["tgt_k"]) == K.OK
+
+
 def test_validate_frequency_lists():
     """A model's own frequency list replaces theta (which is then not read); entries must be
     finite and >= 0 (0: a pair that never turns)."""
