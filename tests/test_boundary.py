@@ -256,3 +256,13 @@ def test_reserve_checks_dims_before_anything():
     assert L.kvmap_reserve(None, None) == K.ERR_INVALID_ARGUMENT
     good = K.Dims(4, 4, 2, 128, 2, 64, K.BF16)
     assert L.kvmap_reserve(None, ctypes.byref(good)) == K.ERR_INVALID_ARGUMENT  # then the NULL ctx
+
+
+def test_timings_refuse_without_context():
+    """kvmap_timings / kvmap_last_timings refuse a NULL context (and a short output array)
+    before touching the device."""
+    import ctypes
+    buf = (ctypes.c_float * 3)()
+    assert K.lib().kvmap_timings(None, 0, buf, 3) == K.ERR_INVALID_ARGUMENT
+    assert K.lib().kvmap_last_timings(None, buf, 3) == K.ERR_INVALID_ARGUMENT
+    assert K.lib().kvmap_timings(None, 0, buf, 2) == K.ERR_INVALID_ARGUMENT

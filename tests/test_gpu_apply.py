@@ -325,3 +325,42 @@ def test_aliasing_refused_and_outputs_untouched(ctx):
     assert e.value.status == K.ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
     assert torch.equal(inp["src_k"], src_before)
+
+
+def test_timing_ring():
+    """kvmap_last_timings / kvmap_timings: nothing held before a timed apply; the RoPE-table
+    time is reported only by the apply that built the tables; untimed applies do not enter the
+    ring; the ring holds the last 128 timed applies and refuses older ones; every duration read
+    back is finite and non-negative, the kernels' positive."""
+    from cross_model_kv_amd import kvmap as K
+    cfg = EDGE[0]  # ragged T, bf16: de-rotation and the long-cache GEMM
+    inp = apply_inputs(cfg, "cuda:0")
+    c = K.Context(0)
+    try:
+        with pytest.raises(K.KvmapError):
+            c.last_timings()
+        with pytest.raises(K.KvmapError):
+            c.timings(0)
+        _run(c, cfg, inp, flags=K.FLAG_TIMING)
+        first = c.last_timings()
+        _run(c, cfg, inp)  # untimed: not recorded
+        _run(c, cfg, inp, flags=K.FLAG_TIMING)
+        second = c.last_timings()
+        print(f"[timing] first {first}, second {second}", flush=True)
+        assert first[0] > 0 and second[0] == 0.0  # tables built once, then cached
+        for t in (first, second):
+            assert all(np.isfinite(v) and v >= 0 for v in t) and t[1] > 0 and t[2] > 0
+        assert c.timings(0) == second and c.timings(1) == first
+        with pytest.raises(K.KvmapError):
+            c.timings(2)
+        with pytest.raises(K.KvmapError):
+            c.timings(-1)
+        for _ in range(130):
+            c.apply(inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"], inp["b_v"],
+                    cfg.theta_src, cfg.theta_tgt, pos0_src=cfg.pos0, flags=K.FLAG_TIMING)
+        torch.cuda.synchronize()
+        assert c.timings(127)[2] > 0
+        with pytest.raises(K.KvmapError):
+            c.timings(128)
+    finally:
+        c.close()
