@@ -17,10 +17,11 @@ recode     kvmap_recode (identity map: RoPE re-encode, one rotation per pair) of
            whole source key cache, timed with HIP events; GB/s against the 8 TB/s HBM peak
 fit        the fit side on its own workload (262,144 calibration tokens, p 8192, q 1024, batches of
            4096): one kvmap_gram call per batch (shift, hi/lo split, co-moments, Chan merge), 64
-           calls timed with HIP events on its stream after at least 0.3 s of warm-up calls; one ridge solve of the merged state on the host and one
-           on the device (fp64, W written in bf16 output-major)
-short      kvmap_apply on the first T tokens (T = 1 .. 256) with the workload's maps: ms against the
-           HBM roofline of reading W and the rows
+           calls timed with HIP events on its stream after at least 0.3 s of warm-up calls; one
+           ridge solve of the merged state on the host and one on the device (fp64, W written in
+           bf16 output-major)
+short      kvmap_apply on the first T tokens (T = 1 .. 8192) with the workload's maps: ms against the
+           larger of the HBM roofline (W and the rows) and the matrix-core roofline
 fit_driver the complete fit (layer selection, then the maps) at the 14B->32B model shape over
            --fit-seqs seeded calibration sequences of 4096 tokens: wall seconds per pass
 library_gemm  context for the roofline: the vendor BLAS (torch.matmul, hipBLASLt on ROCm) on the
@@ -130,12 +131,13 @@ def recode_leg(K, ctx, cfg, src, iters=10, warmup=2):
             "frac_hbm": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
 
 
-def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=3):
-    """Short caches (the short-prefix regime): kvmap_apply of the workload's first T tokens for a
-    few T, with all of the workload's maps.  At these lengths the apply reads all of W (2 x L_tgt
-    x N x F bf16) for little arithmetic, so the bound is HBM: W + the gathered source rows +
-    the written target rows over 8 TB/s.  Caches of up to 128 tokens take the persistent
-    short-cache kernel."""
+def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256, 512, 1024, 2048, 4096, 8192), iters=20, warmup=3):
+    """Short and middle caches (the short-prefix regime): kvmap_apply of the workload's first T
+    tokens for a range of T, with all of the workload's maps.  The roofline is the larger of the
+    HBM time (W, 2 x L_tgt x N x F bf16, + the gathered source rows + the written target rows
+    over 8 TB/s) and the matrix-core time (2 T F N per target layer, K and V, at the bf16 dense
+    peak): HBM bounds the apply up to a few hundred tokens, the matrix cores beyond.  Caches of
+    up to 128 tokens take the persistent short-cache kernel."""
     import torch
     stream = torch.cuda.current_stream()
     w_bytes = 2 * cfg.L_tgt * cfg.N * cfg.F * 2
@@ -163,11 +165,17 @@ def short_leg(K, ctx, cfg, inp, lengths=(1, 16, 64, 128, 256), iters=20, warmup=
         x_bytes = 2 * cfg.L_tgt * cfg.k * cfg.H * T * cfg.d * 2   # gathered per target layer, K and V
         o_bytes = 2 * cfg.L_tgt * cfg.H * T * cfg.d * 2
         roof_ms = (w_bytes + x_bytes + o_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3
+        mfma_ms = 2.0 * 2 * cfg.L_tgt * T * cfg.F * cfg.N / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        bound = max(roof_ms, mfma_ms)
         rows.append({"T": T, "ms": ms, "W_GBps": w_bytes / (ms / 1e3) / 1e9, "hbm_roofline_ms": roof_ms,
-                     "frac_hbm": roof_ms / ms, "kernel": "map_bf16_small" if T <= 128 else "map_bf16"})
-        log(f"short T={T}: {ms:.3f} ms ({w_bytes / (ms / 1e3) / 1e12:.2f} TB/s of W; HBM roofline {roof_ms:.3f} ms)")
+                     "mfma_roofline_ms": mfma_ms, "bound": "hbm" if roof_ms >= mfma_ms else "mfma",
+                     "frac_hbm": roof_ms / ms, "frac_roofline": bound / ms,
+                     "kernel": "map_bf16_small" if T <= 128 else "map_bf16"})
+        log(f"short T={T}: {ms:.3f} ms ({w_bytes / (ms / 1e3) / 1e12:.2f} TB/s of W; HBM roofline {roof_ms:.3f} ms, "
+            f"matrix-core roofline {mfma_ms:.3f} ms: {bound / ms * 100:.0f} % of the larger)")
         del sk, sv, ok_, ov_
-    return {"workload": f"{cfg.name} maps (W {w_bytes / 1e9:.2f} GB bf16) on the first T tokens of the cache",
+    return {"workload": f"{cfg.name} maps (W {w_bytes / 1e9:.2f} GB bf16) on the first T tokens of the cache; "
+                        f"roofline = max(HBM, matrix cores)",
             "lengths": rows}
 
 
