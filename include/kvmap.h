@@ -269,13 +269,15 @@ int kvmap_gram_reset(kvmap_ctx* ctx, kvmap_gram_state* st, void* stream);
 
 /* Merge one batch of n_b rows into st (Chan/Welford pairwise update, KVBridge README
  * fitting section):  X device [n_b][p], Y device [n_b][q], row-major, in `dtype`
- * (bf16 or fp32).  The batch is shifted by its own column means before its co-moments
- * are formed, then
+ * (bf16 or fp32).  The batch's co-moments M_b about its own mean are formed from
+ * shifted values x - c (the batch mean m of x - c is removed exactly), then
  *   delta = mean_b - mean,  mean += delta * n_b / n',  M += M_b + (n * n_b / n') delta delta^T
- * with n' = n + n_b.  bf16 batches: the shift is the column mean rounded to bf16, the
- * shifted values are split into bf16 hi + lo and the co-moments come from three bf16
- * matrix-core passes (hi hi + hi lo + lo hi) with fp32 accumulation; batches of more than
- * 16384 rows are merged in sub-batches of at most 16384 rows.  fp32 batches: fp32 mean,
+ * with n' = n + n_b.  bf16 batches: c is the batch's column mean rounded to bf16 when the
+ * state is empty, else the running mean rounded to bf16 (so a merging batch is read once
+ * before its co-moments); x - c is then exact in fp32, split into bf16 hi + lo, and the
+ * co-moments come from three bf16 matrix-core passes (hi hi + hi lo + lo hi) with fp32
+ * accumulation; batches of more than 16384 rows are merged in sub-batches of at most 16384
+ * rows.  fp32 batches: fp32 mean,
  * fp32 matrix cores.  The context keeps the shifted operands of one sub-batch as scratch
  * ((p + q) * ceil(rows / 32) * 128 bytes, allocated on first use).  n_b = 0 is a no-op.
  * p, q must be multiples of 4 and <= 65536, n_b <= 2^31.  Asynchronous on `stream`;
