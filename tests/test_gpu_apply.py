@@ -370,3 +370,47 @@ def test_timing_ring():
             c.timings(128)
     finally:
         c.close()
+
+
+def test_two_contexts_two_threads():
+    """Two contexts driven from two host threads at once, each on its own stream, with different
+    shapes: every output equals the same apply run alone (contexts share no state)."""
+    import threading
+    from cross_model_kv_amd import kvmap as K
+    cfgs = (EDGE[5], EDGE[0])
+    inps = [apply_inputs(c, "cuda:0") for c in cfgs]
+    ref = []
+    for c, inp in zip(cfgs, inps):
+        cx = K.Context(0)
+        ref.append(_run(cx, c, inp))
+        cx.close()
+    ctxs = [K.Context(0) for _ in cfgs]
+    streams = [torch.cuda.Stream() for _ in cfgs]
+    outs = [[None] * 4 for _ in cfgs]
+    errors = []
+
+    def worker(w):
+        try:
+            c, inp = cfgs[w], inps[w]
+            for it in range(4):
+                ok_ = torch.empty((c.L_tgt, c.H, c.T, c.d), dtype=torch.bfloat16, device="cuda:0")
+                ov_ = torch.empty_like(ok_)
+                ctxs[w].apply(inp["src_k"], inp["src_v"], inp["layer_sel"], inp["W_k"], inp["b_k"], inp["W_v"],
+                              inp["b_v"], c.theta_src, c.theta_tgt, pos0_src=c.pos0, out_k=ok_, out_v=ov_,
+                              stream=streams[w])
+                outs[w][it] = (ok_, ov_)
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in range(len(cfgs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for c in ctxs:
+        c.close()
+    assert not errors, errors
+    for w in range(len(cfgs)):
+        for ok_, ov_ in outs[w]:
+            assert torch.equal(ok_, ref[w][0]) and torch.equal(ov_, ref[w][1])
