@@ -169,10 +169,14 @@ __global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int 
         a[j] = lrj;
         col[r] = lrj;
         rdiag[j] = rj;  // the same value from every lane (d is the wave's broadcast pivot)
-        __syncthreads();
+        // The workgroup is one wave, whose LDS operations complete in issue order, so the
+        // column written above is what the reads below see, and the next step's write comes
+        // after these reads, with no barrier.  The empty asm keeps the compiler from moving LDS
+        // accesses across it; the arithmetic of neighbouring steps may still interleave.
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int m = j + 1; m < RB; ++m) a[m] -= lrj * col[m];
-        __syncthreads();  // every read of col done before the next step writes it
+        asm volatile("" ::: "memory");
     }
     if (bad && r == 0) atomicOr(&g.bad[blockIdx.y], 1);
     // the factor, zero above the diagonal: back to A (coalesced rows, through LDS) and kept in
