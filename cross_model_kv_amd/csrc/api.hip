@@ -785,11 +785,10 @@ static GramScratch gram_scratch(kvmap_ctx* c, int p, int q, int splits) {
     return gram_scratch_at(c->gram, c->gram_split, p, q, splits);
 }
 
-// Checks shared by kvmap_gram and kvmap_gram_noalloc; KVMAP_OK with *empty set for n_b = 0.
-static int check_gram_call(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
-                           const kvmap_gram_state* st, const char* who, bool* empty) {
+// Host checks of a statistics call (no context involved); KVMAP_OK with *empty set for n_b = 0.
+static int check_gram_args(const void* X, const void* Y, int64_t n_b, int32_t dtype, const kvmap_gram_state* st,
+                           const char* who, bool* empty) {
     *empty = false;
-    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: ctx is NULL", who);
     int r = validate_state(st, who);
     if (r) return r;
     if (dtype != KVMAP_DTYPE_BF16 && dtype != KVMAP_DTYPE_F32)
@@ -802,7 +801,31 @@ static int check_gram_call(kvmap_ctx* c, const void* X, const void* Y, int64_t n
     if (!X || !Y) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: NULL batch", who);
     if ((((uintptr_t)X) | ((uintptr_t)Y)) & 15)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: batch pointers must be 16-byte aligned", who);
+    // the batch is read while the state is written: no overlap
+    const size_t es = dtype == KVMAP_DTYPE_BF16 ? 2 : 4;
+    const size_t xb = (size_t)n_b * st->p * es, yb = (size_t)n_b * st->q * es;
+    const size_t p = (size_t)st->p, q = (size_t)st->q;
+    const void* outs[5] = {st->mean_x, st->mean_y, st->M_xx, st->M_xy, st->ss_y};
+    const size_t osz[5] = {p * 4, q * 4, p * (st->xx_block ? (size_t)st->xx_block : p) * 4, p * q * 4, q * 4};
+    for (int i = 0; i < 5; ++i)
+        if (outs[i] && (ranges_overlap(X, xb, outs[i], osz[i]) || ranges_overlap(Y, yb, outs[i], osz[i])))
+            return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: the batch overlaps the state", who);
     return KVMAP_OK;
+}
+
+extern "C" int kvmap_validate_gram(const kvmap_gram_state* st, const void* X, const void* Y, int64_t n_b,
+                                   int32_t dtype) {
+    bool empty = false;
+    const int r = check_gram_args(X, Y, n_b, dtype, st, "kvmap_gram", &empty);
+    return r ? r : ok();
+}
+
+// Checks shared by kvmap_gram and kvmap_gram_noalloc; KVMAP_OK with *empty set for n_b = 0.
+static int check_gram_call(kvmap_ctx* c, const void* X, const void* Y, int64_t n_b, int32_t dtype,
+                           const kvmap_gram_state* st, const char* who, bool* empty) {
+    *empty = false;
+    if (!c) return fail(KVMAP_ERR_INVALID_ARGUMENT, "%s: ctx is NULL", who);
+    return check_gram_args(X, Y, n_b, dtype, st, who, empty);
 }
 
 // The batch merged in sub-batches of at most `sub` rows (Chan merges compose exactly), each

@@ -93,6 +93,8 @@ _SIGS = {
     "kvmap_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "kvmap_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims)]),
     "kvmap_validate_apply_buffers": (ctypes.c_int, [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 8),
+    "kvmap_validate_gram": (ctypes.c_int, [ctypes.POINTER(GramStateC), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int32]),
     "kvmap_validate_apply": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Rope),
                                             ctypes.POINTER(Rope)]),
     "kvmap_apply": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p,
@@ -201,6 +203,14 @@ def validate_apply_buffers(L_src, L_tgt, H, d, k, T, dtype, src_k, src_v, W_k, b
     dm = _dims(L_src, L_tgt, H, d, k, T, dtype)
     addrs = [ctypes.c_void_p(int(a)) if a else None for a in (src_k, src_v, W_k, b_k, W_v, b_v, tgt_k, tgt_v)]
     return lib().kvmap_validate_apply_buffers(ctypes.byref(dm), *addrs)
+
+
+def validate_gram(p, q, n, mean_x, mean_y, M_xx, M_xy, ss_y, xx_block, X, Y, n_b, dtype) -> int:
+    """kvmap_validate_gram on a state and batch given as addresses (integers; nothing is read);
+    returns the status code (host only, needs no GPU)."""
+    st = GramStateC(int(n), int(p), int(q), mean_x or None, mean_y or None, M_xx or None, M_xy or None,
+                    ss_y or None, int(xx_block))
+    return lib().kvmap_validate_gram(ctypes.byref(st), X or None, Y or None, int(n_b), int(dtype))
 
 
 def ridge_solve_host(mean_x, mean_y, M_xx, M_xy, lam: float, n_threads: int = 0):

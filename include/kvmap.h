@@ -285,6 +285,14 @@ int kvmap_gram_reset(kvmap_ctx* ctx, kvmap_gram_state* st, void* stream);
 int kvmap_gram(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b, int32_t dtype,
                kvmap_gram_state* st, void* stream);
 
+/* Host-only checks of a kvmap_gram / kvmap_gram_noalloc call, on the state and the batch
+ * addresses (nothing is read): the state's dims and arrays (SHAPE / INVALID_ARGUMENT), dtype
+ * (UNSUPPORTED), n_b in [0, 2^31] (SHAPE), and for n_b > 0 non-NULL, 16-byte aligned X and Y
+ * whose ranges ([n_b][p] and [n_b][q] in dtype) overlap none of the state's arrays
+ * (INVALID_ARGUMENT).  The statistics calls run exactly these checks, after their context
+ * check, before any device work.  Needs no device. */
+int kvmap_validate_gram(const kvmap_gram_state* st, const void* X, const void* Y, int64_t n_b, int32_t dtype);
+
 /* kvmap_gram for callers that cannot allocate: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, checks and result as kvmap_gram,
  * but the scratch (split partial sums, shift, means, deltas and the bf16 hi/lo operands of a

@@ -70,6 +70,26 @@ static void validation() {
         CHECK(kvmap_validate_apply_buffers(&d, nullptr, sv, wk, bk, wv, bv, tk, tv) == KVMAP_ERR_INVALID_ARGUMENT,
               "NULL input accepted");
     }
+    // statistics call checks on addresses (never read)
+    {
+        char* base = reinterpret_cast<char*>(uintptr_t(3) << 40);
+        kvmap_gram_state gs{};
+        gs.p = 520;
+        gs.q = 68;
+        gs.mean_x = reinterpret_cast<float*>(base);
+        gs.mean_y = reinterpret_cast<float*>(base + 4096);
+        gs.M_xx = reinterpret_cast<float*>(base + 8192);
+        gs.M_xy = reinterpret_cast<float*>(base + 8192 + 520 * 520 * 4);
+        const char* xb = base + (size_t(64) << 20);
+        const char* yb = xb + (size_t(16) << 20);
+        CHECK(kvmap_validate_gram(&gs, xb, yb, 700, KVMAP_DTYPE_BF16) == KVMAP_OK, "good gram call refused: %s",
+              kvmap_last_error());
+        CHECK(kvmap_validate_gram(&gs, gs.M_xx, yb, 700, KVMAP_DTYPE_BF16) == KVMAP_ERR_INVALID_ARGUMENT,
+              "batch over the state accepted");
+        CHECK(kvmap_validate_gram(&gs, xb, yb, -1, KVMAP_DTYPE_BF16) == KVMAP_ERR_SHAPE, "negative n_b accepted");
+        CHECK(kvmap_validate_gram(nullptr, xb, yb, 700, KVMAP_DTYPE_BF16) == KVMAP_ERR_INVALID_ARGUMENT,
+              "NULL state accepted");
+    }
     // kvmap_reserve checks the dims before the context
     kvmap_dims zero{};
     CHECK(kvmap_reserve(nullptr, &zero) == KVMAP_ERR_SHAPE, "zero dims reached the workspace arithmetic");

@@ -266,3 +266,48 @@ def test_timings_refuse_without_context():
     assert K.lib().kvmap_timings(None, 0, buf, 3) == K.ERR_INVALID_ARGUMENT
     assert K.lib().kvmap_last_timings(None, buf, 3) == K.ERR_INVALID_ARGUMENT
     assert K.lib().kvmap_timings(None, 0, buf, 2) == K.ERR_INVALID_ARGUMENT
+
+
+def _gram_addrs(p=520, q=68, n_b=700, dtype=K.BF16, xx_block=0, ss_y=True):
+    """Addresses of a state and a batch laid out apart, 16-byte aligned (never read)."""
+    es = 2 if dtype == K.BF16 else 4
+    sizes = dict(mean_x=p * 4, mean_y=q * 4, M_xx=p * (xx_block or p) * 4, M_xy=p * q * 4, ss_y=q * 4,
+                 X=n_b * p * es, Y=n_b * q * es)
+    addr, base = {}, 1 << 41
+    for k_, n in sizes.items():
+        addr[k_] = base
+        base += (n + 4095) // 4096 * 4096
+    if not ss_y:
+        addr["ss_y"] = 0
+    return addr, sizes
+
+
+def _vg(p=520, q=68, n_b=700, dtype=K.BF16, xx_block=0, n=0, **over):
+    a, _ = _gram_addrs(p, q, n_b, dtype, xx_block)
+    a.update(over)
+    return K.validate_gram(p, q, n, a["mean_x"], a["mean_y"], a["M_xx"], a["M_xy"], a["ss_y"], xx_block,
+                           a["X"], a["Y"], n_b, dtype)
+
+
+def test_validate_gram_accepts_and_refuses():
+    """kvmap_validate_gram: the statistics calls' host checks, before any device work."""
+    a, sz = _gram_addrs()
+    assert _vg() == K.OK
+    assert _vg(dtype=K.F32) == K.OK
+    assert _vg(xx_block=104) == K.OK
+    assert _vg(n_b=0, X=0, Y=0) == K.OK                            # an empty batch is a no-op
+    assert _vg(dtype=7) == K.ERR_UNSUPPORTED
+    assert _vg(n_b=-1) == K.ERR_SHAPE
+    assert _vg(p=522) == K.ERR_SHAPE                                # not a multiple of 4
+    assert _vg(xx_block=12) == K.ERR_SHAPE                          # does not divide p
+    assert _vg(n=-5) == K.ERR_SHAPE
+    assert _vg(X=0) == K.ERR_INVALID_ARGUMENT
+    assert _vg(M_xy=0) == K.ERR_INVALID_ARGUMENT
+    assert _vg(Y=a["Y"] + 8) == K.ERR_INVALID_ARGUMENT             # misaligned
+    assert _vg(X=a["M_xx"]) == K.ERR_INVALID_ARGUMENT              # the batch over the state
+    assert _vg(Y=a["M_xy"] + sz["M_xy"] - 16) == K.ERR_INVALID_ARGUMENT
+    assert _vg(X=a["mean_y"] - 16) == K.ERR_INVALID_ARGUMENT
+    assert _vg(Y=a["ss_y"]) == K.ERR_INVALID_ARGUMENT
+    assert K.last_error() != ""
+    # adjacent, not overlapping
+    assert _vg(Y=a["ss_y"] + sz["ss_y"]) == K.OK
