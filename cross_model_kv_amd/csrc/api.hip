@@ -920,11 +920,21 @@ extern "C" int kvmap_gram_merge(kvmap_ctx* c, kvmap_gram_state* dst, const kvmap
     if (r) return r;
     if (dst->p != src->p || dst->q != src->q)
         return fail(KVMAP_ERR_SHAPE, "kvmap_gram_merge: p/q differ");
-    if (dst->M_xx == src->M_xx) return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src alias");
     if (!dst->ss_y != !src->ss_y)
         return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: ss_y kept by one state only");
     if (dst->xx_block != src->xx_block)
         return fail(KVMAP_ERR_SHAPE, "kvmap_gram_merge: xx_block differs");
+    {
+        // dst is written while src is read: no array of one may overlap an array of the other
+        const size_t p = (size_t)dst->p, q = (size_t)dst->q, bx = dst->xx_block ? (size_t)dst->xx_block : p;
+        const size_t sz[5] = {p * 4, q * 4, p * bx * 4, p * q * 4, q * 4};
+        const void* da[5] = {dst->mean_x, dst->mean_y, dst->M_xx, dst->M_xy, dst->ss_y};
+        const void* sa[5] = {src->mean_x, src->mean_y, src->M_xx, src->M_xy, src->ss_y};
+        for (int i = 0; i < 5; ++i)
+            for (int j = 0; j < 5; ++j)
+                if (da[i] && sa[j] && ranges_overlap(da[i], sz[i], sa[j], sz[j]))
+                    return fail(KVMAP_ERR_INVALID_ARGUMENT, "kvmap_gram_merge: dst and src overlap");
+    }
     if (src->n == 0) return ok();
     DeviceGuard g(c->device);
     r = ensure_gram_scratch(c, dst->p, dst->q, 0);

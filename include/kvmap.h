@@ -319,7 +319,8 @@ int kvmap_gram_noalloc(kvmap_ctx* ctx, const void* X, const void* Y, int64_t n_b
  * accumulated apart and combined (KVBridge README, fitting section headed "Loading": only
  * centered statistics are kept and merged with Chan/Welford updates; "What ships": the
  * statistics are reduced across workers).  Merging an empty state is the identity.
- * Asynchronous on `stream`. */
+ * INVALID_ARGUMENT when any array of dst overlaps any array of src (or one keeps ss_y and the
+ * other does not); SHAPE when p, q or xx_block differ.  Asynchronous on `stream`. */
 int kvmap_gram_merge(kvmap_ctx* ctx, kvmap_gram_state* dst, const kvmap_gram_state* src,
                      void* stream);
 

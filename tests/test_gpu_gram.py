@@ -273,3 +273,26 @@ def test_gram_block_diagonal_state(ctx, dtype, bd):
     print(f"[gram] blocked {dtype} bd {bd}: worst block rel {worst:.2e}, M_xy {r_xy:.2e}, ss_y {r_ss:.2e}", flush=True)
     assert worst <= GRAM_REL and r_xy <= GRAM_REL and r_ss <= GRAM_REL
     assert np.max(np.abs(f(a.mean_x) - ref["mx"])) <= GRAM_REL * np.max(np.abs(ref["mx"]))
+
+
+def test_gram_merge_refuses_overlapping_states(ctx):
+    """A merge whose source shares memory with its destination is refused before any device
+    work, and the destination is left as it was."""
+    from cross_model_kv_amd import kvmap as K
+    (X, Y), = _batches(SMALL, [300])
+    a = ctx.gram_state(SMALL.p, SMALL.q)
+    ctx.gram_reset(a)
+    ctx.gram(a, _dev(X, "bf16"), _dev(Y, "bf16"))
+    b = ctx.gram_state(SMALL.p, SMALL.q)
+    ctx.gram_reset(b)
+    ctx.gram(b, _dev(X, "bf16"), _dev(Y, "bf16"))
+    torch.cuda.synchronize()
+    before = a.M_xx.clone()
+    b.c.M_xy = a.M_xx.data_ptr() + 4096  # b's cross-moments over a's Gram
+    with pytest.raises(K.KvmapError) as e:
+        ctx.gram_merge(a, b)
+    assert e.value.status == K.ERR_INVALID_ARGUMENT
+    with pytest.raises(K.KvmapError):
+        ctx.gram_merge(a, a)
+    torch.cuda.synchronize()
+    assert torch.equal(a.M_xx, before) and a.n == 300
