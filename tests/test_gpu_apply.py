@@ -80,6 +80,14 @@ EDGE = [
     ApplyConfig(205, "H1-d64-k5", 6, 2, 1, 64, 513, 5, 1.0e4, 1.0e4, "bf16", 0.5),
     # several token blocks and heads, small enough for the full oracle
     ApplyConfig(206, "bf16-T1100-H8", 6, 3, 8, 128, 1100, 2, 1.0e6, 1.0e6, "bf16", 0.5),
+    # every source layer selected (k = L_src), one token past the short-cache limit
+    ApplyConfig(207, "k-all-T129", 3, 2, 2, 128, 129, 3, 1.0e4, 1.0e6, "bf16", 0.5),
+    # the short-cache kernel at its limit with k = L_src and head dim 64
+    ApplyConfig(208, "short-T128-k-all-d64", 4, 3, 2, 64, 128, 4, 1.0e4, 5.0e5, "bf16", 0.5),
+    # positions from one million: large angles, different bases
+    ApplyConfig(209, "pos0-1M", 3, 2, 2, 128, 300, 2, 1.0e4, 1.0e6, "bf16", 0.5, pos0=1_000_000),
+    # fp32 with a single token and every layer selected
+    ApplyConfig(210, "fp32-T1-k-all", 2, 3, 1, 64, 1, 2, 1.0e4, 5.0e5, "f32", 0.0),
 ]
 
 

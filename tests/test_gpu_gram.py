@@ -296,3 +296,17 @@ def test_gram_merge_refuses_overlapping_states(ctx):
         ctx.gram_merge(a, a)
     torch.cuda.synchronize()
     assert torch.equal(a.M_xx, before) and a.n == 300
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gram_smallest_state(ctx, dtype):
+    """p = q = 4 (the smallest state: one partial tile each way), batches of 1, 5 and 33 rows
+    with the fit-statistics offsets, against the oracle on every element."""
+    cfg = FIT_STATS_CONFIG.replace(cid=403, p=4, q=4, n_tokens=64, batch=64, nnz=2)
+    parts = _batches(cfg, [1, 5, 33])
+    st = ctx.gram_state(cfg.p, cfg.q)
+    ctx.gram_reset(st)
+    for X, Y in parts:
+        ctx.gram(st, _dev(X, dtype), _dev(Y, dtype))
+    ref = oracle.stats_two_pass(np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    _check_state(st, ref, f"smallest {dtype}")
