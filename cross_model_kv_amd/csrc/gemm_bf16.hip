@@ -271,7 +271,7 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         rd_a(cw, 0, i, fa0);
         if (i < JB) rd_b(cx, 0, i, fb0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
+    auto kstep = [&]() {  // one K-step
 #pragma unroll
         for (int i = 0; i < IB; ++i) {
             rd_a(cw, 1, i, fa1);
@@ -298,7 +298,15 @@ __global__ __launch_bounds__(512) void map_bf16_kernel(MapArgs a, int L_tgt, int
         }
         cw = cw1;
         cx = cx1;
+    };
+    // Two K-steps per trip of the loop (measured 0.4-1.1 % faster than one, same results);
+    // an odd count (d = 64 with k H odd) ends with one more.
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+        kstep();
+        kstep();
     }
+    if (kt < nk) kstep();
     wait_vmcnt<0>();  // the extra tail stages must land before LDS is reused below
     __syncthreads();  // every wave is done reading the pipeline buffers
 
