@@ -330,7 +330,7 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
         bhi[j] = rd_b(cb, 0, j);
         blo[j] = rd_b(cb, 1, j);
     }
-    for (int kb = 0; kb < nkb; ++kb) {
+    auto kstep = [&]() {  // one K-step
 #pragma unroll
         for (int i = 0; i < IB; ++i) {
             alo[i] = rd_a(ca, 1, i);
@@ -365,7 +365,14 @@ __global__ __launch_bounds__(512) void gram_x3_kernel(const uint16_t* __restrict
         }
         ca = ca1;
         cb = cb1;
+    };
+    // two K-steps per trip of the loop, as in the map GEMM; an odd count ends with one more
+    int kb = 0;
+    for (; kb + 2 <= nkb; kb += 2) {
+        kstep();
+        kstep();
     }
+    if (kb < nkb) kstep();
     wait_vmcnt<0>();
 
     // Epilogue: lane holds G[i][j] for j = column (lane & 15) and i = 4 (lane / 16) + r of
