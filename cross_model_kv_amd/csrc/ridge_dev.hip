@@ -440,18 +440,19 @@ __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    static_assert((RB / KB) % 2 == 0, "stages come in pairs");
     const int nkb = nk * (RB / KB);
     fetch(0);
     stash(0);
     if (nkb > 1) fetch(1);
     __syncthreads();
-    for (int kc = 0; kc < nkb; ++kc) {
-        const int cur = kc & 1;
+    // one stage; cur is a constant in both calls below, so every LDS address folds
+    auto kstage = [&](int kc, const int cur) {
         if (kc + 1 < nkb) stash(cur ^ 1);  // that buffer's last reader was stage kc - 1
         if (kc + 2 < nkb) fetch(kc + 2);
         const double* as = As[cur];
         const double* bs = Bs[cur];
-#pragma unroll 2
+#pragma unroll
         for (int kk = 0; kk < KB; kk += 4) {
             const int m = kk + lk;
             double a[4], b[2];
@@ -472,6 +473,10 @@ __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();  // stage kc read by every wave before its buffer is refilled
+    };
+    for (int kc = 0; kc < nkb; kc += 2) {  // nkb = nk RB / KB is even
+        kstage(kc, 0);
+        kstage(kc + 1, 1);
     }
     double cv[4][2][4];  // C read whole before any store (see ridge_update_kernel)
 #pragma unroll
