@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
 // = 64 nk from block k0 (i0, j0: first row and column tile, in tiles of 128; ncol: column tiles;
 // MODE 0 takes the lower triangle of tiles from tile j0 on, and computes the diagonal tiles
 // whole: their upper 64 x 64 quarter is never read).  Twice the arithmetic per operand byte of
-// the 64 x 64 kernel.  4 waves, each a 64 x 64 quarter of C as 4 x 4 blocks of 16 x 16
+// the 64 x 64 kernel.  8 waves, each a 64 x 32 eighth of C as 4 x 2 blocks of 16 x 16
 // (v_mfma_f64_16x16x4f64).  The operands go through LDS in stages of K = 32, two stages
 // deep: the registers holding stage kc + 1 are written to LDS, and stage kc + 2 is requested,
 // before the MFMAs of stage kc, so neither waits on the other.
