@@ -1,7 +1,9 @@
 """Upload seeded workloads to a GPU (torch tensors), generating chunks on host threads.
 
-Only draws and copies happen here: every value equals what synth.workloads returns for
-the same chunk, so the oracle can regenerate any part of the input on the host.
+Only draws and copies happen here.  Every value of apply_inputs and fit_inputs equals what
+synth.workloads returns for the same chunk, so the oracle can regenerate any part of the input on
+the host; device_apply_inputs draws on the device instead (shapes too large for the host), and
+its checks read back the input rows they use.
 """
 
 from __future__ import annotations
@@ -68,6 +70,34 @@ def apply_inputs(cfg: ApplyConfig, device="cuda:0", progress=None) -> dict:
             if progress and done % 64 == 0:
                 progress(done, len(jobs))
     torch.cuda.synchronize(device)
+    return out
+
+
+def device_apply_inputs(cfg: ApplyConfig, device="cuda:0") -> dict:
+    """The inputs of one apply call drawn on `device` with torch's seeded generator, for caches
+    too large to draw on the host (the largest accepted shapes): src_k, src_v ~ N(0, 1); W_k, W_v
+    ~ N(0, 1/F); b_k, b_v ~ N(0, b_var); layer_sel as synth.workloads draws it.  These values do
+    not match synth.workloads: whoever checks them reads back the rows it needs."""
+    torch = _torch()
+    g = torch.Generator(device=device).manual_seed(20260000 + cfg.cid)
+    dt = torch_dtype(cfg.dtype)
+
+    def normal(shape, std):
+        t = torch.empty(shape, dtype=dt, device=device)
+        flat = t.view(-1)
+        step = 1 << 28  # a 1 GiB float32 temporary at most
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            flat[i:i + n].copy_(torch.randn(n, generator=g, device=device, dtype=torch.float32) * std)
+        return t
+
+    out = dict(layer_sel=layer_sel(cfg))
+    for w in ("k", "v"):
+        out[f"src_{w}"] = normal((cfg.L_src, cfg.H, cfg.T, cfg.d), 1.0)
+        out[f"W_{w}"] = normal((cfg.L_tgt, cfg.N, cfg.F), cfg.F ** -0.5)
+        out[f"b_{w}"] = normal((cfg.L_tgt, cfg.N), cfg.b_var ** 0.5)
+    if torch.device(device).type == "cuda":
+        torch.cuda.synchronize(device)
     return out
 
 

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from gpu_common import Tally, compare, to_f64
-from synth.device import apply_inputs
+from synth.device import apply_inputs, device_apply_inputs
 from synth.workloads import APPLY_CONFIGS, ApplyConfig, b_layer, layer_sel, src_layer, to_f64 as s2f, w_layer
 
 pytestmark = pytest.mark.gpu
@@ -232,6 +232,30 @@ def test_full_size_sampled(ctx, cid):
     # determinism at full size
     ok2, ov2 = _run(ctx, cfg, inp)
     assert torch.equal(ok_, ok2) and torch.equal(ov_, ov2)
+
+
+def test_largest_cache(ctx):
+    """The largest cache the boundary accepts at head dim 128: T = 2^24 - 1 tokens, one layer and
+    one head (k = 1), so T * d sits just under the 2^31 limit, the 32-bit byte offsets of the
+    gathered rows reach their top, the last token block is ragged (255 tokens) and the RoPE
+    positions run to 1.7e7.  Inputs are drawn on the device.  Every output element is written
+    (NaN prefill); one row of every 256-token block, the first 256 and the last 300 rows are
+    checked against the oracle."""
+    cfg = ApplyConfig(231, "max-T", 1, 1, 1, 128, (1 << 24) - 1, 1, 1.0e4, 1.0e6, "bf16", 0.0)
+    assert cfg.T * cfg.d < 2 ** 31 <= (cfg.T + 1) * cfg.d
+    print(f"[apply] generating {cfg.name} on the device", flush=True)
+    inp = device_apply_inputs(cfg)
+    shape = (cfg.L_tgt, cfg.H, cfg.T, cfg.d)
+    ok_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    ov_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    _run(ctx, cfg, inp, out_k=ok_, out_v=ov_)
+    assert bool(torch.isfinite(ok_).all()) and bool(torch.isfinite(ov_).all()), "an output tile was not written"
+    rows = np.unique(np.concatenate([_block_rows(cfg.T, seed=231), np.arange(256), np.arange(cfg.T - 300, cfg.T)]))
+    tally = Tally()
+    _check_sampled(cfg, inp, ok_, ov_, [0], rows, tally)
+    print(f"[apply] {cfg.name} total: {tally.summary()}", flush=True)
+    del inp, ok_, ov_
+    torch.cuda.empty_cache()
 
 
 def test_alternating_selections_queue_without_host_wait(ctx):

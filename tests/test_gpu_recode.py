@@ -74,6 +74,24 @@ def test_recode_matches_oracle(ctx, rows, T, d, dtype, ts, tt, ps, pt):
     _check(out, ref, dtype, f"rows {rows} T {T} d {d} {dtype} {ts:g}->{tt:g} pos0 {ps}->{pt}")
 
 
+def test_recode_largest_cache(ctx):
+    """One row of T = 2^24 - 1 tokens at d 128 (T * d just under 2^31, positions to 1.7e7 from
+    pos0 1000), drawn on the device; 3 tokens of every 4096 and the last 300 are checked."""
+    T, d = (1 << 24) - 1, 128
+    g = torch.Generator(device="cuda:0").manual_seed(2026602)
+    x = (torch.randn((1, T, d), generator=g, device="cuda:0") * 2.0).to(torch.bfloat16)
+    out = ctx.recode(x, 1.0e4, 1.0e6, pos0_src=1000, pos0_tgt=1000)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng([2026, 603])
+    toks = np.unique(np.concatenate([rng.integers(0, T, 3 * (T // 4096)), np.arange(T - 300, T)]))
+    idx = torch.as_tensor(toks, device="cuda:0")
+    x64 = x[:, idx, :].float().cpu().double().numpy()
+    ref = _ref(x64, 1000 + toks, 1000 + toks, 1.0e4, 1.0e6)
+    _check(out[:, idx, :], ref, "bf16", f"T {T} d {d} bf16, {len(toks)} sampled tokens")
+    del x, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_recode_equal_bases_is_a_copy(ctx, dtype):
     """theta and pos0 equal on both sides: the angle difference is exactly 0 in fp64, so the
