@@ -258,6 +258,47 @@ def test_largest_cache(ctx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("T", [300, 100])
+def test_largest_map(ctx, T):
+    """The largest map the boundary accepts at d 128 and k 64: H = 45 heads, so N * F =
+    5760 * 368,640 = 2,123,366,400 sits just under 2^31 (4.25 GB per map) and the 32-bit byte
+    offsets of the map rows reach their top.  T = 300 runs the tiled kernel (a ragged second
+    token block, a half-filled last feature tile), T = 100 the short-cache kernel.  Inputs are
+    drawn on the device.  Every output element is written (NaN prefill); six rows of heads 0, 1,
+    22 and 44, K and V, are checked against the oracle, which maps those heads' rows of W."""
+    cfg = ApplyConfig(232, f"max-map-T{T}", 64, 1, 45, 128, T, 64, 1.0e4, 1.0e6, "bf16", 0.0)
+    assert cfg.N * cfg.F < 2 ** 31 <= (cfg.N + cfg.d) * (cfg.F + cfg.k * cfg.d)
+    print(f"[apply] generating {cfg.name} on the device", flush=True)
+    inp = device_apply_inputs(cfg)
+    shape = (cfg.L_tgt, cfg.H, cfg.T, cfg.d)
+    ok_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    ov_ = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    _run(ctx, cfg, inp, out_k=ok_, out_v=ov_)
+    assert bool(torch.isfinite(ok_).all()) and bool(torch.isfinite(ov_).all()), "an output tile was not written"
+    rows = np.array(sorted({0, 1, T // 3, T // 2 + 1, T - 2, T - 1}))
+    heads = [0, 1, 22, 44]
+    rows_t = torch.as_tensor(rows, device="cuda:0")
+    sel = [int(s) for s in inp["layer_sel"][0]]
+    pos = cfg.pos0 + rows
+    xk = oracle.feature_rows([oracle.strip_rope(to_f64(inp["src_k"][s][:, rows_t, :]), pos, cfg.theta_src) for s in sel])
+    xv = oracle.feature_rows([to_f64(inp["src_v"][s][:, rows_t, :]) for s in sel])
+    n_idx = torch.as_tensor(np.concatenate([np.arange(h * cfg.d, (h + 1) * cfg.d) for h in heads]), device="cuda:0")
+    R, nh = len(rows), len(heads)
+    heads_of = lambda y: y.reshape(R, nh, cfg.d).transpose(1, 0, 2)  # [R][nh*d] -> [nh][R][d]
+    yk = oracle.affine(xk, to_f64(inp["W_k"][0][n_idx]), to_f64(inp["b_k"][0][n_idx]))
+    yv = oracle.affine(xv, to_f64(inp["W_v"][0][n_idx]), to_f64(inp["b_v"][0][n_idx]))
+    ref = {0: (oracle.rope(heads_of(yk), pos, cfg.theta_tgt), heads_of(yv))}
+    h_t = torch.as_tensor(heads, device="cuda:0")
+    gk = {0: to_f64(ok_[0][h_t][:, rows_t, :])}
+    gv = {0: to_f64(ov_[0][h_t][:, rows_t, :])}
+    tally = Tally()
+    report, worst = compare(gk, gv, ref, cfg.dtype, tally=tally)
+    print(f"[apply] {cfg.name}: {R} rows x heads {heads}: worst {worst}; {tally.summary()}", flush=True)
+    assert not report, "\n".join(report[:20])
+    del inp, ok_, ov_
+    torch.cuda.empty_cache()
+
+
 def test_alternating_selections_queue_without_host_wait(ctx):
     """Applies with selections the context has not seen are queued behind 30 ms of other work on
     the same stream: the host returns while that work is still running (the selection goes up
