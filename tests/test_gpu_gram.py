@@ -209,6 +209,50 @@ def test_fit_stats_full_size(ctx):
     assert np.all(np.abs(Wb - W) <= 2.0 ** -8 * (1 + 1e-5) * np.abs(W) + 1e-30)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gram_largest_state(ctx, dtype):
+    """The largest state the boundary accepts, p = q = 65,536 (M_xx and M_xy 17.2 GB each, element
+    offsets past 2^32), with ss_y: batches of 300, 77 and 1 rows drawn on the device with
+    per-column offsets ~N(5, 1), so the first goes into the empty state and the others merge.
+    Sampled 96 x 96 of M_xx (both triangles), 96 x 64 of M_xy, the means and ss_y (first and last
+    columns included) against the oracle's two-pass statistics of those columns."""
+    from cross_model_kv_amd import kvmap as K
+    p = q = 65536
+    g = torch.Generator(device="cuda:0").manual_seed(2026604)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ox = 5.0 + torch.randn(p, generator=g, device="cuda:0")
+    oy = 5.0 + torch.randn(q, generator=g, device="cuda:0")
+    rng = np.random.default_rng([2026, 605])
+    cx = np.unique(np.concatenate([[0, p - 1], rng.choice(p, 94, replace=False)]))
+    cy = np.unique(np.concatenate([[0, q - 1], rng.choice(q, 62, replace=False)]))
+    cx_t, cy_t = torch.as_tensor(cx, device="cuda:0"), torch.as_tensor(cy, device="cuda:0")
+    st = ctx.gram_state(p, q, keep_ss_y=True)
+    ctx.gram_reset(st)
+    hx, hy = [], []
+    for n_b in (300, 77, 1):
+        X = (torch.randn((n_b, p), generator=g, device="cuda:0") + ox).to(dt)
+        Y = (torch.randn((n_b, q), generator=g, device="cuda:0") + oy).to(dt)
+        ctx.gram(st, X, Y)
+        hx.append(X[:, cx_t].double().cpu().numpy())
+        hy.append(Y[:, cy_t].double().cpu().numpy())
+    torch.cuda.synchronize()
+    ref = oracle.stats_two_pass(np.concatenate(hx), np.concatenate(hy))
+    f = lambda t: t.double().cpu().numpy()
+    Mxx = f(st.M_xx[cx_t][:, cx_t])
+    Mxy = f(st.M_xy[cx_t][:, cy_t])
+    r_xx, r_xy = _rel(Mxx, ref["Mxx"]), _rel(Mxy, ref["Mxy"])
+    mx = np.max(np.abs(f(st.mean_x[cx_t]) - ref["mx"])) / np.max(np.abs(ref["mx"]))
+    my = np.max(np.abs(f(st.mean_y[cy_t]) - ref["my"])) / np.max(np.abs(ref["my"]))
+    r_ss = _rel(f(st.ss_y[cy_t]), ref["ssy"])
+    print(f"[gram] largest state {dtype}: rel M_xx {r_xx:.2e} M_xy {r_xy:.2e} mean_x {mx:.2e} mean_y {my:.2e} "
+          f"ss_y {r_ss:.2e}", flush=True)
+    assert st.n == 378
+    assert max(r_xx, r_xy, mx, my, r_ss) <= GRAM_REL
+    assert np.max(np.abs(Mxx - Mxx.T)) <= 1e-6 * np.max(np.abs(Mxx))
+    del st
+    torch.cuda.empty_cache()
+
+
 def test_ridge_solve_device_matches_oracle(ctx):
     """kvmap_ridge_solve_device on a GPU-built state (p = 520, q = 68: padded to multiples of
     128 inside, 10 blocks of 64 in 3 panels, so the 128-tile updates of the trailing matrix and
