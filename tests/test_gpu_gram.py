@@ -253,6 +253,44 @@ def test_gram_largest_state(ctx, dtype):
     torch.cuda.empty_cache()
 
 
+def test_ridge_device_largest_state(ctx):
+    """kvmap_ridge_solve_device on the largest state the boundary accepts in p (65,536; q 256):
+    the fp64 system alone is 34 GB and its element offsets pass 2^32.  The state comes from 2,048
+    device-drawn rows (y a noisy multiple of the first q features).  With 2,048 rows M_xx has a
+    63,000-dimensional null space, and the fp32 state's error (at most 1e-2 per entry, but about 13
+    in spectral norm, measured against fp64 statistics of the same rows) leaves M_xx + lambda I
+    indefinite for lambda below about 12.5: at lambda = 0.01 the solve refuses it with
+    KVMAP_ERR_NOT_SPD (checked here), and it runs at lambda = 100.  No host solve finishes at this
+    size, so W is checked by a property that holds at any size: the residual (M_xx + lambda I) W
+    - M_xy, formed in fp64 from the state, relative to ||M_xx + lambda I|| ||W||, within a few
+    fp32 roundings of W; and b = mean_y - mean_x W."""
+    from cross_model_kv_amd import kvmap as K
+    p, q, lam = 65536, 256, 100.0
+    g = torch.Generator(device="cuda:0").manual_seed(2026606)
+    st = ctx.gram_state(p, q)
+    ctx.gram_reset(st)
+    for n_b in (1024, 1024):
+        X = (torch.randn((n_b, p), generator=g, device="cuda:0") + 1.0).to(torch.bfloat16)
+        Y = (0.5 * X[:, :q].float() + 0.1 * torch.randn((n_b, q), generator=g, device="cuda:0")).to(torch.bfloat16)
+        ctx.gram(st, X, Y)
+    del X, Y
+    with pytest.raises(K.KvmapError) as e:
+        ctx.ridge_solve_device(st, 0.01, dtype=torch.float32)
+    assert e.value.status == K.ERR_NOT_SPD
+    W, b = ctx.ridge_solve_device(st, lam, dtype=torch.float32)  # W output-major [q][p]
+    torch.cuda.synchronize()
+    A = st.M_xx.double()
+    A.diagonal().add_(lam)
+    Wt = W.double().t().contiguous()
+    res = float((A @ Wt - st.M_xy.double()).norm() / (A.norm() * Wt.norm()))
+    b_ref = st.mean_y.double() - st.mean_x.double() @ Wt
+    rb = float((b.double() - b_ref).norm() / b_ref.norm())
+    print(f"[gram] device ridge, largest state: relative residual {res:.2e}, b {rb:.2e}", flush=True)
+    assert res <= 1e-6 and rb <= 1e-5
+    del A, Wt, st
+    torch.cuda.empty_cache()
+
+
 def test_ridge_solve_device_matches_oracle(ctx):
     """kvmap_ridge_solve_device on a GPU-built state (p = 520, q = 68: padded to multiples of
     128 inside, 10 blocks of 64 in 3 panels, so the 128-tile updates of the trailing matrix and
