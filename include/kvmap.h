@@ -361,7 +361,9 @@ int kvmap_ridge_solve(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda,
  * rounded up to multiples of 128 (580 MiB at p 8192, q 1024), allocated on first use.  Synchronous:
  * returns after the solve, KVMAP_ERR_NOT_SPD if a pivot was not positive and finite (the
  * outputs are then undefined), INVALID_ARGUMENT / UNSUPPORTED on refused arguments (nothing
- * written). */
+ * written).  A state of fewer rows than features has a large null space, and the rounding
+ * error of its fp32 statistics can exceed a small lambda in spectral norm (about 13 at p 65,536
+ * from 2,048 rows): sym(M_xx) + lambda I is then indefinite, and refused as above. */
 int kvmap_ridge_solve_device(kvmap_ctx* ctx, const kvmap_gram_state* st, double lambda, void* W_out,
                              void* b_out, int32_t dtype, void* stream);
 
