@@ -141,10 +141,16 @@ def mfma(counter_csv, workload, out_json, kernel):
     out = {"kernel": kernel, "workload": workload,
            "kernel_code_fingerprint": kernel_fingerprint(KERNEL_SOURCES[kernel]), "dispatches": len(per),
            "seconds": avg("seconds"), "clock_GHz": avg("clock_GHz"), "mfma_insts": avg("mfma_insts"),
-           "mfma_busy_share": avg("mfma_busy_share"), "per_dispatch": per}
+           "mfma_busy_share": avg("mfma_busy_share")}
+    if len(per) <= 8:
+        out["per_dispatch"] = per
+    else:  # a short summary: the spread over the dispatches and the first three of them
+        out["range"] = {key: [min(p[key] for p in per), max(p[key] for p in per)]
+                        for key in ("seconds", "clock_GHz", "mfma_busy_share")}
+        out["first_dispatches"] = per[:3]
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps({k: v for k, v in out.items() if k != "per_dispatch"}, indent=1))
+    print(json.dumps({k: v for k, v in out.items() if k not in ("per_dispatch", "first_dispatches")}, indent=1))
 
 
 def counters(counter_csv, kernel):
