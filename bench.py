@@ -70,6 +70,20 @@ def traffic_entry(cfg_name, path=TRAFFIC_FILE, kernel="map_bf16_kernel"):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """The host's CPU model and logical CPU count, reported beside the oracle's timing."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count()}
+
+
 def cpu_baseline(cfg, inp, budget_s=12.0):
     """Time the fp64 oracle on whole target layers over the first `rows` tokens until the budget
     is spent; scale to mapped tokens/s of the full workload (all target layers)."""
@@ -104,7 +118,7 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
     return {"value": 1.0 / per_token_all_layers, "unit": "tokens/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"{done_layers} of {cfg.L_tgt} target layers (K and V) x {len(rows)} tokens, fp64 numpy "
-                      f"oracle, {spent:.1f} s; scaled to all target layers"}
+                      f"oracle, {spent:.1f} s; scaled to all target layers", **host_cpu()}
 
 
 def recode_leg(K, ctx, cfg, src, iters=10, warmup=2):
