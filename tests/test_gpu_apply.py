@@ -96,6 +96,32 @@ def test_edge_cases(ctx, cfg):
     _full_check(ctx, cfg)
 
 
+def _random_configs(n=24):
+    """Seeded random small shapes: layer counts, heads, head dim, k, cache length on both sides
+    of the short-cache limit, bases, position offsets, channel scales and dtype."""
+    rng = np.random.default_rng([2026, 700])
+    out = []
+    for i in range(n):
+        L_src = int(rng.integers(1, 10))
+        k = int(rng.integers(1, min(L_src, 6) + 1))
+        H = int(rng.integers(1, 6))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.choice([int(rng.integers(1, 129)), int(rng.integers(129, 700))]))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        thetas = [1.0e4, 5.0e5, 1.0e6]
+        out.append(ApplyConfig(300 + i, f"rand{i}-L{L_src}-{k}-H{H}-d{d}-T{T}-{dtype}", L_src,
+                               int(rng.integers(1, 7)), H, d, T, k, float(rng.choice(thetas)),
+                               float(rng.choice(thetas)), dtype, float(rng.choice([0.0, 0.5])),
+                               pos0=int(rng.choice([0, int(rng.integers(1, 100_000))]))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(), ids=lambda c: c.name)
+def test_random_shapes(ctx, cfg):
+    """Every element against the oracle, for each seeded random shape."""
+    _full_check(ctx, cfg)
+
+
 def test_qwen3_small_pair_full_layers(ctx):
     """Qwen3 0.6B -> 1.7B shape (28 -> 28, H=8, d=128, T=4096, k=4): every element of every
     target layer, K and V, against the oracle (in groups of 4 target layers); the outputs are
