@@ -77,6 +77,36 @@ def test_gram_ragged_batches(ctx, dtype):
     _check_state(st, ref, f"ragged {dtype}")
 
 
+def _random_stats_configs(n=16):
+    """Seeded random statistics calls: p and q (multiples of 4, not of the 256-wide tiles), one to
+    four batches of 1 to 900 rows, bf16 or fp32, with or without ss_y."""
+    rng = np.random.default_rng([2026, 701])
+    out = []
+    for i in range(n):
+        p = 4 * int(rng.integers(1, 201))
+        q = 4 * int(rng.integers(1, 101))
+        sizes = [int(v) for v in rng.integers(1, 901, int(rng.integers(1, 5)))]
+        dtype = "f32" if rng.random() < 0.3 else "bf16"
+        out.append((i, p, q, sizes, dtype, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("i,p,q,sizes,dtype,ssy", _random_stats_configs())
+def test_gram_random_shapes(ctx, i, p, q, sizes, dtype, ssy):
+    """Every element of the state (and ss_y when kept) against the oracle's two-pass statistics."""
+    cfg = FIT_STATS_CONFIG.replace(cid=500 + i, p=p, q=q, n_tokens=sum(sizes), batch=1024)
+    parts = _batches(cfg, sizes)
+    st = ctx.gram_state(p, q, keep_ss_y=ssy)
+    ctx.gram_reset(st)
+    for X, Y in parts:
+        ctx.gram(st, _dev(X, dtype), _dev(Y, dtype))
+    ref = oracle.stats_two_pass(np.concatenate([v[0] for v in parts]), np.concatenate([v[1] for v in parts]))
+    _check_state(st, ref, f"random {i}: p {p} q {q} batches {sizes} {dtype}")
+    if ssy:
+        r = _rel(st.ss_y.double().cpu().numpy(), ref["ssy"])
+        assert r <= GRAM_REL, f"ss_y {r:.2e}"
+
+
 def test_gram_wide_state_every_element(ctx):
     """p = 6144, q = 1024 (396 co-moment tiles, more than one wave of the compute units), bf16
     batches of 1000, 300 and 1000 rows: the first shifted by its own column means, the merging

@@ -74,6 +74,28 @@ def test_recode_matches_oracle(ctx, rows, T, d, dtype, ts, tt, ps, pt):
     _check(out, ref, dtype, f"rows {rows} T {T} d {d} {dtype} {ts:g}->{tt:g} pos0 {ps}->{pt}")
 
 
+def _random_recode_cases(n=16):
+    rng = np.random.default_rng([2026, 702])
+    thetas = [1.0e4, 5.0e5, 1.0e6]
+    out = []
+    for i in range(n):
+        out.append((int(rng.integers(1, 7)), int(rng.integers(1, 3000)), int(rng.choice([64, 128])),
+                    "f32" if rng.random() < 0.3 else "bf16", float(rng.choice(thetas)), float(rng.choice(thetas)),
+                    int(rng.choice([0, int(rng.integers(1, 200_000))])), int(rng.choice([0, int(rng.integers(1, 200_000))]))))
+    return out
+
+
+@pytest.mark.parametrize("rows,T,d,dtype,ts,tt,ps,pt", _random_recode_cases())
+def test_recode_random_cases(ctx, rows, T, d, dtype, ts, tt, ps, pt):
+    """Seeded random rows, lengths, head dims, dtypes, bases and position offsets; every element."""
+    x = _src(rows, T, d, dtype, seed=rows * 31 + T)
+    out = ctx.recode(x, ts, tt, pos0_src=ps, pos0_tgt=pt)
+    torch.cuda.synchronize()
+    x64 = x.float().cpu().double().numpy()
+    ref = _ref(x64, ps + np.arange(T), pt + np.arange(T), ts, tt)
+    _check(out, ref, dtype, f"rows {rows} T {T} d {d} {dtype} {ts:g}->{tt:g} pos0 {ps}->{pt}")
+
+
 def test_recode_largest_cache(ctx):
     """One row of T = 2^24 - 1 tokens at d 128 (T * d just under 2^31, positions to 1.7e7 from
     pos0 1000), drawn on the device; 3 tokens of every 4096 and the last 300 are checked."""
