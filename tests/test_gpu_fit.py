@@ -301,6 +301,45 @@ def test_fit_bf16_matches_oracle(ctx):
         assert np.all(np.abs(gb[n] - w32) <= 2.0 ** -8 * np.abs(w32) + 1e-30), n
 
 
+def _random_fit_configs(n=6):
+    """Seeded random small fits: 2-8 source and 1-6 target layers, k 1-3, 1-4 heads, d 64 or 128,
+    256 or 512 tokens per sequence and enough sequences for n >= 4 p, fp32 or bf16 caches."""
+    rng = np.random.default_rng([2026, 703])
+    thetas = [1.0e4, 5.0e5, 1.0e6]
+    out = []
+    for i in range(n):
+        L_src = int(rng.integers(2, 9))
+        k = int(rng.integers(1, min(3, L_src) + 1))
+        H = int(rng.integers(1, 5))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.choice([256, 512]))
+        dtype = "f32" if rng.random() < 0.5 else "bf16"
+        n_calib = max(2, -(-4 * k * H * d // T))
+        cfg = FITCHECK.replace(cid=600 + i, L_src=L_src, L_tgt=int(rng.integers(1, 7)), H=H, d=d, k=k, T=T,
+                               n_calib=n_calib, holdout_pos0=(), theta_src=float(rng.choice(thetas)),
+                               theta_tgt=float(rng.choice(thetas)), noise_sd=1e-3 if dtype == "f32" else 1e-2)
+        out.append((cfg, dtype))
+    return out
+
+
+@pytest.mark.parametrize("cfg,dtype", _random_fit_configs(),
+                         ids=lambda v: f"L{v.L_src}-{v.L_tgt}-k{v.k}-H{v.H}-d{v.d}-T{v.T}x{v.n_calib}"
+                         if hasattr(v, "L_src") else str(v))
+def test_fit_random_shapes(ctx, cfg, dtype):
+    """Selection equal to the oracle's and to the hidden layers; scores and maps within the
+    fp32 or bf16 bounds above."""
+    pr, st, seqs = _pairs(cfg, dtype)
+    got = _run_fit(ctx, cfg, seqs, out_dtype=torch.float32)
+    ref = _oracle_fit(cfg, pr, st)
+    assert np.array_equal(got["layer_sel"], ref["layer_sel"])
+    assert np.array_equal(got["layer_sel"], pr["draws"]["true_sel"])
+    ref_scores = _oracle_scores(cfg, pr, st, list(range(cfg.L_tgt)))
+    serr = np.max(np.abs(got["scores"] - ref_scores))
+    print(f"[fit] random {cfg.cid} {dtype}: scores max |err| {serr:.2e}", flush=True)
+    assert serr <= (1e-4 if dtype == "f32" else 1e-3)
+    _check_maps(got, ref, 2e-4 if dtype == "f32" else 5e-3, f"random {cfg.cid} {dtype}")
+
+
 def test_fit_selection_full_target_width(ctx):
     """Stage-1 states at the 14B->32B width: 64 target layers of H = 8, d = 128 in one block
     (q = 65536 outputs per state), 2 source layers, k = 1, bf16, 2048 tokens.  Every target
