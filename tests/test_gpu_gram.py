@@ -346,6 +346,37 @@ def test_ridge_solve_device_matches_oracle(ctx):
         assert rw <= 1e-5 and rb <= 1e-5 and rh <= 1e-5
 
 
+def _random_ridge_cases(n=10):
+    """Seeded random device solves: p (multiple of 4, up to 1200: one to 19 blocks of 64), q (up to
+    400), n >= 4 p rows of bf16 or fp32 batches, lambda 0.01 or 3."""
+    rng = np.random.default_rng([2026, 704])
+    out = []
+    for i in range(n):
+        p = 4 * int(rng.integers(1, 301))
+        q = 4 * int(rng.integers(1, 101))
+        out.append((i, p, q, max(4 * p, 64), "f32" if rng.random() < 0.3 else "bf16", float(rng.choice([0.01, 3.0]))))
+    return out
+
+
+@pytest.mark.parametrize("i,p,q,n,dtype,lam", _random_ridge_cases())
+def test_ridge_device_random_shapes(ctx, i, p, q, n, dtype, lam):
+    """W and b of the device solve against the oracle's fp64 ridge of the same fp32 statistics."""
+    cfg = FIT_STATS_CONFIG.replace(cid=520 + i, p=p, q=q, n_tokens=n, batch=1024)
+    st = ctx.gram_state(p, q)
+    ctx.gram_reset(st)
+    for X, Y in _batches(cfg, [n]):
+        ctx.gram(st, _dev(X, dtype), _dev(Y, dtype))
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    stats = dict(n=st.n, mx=f(st.mean_x), my=f(st.mean_y), Mxx=np.triu(f(st.M_xx)) + np.triu(f(st.M_xx), 1).T,
+                 Mxy=f(st.M_xy))
+    Wr, br = oracle.ridge(stats, lam)
+    Wd, bd = ctx.ridge_solve_device(st, lam, dtype=torch.float32)
+    rw, rb = _rel(f(Wd).T, Wr), _rel(f(bd), br)
+    print(f"[ridge] random {i}: p {p} q {q} n {n} {dtype} lambda {lam}: rel W {rw:.2e} b {rb:.2e}", flush=True)
+    assert rw <= 1e-5 and rb <= 1e-5
+
+
 def test_ridge_solve_device_not_spd(ctx):
     """An empty state with lambda = 0 has a zero pivot: KVMAP_ERR_NOT_SPD."""
     from cross_model_kv_amd import kvmap as K
