@@ -180,7 +180,17 @@ def _random_stats(p, q, n, seed):
     return oracle.stats_two_pass(X, Y)
 
 
-@pytest.mark.parametrize("p,q,n", [(8, 4, 50), (64, 16, 500), (300, 40, 1000), (389, 37, 1200)])
+def _random_host_ridge_cases(n=8):
+    rng = np.random.default_rng([2026, 705])
+    out = []
+    for _ in range(n):
+        p = int(rng.integers(1, 400))
+        out.append((p, int(rng.integers(1, min(p, 60) + 1)), int(4 * p + rng.integers(1, 200))))
+    return out
+
+
+@pytest.mark.parametrize("p,q,n", [(8, 4, 50), (64, 16, 500), (300, 40, 1000), (389, 37, 1200)]
+                         + _random_host_ridge_cases())
 def test_ridge_solve_host_matches_oracle(p, q, n):
     st = _random_stats(p, q, n, seed=p)
     lam = 0.01
