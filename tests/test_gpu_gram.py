@@ -355,13 +355,18 @@ def _random_ridge_cases(n=10):
         p = 4 * int(rng.integers(1, 301))
         q = 4 * int(rng.integers(1, 101))
         out.append((i, p, q, max(4 * p, 64), "f32" if rng.random() < 0.3 else "bf16", float(rng.choice([0.01, 3.0]))))
+    # the smallest states and block edges: one padded 128-tile, exactly one and just past one
+    # 64-wide block, q past one 128-tile
+    for j, (p, q) in enumerate([(4, 4), (8, 4), (60, 12), (64, 64), (68, 132)]):
+        out.append((n + j, p, q, max(4 * p, 64), "bf16" if j % 2 else "f32", 0.01))
     return out
 
 
 @pytest.mark.parametrize("i,p,q,n,dtype,lam", _random_ridge_cases())
 def test_ridge_device_random_shapes(ctx, i, p, q, n, dtype, lam):
     """W and b of the device solve against the oracle's fp64 ridge of the same fp32 statistics."""
-    cfg = FIT_STATS_CONFIG.replace(cid=520 + i, p=p, q=q, n_tokens=n, batch=1024)
+    cfg = FIT_STATS_CONFIG.replace(cid=520 + i, p=p, q=q, n_tokens=n, batch=1024,
+                                   nnz=min(FIT_STATS_CONFIG.nnz, p // 2))  # the hidden map's nonzeros per column
     st = ctx.gram_state(p, q)
     ctx.gram_reset(st)
     for X, Y in _batches(cfg, [n]):
