@@ -69,6 +69,23 @@ ROW_CASES = [
 ]
 
 
+def _random_row_cases(n=12):
+    """Seeded random gathers: 1-8 layers of 1-8 heads, 1-599 tokens, d 64 or 128, one to four
+    distinct layers in any order, with or without the strip, position offsets up to 1e5."""
+    rng = np.random.default_rng([2026, 706])
+    out = []
+    for _ in range(n):
+        L, H = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        layers = [int(v) for v in rng.permutation(L)[: int(rng.integers(1, min(L, 4) + 1))]]
+        theta = None if rng.random() < 0.3 else float(rng.choice([1.0e4, 5.0e5, 1.0e6]))
+        out.append((L, H, int(rng.integers(1, 600)), int(rng.choice([64, 128])),
+                    "f32" if rng.random() < 0.4 else "bf16", layers, theta, int(rng.choice([0, int(rng.integers(1, 100_000))]))))
+    return out
+
+
+ROW_CASES = ROW_CASES + _random_row_cases()
+
+
 @pytest.mark.parametrize("L,H,T,d,dtype,layers,theta,pos0", ROW_CASES)
 def test_cache_rows_matches_oracle(ctx, L, H, T, d, dtype, layers, theta, pos0):
     rng = np.random.default_rng([77, L, H, T, d])
@@ -135,11 +152,24 @@ def test_ss_y_streamed_and_merged(ctx, dtype):
     assert e.value.status == K.ERR_INVALID_ARGUMENT
 
 
+def _random_r2_cases(n=8):
+    """Seeded random R^2 calls: p a multiple of 4 up to 600, groups of 4-128 columns (a multiple of
+    4), 1-6 groups, n = 4p + up to 500 rows, lambda 0.01, 1 or 50, bf16 or fp32."""
+    rng = np.random.default_rng([2026, 707])
+    out = []
+    for _ in range(n):
+        p = 4 * int(rng.integers(1, 151))
+        group = 4 * int(rng.integers(1, 33))
+        out.append((4 * p + int(rng.integers(1, 500)), p, group * int(rng.integers(1, 7)), group,
+                    float(rng.choice([0.01, 1.0, 50.0])), "f32" if rng.random() < 0.4 else "bf16"))
+    return out
+
+
 @pytest.mark.parametrize("n,p,q,group,lam,dtype", [
     (3000, 128, 256, 64, 0.01, "f32"),
     (4096, 520, 136, 68, 0.01, "bf16"),
     (2500, 64, 192, 192, 50.0, "f32"),
-])
+] + _random_r2_cases())
 def test_ridge_r2_matches_oracle(ctx, n, p, q, group, lam, dtype):
     """Pooled in-sample R^2 per group of y columns from the statistics, against the oracle's R^2
     of the fitted predictions (oracle.ridge on two-pass statistics, then r2_pooled)."""
