@@ -423,6 +423,56 @@ def test_gram_block_diagonal_state(ctx, dtype, bd):
     assert np.max(np.abs(f(a.mean_x) - ref["mx"])) <= GRAM_REL * np.max(np.abs(ref["mx"]))
 
 
+def _random_merge_cases(n=10):
+    """Seeded random merges: 2-4 states of 1-2 batches each (1-500 rows), full or block-diagonal
+    M_xx (blocks of 4-256 features, a multiple of 4), bf16 or fp32, all merged into the first."""
+    rng = np.random.default_rng([2026, 708])
+    out = []
+    for i in range(n):
+        bd = 0 if rng.random() < 0.4 else 4 * int(rng.integers(1, 65))
+        p = (bd * int(rng.integers(1, 9))) if bd else 4 * int(rng.integers(1, 151))
+        q = 4 * int(rng.integers(1, 41))
+        states = [[int(v) for v in rng.integers(1, 501, int(rng.integers(1, 3)))] for _ in range(int(rng.integers(2, 5)))]
+        out.append((i, p, q, bd, states, "f32" if rng.random() < 0.3 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("i,p,q,bd,states,dtype", _random_merge_cases())
+def test_gram_random_merges(ctx, i, p, q, bd, states, dtype):
+    """The merged state equals the oracle's two-pass statistics of all the rows: M_xx (or its
+    diagonal blocks), M_xy, the means, ss_y and n."""
+    sizes = [n for s_ in states for n in s_]
+    cfg = FIT_STATS_CONFIG.replace(cid=540 + i, p=p, q=q, n_tokens=sum(sizes), batch=1024,
+                                   nnz=min(FIT_STATS_CONFIG.nnz, p // 2))
+    parts = _batches(cfg, sizes)
+    sts, k = [], 0
+    for s_ in states:
+        st = ctx.gram_state(p, q, keep_ss_y=True, xx_block=bd)
+        ctx.gram_reset(st)
+        for _ in s_:
+            ctx.gram(st, _dev(parts[k][0], dtype), _dev(parts[k][1], dtype))
+            k += 1
+        sts.append(st)
+    for st in sts[1:]:
+        ctx.gram_merge(sts[0], st)
+    torch.cuda.synchronize()
+    a = sts[0]
+    ref = oracle.stats_two_pass(np.concatenate([v[0] for v in parts]), np.concatenate([v[1] for v in parts]))
+    f = lambda t: t.double().cpu().numpy()
+    assert a.n == sum(sizes)
+    if bd:
+        Mxx = f(a.M_xx)
+        r_xx = max(_rel(Mxx[g], ref["Mxx"][g * bd:(g + 1) * bd, g * bd:(g + 1) * bd]) for g in range(p // bd))
+    else:
+        r_xx = _rel(f(a.M_xx), ref["Mxx"])
+    r_xy, r_ss = _rel(f(a.M_xy), ref["Mxy"]), _rel(f(a.ss_y), ref["ssy"])
+    mx = np.max(np.abs(f(a.mean_x) - ref["mx"])) / np.max(np.abs(ref["mx"]))
+    my = np.max(np.abs(f(a.mean_y) - ref["my"])) / np.max(np.abs(ref["my"]))
+    print(f"[gram] random merge {i}: p {p} q {q} bd {bd} states {states} {dtype}: M_xx {r_xx:.2e} "
+          f"M_xy {r_xy:.2e} ss_y {r_ss:.2e}", flush=True)
+    assert max(r_xx, r_xy, r_ss, mx, my) <= GRAM_REL
+
+
 def test_gram_merge_refuses_overlapping_states(ctx):
     """A merge whose source shares memory with its destination is refused before any device
     work, and the destination is left as it was."""
