@@ -368,6 +368,17 @@ def test_fit_random_shapes(ctx, cfg, dtype):
     print(f"[fit] random {cfg.cid} {dtype}: scores max |err| {serr:.2e}", flush=True)
     assert serr <= (1e-4 if dtype == "f32" else 1e-3)
     _check_maps(got, ref, 2e-4 if dtype == "f32" else 5e-3, f"random {cfg.cid} {dtype}")
+    # the blocked two-pass mode with random block sizes: the same selection and scores; maps
+    # from statistics merged in another order, each within the 1e-5 statistics bar, so within
+    # the kappa x 2e-5 = 2e-4 bound above (n = 4 p here: less well conditioned than the fit check)
+    rng = np.random.default_rng([2026, 709, cfg.cid])
+    two = _run_fit(ctx, cfg, seqs, out_dtype=torch.float32, two_pass=True,
+                   select_block=int(rng.integers(1, cfg.L_tgt + 1)), map_block=int(rng.integers(1, cfg.L_tgt + 1)))
+    assert np.array_equal(two["layer_sel"], got["layer_sel"])
+    assert np.max(np.abs(two["scores"] - got["scores"])) <= 1e-6
+    for n in ("W_k", "b_k", "W_v", "b_v"):
+        rel = max(np.linalg.norm(two[n][t] - got[n][t]) / np.linalg.norm(got[n][t]) for t in range(cfg.L_tgt))
+        assert rel <= 2e-4, (n, rel)
 
 
 def test_fit_selection_full_target_width(ctx):
