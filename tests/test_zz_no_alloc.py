@@ -71,6 +71,37 @@ def test_noalloc_equals_gram_bit_for_bit(ctx, dtype):
             assert torch.equal(fa[k], fb[k]), k
 
 
+def _random_cases(n=8):
+    """Seeded random shapes small enough that every call fits one static sub-batch: p and q
+    multiples of 4 (p + q at most 2,400), two calls of 1-900 rows, the second smaller."""
+    rng = np.random.default_rng([2026, 710])
+    out = []
+    for i in range(n):
+        p, q = 4 * int(rng.integers(1, 401)), 4 * int(rng.integers(1, 201))
+        r1 = int(rng.integers(2, 901))
+        out.append((i, p, q, r1, int(rng.integers(1, r1)), "f32" if rng.random() < 0.3 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("i,p,q,r1,r2,dtype", _random_cases())
+def test_noalloc_random_shapes_bit_for_bit(ctx, i, p, q, r1, r2, dtype):
+    """Two calls in a row, the second smaller, give the same state bits as kvmap_gram."""
+    cfg = FIT_STATS_CONFIG.replace(cid=560 + i, p=p, q=q, n_tokens=r1 + r2, batch=1024,
+                                   nnz=min(FIT_STATS_CONFIG.nnz, p // 2))
+    X, Y = _rows(cfg, r1 + r2)
+    a, b = _pair(ctx, p, q)
+    for s0, s1 in ((0, r1), (r1, r1 + r2)):
+        print(f"[noalloc] random {i}: {dtype} p={p} q={q} rows {s0}..{s1}", flush=True)
+        x, y = _dev(X[s0:s1], dtype), _dev(Y[s0:s1], dtype)
+        ctx.gram(a, x, y)
+        ctx.gram_noalloc(b, x, y)
+        torch.cuda.synchronize()
+        assert a.n == b.n == s1
+        fa, fb = _fields(a), _fields(b)
+        for k in fa:
+            assert torch.equal(fa[k], fb[k]), k
+
+
 def test_noalloc_sub_batches_at_fit_shape(ctx):
     """p 8192, q 1024 (the 14B->32B fit statistics), bf16: a 4096-row call (three static
     sub-batches of at most 1664 rows), then a 1000-row call (one), against kvmap_gram's state
