@@ -121,19 +121,6 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Factor the diagonal block kb in place (lower triangle) and write the inverse of the factor to
-// Li[kb]; one wave of 64 lanes per system.  The inverse turns every triangular solve with this
-// block (the panel below it and both substitutions) into a 64 x 64 tile product on the matrix
-// cores.  The block lives in registers, lane r holding row r (64 doubles), so that the only
-// LDS traffic is one broadcast column per step:
-//   step j: l_jj = sqrt(a_jj) (lane j's, read with v_readlane) as a_jj rsqrt(a_jj), one reciprocal
-//   square root doing for the root and the division; lane r > j: l_rj = a_rj / l_jj,
-//   published in col[r]; then every lane r: a_rm -= l_rj l_mj for m > j (col[m] = l_mj is a
-//   broadcast LDS read).  Elements above a lane's diagonal are updated too and never used.
-// The inverse X = L^-1 by forward substitution, lane r holding column r:
-//   X_ir = (delta_ir - sum_{m < i} L_im X_mr) / L_ii (times the kept 1 / L_ii), with L_im
-//   broadcast from LDS; the terms
-//   with m < r vanish because X is lower triangular.
 // 1 / sqrt(d) for d > 0 in float64: the hardware estimate refined by two Newton steps
 // y <- y (3 - d y^2) / 2, each of which doubles the correct bits of the estimate.
 __device__ __forceinline__ double rsqrt_f64(double d) {
@@ -143,59 +130,251 @@ __device__ __forceinline__ double rsqrt_f64(double d) {
     return y;
 }
 
-__global__ __launch_bounds__(64) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
-    __shared__ double Ls[RB][RB + 1];
-    __shared__ double col[RB];
-    __shared__ double rdiag[RB];  // 1 / l_jj
+// Factor the diagonal block kb in place (lower triangle) and write the inverse of the factor to
+// Li[kb]; one workgroup of 4 waves per system.  The inverse turns every triangular solve with
+// this block (the panel below it and both substitutions) into a 64 x 64 tile product on the
+// matrix cores.  The block sits in LDS (odd row stride) and is factored in 16-wide sub-blocks
+// (right-looking), so that the bulk of the work is 16 x 16 x 16 products on the fp64 matrix
+// cores and only 16-step chains stay serial.  For each diagonal sub-block k:
+//   wave 0 factors it, 16 lanes holding its rows in registers: step j publishes column j as it
+//     stands (a_mj, m > j) to col[], reads the pivot a_jj from lane j with v_readlane, takes
+//     rj = 1 / sqrt(a_jj), l_rj = a_rj rj (l_jj = a_jj rj = sqrt(a_jj), one reciprocal square
+//     root doing for the root and the division), and every row lane r updates
+//     a_rm -= (l_rj rj) a_mj for m > j.  The next pivot comes from lane j + 1's own registers,
+//     so the chain of pivots never waits for the LDS round trip;
+//   in the same steps, on 16 more lanes, it inverts the factor by right-looking substitution,
+//     lane r holding column r of the inverse: x_j = v_j rj, then v_m -= (x_j rj) a_mj for m > j
+//     (= l_mj x_j), starting from v = e_r;
+//   the sub-blocks below, as transposes: L_ik^T = X_kk A_ik^T (X = L^-1), one per wave;
+//   the trailing sub-blocks: A_ij -= L_ik L_jk^T (k < j <= i).  Wave 0 updates the next
+//     diagonal sub-block from its own panel in registers and factors it at once, while waves
+//     1-3 update the other trailing sub-blocks and the inverse's sub-blocks of row k,
+//     X_km = -X_kk (sum over n = m .. k-1 of L_kn X_nm) for m < k.
+// Two barriers per sub-block: after the factor (and the other waves' work beside it), and after
+// the panels.  Within a wave, LDS operations complete in issue order; a compiler memory fence
+// keeps the compiler from moving them across phases.
+// v_mfma_f64_16x16x4f64: lane (i, k) = (lane & 15, lane >> 4) supplies A[i][k] and B[k][i] of
+// each K = 4 step; accumulator element e of the lane is D[(lane >> 4) + 4 e][lane & 15].  Element
+// e of a product D is then what the lane supplies at step e of the next product for B = D or for
+// A = D^T, so products chain in registers.  Elements above the diagonal of a diagonal sub-block
+// are updated too and never used.
+__global__ __launch_bounds__(256) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
+    constexpr int SB = 16;         // sub-block
+    constexpr int NS = RB / SB;    // sub-blocks per side
+    constexpr int LDL = RB + 1;    // LDS row stride (doubles)
+    __shared__ double Ls[RB * LDL];  // the block: A in, L out (lower triangle)
+    __shared__ double Xs[RB * LDL];  // X = L^-1 (lower triangle; the rest is not written)
+    __shared__ double col[64];       // col[m], m < 16: the published column (lanes 16.. write copies)
     double* A = sys_a(g);
     const int P = g.P;
-    const int r = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const bool isrow = (lane & 16) == 0;
     const int o = kb * RB;
-    for (int i = 0; i < RB; ++i) Ls[i][r] = A[(size_t)(o + i) * P + o + r];  // coalesced rows
-    __syncthreads();
-    double a[RB];
+    auto fence = []() { asm volatile("" ::: "memory"); };
+    const f64x4_t zero4 = {0.0, 0.0, 0.0, 0.0};
+    {   // rows 16 w .. 16 w + 15 of the block (coalesced rows)
+        double v[16];
 #pragma unroll
-    for (int c = 0; c < RB; ++c) a[c] = Ls[r][c];
-    bool bad = false;
+        for (int i = 0; i < 16; ++i) v[i] = A[(size_t)(o + 16 * w + i) * P + o + lane];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-        double d = readlane_f64(a[j], j);
-        if (!(d > 0.0) || !isfinite(d)) {
-            bad = true;
-            d = 1.0;  // keep going with a harmless pivot; the result is refused by the host
+        for (int i = 0; i < 16; ++i) Ls[(16 * w + i) * LDL + lane] = v[i];
+    }
+    fence();
+    // wave 0: factor diagonal sub-block k and invert its factor (Ls rows, Xs columns)
+    auto factor = [&](const int k) {
+        const int k0 = k * SB;
+        // lanes with bit 4 clear hold row r (y = a_r.), the others column r of the inverse
+        // (y = v_.r); lanes 32.. repeat lanes 0..31.  One instruction updates both.
+        double y[SB];
+#pragma unroll
+        for (int c = 0; c < SB; ++c) {
+            double a = Ls[(k0 + r) * LDL + k0 + c];
+            asm volatile("" : "+v"(a));  // load on every lane (no branch), then select
+            y[c] = isrow ? a : (c == r ? 1.0 : 0.0);
         }
-        const double rj = rsqrt_f64(d);  // l_jj = d / sqrt(d) = d rj; l_rj = a_rj / l_jj = a_rj rj
-        const double lrj = (r == j) ? d * rj : a[j] * rj;
-        a[j] = lrj;
-        col[r] = lrj;
-        rdiag[j] = rj;  // the same value from every lane (d is the wave's broadcast pivot)
-        // The workgroup is one wave, whose LDS operations complete in issue order, so the
-        // column written above is what the reads below see, and the next step's write comes
-        // after these reads, with no barrier.  The empty asm keeps the compiler from moving LDS
-        // accesses across it; the arithmetic of neighbouring steps may still interleave.
-        asm volatile("" ::: "memory");
+        fence();
+        double piv = readlane_f64(y[0], 0);
 #pragma unroll
-        for (int m = j + 1; m < RB; ++m) a[m] -= lrj * col[m];
-        asm volatile("" ::: "memory");
-    }
-    if (bad && r == 0) atomicOr(&g.bad[blockIdx.y], 1);
-    // the factor, zero above the diagonal: back to A (coalesced rows, through LDS) and kept in
-    // LDS for the inverse
+        for (int j = 0; j < SB; ++j) {
+            // column j as it stands (a_mj, m > j), for every lane; its LDS round trip runs
+            // while the pivot's reciprocal square root is computed
+            const double aj = y[j];
+            col[lane] = aj;
+            fence();
+            double cm[SB];
 #pragma unroll
-    for (int c = 0; c < RB; ++c) Ls[r][c] = (c <= r) ? a[c] : 0.0;
+            for (int m = j + 1; m < SB; ++m) cm[m] = col[m];
+            __builtin_amdgcn_sched_barrier(0);
+            // rows: l_rj = a_rj rj, and lane j's own a_jj is the pivot, so l_jj = a_jj rj =
+            // sqrt(a_jj); inverse columns: x_j = v_j rj.  The multiplier s = y_j rj makes
+            // a_rm -= s a_mj the update -= l_rj l_mj and v_m -= s a_mj the update -= l_mj x_j.
+            const double rj = rsqrt_f64(piv);
+            y[j] = aj * rj;
+            const double sc = y[j] * rj;
+            // The next pivot is lane j + 1's a_(j+1)(j+1) - s a_(j+1)j, whose column value is its
+            // own aj: the same operands as its update from col below, so the same result (the
+            // lane's own a_(j+1)(j+1) in the next step), with no wait for the LDS round trip.
+            if (j + 1 < SB) piv = readlane_f64(fma(-sc, aj, y[j + 1]), j + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = j + 1; m < SB; ++m) y[m] = fma(-sc, cm[m], y[m]);
+            fence();
+        }
+        // rows of the factor (zero above the diagonal) to Ls, columns of the inverse to Xs;
+        // lanes 32.. store the same values to the same places
+#pragma unroll
+        for (int c = 0; c < SB; ++c) {
+            double* dst = isrow ? &Ls[(k0 + r) * LDL + k0 + c] : &Xs[(k0 + c) * LDL + k0 + r];
+            *dst = (isrow && c > r) ? 0.0 : y[c];
+        }
+        fence();
+    };
+    // D = L_ik^T = X_kk A_ik^T, and L_ik stored over A_ik
+    auto panel = [&](const int k, const int i) {
+        const int k0 = k * SB;
+        f64x4_t D = zero4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            D = __builtin_amdgcn_mfma_f64_16x16x4f64(Xs[(k0 + r) * LDL + k0 + 4 * s + kq],
+                                                     Ls[(i * SB + r) * LDL + k0 + 4 * s + kq], D, 0, 0, 0);
+        fence();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ls[(i * SB + r) * LDL + k0 + kq + 4 * e] = D[e];
+        fence();
+        return D;
+    };
+    // A_ij -= L_ik L_jk^T, the operands from Ls
+    auto trail = [&](const int k, const int i, const int j) {
+        const int k0 = k * SB;
+        f64x4_t C;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) C[e] = Ls[(i * SB + kq + 4 * e) * LDL + j * SB + r];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            C = __builtin_amdgcn_mfma_f64_16x16x4f64(-Ls[(i * SB + r) * LDL + k0 + 4 * s + kq],
+                                                     Ls[(j * SB + r) * LDL + k0 + 4 * s + kq], C, 0, 0, 0);
+        fence();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ls[(i * SB + kq + 4 * e) * LDL + j * SB + r] = C[e];
+        fence();
+    };
+    // A_ii -= L_ik L_ik^T with D = L_ik^T in registers
+    auto trail_diag = [&](const int i, const f64x4_t D) {
+        f64x4_t C;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) C[e] = Ls[(i * SB + kq + 4 * e) * LDL + i * SB + r];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) C = __builtin_amdgcn_mfma_f64_16x16x4f64(-D[s], D[s], C, 0, 0, 0);
+        fence();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ls[(i * SB + kq + 4 * e) * LDL + i * SB + r] = C[e];
+        fence();
+    };
+    // X_im = -X_ii (sum over n = m .. i-1 of L_in X_nm)
+    auto inv = [&](const int i, const int m) {
+        f64x4_t T = zero4, Z = zero4;
+#pragma unroll
+        for (int n = m; n < i; ++n)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                T = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[(i * SB + r) * LDL + n * SB + 4 * s + kq],
+                                                         Xs[(n * SB + 4 * s + kq) * LDL + m * SB + r], T, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            Z = __builtin_amdgcn_mfma_f64_16x16x4f64(-Xs[(i * SB + r) * LDL + i * SB + 4 * s + kq], T[s], Z, 0, 0, 0);
+        fence();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Xs[(i * SB + kq + 4 * e) * LDL + m * SB + r] = Z[e];
+        fence();
+    };
+    if (w == 0) factor(0);
     __syncthreads();
-    for (int i = 0; i < RB; ++i) A[(size_t)(o + i) * P + o + r] = Ls[i][r];
-    double x[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        double v = (i == r) ? 1.0 : 0.0;
-#pragma unroll
-        for (int m = 0; m < i; ++m) v -= Ls[i][m] * x[m];
-        x[i] = v * rdiag[i];
+    // sub-block 0: panels 1, 2, 3 (waves 0, 1, 2); then wave 0 updates and factors sub-block 1,
+    // waves 1-3 update (2, 1), (2, 2); (3, 1), (3, 2); (3, 3)
+    {
+        f64x4_t D = zero4;
+        if (w < 3) D = panel(0, 1 + w);
+        __syncthreads();
+        if (w == 0) {
+            trail_diag(1, D);
+            factor(1);
+        } else if (w == 1) {
+            trail(0, 2, 1);
+            trail(0, 2, 2);
+        } else if (w == 2) {
+            trail(0, 3, 1);
+            trail(0, 3, 2);
+        } else {
+            trail(0, 3, 3);
+        }
+        __syncthreads();
     }
+    // sub-block 1: panels 2, 3 (waves 0, 1); wave 0: (2, 2) and the factor of sub-block 2;
+    // wave 1: (3, 2); wave 2: (3, 3); wave 3: X_10
+    {
+        f64x4_t D = zero4;
+        if (w < 2) D = panel(1, 2 + w);
+        __syncthreads();
+        if (w == 0) {
+            trail_diag(2, D);
+            factor(2);
+        } else if (w == 1) {
+            trail(1, 3, 2);
+        } else if (w == 2) {
+            trail(1, 3, 3);
+        } else {
+            inv(1, 0);
+        }
+        __syncthreads();
+    }
+    // sub-block 2: panel 3 (wave 0); wave 0: (3, 3) and the factor of sub-block 3;
+    // wave 1: X_20; wave 2: X_21
+    {
+        f64x4_t D = zero4;
+        if (w == 0) D = panel(2, 3);
+        __syncthreads();
+        if (w == 0) {
+            trail_diag(3, D);
+            factor(3);
+        } else if (w == 1) {
+            inv(2, 0);
+        } else if (w == 2) {
+            inv(2, 1);
+        }
+        __syncthreads();
+    }
+    // row 3 of the inverse: X_32, X_31, X_30 (waves 0, 1, 2)
+    if (w < 3) inv(3, 2 - w);
+    __syncthreads();
+    // A pivot that is not positive and finite leaves a NaN on the factor's diagonal (the
+    // reciprocal square root of a negative number, zero, infinity or NaN makes l_jj = a_jj rj
+    // NaN, and the chain carries it on), so one look at the diagonal flags the system; the host
+    // refuses its result.
+    if (w == 0) {
+        const double dg = Ls[lane * LDL + lane];
+        if (!(dg > 0.0) || !isfinite(dg)) atomicOr(&g.bad[blockIdx.y], 1);
+    }
+    // the factor and its inverse, zero above the diagonal: to A and to Li (coalesced rows,
+    // 16 per wave)
     double* Li = sys_li(g) + (size_t)kb * RB * RB;
+    {
+        double lv[16], xv[16];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) Li[(size_t)i * RB + r] = x[i];
+        for (int i = 0; i < 16; ++i) {
+            const int row = 16 * w + i;
+            const bool low = lane <= row;
+            const double lx = Ls[row * LDL + lane], xx = Xs[row * LDL + lane];
+            lv[i] = low ? lx : 0.0;
+            xv[i] = low ? xx : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            A[(size_t)(o + 16 * w + i) * P + o + lane] = lv[i];
+            Li[(size_t)(16 * w + i) * RB + lane] = xv[i];
+        }
+    }
 }
 
 // C -= sum over K blocks kb = k0 .. k0 + nk - 1 of op(A) op(B), on 64 x 64 tiles with K = 64
@@ -669,7 +848,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
     for (int b0 = 0; b0 < nb; b0 += kPanel) {
         const int b1 = std::min(nb, b0 + kPanel);
         for (int kb = b0; kb < b1; ++kb) {
-            hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1, un), dim3(RB), 0, s, g, kb);
+            hipLaunchKernelGGL(ridge_potrf_kernel, dim3(1, un), dim3(256), 0, s, g, kb);
             const int below = nb - kb - 1;
             if (below == 0) continue;
             hipLaunchKernelGGL((ridge_update_kernel<3, false>), dim3(below, un), blk, 0, s, g, kb + 1, kb, 1, kb, 1);
