@@ -378,16 +378,13 @@ __global__ __launch_bounds__(256) void ridge_potrf_kernel(const RidgeArgs g, int
 }
 
 // C -= sum over K blocks kb = k0 .. k0 + nk - 1 of op(A) op(B), on 64 x 64 tiles with K = 64
-// per block, on the fp64 matrix cores (MODE 3..5: C = op(A) op(B), one block, C in place).
+// per block, on the fp64 matrix cores (MODE 3: C = op(A) op(B), one block, C in place).
 // The tile list (i0: first row block; j0, ncol: first column block and count):
 //   MODE 0  lower triangle of A:  C = A_IJ (I >= J), op(A) = A_I,kb, op(B) = A_J,kb^T.  TRI: the
 //           whole lower triangle from block j0 on (lower_decode); else the rectangle
 //           I in [i0, ..) x J in [j0, j0 + ncol), tiles with I < J skipped
-//   MODE 1  forward update of the right-hand sides: C = B_I,J, op(A) = L_I,kb, op(B) = Z_kb,J
-//   MODE 2  backward update: C = Z_I,J, op(A) = L_kb,I^T, op(B) = W_kb,J
+//   MODE 2  backward update of the right-hand sides: C = Z_I,J, op(A) = L_kb,I^T, op(B) = W_kb,J
 //   MODE 3  panel below block kb: C = A_I,kb (I > kb) = A_I,kb Li_kb^T
-//   MODE 4  forward diagonal step: C = B_kb,J = Li_kb B_kb,J
-//   MODE 5  backward diagonal step: C = B_kb,J = Li_kb^T B_kb,J
 // Operand tiles are copied to LDS as they lie in memory (64 rows of 64 consecutive doubles,
 // coalesced); A_ROWS / B_ROWS say whether an LDS row is an r (resp. c) index or an m index.
 // 4 waves, each a 32 x 32 quarter of C as 2 x 2 blocks of 16 x 16 (v_mfma_f64_16x16x4f64:
@@ -398,9 +395,10 @@ __global__ __launch_bounds__(256) void ridge_potrf_kernel(const RidgeArgs g, int
 template <int MODE, bool TRI>
 __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, int i0, int j0, int ncol, int k0,
                                                            int nk) {
-    constexpr bool A_ROWS = MODE != 2 && MODE != 5;  // LDS row of A is r (else m)
-    constexpr bool B_ROWS = MODE == 0 || MODE == 3;  // LDS row of B is c (else m)
-    constexpr bool OVERWRITE = MODE >= 3;
+    static_assert(MODE == 0 || MODE == 2 || MODE == 3, "64 x 64 update modes");
+    constexpr bool A_ROWS = MODE != 2;  // LDS row of A is r (else m)
+    constexpr bool B_ROWS = MODE != 2;  // LDS row of B is c (else m)
+    constexpr bool OVERWRITE = MODE == 3;
     __shared__ double As[RB * LDW];
     __shared__ double Bs[RB * LDW];
     double* A = sys_a(g);
@@ -441,18 +439,12 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
         if (MODE == 0) {
             Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
             Bp = A + (size_t)J * RB * P + o; ldb = P;   // rows c, columns m
-        } else if (MODE == 1) {
-            Ap = A + (size_t)I * RB * P + o; lda = P;   // rows r, columns m
-            Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
         } else if (MODE == 2) {
             Ap = A + (size_t)o * P + (size_t)I * RB; lda = P;   // rows m, columns r
             Bp = Bm + (size_t)o * Q + (size_t)J * RB; ldb = Q;  // rows m, columns c
-        } else if (MODE == 3) {
+        } else {
             Ap = C; lda = P;                                    // rows r, columns m
             Bp = Li + (size_t)(k0 + kc) * RB * RB; ldb = RB;    // Li rows c, columns m
-        } else {
-            Ap = Li + (size_t)(k0 + kc) * RB * RB; lda = RB;    // MODE 4: rows r, cols m; 5: rows m, cols r
-            Bp = C; ldb = Q;                                    // rows m, columns c
         }
     };
     // Each thread moves 16 elements of each tile, consecutive threads along the unit stride;
@@ -529,6 +521,146 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
                 const int r = r0 + 16 * i + lk + 4 * e, c = c0 + 16 * j + li;
                 C[(size_t)r * ldc + c] = OVERWRITE ? acc[i][j][e] : cv[i][j][e] - acc[i][j][e];
             }
+}
+
+// Substitution inside one panel of nbk blocks from b0, one workgroup per 64 columns J of the
+// right-hand sides (the rows outside the panel already updated by every earlier panel):
+//   forward  (L Z = B):    for kb = b0 .. b0 + nbk - 1:  Z_kb = Li_kb B_kb,    then B_I -= L_I,kb Z_kb  (I in (kb, b0 + nbk))
+//   backward (L^T W = Z):  for kb = b0 + nbk - 1 .. b0:  W_kb = Li_kb^T Z_kb,  then Z_I -= L_kb,I^T W_kb  (I in [b0, kb))
+// A column block's chain needs no other column block, so the whole chain of a panel is one
+// launch (it had been two launches per block).  The panel's blocks of the right-hand sides stay
+// in registers (accumulator layout, 16 values per block and thread); each product's operand
+// (Li_kb or a 64 x 64 block of L) is read into registers during the previous product and goes
+// through a two-deep LDS ring; the diagonal step's input and result go through LDS as the B
+// operand.  4 waves, each a 32 x 32 quarter of the 64 x 64 block as 2 x 2 blocks of 16 x 16
+// (v_mfma_f64_16x16x4f64, accumulator element e of a lane at row (lane >> 4) + 4 e).
+template <bool BACK>
+__global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs g, int b0, int nbk) {
+    constexpr int MAXB = 4;  // blocks per panel
+    __shared__ double Os[2][RB * LDW];  // operand ring: Os[x][y] = O[x][y], O = Li_kb or a block of L
+    __shared__ double Zs[RB * LDW];     // the diagonal step's input, then
+    __shared__ double Ws[RB * LDW];     // its result
+    const double* A = sys_a(g);
+    const double* Li = sys_li(g);
+    double* Bm = sys_b(g);
+    const int P = g.P, Q = g.Q;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
+    const int li = lane & 15, lk = lane >> 4;
+    const int J = (int)blockIdx.x;
+    f64x4_t z[MAXB][2][2];
+#pragma unroll
+    for (int t = 0; t < MAXB; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    z[t][i][j][e] = (t < nbk) ? Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * RB + c0 + 16 * j + li]
+                                              : 0.0;
+    // the operand of product (t, u): Li_kb (u < 0) or, for the update of row block I = b0 + u,
+    // L_kb,I (backward) or L_I,kb (forward), kb = b0 + t
+    double ro[16];
+    auto fetch = [&](int t, int u) {
+        const int kb = b0 + t, I = b0 + u;
+        const double* src = (u < 0) ? Li + (size_t)kb * RB * RB
+                            : BACK  ? A + (size_t)kb * RB * P + (size_t)I * RB
+                                    : A + (size_t)I * RB * P + (size_t)kb * RB;
+        const int ld = (u < 0) ? RB : P;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int e = v * 256 + tid;
+            ro[v] = src[(size_t)(e >> 6) * ld + (e & 63)];
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int e = v * 256 + tid;
+            Os[buf][(e >> 6) * LDW + (e & 63)] = ro[v];
+        }
+    };
+    // acc (+/-)= op(O) X, op(O) = O^T (backward) or O (forward), X from LDS
+    auto product = [&](f64x4_t (&acc)[2][2], const double* os, const double* xs, bool neg) {
+#pragma unroll
+        for (int kk = 0; kk < RB; kk += 4) {
+            const int m = kk + lk;
+            double a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = r0 + 16 * i + li;
+                const double v = BACK ? os[m * LDW + r] : os[r * LDW + m];
+                a[i] = neg ? -v : v;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = xs[m * LDW + c0 + 16 * j + li];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    auto put = [&](double* xs, const f64x4_t (&v)[2][2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xs[(r0 + 16 * i + lk + 4 * e) * LDW + c0 + 16 * j + li] = v[i][j][e];
+    };
+    // products in order: for each diagonal step t (backward: from the last), (t, -1), then the
+    // updates (t, u) of the panel's row blocks u still to come
+    auto upd_ok = [&](int t, int u) { return BACK ? (u < t) : (u > t && u < nbk); };
+    int q = 0;
+    fetch(BACK ? nbk - 1 : 0, -1);
+#pragma unroll
+    for (int tt = 0; tt < MAXB; ++tt) {
+        const int t = BACK ? MAXB - 1 - tt : tt;
+        if (t >= nbk) continue;
+#pragma unroll
+        for (int u = -1; u < MAXB; ++u) {
+            if (u >= 0 && !upd_ok(t, u)) continue;
+            const int buf = q & 1;
+            stash(buf);  // that buffer's last reader was product q - 2, before the last barrier
+            if (u < 0) put(Zs, z[t]);
+            // the next product's operand
+            {
+                int nu = u + 1;
+                while (nu < MAXB && !upd_ok(t, nu)) ++nu;
+                if (nu < MAXB) fetch(t, nu);
+                else if (BACK ? t > 0 : t + 1 < nbk) fetch(BACK ? t - 1 : t + 1, -1);
+            }
+            __syncthreads();
+            if (u < 0) {
+                f64x4_t acc[2][2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+                product(acc, Os[buf], Zs, false);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) z[t][i][j] = acc[i][j];
+                put(Ws, z[t]);  // Ws's last readers were the previous step's updates, before the barrier
+            } else {
+                product(z[u], Os[buf], Ws, true);
+            }
+            ++q;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXB; ++t)
+        if (t < nbk) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * RB + c0 + 16 * j + li] = z[t][i][j][e];
+        }
 }
 
 // The large updates of MODE 0 (TRI), 1 and 2 of ridge_update_kernel on 128 x 128 tiles of C, K
@@ -808,6 +940,7 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
 // applied to the panel's own columns (and, in the substitutions, its own rows) at once; the
 // rest of the matrix (or of the right-hand sides) is updated once per panel with K = 64 kPanel.
 constexpr int kPanel = 4;
+static_assert(kPanel <= 4, "ridge_panel_subst_kernel holds at most 4 blocks in registers");
 
 // Forward substitution over the panel [b0, b1): each diagonal step a product with the block's
 // inverse, then the rows below the panel updated once with K = the panel.  Reads only the
@@ -817,12 +950,7 @@ static void forward_panel(const RidgeArgs& g, int n, int b0, hipStream_t s) {
     const unsigned un = (unsigned)n;
     const dim3 blk(256);
     const int b1 = std::min(nb, b0 + kPanel);
-    for (int kb = b0; kb < b1; ++kb) {
-        hipLaunchKernelGGL((ridge_update_kernel<4, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
-        const int h = b1 - kb - 1;
-        if (h > 0)
-            hipLaunchKernelGGL((ridge_update_kernel<1, false>), dim3(h * nq, un), blk, 0, s, g, kb + 1, 0, nq, kb, 1);
-    }
+    hipLaunchKernelGGL(ridge_panel_subst_kernel<false>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
     if (nb > b1)
         hipLaunchKernelGGL(ridge_big_kernel<1>, dim3((nb - b1) / 2 * nq2, un), dim3(512), 0, s, g, b1 / 2, 0, nq2, b0,
                            b1 - b0);
@@ -885,6 +1013,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         side_pending = true;
     }
     if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
+    side_pending = false;
     if (ov.fwd) {
         (void)hipEventRecord(ov.fwd_done, ov.fwd);
         (void)hipStreamWaitEvent(s, ov.fwd_done, 0);
@@ -893,18 +1022,34 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
     // right after the panel was factored)
     if (!ov.fwd)
         for (int b0 = 0; b0 < nb; b0 += kPanel) forward_panel(g, n, b0, s);
-    // L^T W = Z, panels from the last
+    // L^T W = Z, panels from the last, with a one-panel lookahead as in the factorisation: once
+    // panel [b0, b1) is solved, its update of the next panel's rows [bp, b0) runs on `s`, so that
+    // panel's chain of diagonal steps can start, and its update of the rows above, [0, bp), on
+    // the side stream.  The next lookahead update writes rows that the side update writes too, so
+    // `s` waits for it first.
     for (int b1 = nb; b1 > 0; b1 -= kPanel) {
         const int b0 = std::max(0, b1 - kPanel);
-        for (int kb = b1 - 1; kb >= b0; --kb) {
-            hipLaunchKernelGGL((ridge_update_kernel<5, false>), dim3(nq, un), blk, 0, s, g, kb, 0, nq, kb, 1);
-            const int h = kb - b0;
-            if (h > 0)
-                hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3(h * nq, un), blk, 0, s, g, b0, 0, nq, kb, 1);
-        }
-        if (b0 > 0)
+        hipLaunchKernelGGL(ridge_panel_subst_kernel<true>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
+        if (b0 == 0) break;
+        if (!ov.side) {
             hipLaunchKernelGGL(ridge_big_kernel<2>, dim3(b0 / 2 * nq2, un), dim3(512), 0, s, g, 0, 0, nq2, b0, b1 - b0);
+            continue;
+        }
+        const int bp = std::max(0, b0 - kPanel);
+        if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
+        // lookahead: rows [bp, b0) in blocks of 64, K = the panel
+        hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3((b0 - bp) * nq, un), blk, 0, s, g, bp, 0, nq, b0,
+                           b1 - b0);
+        side_pending = false;
+        if (bp == 0) continue;
+        (void)hipEventRecord(ov.main_ready, s);
+        (void)hipStreamWaitEvent(ov.side, ov.main_ready, 0);
+        hipLaunchKernelGGL(ridge_big_kernel<2>, dim3(bp / 2 * nq2, un), dim3(512), 0, ov.side, g, 0, 0, nq2, b0,
+                           b1 - b0);
+        (void)hipEventRecord(ov.side_done, ov.side);
+        side_pending = true;
     }
+    if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
 }
 
 }  // namespace
