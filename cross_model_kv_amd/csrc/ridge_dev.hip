@@ -72,15 +72,17 @@ __device__ __forceinline__ void lower_decode(int u, int& I, int& J) {
 
 }  // namespace
 
-// A[i][j] = M_xx[min][max] (+ lambda on the diagonal) for i, j < p; identity padding.  One
-// 64 x 64 tile (I, J) of A per workgroup: the tile is read from M_xx's upper triangle as tile
-// (min, max) -- rows of 64 consecutive floats either way -- through LDS, so that the tiles below
-// the diagonal, which are transposes, are read and written with whole rows too.
+// A[i][j] = M_xx[min][max] (+ lambda on the diagonal) for i, j < p; identity padding.  Only the
+// 64 x 64 tiles on and below the diagonal are written: no kernel of the solve reads A above its
+// diagonal blocks (the large trailing update computes its diagonal 128 x 128 tiles whole, and
+// their upper 64 x 64 quarter is never read).  One tile (I, J), I >= J, per workgroup: the tile
+// is read from M_xx's upper triangle as tile (J, I) -- rows of 64 consecutive floats -- through
+// LDS, so that the transposed tile is read and written with whole rows too.
 __global__ __launch_bounds__(256) void ridge_init_a_kernel(const RidgeArgs g) {
     __shared__ float t[RB][RB + 1];
     const int P = g.P, p = g.p;
-    const int nb = P / RB;
-    const int I = (int)blockIdx.x / nb, J = (int)blockIdx.x % nb;
+    int I, J;
+    lower_decode((int)blockIdx.x, I, J);
     const float* M_xx = g.s[blockIdx.y].M_xx;
     const int tr = min(I, J) * RB, tc = max(I, J) * RB;  // source tile in the upper triangle
     const int tid = threadIdx.x, c = tid & 63;
@@ -962,7 +964,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
                                                         // panel boundary, a multiple of 4 blocks, is even)
     const unsigned un = (unsigned)n;
     const dim3 blk(256);
-    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(nb * nb), un), blk, 0, s, g);
+    hipLaunchKernelGGL(ridge_init_a_kernel, dim3((unsigned)(nb * (nb + 1) / 2), un), blk, 0, s, g);
     hipLaunchKernelGGL(ridge_init_b_kernel, dim3((unsigned)(((int64_t)P * Q + 255) / 256), un), blk, 0, s, g);
     // Factorisation with a one-panel lookahead.  After panel [b0, b1) is factored, its update of
     // the next panel's columns [b1, b2) (rows b1 ..) runs on `s`, and its update of the rest of
