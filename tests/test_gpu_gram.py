@@ -392,6 +392,53 @@ def test_ridge_solve_device_not_spd(ctx):
     assert e.value.status == K.ERR_NOT_SPD
 
 
+# positions of a planted bad entry: each 16-wide sub-block of the first 64-wide diagonal block,
+# the first row of the second block, a later block, and the last row (second panel of 4 blocks)
+_BAD_AT = [0, 5, 17, 40, 63, 64, 130, 299]
+
+
+@pytest.mark.parametrize("kind", ["negative", "zero", "nan", "inf", "nan-off-diagonal"])
+def test_ridge_device_refuses_bad_pivots(ctx, kind):
+    """The diagonal factor flags a system whose pivot is not positive and finite, wherever it
+    falls: M_xx + lambda I with a negative, zero (M_xx_jj = -lambda and row j zero), NaN or +inf
+    diagonal entry, or a NaN off the diagonal (row j, column j / 2), at positions in every
+    16-wide sub-block of a 64-wide diagonal block, in later blocks and in the second panel
+    (p 300: 6 blocks): KVMAP_ERR_NOT_SPD.  The state restored, the solve gives its result again
+    (lambda 0.5, exact in fp32, so that the zero case is an exact zero pivot)."""
+    from cross_model_kv_amd import kvmap as K
+    p, q, lam = 300, 16, 0.5
+    rng = np.random.default_rng(2026)
+    X = rng.standard_normal((900, p))
+    Y = X[:, :q] * 0.5 + 0.1 * rng.standard_normal((900, q))
+    st = ctx.gram_state(p, q)
+    ctx.gram_reset(st)
+    ctx.gram(st, _dev(X, "f32"), _dev(Y, "f32"))
+    W0, b0 = ctx.ridge_solve_device(st, lam, dtype=torch.float32)
+    for j in _BAD_AT:
+        saved = st.M_xx.clone()
+        if kind == "negative":
+            st.M_xx[j, j] = -1e4
+        elif kind == "zero":
+            st.M_xx[j, :] = 0.0
+            st.M_xx[:, j] = 0.0
+            st.M_xx[j, j] = -lam
+        elif kind == "nan":
+            st.M_xx[j, j] = float("nan")
+        elif kind == "inf":
+            st.M_xx[j, j] = float("inf")
+        else:
+            m = j // 2 if j else 1
+            st.M_xx[j, m] = float("nan")
+            st.M_xx[m, j] = float("nan")
+        print(f"[ridge] bad pivot {kind} at {j}", flush=True)
+        with pytest.raises(K.KvmapError) as e:
+            ctx.ridge_solve_device(st, lam, dtype=torch.float32)
+        assert e.value.status == K.ERR_NOT_SPD, (kind, j)
+        st.M_xx.copy_(saved)
+    W1, b1 = ctx.ridge_solve_device(st, lam, dtype=torch.float32)
+    assert torch.equal(W0, W1) and torch.equal(b0, b1)
+
+
 @pytest.mark.parametrize("dtype,bd", [("bf16", 64), ("bf16", 256), ("f32", 64), ("f32", 128)])
 def test_gram_block_diagonal_state(ctx, dtype, bd):
     """A state that keeps M_xx only on its diagonal blocks (xx_block): each block equals the
