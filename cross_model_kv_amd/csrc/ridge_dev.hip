@@ -36,9 +36,7 @@ constexpr int RB = 64;       // block size
 // of the LDS cycles of the trailing update in bank conflicts)
 constexpr int LDW = RB + 1;  // 64 x 64 tile
 constexpr int TB = 128;      // C tile of the large updates (the trailing matrix, the right-hand sides)
-constexpr int KB = 32;       // K per LDS stage of the large updates
-constexpr int LD_R = KB + 1;  // LDS row stride of a stage stored with the tile's rows (128 x 32)
-constexpr int LD_M = TB + 2;  // ... with its K index as rows (32 x 128)
+constexpr int LD_M = TB + 2;  // LDS row stride of a large-update stage stored with its K index as rows
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -670,13 +668,17 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
 // MODE 0 takes the lower triangle of tiles from tile j0 on, and computes the diagonal tiles
 // whole: their upper 64 x 64 quarter is never read).  Twice the arithmetic per operand byte of
 // the 64 x 64 kernel.  8 waves, each a 64 x 32 eighth of C as 4 x 2 blocks of 16 x 16
-// (v_mfma_f64_16x16x4f64).  The operands go through LDS in stages of K = 32, two stages
+// (v_mfma_f64_16x16x4f64).  The operands go through LDS in stages of K = KB, two stages
 // deep: the registers holding stage kc + 1 are written to LDS, and stage kc + 2 is requested,
-// before the MFMAs of stage kc, so neither waits on the other.
-template <int MODE>
+// before the MFMAs of stage kc, so neither waits on the other.  KB = 32 takes 132-135 KiB of
+// LDS, one workgroup per CU; KB = 16 takes 66-68 KiB, two per CU, so that one workgroup's C
+// epilogue overlaps the other's products (faster for batches of systems; for one system,
+// whose serial chain of small kernels runs beside these updates, KB = 32 measured faster).
+template <int MODE, int KB>
 __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i0, int j0, int ncol, int k0,
                                                         int nk) {
     static_assert(MODE == 0 || MODE == 1 || MODE == 2, "large-update modes");
+    constexpr int LD_R = KB + 1;  // LDS row stride of a stage stored with the tile's rows (128 x KB)
     constexpr bool A_ROWS = MODE != 2;  // A stage stored with the rows r (else with m as rows)
     constexpr bool B_ROWS = MODE == 0;  // B stage stored with the columns c as rows (else m)
     constexpr int A_LDS = A_ROWS ? TB * LD_R : KB * LD_M;
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i
             Bp = Bm + (size_t)ko * Q + (size_t)J * TB; ldb = Q;  // rows m, columns c
         }
     };
-    constexpr int PER = TB * KB / 512;  // elements of each stage per thread (8)
+    constexpr int PER = TB * KB / 512;  // elements of each stage per thread (8 at KB = 32)
     double ra[PER], rb[PER];
     auto fetch = [&](int kc) {
         const double* Ap;
@@ -944,6 +946,13 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
 constexpr int kPanel = 4;
 static_assert(kPanel <= 4, "ridge_panel_subst_kernel holds at most 4 blocks in registers");
 
+// A large update: stages of K = 16 for a batch of systems (two workgroups per CU), 32 for one
+template <int MODE>
+void launch_big(dim3 grid, hipStream_t s, const RidgeArgs& g, int i0, int j0, int ncol, int k0, int nk) {
+    if (grid.y > 1) hipLaunchKernelGGL((ridge_big_kernel<MODE, 16>), grid, dim3(512), 0, s, g, i0, j0, ncol, k0, nk);
+    else hipLaunchKernelGGL((ridge_big_kernel<MODE, 32>), grid, dim3(512), 0, s, g, i0, j0, ncol, k0, nk);
+}
+
 // Forward substitution over the panel [b0, b1): each diagonal step a product with the block's
 // inverse, then the rows below the panel updated once with K = the panel.  Reads only the
 // factored panel (its columns of L and its blocks' inverses) and writes B.
@@ -954,8 +963,7 @@ static void forward_panel(const RidgeArgs& g, int n, int b0, hipStream_t s) {
     const int b1 = std::min(nb, b0 + kPanel);
     hipLaunchKernelGGL(ridge_panel_subst_kernel<false>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
     if (nb > b1)
-        hipLaunchKernelGGL(ridge_big_kernel<1>, dim3((nb - b1) / 2 * nq2, un), dim3(512), 0, s, g, b1 / 2, 0, nq2, b0,
-                           b1 - b0);
+        launch_big<1>(dim3((nb - b1) / 2 * nq2, un), s, g, b1 / 2, 0, nq2, b0, b1 - b0);
 }
 
 void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& ov) {
@@ -995,8 +1003,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         if (b1 == nb) break;
         if (!ov.side) {
             const int m = (nb - b1) / 2;  // trailing lower triangle, in tiles of 128
-            hipLaunchKernelGGL(ridge_big_kernel<0>, dim3(m * (m + 1) / 2, un), dim3(512), 0, s, g, 0, b1 / 2, 0, b0,
-                               b1 - b0);
+            launch_big<0>(dim3(m * (m + 1) / 2, un), s, g, 0, b1 / 2, 0, b0, b1 - b0);
             continue;
         }
         const int b2 = std::min(nb, b1 + kPanel);
@@ -1009,8 +1016,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         const int m = (nb - b2) / 2;  // the rest: lower triangle of 128-tiles from b2
         (void)hipEventRecord(ov.main_ready, s);
         (void)hipStreamWaitEvent(ov.side, ov.main_ready, 0);
-        hipLaunchKernelGGL(ridge_big_kernel<0>, dim3(m * (m + 1) / 2, un), dim3(512), 0, ov.side, g, 0, b2 / 2, 0, b0,
-                           b1 - b0);
+        launch_big<0>(dim3(m * (m + 1) / 2, un), ov.side, g, 0, b2 / 2, 0, b0, b1 - b0);
         (void)hipEventRecord(ov.side_done, ov.side);
         side_pending = true;
     }
@@ -1034,7 +1040,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         hipLaunchKernelGGL(ridge_panel_subst_kernel<true>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
         if (b0 == 0) break;
         if (!ov.side) {
-            hipLaunchKernelGGL(ridge_big_kernel<2>, dim3(b0 / 2 * nq2, un), dim3(512), 0, s, g, 0, 0, nq2, b0, b1 - b0);
+            launch_big<2>(dim3(b0 / 2 * nq2, un), s, g, 0, 0, nq2, b0, b1 - b0);
             continue;
         }
         const int bp = std::max(0, b0 - kPanel);
@@ -1046,8 +1052,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         if (bp == 0) continue;
         (void)hipEventRecord(ov.main_ready, s);
         (void)hipStreamWaitEvent(ov.side, ov.main_ready, 0);
-        hipLaunchKernelGGL(ridge_big_kernel<2>, dim3(bp / 2 * nq2, un), dim3(512), 0, ov.side, g, 0, 0, nq2, b0,
-                           b1 - b0);
+        launch_big<2>(dim3(bp / 2 * nq2, un), ov.side, g, 0, 0, nq2, b0, b1 - b0);
         (void)hipEventRecord(ov.side_done, ov.side);
         side_pending = true;
     }
