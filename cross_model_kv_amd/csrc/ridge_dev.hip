@@ -160,7 +160,7 @@ __device__ __forceinline__ double rsqrt_f64(double d) {
 // are updated too and never used.
 __global__ __launch_bounds__(256) void ridge_potrf_kernel(const RidgeArgs g, int kb) {
     constexpr int SB = 16;         // sub-block
-    constexpr int NS = RB / SB;    // sub-blocks per side
+    static_assert(RB / SB == 4, "the phases below are written out for 4 sub-blocks per side");
     constexpr int LDL = RB + 1;    // LDS row stride (doubles)
     __shared__ double Ls[RB * LDL];  // the block: A in, L out (lower triangle)
     __shared__ double Xs[RB * LDL];  // X = L^-1 (lower triangle; the rest is not written)
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
             }
 }
 
-// Substitution inside one panel of nbk blocks from b0, one workgroup per 64 columns J of the
+// Substitution inside one panel of nbk blocks from b0, one workgroup per CW columns J of the
 // right-hand sides (the rows outside the panel already updated by every earlier panel):
 //   forward  (L Z = B):    for kb = b0 .. b0 + nbk - 1:  Z_kb = Li_kb B_kb,    then B_I -= L_I,kb Z_kb  (I in (kb, b0 + nbk))
 //   backward (L^T W = Z):  for kb = b0 + nbk - 1 .. b0:  W_kb = Li_kb^T Z_kb,  then Z_I -= L_kb,I^T W_kb  (I in [b0, kb))
@@ -532,11 +532,12 @@ __global__ __launch_bounds__(256) void ridge_update_kernel(const RidgeArgs g, in
 // in registers (accumulator layout, 16 values per block and thread); each product's operand
 // (Li_kb or a 64 x 64 block of L) is read into registers during the previous product and goes
 // through a two-deep LDS ring; the diagonal step's input and result go through LDS as the B
-// operand.  4 waves, each a 32 x 32 quarter of the 64 x 64 block as 2 x 2 blocks of 16 x 16
-// (v_mfma_f64_16x16x4f64, accumulator element e of a lane at row (lane >> 4) + 4 e).
-template <bool BACK>
+// operand.  4 waves, each a 32 x CW/2 quarter of the 64 x CW block as 2 x CW/32 blocks of
+// 16 x 16 (v_mfma_f64_16x16x4f64, accumulator element e of a lane at row (lane >> 4) + 4 e).
+template <bool BACK, int CW>
 __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs g, int b0, int nbk) {
     constexpr int MAXB = 4;  // blocks per panel
+    constexpr int NJ = CW / 32;  // 16-wide column blocks per wave (CW columns per workgroup)
     __shared__ double Os[2][RB * LDW];  // operand ring: Os[x][y] = O[x][y], O = Li_kb or a block of L
     __shared__ double Zs[RB * LDW];     // the diagonal step's input, then
     __shared__ double Ws[RB * LDW];     // its result
@@ -545,19 +546,19 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
     double* Bm = sys_b(g);
     const int P = g.P, Q = g.Q;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
+    const int r0 = (w >> 1) * 32, c0 = (w & 1) * (CW / 2);
     const int li = lane & 15, lk = lane >> 4;
     const int J = (int)blockIdx.x;
-    f64x4_t z[MAXB][2][2];
+    f64x4_t z[MAXB][2][NJ];
 #pragma unroll
     for (int t = 0; t < MAXB; ++t)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    z[t][i][j][e] = (t < nbk) ? Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * RB + c0 + 16 * j + li]
+                    z[t][i][j][e] = (t < nbk) ? Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * CW + c0 + 16 * j + li]
                                               : 0.0;
     // the operand of product (t, u): Li_kb (u < 0) or, for the update of row block I = b0 + u,
     // L_kb,I (backward) or L_I,kb (forward), kb = b0 + t
@@ -582,11 +583,11 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
         }
     };
     // acc (+/-)= op(O) X, op(O) = O^T (backward) or O (forward), X from LDS
-    auto product = [&](f64x4_t (&acc)[2][2], const double* os, const double* xs, bool neg) {
+    auto product = [&](f64x4_t (&acc)[2][NJ], const double* os, const double* xs, bool neg) {
 #pragma unroll
         for (int kk = 0; kk < RB; kk += 4) {
             const int m = kk + lk;
-            double a[2], b[2];
+            double a[2], b[NJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = r0 + 16 * i + li;
@@ -594,18 +595,18 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
                 a[i] = neg ? -v : v;
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = xs[m * LDW + c0 + 16 * j + li];
+            for (int j = 0; j < NJ; ++j) b[j] = xs[m * LDW + c0 + 16 * j + li];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     };
-    auto put = [&](double* xs, const f64x4_t (&v)[2][2]) {
+    auto put = [&](double* xs, const f64x4_t (&v)[2][NJ]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) xs[(r0 + 16 * i + lk + 4 * e) * LDW + c0 + 16 * j + li] = v[i][j][e];
     };
@@ -633,16 +634,16 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
             }
             __syncthreads();
             if (u < 0) {
-                f64x4_t acc[2][2];
+                f64x4_t acc[2][NJ];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
                 product(acc, Os[buf], Zs, false);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) z[t][i][j] = acc[i][j];
+                    for (int j = 0; j < NJ; ++j) z[t][i][j] = acc[i][j];
                 put(Ws, z[t]);  // Ws's last readers were the previous step's updates, before the barrier
             } else {
                 product(z[u], Os[buf], Ws, true);
@@ -656,10 +657,10 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * RB + c0 + 16 * j + li] = z[t][i][j][e];
+                        Bm[(size_t)((b0 + t) * RB + r0 + 16 * i + lk + 4 * e) * Q + J * CW + c0 + 16 * j + li] = z[t][i][j][e];
         }
 }
 
@@ -672,8 +673,9 @@ __global__ __launch_bounds__(256) void ridge_panel_subst_kernel(const RidgeArgs 
 // deep: the registers holding stage kc + 1 are written to LDS, and stage kc + 2 is requested,
 // before the MFMAs of stage kc, so neither waits on the other.  KB = 32 takes 132-135 KiB of
 // LDS, one workgroup per CU; KB = 16 takes 66-68 KiB, two per CU, so that one workgroup's C
-// epilogue overlaps the other's products (faster for batches of systems; for one system,
-// whose serial chain of small kernels runs beside these updates, KB = 32 measured faster).
+// epilogue overlaps the other's products (faster for batches of systems and for the back
+// substitution; for one system's factorisation and forward substitution, beside which its
+// serial chain of small kernels runs, KB = 32 measured faster).
 template <int MODE, int KB>
 __global__ __launch_bounds__(512) void ridge_big_kernel(const RidgeArgs g, int i0, int j0, int ncol, int k0,
                                                         int nk) {
@@ -945,23 +947,31 @@ RidgeArgs make_args(int n, int p, int q, const RidgeSys* sys, double lambda, voi
 // rest of the matrix (or of the right-hand sides) is updated once per panel with K = 64 kPanel.
 constexpr int kPanel = 4;
 static_assert(kPanel <= 4, "ridge_panel_subst_kernel holds at most 4 blocks in registers");
+// The substitutions inside a panel: 32 columns of the right-hand sides per workgroup for one
+// system (twice the workgroups on the serial chain), 64 for a batch (fewer operand reloads)
+template <bool BACK>
+void launch_subst(const RidgeArgs& g, unsigned un, int b0, int nbk, hipStream_t s) {
+    if (un > 1) hipLaunchKernelGGL((ridge_panel_subst_kernel<BACK, 64>), dim3(g.Q / 64, un), dim3(256), 0, s, g, b0, nbk);
+    else hipLaunchKernelGGL((ridge_panel_subst_kernel<BACK, 32>), dim3(g.Q / 32, un), dim3(256), 0, s, g, b0, nbk);
+}
 
-// A large update: stages of K = 16 for a batch of systems (two workgroups per CU), 32 for one
+// A large update: stages of K = 16 (two workgroups per CU) for a batch of systems and for the
+// back substitution, 32 for the factorisation and forward substitution of one system
 template <int MODE>
 void launch_big(dim3 grid, hipStream_t s, const RidgeArgs& g, int i0, int j0, int ncol, int k0, int nk) {
-    if (grid.y > 1) hipLaunchKernelGGL((ridge_big_kernel<MODE, 16>), grid, dim3(512), 0, s, g, i0, j0, ncol, k0, nk);
+    if (grid.y > 1 || MODE == 2) hipLaunchKernelGGL((ridge_big_kernel<MODE, 16>), grid, dim3(512), 0, s, g, i0, j0, ncol, k0, nk);
     else hipLaunchKernelGGL((ridge_big_kernel<MODE, 32>), grid, dim3(512), 0, s, g, i0, j0, ncol, k0, nk);
 }
 
-// Forward substitution over the panel [b0, b1): each diagonal step a product with the block's
-// inverse, then the rows below the panel updated once with K = the panel.  Reads only the
+// Forward substitution over the panel [b0, b1): the chain inside the panel (each diagonal step a
+// product with the block's inverse) in one launch, then the rows below the panel updated once
+// with K = the panel.  Reads only the
 // factored panel (its columns of L and its blocks' inverses) and writes B.
 static void forward_panel(const RidgeArgs& g, int n, int b0, hipStream_t s) {
-    const int nb = g.P / RB, nq = g.Q / RB, nq2 = g.Q / TB;
+    const int nb = g.P / RB, nq2 = g.Q / TB;
     const unsigned un = (unsigned)n;
-    const dim3 blk(256);
     const int b1 = std::min(nb, b0 + kPanel);
-    hipLaunchKernelGGL(ridge_panel_subst_kernel<false>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
+    launch_subst<false>(g, un, b0, b1 - b0, s);
     if (nb > b1)
         launch_big<1>(dim3((nb - b1) / 2 * nq2, un), s, g, b1 / 2, 0, nq2, b0, b1 - b0);
 }
@@ -1037,7 +1047,7 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
     // `s` waits for it first.
     for (int b1 = nb; b1 > 0; b1 -= kPanel) {
         const int b0 = std::max(0, b1 - kPanel);
-        hipLaunchKernelGGL(ridge_panel_subst_kernel<true>, dim3(nq, un), blk, 0, s, g, b0, b1 - b0);
+        launch_subst<true>(g, un, b0, b1 - b0, s);
         if (b0 == 0) break;
         if (!ov.side) {
             launch_big<2>(dim3(b0 / 2 * nq2, un), s, g, 0, 0, nq2, b0, b1 - b0);
