@@ -256,6 +256,7 @@ extern "C" int kvmap_destroy(kvmap_ctx* c) {
     if (c->ridge_ov.side) (void)hipStreamDestroy(c->ridge_ov.side);
     if (c->ridge_ov.main_ready) (void)hipEventDestroy(c->ridge_ov.main_ready);
     if (c->ridge_ov.side_done) (void)hipEventDestroy(c->ridge_ov.side_done);
+    if (c->ridge_ov.side_done2) (void)hipEventDestroy(c->ridge_ov.side_done2);
     if (c->ridge_ov.fwd) (void)hipStreamDestroy(c->ridge_ov.fwd);
     if (c->ridge_ov.fwd_ready) (void)hipEventDestroy(c->ridge_ov.fwd_ready);
     if (c->ridge_ov.fwd_done) (void)hipEventDestroy(c->ridge_ov.fwd_done);
@@ -971,10 +972,11 @@ extern "C" int kvmap_ridge_solve_host(int32_t p, int32_t q, const float* mean_x,
 }
 
 static int ensure_ridge_scratch(kvmap_ctx* c, size_t need) {
-    if (!c->ridge_ov.side) {  // the lookahead's side stream (default priority) and its two events
+    if (!c->ridge_ov.side) {  // the lookahead's side stream (default priority) and its events
         KVMAP_HIP(hipStreamCreateWithFlags(&c->ridge_ov.side, hipStreamNonBlocking));
         KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.main_ready, hipEventDisableTiming));
         KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.side_done, hipEventDisableTiming));
+        KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.side_done2, hipEventDisableTiming));
         KVMAP_HIP(hipStreamCreateWithFlags(&c->ridge_ov.fwd, hipStreamNonBlocking));
         KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.fwd_ready, hipEventDisableTiming));
         KVMAP_HIP(hipEventCreateWithFlags(&c->ridge_ov.fwd_done, hipEventDisableTiming));

@@ -140,14 +140,16 @@ struct RidgeSys {
 size_t ridge_dev_scratch_bytes(int p, int q, int n);
 // Pivot flags of the n systems (nonzero: not positive definite) inside that scratch.
 int* ridge_dev_flags(void* scratch, int p, int q, int n);
-// A side stream (default priority) and two events for the factorisation's lookahead: the bulk of
-// each panel's trailing update runs there, overlapping the next panel's diagonal chain on the
-// caller's stream.  side NULL: everything on the caller's stream.
+// A side stream (default priority) and events for the lookaheads: the bulk of each panel's
+// trailing update (and, in the back substitution, of its update of the rows above) runs there,
+// overlapping the next panel's chain on the caller's stream.  side NULL: everything on the
+// caller's stream.
 // A second one takes each factored panel's forward substitution.
 struct RidgeOverlap {
     hipStream_t side;
     hipEvent_t main_ready;  // recorded on the caller's stream, waited on by the side stream
     hipEvent_t side_done;   // recorded on the side stream, waited on by the caller's stream
+    hipEvent_t side_done2;  // a second one: the back substitution alternates between the two
     hipStream_t fwd;        // NULL: the forward substitution runs after the factorisation
     hipEvent_t fwd_ready;   // recorded on the caller's stream after each panel, waited on by fwd
     hipEvent_t fwd_done;    // recorded on fwd after the last panel, waited on by the caller's stream

@@ -21,6 +21,8 @@
 // non-finite pivot sets the system's device flag, which the host turns into KVMAP_ERR_NOT_SPD.
 
 #include <algorithm>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -1031,7 +1033,6 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
         side_pending = true;
     }
     if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
-    side_pending = false;
     if (ov.fwd) {
         (void)hipEventRecord(ov.fwd_done, ov.fwd);
         (void)hipStreamWaitEvent(s, ov.fwd_done, 0);
@@ -1040,33 +1041,44 @@ void solve_batch(const RidgeArgs& g, int n, hipStream_t s, const RidgeOverlap& o
     // right after the panel was factored)
     if (!ov.fwd)
         for (int b0 = 0; b0 < nb; b0 += kPanel) forward_panel(g, n, b0, s);
-    // L^T W = Z, panels from the last, with a one-panel lookahead as in the factorisation: once
-    // panel [b0, b1) is solved, its update of the next panel's rows [bp, b0) runs on `s`, so that
-    // panel's chain of diagonal steps can start, and its update of the rows above, [0, bp), on
-    // the side stream.  The next lookahead update writes rows that the side update writes too, so
-    // `s` waits for it first.
-    for (int b1 = nb; b1 > 0; b1 -= kPanel) {
-        const int b0 = std::max(0, b1 - kPanel);
-        launch_subst<true>(g, un, b0, b1 - b0, s);
-        if (b0 == 0) break;
+    // L^T W = Z, panels from the last, with a two-panel lookahead.  Panel k, counted from the
+    // end, is blocks [s_k, e_k).  Once panel k is solved, the caller's stream updates the rows of
+    // panel k + 1 with panels k - 1 and k (K up to 8 blocks), so that panel's chain can start,
+    // and the side stream updates the rows above panel k + 2, [0, s_(k+2)), with panel k.  The
+    // streams then never write the same rows at once: panel k + 1's rows were last written on
+    // the side stream by the update of panel k - 2, which the lookahead waits for (two events in
+    // turn, so that it does not wait for the side update just queued).
+    std::vector<std::pair<int, int>> pan;  // (s_k, e_k)
+    for (int e = nb; e > 0; e -= kPanel) pan.push_back({std::max(0, e - kPanel), e});
+    const int np = (int)pan.size();
+    const hipEvent_t done[2] = {ov.side_done, ov.side_done2};
+    bool pending[2] = {false, false};
+    for (int k = 0; k < np; ++k) {
+        const int sk = pan[k].first, ek = pan[k].second;
+        launch_subst<true>(g, un, sk, ek - sk, s);
+        if (k + 1 == np) break;
         if (!ov.side) {
-            launch_big<2>(dim3(b0 / 2 * nq2, un), s, g, 0, 0, nq2, b0, b1 - b0);
+            launch_big<2>(dim3(sk / 2 * nq2, un), s, g, 0, 0, nq2, sk, ek - sk);
             continue;
         }
-        const int bp = std::max(0, b0 - kPanel);
-        if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
-        // lookahead: rows [bp, b0) in blocks of 64, K = the panel
-        hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3((b0 - bp) * nq, un), blk, 0, s, g, bp, 0, nq, b0,
-                           b1 - b0);
-        side_pending = false;
-        if (bp == 0) continue;
+        if (pending[k % 2]) {  // the side update of panel k - 2
+            (void)hipStreamWaitEvent(s, done[k % 2], 0);
+            pending[k % 2] = false;
+        }
+        const int kend = k > 0 ? pan[k - 1].second : ek;  // panels k - 1 and k
+        const int rs = pan[k + 1].first, re = pan[k + 1].second;
+        hipLaunchKernelGGL((ridge_update_kernel<2, false>), dim3((re - rs) * nq, un), blk, 0, s, g, rs, 0, nq, sk,
+                           kend - sk);
+        const int top = k + 2 < np ? pan[k + 2].first : 0;
+        if (top == 0) continue;
         (void)hipEventRecord(ov.main_ready, s);
         (void)hipStreamWaitEvent(ov.side, ov.main_ready, 0);
-        launch_big<2>(dim3(bp / 2 * nq2, un), ov.side, g, 0, 0, nq2, b0, b1 - b0);
-        (void)hipEventRecord(ov.side_done, ov.side);
-        side_pending = true;
+        launch_big<2>(dim3(top / 2 * nq2, un), ov.side, g, 0, 0, nq2, sk, ek - sk);
+        (void)hipEventRecord(done[k % 2], ov.side);
+        pending[k % 2] = true;
     }
-    if (side_pending) (void)hipStreamWaitEvent(s, ov.side_done, 0);
+    for (int i = 0; i < 2; ++i)
+        if (pending[i]) (void)hipStreamWaitEvent(s, done[i], 0);
 }
 
 }  // namespace
