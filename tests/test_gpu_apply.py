@@ -235,6 +235,8 @@ def test_full_size_sampled(ctx, cid):
         first and last rows: each (target layer, K|V, token block, feature tile) tile of the GEMM
         is checked against the oracle on at least one row.
       * Windows of 24 consecutive rows at the start, middle and end of four target layers.
+      * Every element of the first and the last target layer, K and V (the first and the last
+        (t, K|V) pairs of the tile walk), checked in chunks of 4096 rows.
       * A second apply gives bit-identical outputs.
     The elements with |ref| >= 8 are counted and their errors printed per block."""
     cfg = APPLY_CONFIGS[cid]
@@ -254,6 +256,9 @@ def test_full_size_sampled(ctx, cid):
     rows = np.unique(np.concatenate([np.arange(0, 24), np.arange(T // 2 - 12, T // 2 + 12), np.arange(T - 24, T)]))
     targets = [0, cfg.L_tgt // 3, (2 * cfg.L_tgt) // 3, cfg.L_tgt - 1]
     _check_sampled(cfg, inp, ok_, ov_, targets, rows, tally)
+    for t in (0, cfg.L_tgt - 1):
+        for r0 in range(0, T, 4096):
+            _check_sampled(cfg, inp, ok_, ov_, [t], np.arange(r0, min(r0 + 4096, T)), tally)
     print(f"[apply] {cfg.name} total: {tally.summary()}", flush=True)
     # determinism at full size
     ok2, ov2 = _run(ctx, cfg, inp)
