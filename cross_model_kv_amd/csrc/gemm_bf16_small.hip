@@ -61,12 +61,18 @@ __device__ __forceinline__ ShortItem short_item(int i, int KS, int nN, int L_tgt
     return it;
 }
 
+// Items finish inside the short-cache kernel (bias, target RoPE, bf16 output; no reduce kernel)
+// when the K reduction is not split and a tile holds 64 or 128 tokens.  The host and the kernel
+// both decide by this.
+__host__ __device__ __forceinline__ bool small_fused(int tok, int KS) { return tok >= 64 && KS == 1; }
+
 // Persistent: workgroup g (one per compute unit) takes items g, g + G, g + 2G, ... and streams
 // them through ONE ring of NRING stages (W tile + X tile), each filled by buffer_load_dwordx4
 // ... lds NRING - 1 K-steps ahead of its use.  The ring runs on across items: the loads of an
 // item's first K-steps go out while the previous item's last ones are computed, so W streams
 // without a drain and refill per tile.  At the end of an item its fp32 partial sums are stored
-// and the accumulators cleared.  TOK (16, 32, 64 or 128, at least T) tokens per tile, 8 waves:
+// (or, with an unsplit K reduction at 64 or 128 tokens, its finished bf16 rows) and the
+// accumulators cleared.  TOK (16, 32, 64 or 128, at least T) tokens per tile, 8 waves:
 // WN waves side by side along the features, each FW features (whole 16-feature blocks) x TW
 // tokens as IB x JB blocks of v_mfma_f32_16x16x32_bf16 -- 8 x 1 waves of 32 x 16 at TOK 16,
 // 4 x 2 of 64 x 16 at 32, 2 x 4 of 128 x 16 at 64, 2 x 4 of 128 x 32 at 128 -- so that short
@@ -198,6 +204,70 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
             for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
     const int wn = wave % WN, wp = wave / WN;
     const int kq = lane >> 4;
+
+    // End of an item, split K reduction: its fp32 partial sums, summed by the reduce kernel.
+    auto store_partial = [&](const ShortItem& it) {
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const int p = wp * TW + j * 16 + (lane & 15);
+            if (p >= T) continue;
+            float* dst = part + ((((size_t)it.ks * L_tgt + it.t) * 2 + it.kv) * (size_t)T + p) * N;
+#pragma unroll
+            for (int i = 0; i < IB; ++i) {
+                const int n = it.n0 + wn * FW + i * 16 + kq * 4;
+                if (n < N)
+                    *(float4*)(dst + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        }
+    };
+    // End of an item, whole K reduction at 64 or 128 tokens per tile: a wave's 128 features are
+    // whole heads, so both members (e, e + d/2) of every RoPE pair sit in one lane (blocks i and
+    // i + d/32) and the item finishes here as the reduce kernel would finish it (+ bias, target
+    // RoPE on keys, bf16 into [t][h][p][e]; the same fp32 operations, so the same bits).
+    auto finish_item = [&](const ShortItem& it) {
+        if constexpr (TOK >= 64) {
+            constexpr int HALF = D / 2, PB = HALF / 16, NLO = IB / 2;
+            static_assert(FW % D == 0, "a wave's features are whole heads");
+            const uint16_t* __restrict__ bias = (const uint16_t*)(it.kv ? a.bv : a.bk) + (size_t)it.t * N;
+            uint16_t* __restrict__ out = (uint16_t*)(it.kv ? a.outv : a.outk);
+#pragma unroll
+            for (int li = 0; li < NLO; ++li) {
+                const int i = (li / PB) * 2 * PB + li % PB;         // block of low members
+                const int nl = it.n0 + wn * FW + i * 16 + kq * 4;  // the lane's first low member
+                if (nl >= N) continue;  // a head past the last one (partial last feature tile)
+                const int h = nl / D, e = nl - h * D;
+                const uint2 bl = *(const uint2*)(bias + nl), bh = *(const uint2*)(bias + nl + HALF);
+                const float bL[4] = {bf16lo(bl.x), bf16hi(bl.x), bf16lo(bl.y), bf16hi(bl.y)};
+                const float bH[4] = {bf16lo(bh.x), bf16hi(bh.x), bf16lo(bh.y), bf16hi(bh.y)};
+#pragma unroll
+                for (int j = 0; j < JB; ++j) {
+                    const int64_t p = wp * TW + j * 16 + (lane & 15);
+                    if (p >= T) continue;
+                    float lo[4], hi[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        lo[r] = (0.f + acc[i][j][r]) + bL[r];
+                        hi[r] = (0.f + acc[i + PB][j][r]) + bH[r];
+                    }
+                    if (it.kv == 0) {
+                        const float4* cs4 = (const float4*)(a.tab_tgt + p * HALF + e);
+                        const float4 c01 = cs4[0], c23 = cs4[1];
+                        const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+                        const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float l = lo[r], hh = hi[r];
+                            lo[r] = fmaf(-hh, ss[r], l * cc[r]);
+                            hi[r] = fmaf(l, ss[r], hh * cc[r]);
+                        }
+                    }
+                    uint16_t* dst = out + (((size_t)it.t * H + h) * T + p) * D + e;
+                    *(uint2*)dst = make_uint2(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]));
+                    *(uint2*)(dst + HALF) = make_uint2(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]));
+                }
+            }
+        }
+    };
     const int fx = slot_xor(lane & 15);
     const int arow0 = (wn * FW + (lane & 15)) * 8;
     const int brow0 = W_CHUNKS + (wp * TW + (lane & 15)) * 8;
@@ -250,21 +320,12 @@ __global__ __launch_bounds__(512) void map_bf16_small_kernel(MapArgs a, int L_tg
         issue();
         c_buf = (c_buf + 1 == NRING) ? 0 : c_buf + 1;
         if (--c_left == 0) {
-            // partial sums of the item: lane holds features 4 (lane / 16) + r of each 16 x 16
-            // block, token lane % 16
+            // lane holds features 4 (lane / 16) + r of each 16 x 16 block, token lane % 16
             const ShortItem it = short_item(c_item, KS, nN, L_tgt, kps, nk_all);
-#pragma unroll
-            for (int j = 0; j < JB; ++j) {
-                const int p = wp * TW + j * 16 + (lane & 15);
-                if (p >= T) continue;
-                float* dst = part + ((((size_t)it.ks * L_tgt + it.t) * 2 + it.kv) * (size_t)T + p) * N;
-#pragma unroll
-                for (int i = 0; i < IB; ++i) {
-                    const int n = it.n0 + wn * FW + i * 16 + kq * 4;
-                    if (n < N)
-                        *(float4*)(dst + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                }
-            }
+            if (small_fused(TOK, KS))
+                finish_item(it);
+            else
+                store_partial(it);
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -328,6 +389,9 @@ __global__ __launch_bounds__(256) void map_small_reduce_kernel(MapArgs a, const 
 
 // ---------------------------------------------------------------------------------------
 
+// Tokens per tile: the smallest of 16, 32, 64 and 128 that holds the cache.
+static int small_tok(int64_t T) { return T <= 16 ? 16 : T <= 32 ? 32 : T <= 64 ? 64 : 128; }
+
 SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus) {
     SmallPlan pl;
     pl.nN = (g.N() + SBM - 1) / SBM;
@@ -358,7 +422,8 @@ SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus) {
     pl.KS = (nk_all + pl.kps - 1) / pl.kps;  // every split non-empty
     pl.n_items = tiles * pl.KS;
     pl.grid = std::min(pl.n_items, cus);
-    pl.part_bytes = (size_t)pl.KS * g.L_tgt * 2 * (size_t)g.T * g.N() * sizeof(float);
+    pl.fused = small_fused(small_tok(g.T), pl.KS);
+    pl.part_bytes = pl.fused ? 0 : (size_t)pl.KS * g.L_tgt * 2 * (size_t)g.T * g.N() * sizeof(float);
     return pl;
 }
 
@@ -370,14 +435,12 @@ static void launch_short(const MapArgs& a, const ApplyGeom& g, const SmallPlan& 
 
 template <int D>
 static void launch_short_d(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part, hipStream_t s) {
-    if (g.T <= 16)
-        launch_short<D, 16>(a, g, pl, part, s);
-    else if (g.T <= 32)
-        launch_short<D, 32>(a, g, pl, part, s);
-    else if (g.T <= 64)
-        launch_short<D, 64>(a, g, pl, part, s);
-    else
-        launch_short<D, 128>(a, g, pl, part, s);
+    switch (small_tok(g.T)) {
+        case 16: launch_short<D, 16>(a, g, pl, part, s); break;
+        case 32: launch_short<D, 32>(a, g, pl, part, s); break;
+        case 64: launch_short<D, 64>(a, g, pl, part, s); break;
+        default: launch_short<D, 128>(a, g, pl, part, s); break;
+    }
 }
 
 hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,
@@ -385,14 +448,17 @@ hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const Sma
     if (g.T < 1 || g.T > SBN) return hipErrorInvalidValue;
     const int64_t rthreads = (int64_t)g.L_tgt * 2 * g.T * g.H * (g.d / 8);
     const unsigned rblocks = (unsigned)((rthreads + 255) / 256);
+    if (pl.fused != small_fused(small_tok(g.T), pl.KS)) return hipErrorInvalidValue;  // a plan of another shape
     if (g.d == 128) {
         launch_short_d<128>(a, g, pl, part, s);
-        hipLaunchKernelGGL((map_small_reduce_kernel<128>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
-                           g.T, pl.KS);
+        if (!pl.fused)
+            hipLaunchKernelGGL((map_small_reduce_kernel<128>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
+                               g.T, pl.KS);
     } else {
         launch_short_d<64>(a, g, pl, part, s);
-        hipLaunchKernelGGL((map_small_reduce_kernel<64>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
-                           g.T, pl.KS);
+        if (!pl.fused)
+            hipLaunchKernelGGL((map_small_reduce_kernel<64>), dim3(rblocks), dim3(256), 0, s, a, part, g.L_tgt, g.H,
+                               g.T, pl.KS);
     }
     return hipGetLastError();
 }

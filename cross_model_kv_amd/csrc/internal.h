@@ -63,7 +63,8 @@ hipError_t launch_map_f32(const MapArgs& a, const ApplyGeom& g, hipStream_t s);
 
 // Short caches (gemm_bf16_small.hip): bf16 applies with T <= kSmallT tokens take the persistent
 // short-cache kernel (fp32 partial sums in `part`, then a deterministic reduce with bias and
-// target RoPE); measured faster than the long-cache kernel up to 128 tokens.
+// target RoPE; with an unsplit K reduction at 33 to 128 tokens the kernel finishes the rows
+// itself); measured faster than the long-cache kernel up to 128 tokens.
 #ifndef KVMAP_SMALL_T
 #define KVMAP_SMALL_T 128
 #endif
@@ -71,7 +72,8 @@ constexpr int64_t kSmallT = KVMAP_SMALL_T;
 struct SmallPlan {
     int nN, nP, KS, kps;  // feature tiles, token tiles, K splits, K-steps per split
     int n_items, grid;    // work items (tiles x splits), persistent workgroups
-    size_t part_bytes;    // fp32 partial sums [KS][L_tgt][2][T][N]
+    bool fused;           // items finish in the kernel (no partial sums, no reduce kernel)
+    size_t part_bytes;    // fp32 partial sums [KS][L_tgt][2][T][N]; 0 when fused
 };
 SmallPlan map_bf16_small_plan(const ApplyGeom& g, int cus);
 hipError_t launch_map_bf16_small(const MapArgs& a, const ApplyGeom& g, const SmallPlan& pl, float* part,

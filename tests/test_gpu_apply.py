@@ -369,7 +369,8 @@ def test_alternating_selections_queue_without_host_wait(ctx):
         assert torch.equal(gk, rk) and torch.equal(gv, rv)
 
 
-# ---- short caches (T <= 128: the persistent short-cache kernel with a separate reduce) ---
+# ---- short caches (T <= 128: the persistent short-cache kernel; a separate reduce when the
+# K reduction is split or the tile holds 16 or 32 tokens) ---
 
 SHORT = [
     # 1.5 feature tiles (H=3), 64 tokens: exactly one 64-token tile, L_tgt > L_src
@@ -393,6 +394,17 @@ SHORT = [
     # head dim 64, 3 selected layers, T = 5: 12 splits of one K-step each, so consecutive
     # items of a workgroup read different (selected layer, head) slabs
     ApplyConfig(227, "short-many-items-k3-T5", 4, 48, 4, 64, 5, 3, 1.0e6, 5.0e5, "bf16", 0.5, pos0=7),
+    # Unsplit K reductions at 64- and 128-token tiles, where the short-cache kernel adds the bias,
+    # rotates the keys and writes bf16 itself (no reduce kernel), on a 256-CU device:
+    # 256 tiles (64 target layers x K/V x 2 feature tiles, the second half past N = 384), ragged
+    # 100 tokens in a 128-token tile
+    ApplyConfig(233, "short-fused-T100-H3", 6, 64, 3, 128, 100, 2, 1.0e4, 1.0e6, "bf16", 0.5, pos0=5),
+    # the same at head dim 64 (N = 320: the second feature tile holds one head), ragged 50
+    # tokens in a 64-token tile
+    ApplyConfig(234, "short-fused-d64-T50-H5", 5, 64, 5, 64, 50, 2, 1.0e6, 5.0e5, "bf16", 0.5),
+    # a single K-step (k = 1, one head of 64): one head in the first wave of the tile, the rest
+    # of the tile past N
+    ApplyConfig(235, "short-fused-one-kstep-T40", 2, 3, 1, 64, 40, 1, 1.0e4, 1.0e4, "bf16", 0.5, pos0=3),
 ]
 
 
