@@ -177,8 +177,10 @@ int kvmap_validate_apply_buffers(const kvmap_dims* dims, const void* src_k, cons
  * selection it replaces has not yet run.  In bf16 the de-rotated
  * keys are rounded to bf16 before the map (fp32 accumulation, bf16 output).  bf16 caches of
  * up to 128 tokens take a kernel that streams the maps (the apply is bound by reading W
- * there); its fp32 partial sums live in the workspace and are added in a fixed order, so
- * repeated calls give identical outputs. */
+ * there).  Where its K reduction is split over workgroups, or its tiles hold 16 or 32 tokens,
+ * its fp32 partial sums live in the workspace and a second kernel adds them in a fixed order
+ * with the bias and the target RoPE; otherwise each workgroup finishes its rows itself.
+ * Either way repeated calls give identical outputs. */
 int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
                 const void* src_k, const void* src_v, const int32_t* layer_sel,
                 const void* W_k, const void* b_k, const void* W_v, const void* b_v,
@@ -189,7 +191,8 @@ int kvmap_apply(kvmap_ctx* ctx, const kvmap_dims* dims,
  * launched, measured with HIP events recorded on the apply's stream:
  *   ms[0] RoPE-table build (0 if cached), ms[1] key de-rotation producer,
  *   ms[2] map GEMM (K and V of all target layers: one launch; for bf16 caches of up to 128
- *         tokens the short-cache kernel and the reduce that adds its partial sums).
+ *         tokens the short-cache kernel and, where it runs, the reduce that adds its partial
+ *         sums).
  * Synchronises on the events.  n_ms must be >= 3. */
 int kvmap_last_timings(kvmap_ctx* ctx, float* ms, int n_ms);
 /* The same durations for an earlier timed apply: back = 0 is the most recent, up to 127 back
